@@ -1,0 +1,202 @@
+/*
+ * var_attn.h -- C ABI of libvarattn.so: next-scale (scale-wise) attention for
+ * visual-autoregressive (VAR) generation on AMD Instinct MI355X (gfx950).
+ *
+ * The problem, as the source pages state it:
+ *  - Next-scale prediction emits one whole h_k x w_k token grid per step, with
+ *    a KV cache over the earlier scales ("ARVAR: Accelerating Visual
+ *    Autoregressive Model via Attention Retrospect", Background & Motivation).
+ *  - Every step attends to all tokens of all historical scales ("SparVAR:
+ *    Exploring Sparsity in Visual AutoRegressive Modeling for Training-Free
+ *    Acceleration", abstract).  Within the current scale every token sees every
+ *    other one (the grid is predicted at once).
+ *  - Classifier-free guidance runs the conditional and unconditional branches
+ *    concatenated along the batch ("ARVAR ...", Key Design 1).
+ *  - A block-wise sparse variant keeps attention-sink scales and a cross-scale
+ *    local window found through an index mapping ("SparVAR ...", abstract).
+ *  - A pruned step gathers the retained query positions, computes them, and
+ *    scatters the results over an upsampled earlier output ("ARVAR ...", Key
+ *    Designs 2 and 3, Equations (8)-(9)).
+ *
+ * Token numbering: grids are row-major and concatenated in scale order;
+ * off[k] = sum_{j<k} h_j*w_j.  Scales are 0-based in this ABI.
+ *
+ * Conventions for every call:
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, keeps no state between calls and never frees.
+ *  - Host-side argument checks run before any HIP call; a failed check returns
+ *    its status and launches nothing.  Calls are asynchronous: they enqueue on
+ *    `stream` (a hipStream_t; NULL = the legacy default stream) and return.
+ *  - Errors are return codes; var_last_error() gives a thread-local detail
+ *    string for the last failing call on the calling thread.
+ *  - Sizes that the library cannot see (allocation extents) are the caller's
+ *    contract and are stated per argument.
+ */
+#ifndef VAR_ATTN_H
+#define VAR_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum var_status {
+    VAR_OK = 0,
+    VAR_ERR_NULL = 1,        /* a required pointer is NULL                          */
+    VAR_ERR_SCHEDULE = 2,    /* bad scale schedule (count, sizes, token total)       */
+    VAR_ERR_RANGE = 3,       /* bad scale range, batch/heads, n_sel or tile sizes    */
+    VAR_ERR_UNSUPPORTED = 4, /* dtype / head_dim / tile combination not implemented  */
+    VAR_ERR_STRIDE = 5,      /* stride or alignment outside what the kernels accept  */
+    VAR_ERR_CAPACITY = 6,    /* col_idx capacity below n_qt * n_kt                   */
+    VAR_ERR_INDEX = 7,       /* inconsistent index arguments                         */
+    VAR_ERR_HIP = 8          /* the HIP runtime reported an error at launch          */
+} var_status;
+
+typedef enum var_dtype { VAR_F32 = 0, VAR_BF16 = 1 } var_dtype;
+
+#define VAR_MAX_SCALES 32
+
+/* Scale schedule: host arrays h[num_scales], w[num_scales] (grid rows, cols).
+ * 1 <= num_scales <= VAR_MAX_SCALES, 1 <= h, w <= 4096, total tokens < 2^24.  */
+typedef struct var_schedule {
+    int32_t num_scales;
+    const int32_t* h;
+    const int32_t* w;
+} var_schedule;
+
+/* Element strides of a [batch, head, token, dim] tensor; dim stride is 1. */
+typedef struct var_layout {
+    int64_t batch;
+    int64_t head;
+    int64_t token;
+} var_layout;
+
+typedef struct var_attn_desc {
+    int32_t batch;          /* B >= 1 (CFG: index 0 = cond, 1 = uncond)            */
+    int32_t heads;          /* H >= 1                                              */
+    int32_t head_dim;       /* D: 64 or 128 for bf16 input; 32 or 64 for f32       */
+    int32_t q_scale_begin;  /* queries are tokens [off[b], off[e]) ...              */
+    int32_t q_scale_end;    /* ... and keys are tokens [0, off[e])                 */
+    float softmax_scale;    /* 0 => 1/sqrt(head_dim)                               */
+    var_dtype in_dtype;     /* dtype of q, k, v                                    */
+    var_dtype out_dtype;    /* dtype of o (bf16 in: f32 or bf16; f32 in: f32)      */
+} var_attn_desc;
+
+typedef struct var_mask_params {
+    int32_t tile_q;            /* query rows per tile (>= 1; the sparse kernel uses 64) */
+    int32_t tile_k;            /* key tokens per tile (>= 1; the sparse kernel uses 64) */
+    int32_t sink_scales;       /* keys in scales [0, sink_scales) are always selected   */
+    int32_t local_from_scale;  /* window rule applies to key scales >= this             */
+    int32_t radius_y;          /* window half-height in key-grid rows (>= 0)            */
+    int32_t radius_x;          /* window half-width  in key-grid cols (>= 0)            */
+} var_mask_params;
+
+/*
+ * Token extent of a call (host only, no HIP call).  For queries of scales
+ * [q_scale_begin, q_scale_end): first_token = off[b], n_q = off[e] - off[b],
+ * kv_len = off[e].  Any output pointer may be NULL.
+ */
+var_status var_schedule_extent(const var_schedule* sched, int32_t q_scale_begin, int32_t q_scale_end,
+                               int64_t* first_token, int64_t* n_q, int64_t* kv_len);
+
+/*
+ * Dense block-causal next-scale attention (the definition on the SparVAR and
+ * ARVAR pages above): the query at token t of scale s(t) attends to every key
+ * u < off[e] with s(u) <= s(t), with O = softmax(scale * q k^T) v computed
+ * exactly (online softmax, fp32 accumulation).
+ *
+ *  q      [B][H][n_q][D] (layout q_l): row j is token off[b] + j.
+ *  k, v   [B][H][>= kv_len][D] (k_l, v_l): the KV cache; tokens [0, kv_len) read.
+ *  o      [B][H][rows][D] (o_l), written; rows = n_sel if q_index else n_q.
+ *  lse    NULL or [B][H][rows] contiguous fp32, written: natural-log
+ *         log-sum-exp of the scaled logits (-inf for a row that sees no key).
+ *  q_index NULL (then n_sel must be 0) or device int32[n_sel]: output row i is
+ *         the query at position q_index[i] in [0, n_q) of q (fused gather of
+ *         pruned queries, "ARVAR ...", Key Design 2).  Any order; values out of
+ *         range are the caller's contract (the kernel clamps them, never
+ *         reading outside q).
+ * Alignment: q, k, v, o 16-byte aligned; token/head/batch strides multiples
+ * of 8 elements (bf16) or 4 elements (f32).
+ */
+var_status var_attn_dense(const var_schedule* sched, const var_attn_desc* desc,
+                          const void* q, var_layout q_l, const void* k, var_layout k_l,
+                          const void* v, var_layout v_l, void* o, var_layout o_l,
+                          float* lse, const int32_t* q_index, int32_t n_sel, void* stream);
+
+/*
+ * Tile mask of the block-sparse variant ("SparVAR ...", abstract: attention
+ * sinks, cross-scale locality through an index map, block-wise sparsity).
+ * A (query, key) pair is selected when s(key) <= s(query) and either
+ * s(key) < sink_scales, or s(key) >= local_from_scale and, with j = s(key),
+ * q = s(query):  |y_q*h_j - y_k*h_q| <= radius_y*h_q  and
+ *                |x_q*w_j - x_k*w_q| <= radius_x*w_q  (exact integers).
+ * Tile (r, c) is kept when some selected pair has its query among rows
+ * [r*tile_q, (r+1)*tile_q) of the call (rows as in var_attn_dense, i.e. after
+ * the q_index gather) and its key in tokens [c*tile_k, (c+1)*tile_k) of
+ * [0, kv_len).  Output CSR, one list shared by every (batch, head):
+ *  row_ptr  device int32[n_qt + 1]; col_idx device int32[col_capacity] with
+ *  col_capacity >= n_qt * n_kt (the buffer doubles as the build's staging
+ *  area; entries past row_ptr[n_qt] are left unspecified).  Each row lists
+ *  its kept key tiles in ascending order.
+ *  n_qt = ceil(rows / tile_q), n_kt = ceil(kv_len / tile_k).
+ * q_index as in var_attn_dense (device, positions in [0, n_q)).
+ */
+var_status var_tile_mask_dims(const var_schedule* sched, int32_t q_scale_begin, int32_t q_scale_end,
+                              const var_mask_params* mp, int32_t n_sel_or_0,
+                              int32_t* n_qt, int32_t* n_kt);
+var_status var_build_tile_mask(const var_schedule* sched, int32_t q_scale_begin, int32_t q_scale_end,
+                               const var_mask_params* mp, const int32_t* q_index, int32_t n_sel,
+                               int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                               void* stream);
+
+/*
+ * Block-sparse next-scale attention: var_attn_dense restricted to the kept
+ * tiles of a CSR tile mask (as produced by var_build_tile_mask; any CSR with
+ * in-range columns is accepted).  Inside a kept tile every block-causally
+ * visible pair is attended.  tile_q = tile_k = 64 only.  Arguments as in
+ * var_attn_dense; row_ptr / col_idx are device arrays with n_qt + 1 and
+ * row_ptr[n_qt] entries.  A row whose kept tiles hold no visible key gets
+ * O = 0 and LSE = -inf.
+ */
+var_status var_attn_block_sparse(const var_schedule* sched, const var_attn_desc* desc,
+                                 const void* q, var_layout q_l, const void* k, var_layout k_l,
+                                 const void* v, var_layout v_l, void* o, var_layout o_l,
+                                 float* lse, const int32_t* q_index, int32_t n_sel,
+                                 const int32_t* row_ptr, const int32_t* col_idx,
+                                 int32_t tile_q, int32_t tile_k, void* stream);
+
+/*
+ * Structural reconstruction of a pruned grid ("ARVAR ...", Key Design 3,
+ * Equations (8)-(9)): out = Scatter(Up(base; h_out, w_out), q_index, upd).
+ * Up is nearest neighbour with source (floor(y*h_in/h_out), floor(x*w_in/w_out));
+ * Scatter overwrites row q_index[i] with upd row i.  Rows are copied bit for
+ * bit.  For each map m in [0, maps) (e.g. m = b*H + h):
+ *   base  rows at base + m*base_map_stride + t*base_row_stride, t < h_in*w_in
+ *   upd   rows at upd  + m*upd_map_stride  + i*upd_row_stride,  i < n_sel
+ *   out   rows at out  + m*out_map_stride  + t*out_row_stride,  t < h_out*w_out
+ * each row holding row_elems contiguous elements of `dtype`; strides are in
+ * elements.  q_index: device int32[n_sel], strictly ascending, in
+ * [0, h_out*w_out).  err_flag: NULL or a device int32 the caller has zeroed;
+ * the kernel ORs in 1 for an out-of-range index and 2 for a non-ascending
+ * (duplicate or unsorted) pair; rows are then unspecified but every access
+ * stays in bounds.
+ */
+var_status var_scatter_restore(int32_t maps, int32_t row_elems, var_dtype dtype,
+                               const void* base, int64_t base_map_stride, int64_t base_row_stride,
+                               int32_t h_in, int32_t w_in,
+                               const void* upd, int64_t upd_map_stride, int64_t upd_row_stride,
+                               const int32_t* q_index, int32_t n_sel,
+                               void* out, int64_t out_map_stride, int64_t out_row_stride,
+                               int32_t h_out, int32_t w_out, int32_t* err_flag, void* stream);
+
+/* Static name of a status code. */
+const char* var_status_string(var_status s);
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* var_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VAR_ATTN_H */

@@ -1,0 +1,286 @@
+"""Thin ctypes binding over libvarattn.so (include/var_attn.h).
+
+Argument marshalling only: tensors become device pointers plus element
+strides, the schedule becomes two int32 host arrays, the current torch stream
+becomes the hipStream_t.  Every computation happens in the library's HIP
+kernels; there is no fallback.  Importing this module raises if the library
+has not been built (``python -m scale_wise_attention_amd.build``).
+
+Functions carry the C names: ``var_attn_dense``, ``var_build_tile_mask``,
+``var_attn_block_sparse``, ``var_scatter_restore`` (plus the host-only helpers
+``var_schedule_extent`` and ``var_tile_mask_dims``).
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvarattn.so")
+
+VAR_F32 = 0
+VAR_BF16 = 1
+
+STATUS = {0: "VAR_OK", 1: "VAR_ERR_NULL", 2: "VAR_ERR_SCHEDULE", 3: "VAR_ERR_RANGE",
+          4: "VAR_ERR_UNSUPPORTED", 5: "VAR_ERR_STRIDE", 6: "VAR_ERR_CAPACITY",
+          7: "VAR_ERR_INDEX", 8: "VAR_ERR_HIP"}
+MAX_SCALES = 32
+
+EXPORTED = ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_build_tile_mask",
+            "var_attn_block_sparse", "var_scatter_restore", "var_status_string", "var_last_error")
+
+
+class VarAttnError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        self.status_name = STATUS.get(status, f"status {status}")
+        super().__init__(f"{self.status_name}: {detail}")
+
+
+class Schedule(ctypes.Structure):
+    _fields_ = [("num_scales", ctypes.c_int32), ("h", ctypes.POINTER(ctypes.c_int32)),
+                ("w", ctypes.POINTER(ctypes.c_int32))]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("token", ctypes.c_int64)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("q_scale_begin", ctypes.c_int32), ("q_scale_end", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int)]
+
+
+class MaskParams(ctypes.Structure):
+    _fields_ = [("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32), ("sink_scales", ctypes.c_int32),
+                ("local_from_scale", ctypes.c_int32), ("radius_y", ctypes.c_int32), ("radius_x", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m scale_wise_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64 = ctypes.c_int32, ctypes.c_int64
+    SP = ctypes.POINTER(Schedule)
+    lib.var_schedule_extent.argtypes = [SP, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.var_attn_dense.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, Layout, P, Layout,
+                                   P, P, i32, P]
+    lib.var_tile_mask_dims.argtypes = [SP, i32, i32, ctypes.POINTER(MaskParams), i32,
+                                       ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.var_build_tile_mask.argtypes = [SP, i32, i32, ctypes.POINTER(MaskParams), P, i32, P, P, i64, P]
+    lib.var_attn_block_sparse.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, Layout, P, Layout,
+                                          P, P, i32, P, P, i32, i32, P]
+    lib.var_scatter_restore.argtypes = [i32, i32, ctypes.c_int, P, i64, i64, i32, i32, P, i64, i64, P, i32,
+                                        P, i64, i64, i32, i32, P, P]
+    for name in ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_build_tile_mask",
+                 "var_attn_block_sparse", "var_scatter_restore"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.var_status_string.argtypes = [ctypes.c_int]
+    lib.var_status_string.restype = ctypes.c_char_p
+    lib.var_last_error.argtypes = []
+    lib.var_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+def _check(status):
+    if status != 0:
+        raise VarAttnError(status, LIB.var_last_error().decode())
+
+
+def make_schedule(h, w):
+    """ctypes schedule; keeps its host arrays alive on the returned object."""
+    h = [int(a) for a in h]
+    w = [int(a) for a in w]
+    if len(h) != len(w):
+        raise ValueError("h and w differ in length")
+    ha = (ctypes.c_int32 * max(1, len(h)))(*h)
+    wa = (ctypes.c_int32 * max(1, len(w)))(*w)
+    s = Schedule(len(h), ctypes.cast(ha, ctypes.POINTER(ctypes.c_int32)), ctypes.cast(wa, ctypes.POINTER(ctypes.c_int32)))
+    s._keep = (ha, wa)
+    return s
+
+
+def _as_schedule(schedule):
+    if isinstance(schedule, Schedule):
+        return schedule
+    h, w = schedule
+    return make_schedule(h, w)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _layout(t):
+    """[B, H, T, D] tensor -> element strides; the last dim must be contiguous."""
+    if t.dim() != 4:
+        raise ValueError("expected a [batch, head, token, dim] tensor")
+    if t.stride(3) != 1:
+        raise ValueError("the head dimension must be contiguous (stride 1)")
+    return Layout(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _dtype_code(dt):
+    if dt == torch.bfloat16:
+        return VAR_BF16
+    if dt == torch.float32:
+        return VAR_F32
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def var_schedule_extent(schedule, q_scale_begin, q_scale_end):
+    """(first_token, n_q, kv_len) of queries of scales [begin, end)."""
+    s = _as_schedule(schedule)
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(LIB.var_schedule_extent(ctypes.byref(s), q_scale_begin, q_scale_end, ctypes.byref(a),
+                                   ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def _check_index(q_index, device):
+    if q_index is None:
+        return
+    if q_index.dtype != torch.int32 or q_index.dim() != 1 or not q_index.is_contiguous():
+        raise ValueError("q_index must be a contiguous 1-D int32 tensor")
+    if q_index.device != device:
+        raise ValueError("q_index must live on the tensors' device")
+
+
+def _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype, softmax_scale, q_index, want_lse):
+    s = _as_schedule(schedule)
+    _, n_q, kv_len = var_schedule_extent(s, q_scale_begin, q_scale_end)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4 or not t.is_cuda:
+            raise ValueError(f"{name} must be a 4-D device tensor [batch, head, token, dim]")
+    B, H, _, D = q.shape
+    if k.shape[0] != B or v.shape[0] != B or k.shape[1] != H or v.shape[1] != H or k.shape[3] != D or v.shape[3] != D:
+        raise ValueError("q, k, v disagree in batch, heads or head_dim")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if q.device != k.device or q.device != v.device:
+        raise ValueError("q, k, v must share a device")
+    if q.shape[2] < n_q:
+        raise ValueError(f"q holds {q.shape[2]} tokens, the scales need {n_q}")
+    if k.shape[2] < kv_len or v.shape[2] < kv_len:
+        raise ValueError(f"k/v hold fewer than kv_len={kv_len} tokens")
+    _check_index(q_index, q.device)
+    rows = n_q if q_index is None else int(q_index.numel())
+    if out is None:
+        odt = out_dtype if out_dtype is not None else torch.float32
+        out = torch.empty((B, H, rows, D), dtype=odt, device=q.device)
+    elif tuple(out.shape) != (B, H, rows, D) or out.device != q.device:
+        raise ValueError(f"out must have shape {(B, H, rows, D)} on q's device")
+    lse = torch.empty((B, H, rows), dtype=torch.float32, device=q.device) if want_lse else None
+    desc = AttnDesc(B, H, D, q_scale_begin, q_scale_end, float(softmax_scale), _dtype_code(q.dtype),
+                    _dtype_code(out.dtype))
+    return s, desc, out, lse, rows
+
+
+def var_attn_dense(schedule, q, k, v, q_scale_begin, q_scale_end, out=None, out_dtype=None,
+                   softmax_scale=0.0, q_index=None, return_lse=False):
+    """Dense block-causal attention of the queries of scales [begin, end).
+
+    q [B, H, n_q, D] (row j = token off[begin] + j), k / v [B, H, >= kv_len, D];
+    returns out [B, H, rows, D] (and lse [B, H, rows]); rows = len(q_index) or n_q.
+    """
+    s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
+                                           softmax_scale, q_index, return_lse)
+    n_sel = rows if q_index is not None else 0
+    _check(LIB.var_attn_dense(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k), _layout(k),
+                              _ptr(v), _layout(v), _ptr(out), _layout(out), _ptr(lse), _ptr(q_index), n_sel,
+                              _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+def var_tile_mask_dims(schedule, q_scale_begin, q_scale_end, mask_params, n_sel=0):
+    s = _as_schedule(schedule)
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(LIB.var_tile_mask_dims(ctypes.byref(s), q_scale_begin, q_scale_end, ctypes.byref(mask_params), n_sel,
+                                  ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def mask_params(tile_q=64, tile_k=64, sink_scales=7, local_from_scale=7, radius_y=2, radius_x=2):
+    return MaskParams(tile_q, tile_k, sink_scales, local_from_scale, radius_y, radius_x)
+
+
+def var_build_tile_mask(schedule, q_scale_begin, q_scale_end, params, q_index=None, device="cuda",
+                        row_ptr=None, col_idx=None):
+    """Device CSR (row_ptr int32 [n_qt+1], col_idx int32 [n_qt*n_kt] staging buffer)."""
+    s = _as_schedule(schedule)
+    n_sel = 0 if q_index is None else int(q_index.numel())
+    dev = q_index.device if q_index is not None else torch.device(device)
+    _check_index(q_index, dev)
+    n_qt, n_kt = var_tile_mask_dims(s, q_scale_begin, q_scale_end, params, n_sel)
+    if row_ptr is None:
+        row_ptr = torch.empty(n_qt + 1, dtype=torch.int32, device=dev)
+    if col_idx is None:
+        col_idx = torch.empty(max(1, n_qt * n_kt), dtype=torch.int32, device=dev)
+    if row_ptr.numel() < n_qt + 1 or row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+        raise ValueError("row_ptr must be int32 with n_qt+1 entries; col_idx int32")
+    _check(LIB.var_build_tile_mask(ctypes.byref(s), q_scale_begin, q_scale_end, ctypes.byref(params),
+                                   _ptr(q_index), n_sel, _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                                   _stream(dev)))
+    return row_ptr, col_idx
+
+
+def var_attn_block_sparse(schedule, q, k, v, q_scale_begin, q_scale_end, row_ptr, col_idx, out=None,
+                          out_dtype=None, softmax_scale=0.0, q_index=None, return_lse=False, tile_q=64, tile_k=64):
+    s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
+                                           softmax_scale, q_index, return_lse)
+    n_sel = rows if q_index is not None else 0
+    n_qt = -(-rows // tile_q)
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous 1-D int32 tensor on q's device")
+    if row_ptr.numel() < n_qt + 1:
+        raise ValueError(f"row_ptr needs {n_qt + 1} entries")
+    _check(LIB.var_attn_block_sparse(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k), _layout(k),
+                                     _ptr(v), _layout(v), _ptr(out), _layout(out), _ptr(lse), _ptr(q_index), n_sel,
+                                     _ptr(row_ptr), _ptr(col_idx), tile_q, tile_k, _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+def var_scatter_restore(base, h_in, w_in, upd, q_index, h_out, w_out, out=None, err_flag=None):
+    """base [M, h_in*w_in, E], upd [M, n_sel, E], q_index int32 [n_sel] -> out [M, h_out*w_out, E].
+
+    Tensors of 4 dims [B, H, T, E] are accepted and treated as M = B*H maps
+    (they must then be viewable as [B*H, T, E]).
+    """
+    def as3(t):
+        return t.view(-1, t.shape[-2], t.shape[-1]) if t.dim() == 4 else t
+
+    b3 = as3(base)
+    M, _, E = b3.shape
+    n_sel = 0 if q_index is None else int(q_index.numel())
+    u3 = as3(upd) if (upd is not None and n_sel > 0) else None
+    if out is None:
+        shape = (*base.shape[:-2], h_out * w_out, E)
+        out = torch.empty(shape, dtype=base.dtype, device=base.device)
+    o3 = as3(out)
+    _check_index(q_index, base.device)
+    if b3.shape[1] < h_in * w_in:
+        raise ValueError("base holds fewer than h_in*w_in rows")
+    if o3.shape[0] != M or o3.shape[2] != E or o3.shape[1] < h_out * w_out or o3.dtype != base.dtype:
+        raise ValueError("out must be [maps, >= h_out*w_out, E] of base's dtype")
+    if u3 is not None and (u3.shape[0] != M or u3.shape[2] != E or u3.shape[1] < n_sel or u3.dtype != base.dtype):
+        raise ValueError("upd must be [maps, >= n_sel, E] of base's dtype")
+    for t in (b3, o3) + ((u3,) if u3 is not None else ()):
+        if t.stride(2) != 1 or not t.is_cuda or t.device != base.device:
+            raise ValueError("rows must be contiguous device tensors on one device")
+    _check(LIB.var_scatter_restore(M, E, _dtype_code(base.dtype), _ptr(b3), b3.stride(0), b3.stride(1), h_in, w_in,
+                                   _ptr(u3), u3.stride(0) if u3 is not None else 0,
+                                   u3.stride(1) if u3 is not None else 0, _ptr(q_index), n_sel,
+                                   _ptr(o3), o3.stride(0), o3.stride(1), h_out, w_out, _ptr(err_flag),
+                                   _stream(base.device)))
+    return out

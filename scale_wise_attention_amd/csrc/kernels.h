@@ -1,0 +1,78 @@
+// Internal interface between the C-ABI host layer (var_attn_api.cpp) and the
+// gfx950 kernels.  Not installed; the public interface is include/var_attn.h.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "../../include/var_attn.h"
+
+namespace varattn {
+
+// Everything one attention launch needs.  Passed by value as kernel argument.
+struct AttnParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    const int32_t* q_index;   // nullable
+    const int32_t* row_ptr;   // sparse only
+    const int32_t* col_idx;   // sparse only
+    int64_t q_sb, q_sh, q_st;
+    int64_t k_sb, k_sh, k_st;
+    int64_t v_sb, v_sh, v_st;
+    int64_t o_sb, o_sh, o_st;
+    int32_t B, H;
+    int32_t n_rows;      // output rows per (b, h): n_sel or n_q
+    int32_t n_q;         // query tokens of the call
+    int32_t q_first;     // token index of query row 0
+    int32_t kv_len;      // keys [0, kv_len)
+    int32_t n_qtiles;    // query tiles per (b, h) of this launch
+    int32_t num_scales;
+    int32_t step_mode;   // every query lies in the last scale => key limit is kv_len
+    float scale;         // softmax scale
+    float scale_log2;    // scale * log2(e)
+    int32_t scale_end[VAR_MAX_SCALES];  // off[s + 1]
+};
+
+struct MaskParams {
+    const int32_t* q_index;   // nullable
+    int32_t* row_ptr;
+    int32_t* col_idx;
+    int32_t n_rows, n_q, q_first, kv_len;
+    int32_t n_qt, n_kt;
+    int32_t tile_q, tile_k;
+    int32_t sink_scales, local_from_scale, radius_y, radius_x;
+    int32_t num_scales;
+    int32_t off[VAR_MAX_SCALES + 1];
+    int32_t h[VAR_MAX_SCALES];
+    int32_t w[VAR_MAX_SCALES];
+};
+
+struct ScatterParams {
+    const unsigned char* base;
+    const unsigned char* upd;
+    unsigned char* out;
+    const int32_t* q_index;
+    int32_t* err_flag;
+    int64_t base_map_stride, base_row_stride;   // bytes
+    int64_t upd_map_stride, upd_row_stride;     // bytes
+    int64_t out_map_stride, out_row_stride;     // bytes
+    int32_t maps, row_bytes, n_sel;
+    int32_t h_in, w_in, h_out, w_out;
+    int32_t unit;     // copy width in bytes (16, 4 or 2) dividing rows, strides and pointers
+};
+
+// Launchers: return the hipError_t of the launch.
+hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, bool out_bf16, bool sparse, hipStream_t s);
+hipError_t launch_attn_f32(const AttnParams& p, int head_dim, bool sparse, hipStream_t s);
+hipError_t launch_tile_mask(const MaskParams& p, hipStream_t s);
+hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
+hipError_t launch_zero_i32(int32_t* p, hipStream_t s);
+
+// Query-tile height of the bf16 kernels (rows per workgroup).
+int attn_bf16_rows_per_tile(int head_dim, bool sparse);
+constexpr int kF32RowsPerTile = 64;
+
+}  // namespace varattn

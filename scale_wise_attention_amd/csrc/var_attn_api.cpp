@@ -1,0 +1,357 @@
+// C-ABI host layer of libvarattn.so (declared in include/var_attn.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, derives the schedule offsets, fills the kernel's parameter
+// block and enqueues the kernel(s) on the caller's stream.  Nothing is
+// allocated, nothing is cached between calls.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+#define VAR_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+var_status fail(var_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+var_status ok() {
+    g_last_error[0] = '\0';
+    return VAR_OK;
+}
+
+var_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(VAR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct Offsets {
+    int32_t off[VAR_MAX_SCALES + 1];
+    int32_t num_scales;
+};
+
+constexpr int64_t kMaxTokens = 1 << 24;
+
+var_status check_schedule(const var_schedule* s, Offsets* o) {
+    if (!s) return fail(VAR_ERR_NULL, "schedule is NULL");
+    if (s->num_scales < 1 || s->num_scales > VAR_MAX_SCALES)
+        return fail(VAR_ERR_SCHEDULE, "num_scales=%d outside [1, %d]", s->num_scales, VAR_MAX_SCALES);
+    if (!s->h || !s->w) return fail(VAR_ERR_NULL, "schedule h or w is NULL");
+    int64_t acc = 0;
+    o->off[0] = 0;
+    for (int k = 0; k < s->num_scales; ++k) {
+        if (s->h[k] < 1 || s->h[k] > 4096 || s->w[k] < 1 || s->w[k] > 4096)
+            return fail(VAR_ERR_SCHEDULE, "scale %d has grid %dx%d outside [1, 4096]", k, s->h[k], s->w[k]);
+        acc += (int64_t)s->h[k] * s->w[k];
+        if (acc >= kMaxTokens) return fail(VAR_ERR_SCHEDULE, "schedule exceeds %lld tokens", (long long)kMaxTokens);
+        o->off[k + 1] = (int32_t)acc;
+    }
+    o->num_scales = s->num_scales;
+    return VAR_OK;
+}
+
+var_status check_range(const Offsets& o, int32_t b, int32_t e) {
+    if (b < 0 || e > o.num_scales || b >= e)
+        return fail(VAR_ERR_RANGE, "scale range [%d, %d) invalid for %d scales", b, e, o.num_scales);
+    return VAR_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+var_status check_layout(const char* name, const var_layout& l, int D, int elem_bytes) {
+    const int64_t m = 16 / elem_bytes;   // elements per 16 bytes
+    if (l.batch < 0 || l.head < 0 || l.token < D)
+        return fail(VAR_ERR_STRIDE, "%s strides (%lld, %lld, %lld) invalid for head_dim %d", name,
+                    (long long)l.batch, (long long)l.head, (long long)l.token, D);
+    if (l.batch % m || l.head % m || l.token % m)
+        return fail(VAR_ERR_STRIDE, "%s strides must be multiples of %lld elements", name, (long long)m);
+    return VAR_OK;
+}
+
+// Common validation + parameter fill for the two attention entry points.
+var_status prepare_attn(const var_schedule* sched, const var_attn_desc* d, const void* q, var_layout ql,
+                        const void* k, var_layout kl, const void* v, var_layout vl, void* o, var_layout ol,
+                        float* lse, const int32_t* q_index, int32_t n_sel, varattn::AttnParams* p,
+                        bool* nothing_to_do) {
+    *nothing_to_do = false;
+    Offsets off;
+    var_status st = check_schedule(sched, &off);
+    if (st != VAR_OK) return st;
+    if (!d) return fail(VAR_ERR_NULL, "desc is NULL");
+    st = check_range(off, d->q_scale_begin, d->q_scale_end);
+    if (st != VAR_OK) return st;
+    if (d->batch < 1 || d->heads < 1 || (int64_t)d->batch * d->heads > (1 << 20))
+        return fail(VAR_ERR_RANGE, "batch=%d heads=%d invalid", d->batch, d->heads);
+    if (d->in_dtype == VAR_BF16) {
+        if (d->head_dim != 64 && d->head_dim != 128)
+            return fail(VAR_ERR_UNSUPPORTED, "bf16 input supports head_dim 64 or 128, got %d", d->head_dim);
+        if (d->out_dtype != VAR_F32 && d->out_dtype != VAR_BF16)
+            return fail(VAR_ERR_UNSUPPORTED, "unknown out_dtype %d", (int)d->out_dtype);
+    } else if (d->in_dtype == VAR_F32) {
+        if (d->head_dim != 32 && d->head_dim != 64)
+            return fail(VAR_ERR_UNSUPPORTED, "f32 input supports head_dim 32 or 64, got %d", d->head_dim);
+        if (d->out_dtype != VAR_F32)
+            return fail(VAR_ERR_UNSUPPORTED, "f32 input requires f32 output");
+    } else {
+        return fail(VAR_ERR_UNSUPPORTED, "unknown in_dtype %d", (int)d->in_dtype);
+    }
+    if (!(d->softmax_scale >= 0.f) || std::isinf(d->softmax_scale))
+        return fail(VAR_ERR_RANGE, "softmax_scale must be finite and >= 0 (0 = 1/sqrt(D))");
+    const int32_t first = off.off[d->q_scale_begin];
+    const int32_t n_q = off.off[d->q_scale_end] - first;
+    int32_t rows = n_q;
+    if (q_index) {
+        if (n_sel < 0 || n_sel > n_q) return fail(VAR_ERR_INDEX, "n_sel=%d outside [0, n_q=%d]", n_sel, n_q);
+        rows = n_sel;
+    } else if (n_sel != 0) {
+        return fail(VAR_ERR_INDEX, "n_sel=%d given without q_index", n_sel);
+    }
+    if (rows == 0) {   // nothing to compute; o and lse may be empty (NULL) tensors
+        *nothing_to_do = true;
+        return ok();
+    }
+    if (!q || !k || !v || !o) return fail(VAR_ERR_NULL, "q, k, v and o must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(VAR_ERR_STRIDE, "q, k, v and o must be 16-byte aligned");
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(VAR_ERR_STRIDE, "lse must be 4-byte aligned");
+    const int ib = d->in_dtype == VAR_BF16 ? 2 : 4;
+    const int ob = d->out_dtype == VAR_BF16 ? 2 : 4;
+    if ((st = check_layout("q", ql, d->head_dim, ib)) != VAR_OK) return st;
+    if ((st = check_layout("k", kl, d->head_dim, ib)) != VAR_OK) return st;
+    if ((st = check_layout("v", vl, d->head_dim, ib)) != VAR_OK) return st;
+    // the bf16 output is written 4 elements (8 bytes) at a time, f32 4 at a time (16 bytes)
+    if (ol.batch < 0 || ol.head < 0 || ol.token < d->head_dim || ol.batch % 4 || ol.head % 4 || ol.token % 4)
+        return fail(VAR_ERR_STRIDE, "o strides must be non-negative multiples of 4 elements, token >= head_dim");
+    (void)ob;
+    std::memset(p, 0, sizeof(*p));
+    p->q = q; p->k = k; p->v = v; p->o = o; p->lse = lse; p->q_index = q_index;
+    p->q_sb = ql.batch; p->q_sh = ql.head; p->q_st = ql.token;
+    p->k_sb = kl.batch; p->k_sh = kl.head; p->k_st = kl.token;
+    p->v_sb = vl.batch; p->v_sh = vl.head; p->v_st = vl.token;
+    p->o_sb = ol.batch; p->o_sh = ol.head; p->o_st = ol.token;
+    p->B = d->batch; p->H = d->heads;
+    p->n_rows = rows; p->n_q = n_q; p->q_first = first;
+    p->kv_len = off.off[d->q_scale_end];
+    p->num_scales = d->q_scale_end;   // scales beyond the call's last are never visible
+    p->step_mode = (d->q_scale_end - d->q_scale_begin == 1) ? 1 : 0;
+    const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
+    p->scale = scale;
+    p->scale_log2 = scale * 1.4426950408889634f;
+    for (int s = 0; s < VAR_MAX_SCALES; ++s) p->scale_end[s] = s < off.num_scales ? off.off[s + 1] : off.off[off.num_scales];
+    return ok();
+}
+
+}  // namespace
+
+VAR_EXPORT const char* var_status_string(var_status s) {
+    switch (s) {
+        case VAR_OK: return "VAR_OK";
+        case VAR_ERR_NULL: return "VAR_ERR_NULL";
+        case VAR_ERR_SCHEDULE: return "VAR_ERR_SCHEDULE";
+        case VAR_ERR_RANGE: return "VAR_ERR_RANGE";
+        case VAR_ERR_UNSUPPORTED: return "VAR_ERR_UNSUPPORTED";
+        case VAR_ERR_STRIDE: return "VAR_ERR_STRIDE";
+        case VAR_ERR_CAPACITY: return "VAR_ERR_CAPACITY";
+        case VAR_ERR_INDEX: return "VAR_ERR_INDEX";
+        case VAR_ERR_HIP: return "VAR_ERR_HIP";
+    }
+    return "VAR_ERR_UNKNOWN";
+}
+
+VAR_EXPORT const char* var_last_error(void) { return g_last_error; }
+
+VAR_EXPORT var_status var_schedule_extent(const var_schedule* sched, int32_t b, int32_t e, int64_t* first_token,
+                                          int64_t* n_q, int64_t* kv_len) {
+    Offsets off;
+    var_status st = check_schedule(sched, &off);
+    if (st != VAR_OK) return st;
+    if ((st = check_range(off, b, e)) != VAR_OK) return st;
+    if (first_token) *first_token = off.off[b];
+    if (n_q) *n_q = off.off[e] - off.off[b];
+    if (kv_len) *kv_len = off.off[e];
+    return ok();
+}
+
+VAR_EXPORT var_status var_attn_dense(const var_schedule* sched, const var_attn_desc* desc, const void* q,
+                                     var_layout q_l, const void* k, var_layout k_l, const void* v, var_layout v_l,
+                                     void* o, var_layout o_l, float* lse, const int32_t* q_index, int32_t n_sel,
+                                     void* stream) {
+    varattn::AttnParams p;
+    bool none = false;
+    var_status st = prepare_attn(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, &p, &none);
+    if (st != VAR_OK || none) return st;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (desc->in_dtype == VAR_BF16) {
+        const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false);
+        p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
+        return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, desc->out_dtype == VAR_BF16, false, s),
+                          "var_attn_dense launch");
+    }
+    p.n_qtiles = (p.n_rows + varattn::kF32RowsPerTile - 1) / varattn::kF32RowsPerTile;
+    return hip_status(varattn::launch_attn_f32(p, desc->head_dim, false, s), "var_attn_dense launch");
+}
+
+VAR_EXPORT var_status var_attn_block_sparse(const var_schedule* sched, const var_attn_desc* desc, const void* q,
+                                            var_layout q_l, const void* k, var_layout k_l, const void* v,
+                                            var_layout v_l, void* o, var_layout o_l, float* lse,
+                                            const int32_t* q_index, int32_t n_sel, const int32_t* row_ptr,
+                                            const int32_t* col_idx, int32_t tile_q, int32_t tile_k,
+                                            void* stream) {
+    if (tile_q != 64 || tile_k != 64)
+        return fail(VAR_ERR_UNSUPPORTED, "block-sparse attention supports 64x64 tiles, got %dx%d", tile_q, tile_k);
+    if (!row_ptr || !col_idx) return fail(VAR_ERR_NULL, "row_ptr and col_idx must be non-NULL");
+    varattn::AttnParams p;
+    bool none = false;
+    var_status st = prepare_attn(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, &p, &none);
+    if (st != VAR_OK || none) return st;
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.n_qtiles = (p.n_rows + 63) / 64;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (desc->in_dtype == VAR_BF16)
+        return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, desc->out_dtype == VAR_BF16, true, s),
+                          "var_attn_block_sparse launch");
+    return hip_status(varattn::launch_attn_f32(p, desc->head_dim, true, s), "var_attn_block_sparse launch");
+}
+
+namespace {
+var_status mask_dims(const var_schedule* sched, int32_t b, int32_t e, const var_mask_params* mp, bool has_index,
+                     int32_t n_sel, Offsets* off, int32_t* rows, int32_t* n_qt, int32_t* n_kt) {
+    var_status st = check_schedule(sched, off);
+    if (st != VAR_OK) return st;
+    if ((st = check_range(*off, b, e)) != VAR_OK) return st;
+    if (!mp) return fail(VAR_ERR_NULL, "mask params are NULL");
+    if (mp->tile_q < 1 || mp->tile_k < 1 || mp->tile_q > 4096 || mp->tile_k > 4096)
+        return fail(VAR_ERR_RANGE, "tile sizes %dx%d outside [1, 4096]", mp->tile_q, mp->tile_k);
+    if (mp->radius_y < 0 || mp->radius_x < 0 || mp->radius_y > 4096 || mp->radius_x > 4096)
+        return fail(VAR_ERR_RANGE, "radii must lie in [0, 4096]");
+    if (mp->sink_scales < 0 || mp->local_from_scale < 0)
+        return fail(VAR_ERR_RANGE, "sink_scales and local_from_scale must be >= 0");
+    const int32_t n_q = off->off[e] - off->off[b];
+    if (has_index) {
+        if (n_sel < 0 || n_sel > n_q) return fail(VAR_ERR_INDEX, "n_sel=%d outside [0, n_q=%d]", n_sel, n_q);
+        *rows = n_sel;
+    } else {
+        if (n_sel != 0) return fail(VAR_ERR_INDEX, "n_sel=%d given without q_index", n_sel);
+        *rows = n_q;
+    }
+    *n_qt = (*rows + mp->tile_q - 1) / mp->tile_q;
+    *n_kt = (off->off[e] + mp->tile_k - 1) / mp->tile_k;
+    return VAR_OK;
+}
+}  // namespace
+
+VAR_EXPORT var_status var_tile_mask_dims(const var_schedule* sched, int32_t b, int32_t e, const var_mask_params* mp,
+                                         int32_t n_sel_or_0, int32_t* n_qt, int32_t* n_kt) {
+    Offsets off;
+    int32_t rows, a, c;
+    var_status st = mask_dims(sched, b, e, mp, n_sel_or_0 > 0, n_sel_or_0, &off, &rows, &a, &c);
+    if (st != VAR_OK) return st;
+    if (n_qt) *n_qt = a;
+    if (n_kt) *n_kt = c;
+    return ok();
+}
+
+VAR_EXPORT var_status var_build_tile_mask(const var_schedule* sched, int32_t b, int32_t e, const var_mask_params* mp,
+                                          const int32_t* q_index, int32_t n_sel, int32_t* row_ptr, int32_t* col_idx,
+                                          int64_t col_capacity, void* stream) {
+    Offsets off;
+    int32_t rows, n_qt, n_kt;
+    var_status st = mask_dims(sched, b, e, mp, q_index != nullptr, n_sel, &off, &rows, &n_qt, &n_kt);
+    if (st != VAR_OK) return st;
+    if (!row_ptr || (!col_idx && n_qt > 0)) return fail(VAR_ERR_NULL, "row_ptr and col_idx must be non-NULL");
+    if (col_capacity < (int64_t)n_qt * n_kt)
+        return fail(VAR_ERR_CAPACITY, "col_capacity=%lld below n_qt*n_kt=%lld", (long long)col_capacity,
+                    (long long)n_qt * n_kt);
+    if ((int64_t)n_qt * n_kt >= (int64_t)1 << 31) return fail(VAR_ERR_RANGE, "tile mask too large");
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (n_qt == 0) {
+        // empty query set: row_ptr = {0}
+        return hip_status(varattn::launch_zero_i32(row_ptr, s), "var_build_tile_mask launch");
+    }
+    varattn::MaskParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q_index = q_index;
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.n_rows = rows;
+    p.q_first = off.off[b];
+    p.n_q = off.off[e] - off.off[b];
+    p.kv_len = off.off[e];
+    p.n_qt = n_qt;
+    p.n_kt = n_kt;
+    p.tile_q = mp->tile_q;
+    p.tile_k = mp->tile_k;
+    p.sink_scales = mp->sink_scales;
+    p.local_from_scale = mp->local_from_scale;
+    p.radius_y = mp->radius_y;
+    p.radius_x = mp->radius_x;
+    p.num_scales = e;
+    for (int i = 0; i <= VAR_MAX_SCALES; ++i) p.off[i] = i <= off.num_scales ? off.off[i] : off.off[off.num_scales];
+    for (int i = 0; i < VAR_MAX_SCALES; ++i) {
+        p.h[i] = i < off.num_scales ? sched->h[i] : 1;
+        p.w[i] = i < off.num_scales ? sched->w[i] : 1;
+    }
+    return hip_status(varattn::launch_tile_mask(p, s), "var_build_tile_mask launch");
+}
+
+VAR_EXPORT var_status var_scatter_restore(int32_t maps, int32_t row_elems, var_dtype dtype, const void* base,
+                                          int64_t base_map_stride, int64_t base_row_stride, int32_t h_in,
+                                          int32_t w_in, const void* upd, int64_t upd_map_stride,
+                                          int64_t upd_row_stride, const int32_t* q_index, int32_t n_sel, void* out,
+                                          int64_t out_map_stride, int64_t out_row_stride, int32_t h_out,
+                                          int32_t w_out, int32_t* err_flag, void* stream) {
+    if (dtype != VAR_F32 && dtype != VAR_BF16) return fail(VAR_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (maps < 0 || row_elems < 1) return fail(VAR_ERR_RANGE, "maps=%d row_elems=%d invalid", maps, row_elems);
+    if (h_in < 1 || w_in < 1 || h_out < 1 || w_out < 1 || (int64_t)h_in * w_in >= kMaxTokens ||
+        (int64_t)h_out * w_out >= kMaxTokens)
+        return fail(VAR_ERR_RANGE, "grid sizes invalid");
+    if (n_sel < 0 || (int64_t)n_sel > (int64_t)h_out * w_out)
+        return fail(VAR_ERR_INDEX, "n_sel=%d outside [0, h_out*w_out]", n_sel);
+    if (!base || !out || (n_sel > 0 && (!upd || !q_index)))
+        return fail(VAR_ERR_NULL, "base, out (and upd, q_index when n_sel > 0) must be non-NULL");
+    const int eb = dtype == VAR_BF16 ? 2 : 4;
+    const int64_t strides[6] = {base_map_stride, base_row_stride, upd_map_stride, upd_row_stride, out_map_stride,
+                                out_row_stride};
+    for (int i = 0; i < 6; ++i)
+        if (strides[i] < 0) return fail(VAR_ERR_STRIDE, "strides must be non-negative");
+    if (base_row_stride < row_elems || out_row_stride < row_elems || (n_sel > 0 && upd_row_stride < row_elems))
+        return fail(VAR_ERR_STRIDE, "row strides must be >= row_elems");
+    if (maps == 0) return ok();
+    varattn::ScatterParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.base = static_cast<const unsigned char*>(base);
+    p.upd = static_cast<const unsigned char*>(upd);
+    p.out = static_cast<unsigned char*>(out);
+    p.q_index = q_index;
+    p.err_flag = err_flag;
+    p.base_map_stride = base_map_stride * eb;
+    p.base_row_stride = base_row_stride * eb;
+    p.upd_map_stride = upd_map_stride * eb;
+    p.upd_row_stride = upd_row_stride * eb;
+    p.out_map_stride = out_map_stride * eb;
+    p.out_row_stride = out_row_stride * eb;
+    p.maps = maps;
+    p.row_bytes = row_elems * eb;
+    p.n_sel = n_sel;
+    p.h_in = h_in; p.w_in = w_in; p.h_out = h_out; p.w_out = w_out;
+    // widest copy unit dividing every byte offset the kernel forms
+    uint64_t g = (uint64_t)p.row_bytes | (uint64_t)reinterpret_cast<uintptr_t>(base) |
+                 (uint64_t)reinterpret_cast<uintptr_t>(out);
+    if (n_sel > 0) g |= (uint64_t)reinterpret_cast<uintptr_t>(upd) | (uint64_t)p.upd_map_stride | (uint64_t)p.upd_row_stride;
+    g |= (uint64_t)p.base_map_stride | (uint64_t)p.base_row_stride | (uint64_t)p.out_map_stride |
+         (uint64_t)p.out_row_stride;
+    p.unit = (g & 15u) == 0 ? 16 : ((g & 3u) == 0 ? 4 : 2);
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return hip_status(varattn::launch_scatter(p, s), "var_scatter_restore launch");
+}

@@ -1,0 +1,163 @@
+"""The C ABI on the CPU: the library loads, exports exactly the declared
+symbols, and rejects bad arguments on the host before any HIP call (every
+case below fails validation, so no device is touched)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "var_attn.h")
+
+
+@pytest.fixture(scope="module")
+def api():
+    from scale_wise_attention_amd import api as _api
+    return _api
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:var_status|const char\*)\s+(var_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_match_header(api):
+    declared = _declared()
+    assert len(declared) == 8
+    for name in declared:
+        assert hasattr(api.LIB, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(ln.split()[-1] for ln in nm.splitlines() if " T " in ln and ln.split()[-1].startswith("var_"))
+    assert exported == declared
+    assert sorted(api.EXPORTED) == declared
+
+
+def test_status_strings(api):
+    for code, name in api.STATUS.items():
+        assert api.LIB.var_status_string(code).decode() == name
+    assert api.LIB.var_status_string(99).decode() == "VAR_ERR_UNKNOWN"
+
+
+W1024 = [1, 2, 4, 6, 8, 12, 16, 20, 24, 32, 40, 48, 64]
+
+
+def test_extent_and_mask_dims(api):
+    assert api.var_schedule_extent((W1024, W1024), 12, 13) == (6425, 4096, 10521)
+    assert api.var_schedule_extent((W1024, W1024), 0, 13) == (0, 10521, 10521)
+    assert api.var_schedule_extent(([1, 2, 3, 4], [1, 2, 3, 4]), 1, 3) == (1, 13, 14)
+    assert api.var_tile_mask_dims((W1024, W1024), 12, 13, api.mask_params()) == (64, 165)
+    assert api.var_tile_mask_dims((W1024, W1024), 12, 13, api.mask_params(), n_sel=1638) == (26, 165)
+    assert api.var_tile_mask_dims(([1, 2, 3, 4], [1, 2, 3, 4]), 0, 4, api.mask_params(4, 4, 1, 1, 0, 0)) == (8, 8)
+
+
+FAKE = 1 << 20   # aligned non-null stand-in for a device pointer; never dereferenced
+
+
+def _dense(api, sched, desc, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, q_index=None, n_sel=0, layout=None):
+    L = layout or api.Layout(2 * 16 * 4096 * 128, 4096 * 128, 128)
+    P = ctypes.c_void_p
+    return api.LIB.var_attn_dense(ctypes.byref(sched) if sched is not None else None,
+                                  ctypes.byref(desc) if desc is not None else None,
+                                  P(q), L, P(k), L, P(v), L, P(o), L, P(lse), P(q_index), n_sel, P(0))
+
+
+def _desc(api, **kw):
+    d = dict(batch=2, heads=16, head_dim=128, q_scale_begin=12, q_scale_end=13, softmax_scale=0.0,
+             in_dtype=api.VAR_BF16, out_dtype=api.VAR_F32)
+    d.update(kw)
+    return api.AttnDesc(**d)
+
+
+def _code(api, name):
+    return {v: k for k, v in api.STATUS.items()}[name]
+
+
+def test_dense_validation_errors(api):
+    s = api.make_schedule(W1024, W1024)
+    E = lambda n: _code(api, n)
+    assert _dense(api, None, _desc(api)) == E("VAR_ERR_NULL")
+    assert _dense(api, s, None) == E("VAR_ERR_NULL")
+    assert _dense(api, api.make_schedule([], []), _desc(api)) == E("VAR_ERR_SCHEDULE")
+    assert _dense(api, api.make_schedule([0], [4]), _desc(api, q_scale_begin=0, q_scale_end=1)) == E("VAR_ERR_SCHEDULE")
+    assert _dense(api, api.make_schedule([4097], [4]), _desc(api, q_scale_begin=0, q_scale_end=1)) == E("VAR_ERR_SCHEDULE")
+    assert _dense(api, api.make_schedule([1] * 33, [1] * 33), _desc(api, q_scale_begin=0, q_scale_end=1)) == E("VAR_ERR_SCHEDULE")
+    assert _dense(api, s, _desc(api, q_scale_begin=12, q_scale_end=14)) == E("VAR_ERR_RANGE")
+    assert _dense(api, s, _desc(api, q_scale_begin=5, q_scale_end=5)) == E("VAR_ERR_RANGE")
+    assert _dense(api, s, _desc(api, batch=0)) == E("VAR_ERR_RANGE")
+    assert _dense(api, s, _desc(api, head_dim=96)) == E("VAR_ERR_UNSUPPORTED")
+    assert _dense(api, s, _desc(api, head_dim=128, in_dtype=api.VAR_F32)) == E("VAR_ERR_UNSUPPORTED")
+    assert _dense(api, s, _desc(api, head_dim=64, in_dtype=api.VAR_F32, out_dtype=api.VAR_BF16)) == E("VAR_ERR_UNSUPPORTED")
+    assert _dense(api, s, _desc(api, in_dtype=7)) == E("VAR_ERR_UNSUPPORTED")
+    assert _dense(api, s, _desc(api, softmax_scale=-1.0)) == E("VAR_ERR_RANGE")
+    assert _dense(api, s, _desc(api, softmax_scale=float("nan"))) == E("VAR_ERR_RANGE")
+    assert _dense(api, s, _desc(api), q=0) == E("VAR_ERR_NULL")
+    assert _dense(api, s, _desc(api), o=0) == E("VAR_ERR_NULL")
+    assert _dense(api, s, _desc(api), k=FAKE + 8) == E("VAR_ERR_STRIDE")
+    assert _dense(api, s, _desc(api), layout=api.Layout(0, 0, 100)) == E("VAR_ERR_STRIDE")
+    assert _dense(api, s, _desc(api), layout=api.Layout(0, 0, 132)) == E("VAR_ERR_STRIDE")
+    assert _dense(api, s, _desc(api), lse=FAKE + 2) == E("VAR_ERR_STRIDE")
+    assert _dense(api, s, _desc(api), n_sel=5) == E("VAR_ERR_INDEX")
+    assert _dense(api, s, _desc(api), q_index=FAKE, n_sel=4097) == E("VAR_ERR_INDEX")
+    assert _dense(api, s, _desc(api), q_index=FAKE, n_sel=3, o=0) == E("VAR_ERR_NULL")
+    assert _dense(api, s, _desc(api), q_index=FAKE, n_sel=-1) == E("VAR_ERR_INDEX")
+    assert "n_sel" in api.LIB.var_last_error().decode()
+
+
+def test_empty_selection_returns_ok_without_launch(api):
+    s = api.make_schedule(W1024, W1024)
+    assert _dense(api, s, _desc(api), q_index=FAKE, n_sel=0) == 0
+    assert api.LIB.var_last_error().decode() == ""
+    assert _dense(api, s, _desc(api), q_index=FAKE, n_sel=0, o=0) == 0   # empty output tensor
+
+
+def test_sparse_and_mask_validation_errors(api):
+    s = api.make_schedule(W1024, W1024)
+    E = lambda n: _code(api, n)
+    L = api.Layout(2 * 16 * 4096 * 128, 4096 * 128, 128)
+    P = ctypes.c_void_p
+    d = _desc(api)
+    r = api.LIB.var_attn_block_sparse(ctypes.byref(s), ctypes.byref(d), P(FAKE), L, P(FAKE), L, P(FAKE), L, P(FAKE), L,
+                                      P(0), P(0), 0, P(FAKE), P(FAKE), 32, 64, P(0))
+    assert r == E("VAR_ERR_UNSUPPORTED")
+    r = api.LIB.var_attn_block_sparse(ctypes.byref(s), ctypes.byref(d), P(FAKE), L, P(FAKE), L, P(FAKE), L, P(FAKE), L,
+                                      P(0), P(0), 0, P(0), P(FAKE), 64, 64, P(0))
+    assert r == E("VAR_ERR_NULL")
+    mp = api.mask_params()
+    build = api.LIB.var_build_tile_mask
+    assert build(ctypes.byref(s), 12, 13, ctypes.byref(mp), P(0), 0, P(FAKE), P(FAKE), 64 * 165 - 1, P(0)) == E("VAR_ERR_CAPACITY")
+    assert build(ctypes.byref(s), 12, 13, None, P(0), 0, P(FAKE), P(FAKE), 64 * 165, P(0)) == E("VAR_ERR_NULL")
+    assert build(ctypes.byref(s), 12, 13, ctypes.byref(mp), P(0), 0, P(0), P(FAKE), 64 * 165, P(0)) == E("VAR_ERR_NULL")
+    assert build(ctypes.byref(s), 12, 13, ctypes.byref(mp), P(0), 3, P(FAKE), P(FAKE), 64 * 165, P(0)) == E("VAR_ERR_INDEX")
+    bad = api.mask_params(0, 64)
+    assert build(ctypes.byref(s), 12, 13, ctypes.byref(bad), P(0), 0, P(FAKE), P(FAKE), 10 ** 6, P(0)) == E("VAR_ERR_RANGE")
+    bad = api.mask_params(64, 64, 7, 7, -1, 2)
+    assert build(ctypes.byref(s), 12, 13, ctypes.byref(bad), P(0), 0, P(FAKE), P(FAKE), 10 ** 6, P(0)) == E("VAR_ERR_RANGE")
+
+
+def test_scatter_validation_errors(api):
+    E = lambda n: _code(api, n)
+    P = ctypes.c_void_p
+    f = api.LIB.var_scatter_restore
+    ok_args = dict(maps=32, row_elems=128, dtype=api.VAR_BF16, base=FAKE, bms=2304 * 128, brs=128, h_in=48, w_in=48,
+                   upd=FAKE, ums=1638 * 128, urs=128, q_index=FAKE, n_sel=1638, out=FAKE, oms=4096 * 128, ors=128,
+                   h_out=64, w_out=64)
+
+    def call(**kw):
+        a = dict(ok_args)
+        a.update(kw)
+        return f(a["maps"], a["row_elems"], a["dtype"], P(a["base"]), a["bms"], a["brs"], a["h_in"], a["w_in"],
+                 P(a["upd"]), a["ums"], a["urs"], P(a["q_index"]), a["n_sel"], P(a["out"]), a["oms"], a["ors"],
+                 a["h_out"], a["w_out"], P(0), P(0))
+
+    assert call(dtype=5) == E("VAR_ERR_UNSUPPORTED")
+    assert call(row_elems=0) == E("VAR_ERR_RANGE")
+    assert call(h_out=0) == E("VAR_ERR_RANGE")
+    assert call(n_sel=4097) == E("VAR_ERR_INDEX")
+    assert call(base=0) == E("VAR_ERR_NULL")
+    assert call(q_index=0) == E("VAR_ERR_NULL")
+    assert call(brs=64) == E("VAR_ERR_STRIDE")
+    assert call(oms=-1) == E("VAR_ERR_STRIDE")
+    assert call(maps=0) == 0   # nothing to do, nothing launched

@@ -1,0 +1,214 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+Tolerances: float32 inputs max-abs <= 1e-5; bf16 inputs with float32
+accumulation max-abs <= 1e-2 and mean-abs <= 1e-3 (both for fp32 and bf16
+outputs); tile masks, indices and scatter results bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from scale_wise_attention_amd.inputs import WORKLOADS, make_qkv, pruned_index
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-5
+BF16_MAX, BF16_MEAN = 1e-2, 1e-3
+
+
+@pytest.fixture(scope="module")
+def api():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from scale_wise_attention_amd import api as _api
+    return _api
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _sched(wl):
+    return (wl.h, wl.w)
+
+
+def _check(got, ref, dtype, what):
+    err = np.abs(got.astype(np.float64) - ref)
+    mx, mean = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    print(f"[{what}] max-abs {mx:.3e} mean-abs {mean:.3e}", flush=True)
+    if dtype == "f32":
+        assert mx <= F32_TOL, what
+    else:
+        assert mx <= BF16_MAX and mean <= BF16_MEAN, what
+
+
+def _steps(api, wl, q, k, v, out_dtype=None):
+    off = oracle.offsets(wl.h, wl.w)
+    outs = []
+    for s in range(wl.num_scales):
+        qs = q[:, :, off[s]:off[s + 1]]
+        outs.append(api.var_attn_dense(_sched(wl), qs, k, v, s, s + 1, out_dtype=out_dtype))
+    return outs
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_fp32_steps_and_full_sequence(api, seed):
+    wl = WORKLOADS["tiny_fp32"]
+    q, k, v = make_qkv(wl, seed, device="cuda")
+    qn, kn, vn = _np(q), _np(k), _np(v)
+    off = oracle.offsets(wl.h, wl.w)
+    for s, o in enumerate(_steps(api, wl, q, k, v)):
+        ref = oracle.attention(qn[:, :, off[s]:off[s + 1]], kn, vn, wl.h, wl.w, s, s + 1)
+        _check(_np(o), ref, "f32", f"tiny step {s}")
+    o, lse = api.var_attn_dense(_sched(wl), q, k, v, 0, wl.num_scales, return_lse=True)
+    ref, ref_lse = oracle.attention(qn, kn, vn, wl.h, wl.w, 0, wl.num_scales, return_lse=True)
+    _check(_np(o), ref, "f32", "tiny full sequence")
+    assert np.max(np.abs(_np(lse) - ref_lse)) <= F32_TOL
+    # the first token sees only itself: O = v_0 exactly
+    assert torch.equal(o[:, :, 0].cpu(), v[:, :, 0].cpu())
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_var256_all_steps_bf16(api, seed):
+    wl = WORKLOADS["var256"]
+    q, k, v = make_qkv(wl, seed, device="cuda")
+    qn, kn, vn = _np(q), _np(k), _np(v)
+    off = oracle.offsets(wl.h, wl.w)
+    for s, o in enumerate(_steps(api, wl, q, k, v)):
+        ref = oracle.attention(qn[:, :, off[s]:off[s + 1]], kn, vn, wl.h, wl.w, s, s + 1)
+        _check(_np(o), ref, "bf16", f"var256 seed {seed} step {s}")
+
+
+def test_var256_full_sequence_block_causal_and_lse(api):
+    wl = WORKLOADS["var256"]
+    q, k, v = make_qkv(wl, 5, device="cuda")
+    o, lse = api.var_attn_dense(_sched(wl), q, k, v, 0, wl.num_scales, return_lse=True)
+    ref, ref_lse = oracle.attention(_np(q), _np(k), _np(v), wl.h, wl.w, 0, wl.num_scales, return_lse=True)
+    _check(_np(o), ref, "bf16", "var256 full sequence")
+    assert np.max(np.abs(_np(lse) - ref_lse)) <= 1e-3
+    # scale-1 query: v_0 (its only key).  The bf16 kernel folds scale*log2(e) into one FMA, so
+    # its single weight is exp2(rounding error of s*c) = 1 +- 1e-6 rather than exactly 1.
+    v0 = v[:, :, 0].float()
+    assert float(((o[:, :, 0] - v0).abs() / v0.abs().clamp_min(1e-3)).max()) <= 2e-6
+    # a middle range of scales
+    off = oracle.offsets(wl.h, wl.w)
+    o2 = api.var_attn_dense(_sched(wl), q[:, :, off[3]:off[7]], k, v, 3, 7)
+    ref2 = oracle.attention(_np(q)[:, :, off[3]:off[7]], _np(k), _np(v), wl.h, wl.w, 3, 7)
+    _check(_np(o2), ref2, "bf16", "var256 scales 3..6")
+
+
+def test_var256_bf16_output(api):
+    wl = WORKLOADS["var256"]
+    q, k, v = make_qkv(wl, 3, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    s = wl.num_scales - 1
+    o = api.var_attn_dense(_sched(wl), q[:, :, off[s]:], k, v, s, s + 1, out_dtype=torch.bfloat16)
+    assert o.dtype == torch.bfloat16
+    ref = oracle.attention(_np(q)[:, :, off[s]:], _np(k), _np(v), wl.h, wl.w, s, s + 1)
+    _check(_np(o), ref, "bf16", "var256 last step bf16 out")
+
+
+def test_var512_all_steps(api):
+    wl = WORKLOADS["var512"]
+    q, k, v = make_qkv(wl, 0, device="cuda")
+    qn, kn, vn = _np(q), _np(k), _np(v)
+    off = oracle.offsets(wl.h, wl.w)
+    for s, o in enumerate(_steps(api, wl, q, k, v)):
+        ref = oracle.attention(qn[:, :, off[s]:off[s + 1]], kn, vn, wl.h, wl.w, s, s + 1)
+        _check(_np(o), ref, "bf16", f"var512 step {s}")
+
+
+def test_gather_rows_match_oracle_and_dense_rows(api):
+    wl = WORKLOADS["var512"]
+    q, k, v = make_qkv(wl, 1, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    s = wl.num_scales - 1
+    qs = q[:, :, off[s]:]
+    n_q = off[s + 1] - off[s]
+    for sel in (pruned_index(n_q, 0.4, 1), np.array([n_q - 1], np.int32), np.arange(n_q, dtype=np.int32)[::-7].copy()):
+        idx = torch.from_numpy(sel).cuda()
+        o = api.var_attn_dense(_sched(wl), qs, k, v, s, s + 1, q_index=idx)
+        ref = oracle.attention(_np(qs), _np(k), _np(v), wl.h, wl.w, s, s + 1, q_index=sel)
+        _check(_np(o), ref, "bf16", f"var512 gather n_sel={sel.size}")
+        full = api.var_attn_dense(_sched(wl), qs, k, v, s, s + 1)
+        # the same query computed in another tile: equal up to the bf16 rounding of its weights
+        assert float((o - full[:, :, idx.long()]).abs().max()) <= 5e-3
+
+
+def test_empty_selection_is_a_noop(api):
+    wl = WORKLOADS["var256"]
+    q, k, v = make_qkv(wl, 0, device="cuda")
+    idx = torch.zeros(0, dtype=torch.int32, device="cuda")
+    o = api.var_attn_dense(_sched(wl), q[:, :, 424:], k, v, 9, 10, q_index=idx)
+    assert o.shape == (2, 16, 0, 64)
+
+
+def _sample_rows(n, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(n, size=min(count, n), replace=False).tolist())
+    rows.update([0, n - 1, min(63, n - 1), min(64, n - 1), min(127, n - 1), min(128, n - 1)])
+    return np.array(sorted(rows))
+
+
+def test_var1024_last_step_full_size_sampled(api):
+    """Full 1024px last step (4096 x 10521, B=2, H=16, D=128) as the benchmark launches it."""
+    wl = WORKLOADS["var1024"]
+    q, k, v = make_qkv(wl, 0, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    s = wl.num_scales - 1
+    qs = q[:, :, off[s]:]
+    o = api.var_attn_dense(_sched(wl), qs, k, v, s, s + 1)
+    on = _np(o)
+    qn, kn, vn = _np(qs), _np(k), _np(v)
+    rows = _sample_rows(4096, 96, 0)
+    for (b, h) in [(0, 0), (0, 7), (1, 3), (1, 15)]:
+        ref = oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1],
+                               wl.h, wl.w, s, s + 1, rows=rows)
+        _check(on[b:b + 1, h:h + 1, rows], ref, "bf16", f"var1024 last step b{b} h{h}")
+
+
+def test_var1024_all_steps_one_head(api):
+    wl = WORKLOADS["var1024"]
+    q, k, v = make_qkv(wl, 1, device="cuda")
+    qn, kn, vn = _np(q), _np(k), _np(v)
+    off = oracle.offsets(wl.h, wl.w)
+    outs = _steps(api, wl, q, k, v)
+    for s, o in enumerate(outs):
+        rows = _sample_rows(off[s + 1] - off[s], 64, s)
+        for (b, h) in [(0, 5), (1, 12)]:
+            ref = oracle.attention(qn[b:b + 1, h:h + 1, off[s]:off[s + 1]], kn[b:b + 1, h:h + 1],
+                                   vn[b:b + 1, h:h + 1], wl.h, wl.w, s, s + 1, rows=rows)
+            _check(_np(o[b:b + 1, h:h + 1])[:, :, rows], ref, "bf16", f"var1024 step {s} b{b} h{h}")
+
+
+def test_deterministic_runs(api):
+    wl = WORKLOADS["var512"]
+    q, k, v = make_qkv(wl, 2, device="cuda")
+    a = api.var_attn_dense(_sched(wl), q[:, :, 1216:], k, v, 9, 10)
+    b = api.var_attn_dense(_sched(wl), q[:, :, 1216:], k, v, 9, 10)
+    assert torch.equal(a, b)
+
+
+def test_strided_views(api):
+    """Non-contiguous [B, H, T, D] views (token-major storage) go through the strides."""
+    wl = WORKLOADS["var256"]
+    q, k, v = make_qkv(wl, 4, device="cuda")
+    qt = q.transpose(1, 2).contiguous().transpose(1, 2)   # storage [B, T, H, D]
+    kt = k.transpose(1, 2).contiguous().transpose(1, 2)
+    vt = v.transpose(1, 2).contiguous().transpose(1, 2)
+    s = wl.num_scales - 1
+    a = api.var_attn_dense(_sched(wl), q[:, :, 424:], k, v, s, s + 1)
+    b = api.var_attn_dense(_sched(wl), qt[:, :, 424:], kt, vt, s, s + 1)
+    assert torch.equal(a, b)
+
+
+def test_invalid_shapes_raise_before_launch(api):
+    wl = WORKLOADS["var256"]
+    q, k, v = make_qkv(wl, 0, device="cuda")
+    with pytest.raises(ValueError):
+        api.var_attn_dense(_sched(wl), q[:, :, :10], k, v, 9, 10)          # too few query rows
+    with pytest.raises(ValueError):
+        api.var_attn_dense(_sched(wl), q, k[:, :, :100], v, 9, 10)         # KV shorter than kv_len
+    with pytest.raises(api.VarAttnError):
+        api.var_attn_dense(_sched(wl), q, k, v, 9, 11)                     # bad scale range
