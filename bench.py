@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark of next-scale attention for a 1024px VAR generation on one MI355X.
+
+One benchmark step is one pass of the whole hot path over one batch of
+synthetic input (grids 1,2,4,6,8,12,16,20,24,32,40,48,64 = 10521 tokens,
+B=2 (CFG cond + uncond), H=16, D=128, bf16 in, fp32 accumulate, bf16 out):
+
+  1. dense block-causal attention, one launch per scale step (13 launches);
+  2. block-sparse generation: per scale step, the tile mask (64x64 tiles,
+     7 sink scales, window radius 2) is built on the device and the sparse
+     kernel walks it; the last step keeps a seeded 40 % subset of its 4096
+     queries (fused gather), and its outputs are scattered over the
+     nearest-upsampled 48x48 output of the previous step.
+
+The pass is captured once into a HIP graph and replayed (launch overhead of
+the 13+28 launches off the host); every kernel of the pass runs in every
+replay.  ``value`` is effective TFLOP/s over the pass: algorithmic FLOPs of
+the dense generation plus the sparse generation (computed tiles only),
+divided by the measured time.  Per-step times, the dense last step against
+the bf16 MFMA peak and the sparse speedup are reported alongside.
+
+``--gpus N`` with N > 1 is refused: this path runs on one GPU.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "effective attn TFLOP/s + ms/step at 1024px (dense & block-sparse), % MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk (the published 2.5 PFLOP/s)
+HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dense_attn_1024_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "scale_wise_attention_amd", "csrc", "attn_bf16.hip")
+
+
+def _kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _read_traffic():
+    """HBM bytes per dense launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for ln in f:
+                if "=" in ln and not ln.startswith("#"):
+                    a, b = ln.split("=", 1)
+                    fields[a.strip()] = b.strip()
+        if fields.get("kernel_source_sha256_16") != _kernel_hash():
+            return None
+        return float(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, q, k, v, heads):
+    """The oracle (as it stands) on a bounded sample: the dense last step for `heads` (b, h) pairs."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    K = wl.num_scales
+    off = [0]
+    for g in wl.grids:
+        off.append(off[-1] + g * g)
+    qn = q[:, :, off[K - 1]:off[K]].float().cpu().numpy()
+    kn = k.float().cpu().numpy()
+    vn = v.float().cpu().numpy()
+    pairs = [(b, h) for b in range(wl.batch) for h in range(wl.heads)][:heads]
+    n, L = off[K] - off[K - 1], off[K]
+    t0 = time.perf_counter()
+    for (b, h) in pairs:
+        oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], wl.h, wl.w, K - 1, K)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * wl.head_dim * n * L * len(pairs)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"dense last step (4096 queries x 10521 keys, D=128) for {len(pairs)} of 32 (batch, head) "
+                      f"pairs, NumPy float64: {dt:.2f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=20, help="repetitions per launch for the per-step timings")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="(b, h) pairs in the oracle's CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this path runs on one GPU; --gpus must be 1 (nothing to shard here, "
+              "see the sharding paragraph of the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from scale_wise_attention_amd import api
+    from scale_wise_attention_amd import accounting as acc
+    from scale_wise_attention_amd.inputs import WORKLOADS, make_qkv, pruned_index
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WORKLOADS["var1024_sparse"]
+    K = wl.num_scales
+    sched = api.make_schedule(wl.h, wl.w)
+    q, k, v = make_qkv(wl, 0, device=dev)
+    off = [0]
+    for g in wl.grids:
+        off.append(off[-1] + g * g)
+    qsteps = [q[:, :, off[s]:off[s + 1]] for s in range(K)]
+    sel = pruned_index(4096, wl.prune_keep, 0)
+    sel_t = torch.from_numpy(sel).to(dev)
+    n_sel = int(sel.size)
+    mp = api.mask_params(wl.tile, wl.tile, wl.sink_scales, wl.local_from_scale, wl.radius, wl.radius)
+    B, H, D = wl.batch, wl.heads, wl.head_dim
+    bf = torch.bfloat16
+
+    # ---- buffers (allocated once, outside every timed region) ---------------
+    dense_out = [torch.empty(B, H, off[s + 1] - off[s], D, dtype=bf, device=dev) for s in range(K)]
+    sparse_out = [torch.empty(B, H, off[s + 1] - off[s], D, dtype=bf, device=dev) for s in range(K - 1)]
+    pruned_out = torch.empty(B, H, n_sel, D, dtype=bf, device=dev)
+    restored = torch.empty(B, H, 4096, D, dtype=bf, device=dev)
+    csr = []
+    for s in range(K):
+        idx = sel_t if s == K - 1 else None
+        n_qt, n_kt = api.var_tile_mask_dims(sched, s, s + 1, mp, n_sel if idx is not None else 0)
+        csr.append((torch.empty(n_qt + 1, dtype=torch.int32, device=dev),
+                    torch.empty(max(1, n_qt * n_kt), dtype=torch.int32, device=dev), idx))
+
+    # the last step block-sparse over all 4096 queries (sparse speedup at equal work)
+    n_qt_full, n_kt_full = api.var_tile_mask_dims(sched, K - 1, K, mp, 0)
+    full_rp = torch.empty(n_qt_full + 1, dtype=torch.int32, device=dev)
+    full_ci = torch.empty(n_qt_full * n_kt_full, dtype=torch.int32, device=dev)
+    full_out = torch.empty(B, H, 4096, D, dtype=bf, device=dev)
+
+    def sparse_full_last_step():
+        api.var_build_tile_mask(sched, K - 1, K, mp, row_ptr=full_rp, col_idx=full_ci)
+        api.var_attn_block_sparse(sched, qsteps[K - 1], k, v, K - 1, K, full_rp, full_ci, out=full_out)
+
+    def dense_step(s):
+        api.var_attn_dense(sched, qsteps[s], k, v, s, s + 1, out=dense_out[s])
+
+    def mask_step(s):
+        rp, ci, idx = csr[s]
+        api.var_build_tile_mask(sched, s, s + 1, mp, q_index=idx, row_ptr=rp, col_idx=ci)
+
+    def sparse_step(s):
+        rp, ci, idx = csr[s]
+        out = pruned_out if s == K - 1 else sparse_out[s]
+        api.var_attn_block_sparse(sched, qsteps[s], k, v, s, s + 1, rp, ci, out=out, q_index=idx)
+
+    def scatter_step():
+        api.var_scatter_restore(sparse_out[K - 2], wl.grids[K - 2], wl.grids[K - 2], pruned_out, sel_t,
+                                wl.grids[K - 1], wl.grids[K - 1], out=restored)
+
+    def run_pass():
+        for s in range(K):
+            dense_step(s)
+        for s in range(K):
+            mask_step(s)
+            sparse_step(s)
+        scatter_step()
+
+    # ---- algorithmic work ---------------------------------------------------
+    run_pass()
+    torch.cuda.synchronize()
+    dense_flops = [acc.dense_step_flops(wl, s) for s in range(K)]
+    sparse_flops = []
+    for s in range(K):
+        rp, ci, idx = csr[s]
+        rp_h = rp.cpu().numpy()
+        ci_h = ci.cpu().numpy()
+        rows = n_sel if idx is not None else off[s + 1] - off[s]
+        sparse_flops.append(acc.sparse_step_flops(wl, rp_h, ci_h, rows, off[s + 1]))
+    pass_flops = sum(dense_flops) + sum(sparse_flops)
+
+    # ---- whole-pass throughput (graph replay unless --eager) ---------------
+    stream = torch.cuda.current_stream()
+    graph = None
+    if not args.eager:
+        try:
+            g = torch.cuda.CUDAGraph()
+            s_cap = torch.cuda.Stream()
+            s_cap.wait_stream(stream)
+            with torch.cuda.stream(s_cap):
+                run_pass()          # warm the capture stream
+            stream.wait_stream(s_cap)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                run_pass()
+            torch.cuda.synchronize()
+            graph = g
+        except Exception as e:     # capture not available: fall back to eager launches
+            print(f"bench.py: graph capture failed ({e}); timing eager launches", file=sys.stderr)
+            graph = None
+
+    def one_step():
+        if graph is not None:
+            graph.replay()
+        else:
+            run_pass()
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        one_step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    value = pass_flops / (ms_per_step * 1e-3) / 1e12
+
+    # ---- per-launch timings (events on the launch stream, median of reps) --
+    def time_launch(fn, reps):
+        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in es:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in es]
+
+    R = args.reps
+    dense_ms = [statistics.median(time_launch(lambda s=s: dense_step(s), R)) for s in range(K)]
+    mask_ms = [statistics.median(time_launch(lambda s=s: mask_step(s), R)) for s in range(K)]
+    sparse_ms = [statistics.median(time_launch(lambda s=s: sparse_step(s), R)) for s in range(K)]
+    scatter_ms = statistics.median(time_launch(scatter_step, R))
+    sparse_full_ms = statistics.median(time_launch(sparse_full_last_step, R))
+    sparse_full_flops = acc.sparse_step_flops(wl, full_rp.cpu().numpy(), full_ci.cpu().numpy(), 4096, off[K])
+
+    def gen_time_ms(fn):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(R):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / R
+
+    dense_gen_ms = gen_time_ms(lambda: [dense_step(s) for s in range(K)])
+
+    def sparse_gen():
+        for s in range(K):
+            mask_step(s)
+            sparse_step(s)
+        scatter_step()
+
+    sparse_gen_ms = gen_time_ms(sparse_gen)
+
+    # dominant kernel: the dense bf16 attention kernel, averaged over its launches in one step
+    avg_launch_ms = sum(dense_ms) / K
+    avg_flops = sum(dense_flops) / K
+    achieved = avg_flops / (avg_launch_ms * 1e-3) / 1e12
+    traffic = _read_traffic()
+    last = K - 1
+    last_tflops = dense_flops[last] / (dense_ms[last] * 1e-3) / 1e12
+    sparse_last_ms = mask_ms[last] + sparse_ms[last]
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V with a shared sink direction on the first 7 scales)",
+        "config": {
+            "workload": "1024px VAR generation: grids 1,2,4,6,8,12,16,20,24,32,40,48,64 (10521 tokens), "
+                        "B=2 (CFG), H=16, D=128, bf16 in / fp32 accumulate / bf16 out; dense block-causal "
+                        "(13 launches) + block-sparse (64x64 tiles, 7 sink scales, radius 2; mask built per "
+                        "step) with the last step pruned to 1638 of 4096 queries and scattered over 48x48",
+            "launch": "hipGraph replay of the whole pass" if graph is not None else "eager",
+            "pass_gflop": round(pass_flops / 1e9, 3),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "attn_bf16_kernel<128,4,bf16 out,dense>",
+            "launches_per_step": K,
+            "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+            "algorithmic_gflop_per_launch": round(avg_flops / 1e9, 3),
+        },
+        "dense": {
+            "generation_ms": round(dense_gen_ms, 4),
+            "generation_tflops": round(sum(dense_flops) / (dense_gen_ms * 1e-3) / 1e12, 2),
+            "per_step_ms": [round(x, 4) for x in dense_ms],
+            "last_step_ms": round(dense_ms[last], 4),
+            "last_step_gflop": round(dense_flops[last] / 1e9, 3),
+            "last_step_tflops": round(last_tflops, 2),
+            "last_step_frac_peak": round(last_tflops / PEAK_BF16_TFLOPS, 4),
+        },
+        "sparse": {
+            "generation_ms": round(sparse_gen_ms, 4),
+            "generation_tflops": round(sum(sparse_flops) / (sparse_gen_ms * 1e-3) / 1e12, 2),
+            "per_step_attn_ms": [round(x, 4) for x in sparse_ms],
+            "per_step_mask_ms": [round(x, 4) for x in mask_ms],
+            "last_step_pruned_attn_ms": round(sparse_ms[last], 4),
+            "last_step_pruned_gflop": round(sparse_flops[last] / 1e9, 3),
+            "scatter_ms": round(scatter_ms, 4),
+            "scatter_gbps": round(acc.scatter_bytes(B * H, D * 2, n_sel, 4096) / (scatter_ms * 1e-3) / 1e9, 1),
+            "last_step_unpruned_ms": round(sparse_full_ms, 4),
+            "last_step_unpruned_gflop": round(sparse_full_flops / 1e9, 3),
+            "last_step_unpruned_tflops": round(sparse_full_flops / (sparse_full_ms * 1e-3) / 1e12, 2),
+            "speedup_last_step_unpruned_vs_dense": round(dense_ms[last] / sparse_full_ms, 3),
+            "speedup_last_step_pruned_vs_dense": round(dense_ms[last] / (sparse_last_ms + scatter_ms), 3),
+            "speedup_generation_vs_dense": round(dense_gen_ms / sparse_gen_ms, 3),
+        },
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(wl, q, k, v, args.cpu_heads)
+        cb.pop("seconds", None)
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -196,6 +196,8 @@ def var_attn_dense(schedule, q, k, v, q_scale_begin, q_scale_end, out=None, out_
     s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
                                            softmax_scale, q_index, return_lse)
     n_sel = rows if q_index is not None else 0
+    if q_index is not None and n_sel == 0:   # an empty selection has no device pointer: nothing to compute
+        return (out, lse) if return_lse else out
     _check(LIB.var_attn_dense(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k), _layout(k),
                               _ptr(v), _layout(v), _ptr(out), _layout(out), _ptr(lse), _ptr(q_index), n_sel,
                               _stream(q.device)))
@@ -222,14 +224,21 @@ def var_build_tile_mask(schedule, q_scale_begin, q_scale_end, params, q_index=No
     dev = q_index.device if q_index is not None else torch.device(device)
     _check_index(q_index, dev)
     n_qt, n_kt = var_tile_mask_dims(s, q_scale_begin, q_scale_end, params, n_sel)
+    if q_index is not None and n_sel == 0:
+        n_qt = 0          # empty selection: row_ptr = [0]
     if row_ptr is None:
         row_ptr = torch.empty(n_qt + 1, dtype=torch.int32, device=dev)
     if col_idx is None:
         col_idx = torch.empty(max(1, n_qt * n_kt), dtype=torch.int32, device=dev)
     if row_ptr.numel() < n_qt + 1 or row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
         raise ValueError("row_ptr must be int32 with n_qt+1 entries; col_idx int32")
+    qi = _ptr(q_index)
+    if q_index is not None and n_sel == 0:
+        # an empty tensor has no device pointer; the ABI tells "empty selection" from "no
+        # selection" by a non-NULL q_index with n_sel = 0 (never read), so pass row_ptr's address
+        qi = _ptr(row_ptr)
     _check(LIB.var_build_tile_mask(ctypes.byref(s), q_scale_begin, q_scale_end, ctypes.byref(params),
-                                   _ptr(q_index), n_sel, _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
+                                   qi, n_sel, _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
                                    _stream(dev)))
     return row_ptr, col_idx
 
@@ -239,6 +248,8 @@ def var_attn_block_sparse(schedule, q, k, v, q_scale_begin, q_scale_end, row_ptr
     s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
                                            softmax_scale, q_index, return_lse)
     n_sel = rows if q_index is not None else 0
+    if q_index is not None and n_sel == 0:
+        return (out, lse) if return_lse else out
     n_qt = -(-rows // tile_q)
     for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
         if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or t.device != q.device:

@@ -1,37 +1,47 @@
 // Block-causal next-scale attention, bf16 in / fp32 accumulate, for gfx950.
 //
-// Computes, for every query row of the call, O = softmax(scale * q K^T) V over
-// the keys the row may see: all keys of its own and earlier scales ("SparVAR:
+// For every query row of the call: O = softmax(scale * q K^T) V over the keys
+// the row may see, i.e. all keys of its own and earlier scales ("SparVAR:
 // Exploring Sparsity in Visual AutoRegressive Modeling for Training-Free
 // Acceleration", abstract: each step attends to all tokens of the historical
 // scales; "ARVAR: Accelerating Visual Autoregressive Model via Attention
 // Retrospect", Background & Motivation: a whole grid per step with a KV
-// cache).  A key u is visible to token t iff u < end of t's scale, so
-// visibility is one key limit per query.  The block-sparse variant walks the
-// kept key tiles of its query tile instead of all of them ("SparVAR ...",
-// abstract: block-wise sparse attention); the optional q_index fuses the
-// gather of pruned queries ("ARVAR ...", Key Design 2).
+// cache).  Key u is visible to token t iff u < end of t's scale: one key
+// limit per query.  The block-sparse variant visits only the kept key tiles
+// of each 64-row query tile ("SparVAR ...", abstract: block-wise sparse
+// attention); q_index fuses the gather of pruned queries ("ARVAR ...", Key
+// Design 2).
 //
-// Design (one workgroup = NW waves = 32*NW query rows of one (batch, head)):
-//  * Each wave owns 32 queries.  It computes S^T = K Q^T with
-//    v_mfma_f32_32x32x16_bf16 (keys on M, queries on N), so every lane holds
-//    16 logits of ONE query and lane l^32 holds the other 16 of a 32-key
-//    block: the row max / row sum need one cross-lane exchange per tile.
-//  * The same registers, converted to bf16, are directly the B operand of
-//    O^T += V^T P^T (d on M, queries on N, keys on K): the MFMA's k-order is
-//    matched by permuting the keys of V^T inside LDS, so P never moves.
-//  * Q stays in registers for the whole key loop (B operand of S^T).
-//  * K (row-major, 16-byte chunks XOR-swizzled) and V^T (transposed through
-//    registers, keys permuted, 16-byte chunks XOR-swizzled) are staged in a
-//    double-buffered LDS ring: one barrier per 64-key tile, the next tile's
-//    global loads in flight during the current tile's MFMAs.
+// Design (one workgroup = 4 waves = 256 query rows of one (batch, head); one
+// wave per SIMD):
+//  * Each wave owns 64 queries in two 32-query column blocks.  S^T = K Q^T is
+//    computed with v_mfma_f32_32x32x16_bf16 (keys on M, queries on N), so a
+//    lane holds 16 logits of each of its two queries and lane l^32 holds the
+//    other 16 of every 32-key block.  Every K operand read from LDS feeds two
+//    MFMAs (one per query block), halving LDS traffic per FLOP.
+//  * The same registers, rounded to bf16, are the B operand of
+//    O^T += V^T P^T (d on M, queries on N, keys on K).  The MFMA's k order is
+//    matched by permuting keys inside the V^T tile in LDS, so P never moves
+//    between lanes.  Q stays in registers for the whole key loop.
+//  * Per 64-key tile: S^T = K Q^T, the row max, then the weights of each
+//    16-key chunk are exponentiated and rounded while the matrix core runs
+//    the P V^T MFMAs of the previous chunk.  K and V of the next tile are in
+//    flight (global -> registers) during the whole tile and land in the
+//    other half of a double-buffered LDS ring (V transposed on the way): one
+//    barrier per tile.
 //  * Online softmax in the log2 domain (scale*log2(e) folded into one FMA
-//    before v_exp_f32), with lazy rescaling: the running reference max only
-//    moves when some row's max grows by more than 2^8, so O is rescaled
-//    rarely.
-//  * Workgroup ids are remapped so that the query tiles of one (batch, head)
-//    run on the same XCD and share its L2 for K and V.
+//    before v_exp_f32) with lazy rescaling: the reference max of a row moves
+//    only when the row's max grows by more than 2^8, so O is rarely rescaled.
+//    Row sums accumulate the bf16-rounded weights with v_dot2 (the same
+//    weights that multiply V).
+//  * Block-sparse: a workgroup's 4 waves cover 4 consecutive 64-row query
+//    tiles; the workgroup walks the merged (union) list of their kept key
+//    tiles and each wave computes only the tiles of its own list.
+//  * Workgroup ids are remapped so the query tiles of one (batch, head) run
+//    on one XCD and share its L2 for K and V.
 #include <hip/hip_runtime.h>
+
+#include <climits>
 
 #include "kernels.h"
 
@@ -39,10 +49,15 @@ namespace varattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+constexpr int NW = 4;                  // waves per workgroup
+constexpr int NT = NW * 64;            // threads per workgroup
+constexpr int QW = 64;                 // query rows per wave
+constexpr int QT = NW * QW;            // query rows per workgroup
 constexpr int KT = 64;                 // keys per tile (= sparse tile width)
 constexpr float kRescaleLog2 = 8.0f;   // lazy-rescale threshold (log2 units)
 
@@ -54,11 +69,6 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
     return x * q + (x < r ? x : r) + j;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
-}
 __device__ __forceinline__ int wave_min_i(int v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m));
@@ -69,8 +79,9 @@ __device__ __forceinline__ int wave_max_i(int v) {
     for (int m = 32; m >= 1; m >>= 1) v = max(v, __shfl_xor(v, m));
     return v;
 }
+__device__ __forceinline__ float swap_halves(float v) { return __shfl_xor(v, 32); }
 
-// K tile: row r (key), 16-byte chunk c -> swizzled chunk.
+// K tile: row r (key), 16-byte chunk c -> stored at chunk c ^ k_swz(r).
 template <int D>
 __device__ __forceinline__ int k_swz(int r) {
     if constexpr (D == 128) return r & 15;        // 256-byte rows
@@ -87,29 +98,35 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-template <int D, int NW, bool OUT_BF16, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const AttnParams p) {
-    constexpr int NT = NW * 64;
-    constexpr int QT = NW * 32;
+__device__ __forceinline__ float max3(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
+
+// One entry of the key-tile walk: tile index (-1 = end) and the waves that use it.
+struct TileEnt {
+    int tile;
+    int mask;
+};
+
+template <int D, bool OUT_BF16, bool SPARSE>
+__global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
     constexpr int KCH = D / 8;                 // 16-byte chunks per K row
     constexpr int K_BYTES = KT * D * 2;
     constexpr int V_BYTES = KT * D * 2;
-    constexpr int BUF = K_BYTES + V_BYTES;
-    constexpr int K_PER_T = KT * KCH / NT;     // 16-byte K chunks per thread
     constexpr int V_UNITS = (KT / 4) * (D / 4);
     constexpr int V_PER_T = V_UNITS / NT;      // 4x4 V blocks per thread
-    static_assert(K_PER_T * NT == KT * KCH, "K tile split");
+    static_assert(K_BYTES % (1024 * NW) == 0, "K tile split into 1 KB wave segments");
     static_assert(V_PER_T * NT == V_UNITS, "V tile split");
     constexpr int SK = D / 16;                 // k-steps of S^T = K Q^T
     constexpr int MO = D / 32;                 // 32-row blocks of O^T
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * BUF];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * K_BYTES + 2 * V_BYTES];
+    unsigned char* const Kbuf = smem;
+    unsigned char* const Vbuf = smem + 2 * K_BYTES;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5;      // lane half
-    const int n = lane & 31;      // query column inside the wave
+    const int n = lane & 31;      // column inside a 32-query block
 
     const int item = xcd_remap(blockIdx.x, gridDim.x);
     const int qtile = item % p.n_qtiles;
@@ -117,33 +134,47 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const AttnParams p) 
     const int b = bh / p.H;
     const int h = bh - b * p.H;
 
-    // ---- this lane's query row ------------------------------------------
-    const int my_row = qtile * QT + wave * 32 + n;
-    const bool row_valid = my_row < p.n_rows;
-    const int row_c = row_valid ? my_row : (p.n_rows - 1);
-    int pos = p.q_index ? p.q_index[row_c] : row_c;
-    pos = pos < 0 ? 0 : (pos >= p.n_q ? p.n_q - 1 : pos);
-    const int tok = p.q_first + pos;
-    int klim = p.kv_len;
-    if (!p.step_mode) {
+    // ---- this lane's two query rows ------------------------------------
+    int my_row[2], klim[2];
+    bool row_valid[2];
+    bf16x8 qreg[2][SK];
 #pragma unroll
-        for (int s = VAR_MAX_SCALES - 1; s >= 0; --s)
-            if (s < p.num_scales && tok < p.scale_end[s]) klim = p.scale_end[s];
+    for (int qb = 0; qb < 2; ++qb) {
+        my_row[qb] = qtile * QT + wave * QW + 32 * qb + n;
+        row_valid[qb] = my_row[qb] < p.n_rows;
+        const int row_c = row_valid[qb] ? my_row[qb] : (p.n_rows - 1);
+        int pos = p.q_index ? p.q_index[row_c] : row_c;
+        pos = pos < 0 ? 0 : (pos >= p.n_q ? p.n_q - 1 : pos);
+        const int tok = p.q_first + pos;
+        int kl = p.kv_len;
+        if (!p.step_mode) {
+#pragma unroll
+            for (int s = VAR_MAX_SCALES - 1; s >= 0; --s)
+                if (s < p.num_scales && tok < p.scale_end[s]) kl = p.scale_end[s];
+        }
+        klim[qb] = kl;
+        const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)pos * p.q_st;
+#pragma unroll
+        for (int ks = 0; ks < SK; ++ks)
+            qreg[qb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks + 8 * g));
     }
-    const int w_kmin = wave_min_i(klim);
-    const int w_kmax = wave_max_i(klim);
+    const int w_kmin = __builtin_amdgcn_readfirstlane(wave_min_i(min(klim[0], klim[1])));
+    const int w_kmax = __builtin_amdgcn_readfirstlane(wave_max_i(max(klim[0], klim[1])));
 
-    const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)pos * p.q_st;
-    bf16x8 qreg[SK];
-#pragma unroll
-    for (int ks = 0; ks < SK; ++ks)
-        qreg[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks + 8 * g));
-
-    // ---- key-tile list ------------------------------------------------------
-    int n_tiles, list_begin = 0;
+    // ---- key-tile walk (workgroup-uniform) ------------------------------
+    const int n_kt_all = (p.kv_len + KT - 1) / KT;
+    int dense_end = 0;      // dense: tiles [0, dense_end)
+    int dense_next = 0;
+    int lptr[NW], lend[NW], lhead[NW];   // sparse: one list per wave's query tile
     if constexpr (SPARSE) {
-        list_begin = p.row_ptr[qtile];
-        n_tiles = p.row_ptr[qtile + 1] - list_begin;
+        const int n_qt = (p.n_rows + KT - 1) / KT;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int r = qtile * NW + w;
+            lptr[w] = r < n_qt ? p.row_ptr[r] : 0;
+            lend[w] = r < n_qt ? p.row_ptr[r + 1] : 0;
+            lhead[w] = lptr[w] < lend[w] ? p.col_idx[lptr[w]] : INT_MAX;
+        }
     } else {
         int* red = reinterpret_cast<int*>(smem);
         if (lane == 0) red[wave] = w_kmax;
@@ -152,33 +183,64 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const AttnParams p) 
 #pragma unroll
         for (int i = 1; i < NW; ++i) m = max(m, red[i]);
         __syncthreads();
-        n_tiles = (m + KT - 1) / KT;
+        dense_end = (m + KT - 1) / KT;
     }
+    auto next_tile = [&]() __attribute__((always_inline)) -> TileEnt {
+        TileEnt e;
+        if constexpr (SPARSE) {
+            int c = INT_MAX;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) c = min(c, lhead[w]);
+            e.tile = -1;
+            e.mask = 0;
+            if (c != INT_MAX) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    if (lhead[w] == c) {
+                        e.mask |= 1 << w;
+                        ++lptr[w];
+                        lhead[w] = lptr[w] < lend[w] ? p.col_idx[lptr[w]] : INT_MAX;
+                    }
+                }
+                // a column outside [0, n_kt) cannot come from the mask builder; clamp so loads stay in bounds
+                e.tile = min(max(c, 0), n_kt_all - 1);
+            }
+        } else {
+            e.tile = dense_next < dense_end ? dense_next : -1;
+            e.mask = (1 << NW) - 1;
+            ++dense_next;
+        }
+        return e;
+    };
+    auto mine = [&](const TileEnt& e) __attribute__((always_inline)) -> bool {
+        if constexpr (SPARSE) return e.tile >= 0 && ((e.mask >> wave) & 1);
+        else return e.tile >= 0 && e.tile * KT < w_kmax;
+    };
 
     const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + h * p.k_sh;
     const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + h * p.v_sh;
     const int kv_last = p.kv_len - 1;
 
-    u32x4 kreg[K_PER_T];
     u32x2 vreg[V_PER_T][4];
 
-    auto tile_base = [&](int it) __attribute__((always_inline)) -> int {
-        if constexpr (SPARSE) {
-            // a column outside [0, n_kt) cannot come from the mask builder; clamp so loads stay in bounds
-            const int c = p.col_idx[list_begin + it];
-            return min(max(c, 0), (p.kv_len - 1) / KT) * KT;
-        } else {
-            return it * KT;
+    // K tile straight from global memory into LDS (no registers): each lane of a
+    // wave writes 16 bytes at lane*16 of the wave's 1 KB segment, so the
+    // swizzle is applied by choosing which global chunk each lane fetches.
+    auto load_k = [&](int kbase, int slot) __attribute__((always_inline)) {
+        constexpr int ROWS_PER_SEG = 1024 / (D * 2);
+        constexpr int SEG_PER_WAVE = K_BYTES / 1024 / NW;
+        unsigned char* Ks = Kbuf + slot * K_BYTES;
+#pragma unroll
+        for (int i = 0; i < SEG_PER_WAVE; ++i) {
+            const int seg = wave * SEG_PER_WAVE + i;
+            const int r = seg * ROWS_PER_SEG + lane / KCH;
+            const int c = (lane % KCH) ^ k_swz<D>(r);
+            const int key = min(kbase + r, kv_last);
+            __builtin_amdgcn_global_load_lds(kp + (int64_t)key * p.k_st + c * 8,
+                                             (__attribute__((address_space(3))) void*)(Ks + seg * 1024), 16, 0, 0);
         }
     };
-    auto load_tile = [&](int kbase) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < K_PER_T; ++j) {
-            const int c = tid + NT * j;
-            const int r = c / KCH, col = c % KCH;
-            const int key = min(kbase + r, kv_last);
-            kreg[j] = *reinterpret_cast<const u32x4*>(kp + (int64_t)key * p.k_st + col * 8);
-        }
+    auto load_v = [&](int kbase) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < V_PER_T; ++j) {
             const int u = tid + NT * j;
@@ -190,15 +252,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const AttnParams p) 
             }
         }
     };
-    auto store_tile = [&](int buf) __attribute__((always_inline)) {
-        unsigned char* Ks = smem + buf * BUF;
-        unsigned char* Vs = Ks + K_BYTES;
-#pragma unroll
-        for (int j = 0; j < K_PER_T; ++j) {
-            const int c = tid + NT * j;
-            const int r = c / KCH, col = c % KCH;
-            *reinterpret_cast<u32x4*>(Ks + (r * KCH + (col ^ k_swz<D>(r))) * 16) = kreg[j];
-        }
+    auto store_v = [&](int slot) __attribute__((always_inline)) {
+        unsigned char* Vs = Vbuf + slot * V_BYTES;
 #pragma unroll
         for (int j = 0; j < V_PER_T; ++j) {
             const int u = tid + NT * j;
@@ -222,103 +277,155 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const AttnParams p) 
         }
     };
 
-    f32x16 oacc[MO];
+    // S^T of one 32-key half: s[qb] holds keys kb0 + 8(r/4) + 4g + (r%4) of query 32qb + n.
+    auto qk_half = [&](int slot, int half, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        const unsigned char* Ks = Kbuf + slot * K_BYTES;
+        s[0] = s[1] = f32x16{};
+        const int r = 32 * half + n;
 #pragma unroll
-    for (int i = 0; i < MO; ++i) oacc[i] = f32x16{};
-    float mref = -INFINITY;   // reference max (raw logit units)
-    float lsum = 0.f;         // this lane's partial row sum
+        for (int ks = 0; ks < SK; ++ks) {
+            const int chunk = 2 * ks + g;
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (r * KCH + (chunk ^ k_swz<D>(r))) * 16);
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0][ks], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[1][ks], s[1], 0, 0, 0);
+        }
+    };
+
+    f32x16 oacc[MO][2];
+#pragma unroll
+    for (int i = 0; i < MO; ++i) oacc[i][0] = oacc[i][1] = f32x16{};
+    float mref[2] = {-INFINITY, -INFINITY};   // reference max per query (raw logit units)
+    float lsum[2] = {0.f, 0.f};               // this lane's partial row sums
     const float c2 = p.scale_log2;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    if (n_tiles > 0) {
-        load_tile(tile_base(0));
-        store_tile(0);
-    }
-    __syncthreads();
-
-    for (int it = 0; it < n_tiles; ++it) {
-        const int cur = it & 1;
-        const int kbase = tile_base(it);
-        const bool has_next = it + 1 < n_tiles;
-        if (has_next) load_tile(tile_base(it + 1));
-
-        if (kbase < w_kmax) {
-            const unsigned char* Ks = smem + cur * BUF;
-            const unsigned char* Vs = Ks + K_BYTES;
-            f32x16 s0 = f32x16{}, s1 = f32x16{};
+    // masking + row max + (rare) rescale of O for one 32-key half starting at kb0;
+    // returns the exponent offsets
+    auto softmax_max = [&](f32x16 (&s)[2], int kb0, float (&nb)[2]) __attribute__((always_inline)) {
+        if (kb0 + 32 > w_kmin) {
 #pragma unroll
-            for (int ks = 0; ks < SK; ++ks) {
-                const int chunk = 2 * ks + g;
-                const int r0 = n, r1 = n + 32;
-                const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(Ks + (r0 * KCH + (chunk ^ k_swz<D>(r0))) * 16);
-                const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(Ks + (r1 * KCH + (chunk ^ k_swz<D>(r1))) * 16);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], s1, 0, 0, 0);
-            }
-            // keys held by this lane: kbase + 8*(r/4) + 4*g + (r&3) (+32 for s1)
-            if (kbase + KT > w_kmin) {
+            for (int r = 0; r < 16; ++r) {
+                const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kbase + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key >= klim) s0[r] = -INFINITY;
-                    if (key + 32 >= klim) s1[r] = -INFINITY;
-                }
-            }
-            float mt = fmaxf(s0[0], s1[0]);
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const bool grow = (mt - mref) * c2 > kRescaleLog2;
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                const float mnew = fmaxf(mref, mt);
-                const float alpha = (mref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mref - mnew) * c2);
-#pragma unroll
-                for (int i = 0; i < MO; ++i) oacc[i] *= alpha;
-                lsum *= alpha;
-                mref = mnew;
-            }
-            const float nb = (mref == -INFINITY) ? 0.f : -mref * c2;
-            uint32_t pk[16];
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c2, nb));
-                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r + 1], c2, nb));
-                const float f0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c2, nb));
-                const float f1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r + 1], c2, nb));
-                lsum += (e0 + e1) + (f0 + f1);
-                pk[r / 2] = f32x2_to_bf16x2(e0, e1);
-                pk[8 + r / 2] = f32x2_to_bf16x2(f0, f1);
-            }
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                // keys 16ks..16ks+15: registers 8*(ks&1)..+7 of block ks>>1
-                const u32x4 bw = u32x4{pk[4 * ks + 0], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
-                const bf16x8 bop = __builtin_bit_cast(bf16x8, bw);
-                const int chunk = 2 * ks + g;
-#pragma unroll
-                for (int mb = 0; mb < MO; ++mb) {
-                    const int d = 32 * mb + n;
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + d * 128 + ((chunk ^ v_swz(d)) * 16));
-                    oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop, oacc[mb], 0, 0, 0);
-                }
+                for (int qb = 0; qb < 2; ++qb)
+                    if (key >= klim[qb]) s[qb][r] = -INFINITY;
             }
         }
-        if (has_next) store_tile(cur ^ 1);
+        float mt[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float ma = max3(s[qb][0], s[qb][1], s[qb][2]);
+            float mb = max3(s[qb][3], s[qb][4], s[qb][5]);
+            ma = max3(ma, s[qb][6], s[qb][7]);
+            mb = max3(mb, s[qb][8], s[qb][9]);
+            ma = max3(ma, s[qb][10], s[qb][11]);
+            mb = max3(mb, s[qb][12], s[qb][13]);
+            ma = max3(ma, s[qb][14], s[qb][15]);
+            const float m = __builtin_fmaxf(ma, mb);
+            mt[qb] = __builtin_fmaxf(m, swap_halves(m));
+        }
+        const bool grow = ((mt[0] - mref[0]) * c2 > kRescaleLog2) || ((mt[1] - mref[1]) * c2 > kRescaleLog2);
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const float mnew = __builtin_fmaxf(mref[qb], mt[qb]);
+                const float alpha = (mref[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mref[qb] - mnew) * c2);
+#pragma unroll
+                for (int i = 0; i < MO; ++i) oacc[i][qb] *= alpha;
+                lsum[qb] *= alpha;
+                mref[qb] = mnew;
+            }
+        }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) nb[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c2;
+    };
+    // weights of 16-key chunk c (0 or 1) of a half (MFMA k order): 4 bf16 pairs per query block
+    auto exp_chunk = [&](const f32x16 (&s)[2], const float (&nb)[2], int c, u32x4 (&w)[2])
+                         __attribute__((always_inline)) {
+        const int r0 = 8 * c;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r0 + 2 * i], c2, nb[qb]));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r0 + 2 * i + 1], c2, nb[qb]));
+                const uint32_t pr = f32x2_to_bf16x2(e0, e1);
+                w[qb][i] = pr;
+                lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr), ones, lsum[qb], false);
+            }
+        }
+    };
+    // O^T += V^T P^T for the 16-key chunk ks (0..3) of the tile
+    auto pv_chunk = [&](int slot, int ks, const u32x4 (&w)[2]) __attribute__((always_inline)) {
+        const unsigned char* Vs = Vbuf + slot * V_BYTES;
+        const bf16x8 b0 = __builtin_bit_cast(bf16x8, w[0]);
+        const bf16x8 b1 = __builtin_bit_cast(bf16x8, w[1]);
+        const int chunk = 2 * ks + g;
+#pragma unroll
+        for (int mb = 0; mb < MO; ++mb) {
+            const int d = 32 * mb + n;
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + d * 128 + ((chunk ^ v_swz(d)) * 16));
+            oacc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, oacc[mb][0], 0, 0, 0);
+            oacc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, oacc[mb][1], 0, 0, 0);
+        }
+    };
+
+    // ---- prologue ---------------------------------------------------------
+    TileEnt e0 = next_tile();
+    TileEnt e1 = next_tile();
+    if (e0.tile >= 0) {
+        load_k(e0.tile * KT, 0);
+        load_v(e0.tile * KT);
+        store_v(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K bytes are in LDS
+    __syncthreads();
+
+    // ---- main loop ---------------------------------------------------------
+    int j = 0;
+    while (e0.tile >= 0) {
+        const int slot = j & 1;
+        if (e1.tile >= 0) {
+            load_k(e1.tile * KT, slot ^ 1);
+            load_v(e1.tile * KT);
+        }
+        if (mine(e0)) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                f32x16 s[2];
+                float nb[2];
+                qk_half(slot, half, s);
+                softmax_max(s, e0.tile * KT + 32 * half, nb);
+                u32x4 w0[2], w1[2];
+                exp_chunk(s, nb, 0, w0);
+                exp_chunk(s, nb, 1, w1);
+                pv_chunk(slot, 2 * half, w0);
+                pv_chunk(slot, 2 * half + 1, w1);
+            }
+        }
+        if (e1.tile >= 0) store_v(slot ^ 1);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next K tile is in LDS
         __syncthreads();
+        e0 = e1;
+        e1 = next_tile();
+        ++j;
     }
 
     // ---- epilogue --------------------------------------------------------
-    const float ltot = lsum + __shfl_xor(lsum, 32);
-    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
-    if (row_valid) {
-        unsigned char* ob = reinterpret_cast<unsigned char*>(p.o);
+    unsigned char* ob = reinterpret_cast<unsigned char*>(p.o);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+        const float ltot = lsum[qb] + swap_halves(lsum[qb]);
+        const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+        if (!row_valid[qb]) continue;
 #pragma unroll
         for (int mb = 0; mb < MO; ++mb) {
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const int d0 = 32 * mb + 8 * a + 4 * g;
-                const float x0 = oacc[mb][4 * a + 0] * inv, x1 = oacc[mb][4 * a + 1] * inv;
-                const float x2 = oacc[mb][4 * a + 2] * inv, x3 = oacc[mb][4 * a + 3] * inv;
-                const int64_t e = b * p.o_sb + h * p.o_sh + (int64_t)my_row * p.o_st + d0;
+                const float x0 = oacc[mb][qb][4 * a + 0] * inv, x1 = oacc[mb][qb][4 * a + 1] * inv;
+                const float x2 = oacc[mb][qb][4 * a + 2] * inv, x3 = oacc[mb][qb][4 * a + 3] * inv;
+                const int64_t e = b * p.o_sb + h * p.o_sh + (int64_t)my_row[qb] * p.o_st + d0;
                 if constexpr (OUT_BF16) {
                     *reinterpret_cast<u32x2*>(ob + e * 2) = u32x2{f32x2_to_bf16x2(x0, x1), f32x2_to_bf16x2(x2, x3)};
                 } else {
@@ -327,16 +434,16 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(const AttnParams p) 
             }
         }
         if (p.lse && g == 0) {
-            const float l = ltot > 0.f ? mref * p.scale + __logf(ltot) : -INFINITY;
-            p.lse[(int64_t)(b * p.H + h) * p.n_rows + my_row] = l;
+            const float l = ltot > 0.f ? mref[qb] * p.scale + __logf(ltot) : -INFINITY;
+            p.lse[(int64_t)(b * p.H + h) * p.n_rows + my_row[qb]] = l;
         }
     }
 }
 
-template <int D, int NW, bool OB, bool SP>
+template <int D, bool OB, bool SP>
 hipError_t launch_one(const AttnParams& p, hipStream_t s) {
     const int grid = p.n_qtiles * p.B * p.H;
-    hipLaunchKernelGGL((attn_bf16_kernel<D, NW, OB, SP>), dim3(grid), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, OB, SP>), dim3(grid), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 
@@ -344,16 +451,17 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
 
 int attn_bf16_rows_per_tile(int head_dim, bool sparse) {
     (void)head_dim;
-    return sparse ? 64 : 128;
+    (void)sparse;
+    return QT;
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int D, bool out_bf16, bool sparse, hipStream_t s) {
     if (sparse) {
-        if (D == 128) return out_bf16 ? launch_one<128, 2, true, true>(p, s) : launch_one<128, 2, false, true>(p, s);
-        return out_bf16 ? launch_one<64, 2, true, true>(p, s) : launch_one<64, 2, false, true>(p, s);
+        if (D == 128) return out_bf16 ? launch_one<128, true, true>(p, s) : launch_one<128, false, true>(p, s);
+        return out_bf16 ? launch_one<64, true, true>(p, s) : launch_one<64, false, true>(p, s);
     }
-    if (D == 128) return out_bf16 ? launch_one<128, 4, true, false>(p, s) : launch_one<128, 4, false, false>(p, s);
-    return out_bf16 ? launch_one<64, 4, true, false>(p, s) : launch_one<64, 4, false, false>(p, s);
+    if (D == 128) return out_bf16 ? launch_one<128, true, false>(p, s) : launch_one<128, false, false>(p, s);
+    return out_bf16 ? launch_one<64, true, false>(p, s) : launch_one<64, false, false>(p, s);
 }
 
 }  // namespace varattn

@@ -11,10 +11,11 @@
 // A tile is kept if it holds one selected pair.
 //
 // Instead of enumerating pairs, each (query row, key tile) test is closed
-// form: the window maps to an integer rectangle [ylo, yhi] x [xlo, xhi] of
-// grid j, and the tile's keys of scale j form a row-major interval of that
-// grid (a partial first row, full middle rows, a partial last row); the test
-// is whether the interval meets the rectangle.
+// form: the tile's keys of scale j form a row-major interval of grid j (a
+// partial first row, full middle rows, a partial last row: three
+// rectangles), and for a rectangle the window test separates into one test
+// per axis: is there a key row y_k in [y0, y1] with y_k*h_q inside
+// [y_q*h_j - R*h_q, y_q*h_j + R*h_q] (same for columns)?
 //
 // Two launches: (1) one workgroup per query tile tests every key tile, and
 // writes its kept columns, compacted in ascending order, at col_idx[r*n_kt]
@@ -27,77 +28,97 @@
 namespace varattn {
 namespace {
 
-__device__ __forceinline__ int floor_div(int a, int b) {  // b > 0
-    int q = a / b;
-    return (a % b != 0 && a < 0) ? q - 1 : q;
-}
-__device__ __forceinline__ int ceil_div(int a, int b) {   // b > 0
-    return -floor_div(-a, b);
-}
-
-// Does the row-major interval [p0, p1) of a grid with `w` columns contain a
-// point of [ylo, yhi] x [xlo, xhi]?  (p0 < p1; rectangle already clipped.)
-__device__ __forceinline__ bool interval_meets_rect(int p0, int p1, int w, int ylo, int yhi, int xlo, int xhi) {
-    if (ylo > yhi || xlo > xhi) return false;
-    const int y0 = p0 / w, x0 = p0 % w;
-    const int y1 = (p1 - 1) / w, x1 = (p1 - 1) % w;
-    if (y0 == y1) return y0 >= ylo && y0 <= yhi && max(x0, xlo) <= min(x1, xhi);
-    if (y0 >= ylo && y0 <= yhi && max(x0, xlo) <= xhi) return true;          // partial first row
-    if (y1 >= ylo && y1 <= yhi && xlo <= min(x1, xhi)) return true;          // partial last row
-    return max(y0 + 1, ylo) <= min(y1 - 1, yhi);                              // full middle rows
+// Is there an integer y in [lo, hi] with a <= y*m <= b  (m >= 1, a <= b)?
+// For b - a >= m every long-enough window holds a multiple of m, so the test
+// reduces to interval overlap; a shorter window (radius 0) needs the exact check.
+__device__ __forceinline__ bool axis_hit(int lo, int hi, int a, int b, int m) {
+    if (lo > hi) return false;
+    const int L = max(lo * m, a), H = min(hi * m, b);
+    if (L > H) return false;
+    if (b - a >= m) return true;
+    // window shorter than one step: some multiple of m must lie in [L, H]
+    const int r = ((L % m) + m) % m;
+    return r == 0 || L + (m - r) <= H;
 }
 
-__device__ bool tile_kept(const MaskParams& p, int r, int c) {
-    const int k0 = c * p.tile_k;
-    const int k1 = min(k0 + p.tile_k, p.kv_len);
-    const int i_end = min((r + 1) * p.tile_q, p.n_rows);
-    for (int i = r * p.tile_q; i < i_end; ++i) {
-        int pos = p.q_index ? p.q_index[i] : i;
-        pos = pos < 0 ? 0 : (pos >= p.n_q ? p.n_q - 1 : pos);
-        const int t = p.q_first + pos;
-        int qs = 0;
-        while (qs + 1 < p.num_scales && t >= p.off[qs + 1]) ++qs;
-        const int hq = p.h[qs], wq = p.w[qs];
-        const int yq = (t - p.off[qs]) / wq, xq = (t - p.off[qs]) % wq;
-        // key scales overlapping [k0, k1), visible (j <= qs)
-        int j = 0;
-        while (j + 1 < p.num_scales && k0 >= p.off[j + 1]) ++j;
-        for (; j <= qs && p.off[j] < k1; ++j) {
-            const int a = max(k0, p.off[j]) - p.off[j];
-            const int e = min(k1, p.off[j + 1]) - p.off[j];
-            if (a >= e) continue;
-            if (j < p.sink_scales) return true;
-            if (j < p.local_from_scale) continue;
-            const int hj = p.h[j], wj = p.w[j];
-            const int ylo = max(0, ceil_div(yq * hj - p.radius_y * hq, hq));
-            const int yhi = min(hj - 1, floor_div(yq * hj + p.radius_y * hq, hq));
-            const int xlo = max(0, ceil_div(xq * wj - p.radius_x * wq, wq));
-            const int xhi = min(wj - 1, floor_div(xq * wj + p.radius_x * wq, wq));
-            if (interval_meets_rect(a, e, wj, ylo, yhi, xlo, xhi)) return true;
-        }
-    }
-    return false;
+// The keys of one scale inside a key tile are the row-major interval from
+// (y0, x0) to (y1, x1) of a grid with w columns: up to three rectangles
+// (partial first row, full middle rows, partial last row).  Window on key
+// rows: ya <= y_k*hq <= yb; on key columns: xa <= x_k*wq <= xb.
+__device__ __forceinline__ bool seg_hit(int y0, int x0, int y1, int x1, int w, int ya, int yb, int xa, int xb,
+                                        int hq, int wq) {
+    if (y0 == y1) return axis_hit(y0, y0, ya, yb, hq) && axis_hit(x0, x1, xa, xb, wq);
+    if (axis_hit(y0, y0, ya, yb, hq) && axis_hit(x0, w - 1, xa, xb, wq)) return true;
+    if (axis_hit(y1, y1, ya, yb, hq) && axis_hit(0, x1, xa, xb, wq)) return true;
+    return axis_hit(y0 + 1, y1 - 1, ya, yb, hq) && axis_hit(0, w - 1, xa, xb, wq);
 }
 
-// One workgroup (256 threads) per query tile.
+constexpr int kQChunk = 256;   // query rows staged in LDS at a time
+
+// One workgroup (256 threads) per query tile; thread = key tile.  The tile's
+// query rows are staged in LDS (scale, y, x) in chunks.  Each thread walks
+// the scales present in its key tile, forms that scale's segment once, and
+// tests every staged query against it with multiplications and compares.
 __global__ __launch_bounds__(256) void mask_rows_kernel(const MaskParams p) {
     __shared__ int wave_cnt[4];
     __shared__ int running;
+    __shared__ int qs_l[kQChunk], yq_l[kQChunk], xq_l[kQChunk];
     const int r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) running = 0;
-    __syncthreads();
+    const int i0 = r * p.tile_q;
+    const int i_end = min(i0 + p.tile_q, p.n_rows);
     int* out = p.col_idx + (int64_t)r * p.n_kt;
     for (int c0 = 0; c0 < p.n_kt; c0 += 256) {
         const int c = c0 + tid;
-        const bool kept = c < p.n_kt && tile_kept(p, r, c);
-        const uint64_t ballot = __ballot(kept);
+        const bool active = c < p.n_kt;
+        const int k0 = c * p.tile_k, k1 = min(k0 + p.tile_k, p.kv_len);
+        int j_first = 0;
+        if (active)
+            while (j_first + 1 < p.num_scales && k0 >= p.off[j_first + 1]) ++j_first;
+        bool kept = false;
+        for (int q0 = i0; q0 < i_end; q0 += kQChunk) {
+            const int nq = min(kQChunk, i_end - q0);
+            __syncthreads();
+            for (int t = tid; t < nq; t += 256) {
+                int pos = p.q_index ? p.q_index[q0 + t] : q0 + t;
+                pos = pos < 0 ? 0 : (pos >= p.n_q ? p.n_q - 1 : pos);
+                const int tok = p.q_first + pos;
+                int qs = 0;
+                while (qs + 1 < p.num_scales && tok >= p.off[qs + 1]) ++qs;
+                qs_l[t] = qs;
+                yq_l[t] = (tok - p.off[qs]) / p.w[qs];
+                xq_l[t] = (tok - p.off[qs]) % p.w[qs];
+            }
+            __syncthreads();
+            if (!active || kept) continue;
+            for (int j = j_first; j < p.num_scales && p.off[j] < k1 && !kept; ++j) {
+                const int a = max(k0, p.off[j]) - p.off[j];
+                const int e = min(k1, p.off[j + 1]) - p.off[j];
+                if (a >= e) continue;
+                const bool sink = j < p.sink_scales;
+                if (!sink && j < p.local_from_scale) continue;
+                const int hj = p.h[j], wj = p.w[j];
+                const int y0 = a / wj, x0 = a % wj, y1 = (e - 1) / wj, x1 = (e - 1) % wj;
+                for (int t = 0; t < nq; ++t) {
+                    const int qs = qs_l[t];
+                    if (j > qs) continue;                 // key scale not visible to this query
+                    if (sink) { kept = true; break; }
+                    const int hq = p.h[qs], wq = p.w[qs];
+                    const int yq = yq_l[t], xq = xq_l[t];
+                    const int ya = yq * hj - p.radius_y * hq, yb = yq * hj + p.radius_y * hq;
+                    const int xa = xq * wj - p.radius_x * wq, xb = xq * wj + p.radius_x * wq;
+                    if (seg_hit(y0, x0, y1, x1, wj, ya, yb, xa, xb, hq, wq)) { kept = true; break; }
+                }
+            }
+        }
+        const uint64_t ballot = __ballot(kept && active);
         const int before = __popcll(ballot & ((1ull << lane) - 1ull));
         if (lane == 0) wave_cnt[wave] = __popcll(ballot);
         __syncthreads();
         int base = running;
         for (int w = 0; w < wave; ++w) base += wave_cnt[w];
-        if (kept) out[base + before] = c;
+        if (kept && active) out[base + before] = c;
         __syncthreads();
         if (tid == 0) running += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
         __syncthreads();

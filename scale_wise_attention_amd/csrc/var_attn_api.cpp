@@ -216,11 +216,15 @@ VAR_EXPORT var_status var_attn_block_sparse(const var_schedule* sched, const var
     if (st != VAR_OK || none) return st;
     p.row_ptr = row_ptr;
     p.col_idx = col_idx;
-    p.n_qtiles = (p.n_rows + 63) / 64;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (desc->in_dtype == VAR_BF16)
+    if (desc->in_dtype == VAR_BF16) {
+        // each workgroup covers a whole number of 64-row tiles of the mask
+        const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, true);
+        p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
         return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, desc->out_dtype == VAR_BF16, true, s),
                           "var_attn_block_sparse launch");
+    }
+    p.n_qtiles = (p.n_rows + varattn::kF32RowsPerTile - 1) / varattn::kF32RowsPerTile;
     return hip_status(varattn::launch_attn_f32(p, desc->head_dim, true, s), "var_attn_block_sparse launch");
 }
 

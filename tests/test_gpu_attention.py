@@ -86,7 +86,10 @@ def test_var256_full_sequence_block_causal_and_lse(api):
     o, lse = api.var_attn_dense(_sched(wl), q, k, v, 0, wl.num_scales, return_lse=True)
     ref, ref_lse = oracle.attention(_np(q), _np(k), _np(v), wl.h, wl.w, 0, wl.num_scales, return_lse=True)
     _check(_np(o), ref, "bf16", "var256 full sequence")
-    assert np.max(np.abs(_np(lse) - ref_lse)) <= 1e-3
+    # the bf16 kernel sums the bf16-rounded weights (the ones that multiply V): each carries a
+    # relative rounding error <= 2^-9, so l is within a factor (1 +- 2^-9) and LSE within
+    # ln(1 + 2^-9) = 1.95e-3, plus fp32 rounding of the logits
+    assert np.max(np.abs(_np(lse) - ref_lse)) <= 2.5e-3
     # scale-1 query: v_0 (its only key).  The bf16 kernel folds scale*log2(e) into one FMA, so
     # its single weight is exp2(rounding error of s*c) = 1 +- 1e-6 rather than exactly 1.
     v0 = v[:, :, 0].float()
@@ -141,6 +144,10 @@ def test_empty_selection_is_a_noop(api):
     q, k, v = make_qkv(wl, 0, device="cuda")
     idx = torch.zeros(0, dtype=torch.int32, device="cuda")
     o = api.var_attn_dense(_sched(wl), q[:, :, 424:], k, v, 9, 10, q_index=idx)
+    assert o.shape == (2, 16, 0, 64)
+    rp, ci = api.var_build_tile_mask(_sched(wl), 9, 10, api.mask_params(), q_index=idx)
+    assert rp.cpu().tolist() == [0]
+    o = api.var_attn_block_sparse(_sched(wl), q[:, :, 424:], k, v, 9, 10, rp, ci, q_index=idx)
     assert o.shape == (2, 16, 0, 64)
 
 

@@ -1,0 +1,65 @@
+"""The hot path captured into a HIP graph: every replay must equal the eager run.
+
+Replays are interleaved with eager work and host synchronisations, and every
+replay is checked (not only the first)."""
+
+import pytest
+import torch
+
+import oracle
+from scale_wise_attention_amd.inputs import WORKLOADS, make_qkv, pruned_index
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replays_match_eager():
+    assert torch.cuda.is_available()
+    from scale_wise_attention_amd import api
+    wl = WORKLOADS["var512"]
+    dev = torch.device("cuda:0")
+    q, k, v = make_qkv(wl, 0, device=dev)
+    off = oracle.offsets(wl.h, wl.w)
+    K = wl.num_scales
+    s = K - 1
+    qs = q[:, :, off[s]:]
+    sel = torch.from_numpy(pruned_index(1024, 0.4, 0)).to(dev)
+    mp = api.mask_params(64, 64, 3, 3, 2, 2)
+    n_qt, n_kt = api.var_tile_mask_dims((wl.h, wl.w), s, s + 1, mp, sel.numel())
+    rp = torch.empty(n_qt + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(n_qt * n_kt, dtype=torch.int32, device=dev)
+    dense = torch.empty(2, 30, 1024, 64, dtype=torch.bfloat16, device=dev)
+    prev = torch.empty(2, 30, 576, 64, dtype=torch.bfloat16, device=dev)
+    upd = torch.empty(2, 30, sel.numel(), 64, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(2, 30, 1024, 64, dtype=torch.bfloat16, device=dev)
+
+    def run():
+        api.var_attn_dense((wl.h, wl.w), qs, k, v, s, s + 1, out=dense)
+        api.var_attn_dense((wl.h, wl.w), q[:, :, off[s - 1]:off[s]], k, v, s - 1, s, out=prev)
+        api.var_build_tile_mask((wl.h, wl.w), s, s + 1, mp, q_index=sel, row_ptr=rp, col_idx=ci)
+        api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, s, s + 1, rp, ci, out=upd, q_index=sel)
+        api.var_scatter_restore(prev, 24, 24, upd, sel, 32, 32, out=out)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (dense, rp, ci[: int(rp[-1].item())], upd, out)]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        for t in (dense, rp, ci, upd, out):
+            t.fill_(0) if t.dtype != torch.int32 else t.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (dense, rp, ci[: int(rp[-1].item())], upd, out)
+        for a, b in zip(eager, got):
+            assert torch.equal(a, b), f"replay {rep}"
+        # eager work between replays
+        _ = (q[:, :, :100].float() * 2).sum().item()
