@@ -20,6 +20,10 @@ LIB_NAME = "libvarattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["attn_bf16.hip", "attn_f32.hip", "tile_mask.hip", "scatter.hip", "var_attn_api.cpp"]
+# The bf16 attention kernels run with the IEEE mode bit off and without NaN
+# semantics (infinities stay honoured: masked logits are -inf): max/min then
+# need no NaN-quieting instructions in the softmax.
+PER_FILE_FLAGS = {"attn_bf16.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -45,7 +49,7 @@ def hipcc_path():
 
 def _compile(hipcc, src, extra):
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON_FLAGS + extra
+    cmd = [hipcc, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON_FLAGS + PER_FILE_FLAGS.get(src, []) + extra
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -29,11 +29,15 @@
 //    flight (global -> registers) during the whole tile and land in the
 //    other half of a double-buffered LDS ring (V transposed on the way): one
 //    barrier per tile.
-//  * Online softmax in the log2 domain (scale*log2(e) folded into one FMA
-//    before v_exp_f32) with lazy rescaling: the reference max of a row moves
-//    only when the row's max grows by more than 2^8, so O is rarely rescaled.
-//    Row sums accumulate the bf16-rounded weights with v_dot2 (the same
-//    weights that multiply V).
+//  * Softmax in the log2 domain (scale*log2(e) folded into one FMA before
+//    v_exp_f32) against a fixed reference max per row: the max of the row's
+//    first tile.  Later weights may exceed 1 (bounded by 2^64, exact in fp32
+//    and bf16 range), so the accumulators are never rescaled and the loop
+//    body has no control flow around them.  If some row's max ever grows by
+//    more than 64 (log2 units) the workgroup runs the pass a second time
+//    with the exact row max found by the first pass (which then cannot
+//    grow).  Row sums accumulate the bf16-rounded weights with v_dot2 (the
+//    same weights that multiply V).
 //  * Block-sparse: a workgroup's 4 waves cover 4 consecutive 64-row query
 //    tiles; the workgroup walks the merged (union) list of their kept key
 //    tiles and each wave computes only the tiles of its own list.
@@ -59,7 +63,7 @@ constexpr int NT = NW * 64;            // threads per workgroup
 constexpr int QW = 64;                 // query rows per wave
 constexpr int QT = NW * QW;            // query rows per workgroup
 constexpr int KT = 64;                 // keys per tile (= sparse tile width)
-constexpr float kRescaleLog2 = 8.0f;   // lazy-rescale threshold (log2 units)
+constexpr float kGrowLog2 = 64.0f;     // weight bound 2^64 relative to the reference max
 
 __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
     // The dispatcher places workgroup i on XCD i % 8.  Give each XCD a
@@ -93,9 +97,10 @@ __device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// round-to-nearest-even pair conversion: one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
-    const __bf16 x = (__bf16)a, y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
@@ -212,6 +217,19 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
         }
         return e;
     };
+    auto reset_walk = [&]() __attribute__((always_inline)) {
+        if constexpr (SPARSE) {
+            const int n_qt = (p.n_rows + KT - 1) / KT;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const int r = qtile * NW + w;
+                lptr[w] = r < n_qt ? p.row_ptr[r] : 0;
+                lhead[w] = lptr[w] < lend[w] ? p.col_idx[lptr[w]] : INT_MAX;
+            }
+        } else {
+            dense_next = 0;
+        }
+    };
     auto mine = [&](const TileEnt& e) __attribute__((always_inline)) -> bool {
         if constexpr (SPARSE) return e.tile >= 0 && ((e.mask >> wave) & 1);
         else return e.tile >= 0 && e.tile * KT < w_kmax;
@@ -223,32 +241,63 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
 
     u32x2 vreg[V_PER_T][4];
 
+    // Per-lane byte offsets inside a tile (rows of a 64-key tile; the host
+    // guarantees 64 rows of K and V fit 32-bit offsets).  Interior tiles add
+    // only a uniform 64-bit tile base; the tail tile clamps rows to kv_len-1.
+    constexpr int ROWS_PER_SEG = 1024 / (D * 2);
+    constexpr int SEG_PER_WAVE = K_BYTES / 1024 / NW;
+    const char* const kbytes = reinterpret_cast<const char*>(kp);
+    const char* const vbytes = reinterpret_cast<const char*>(vp);
+    uint32_t k_off[SEG_PER_WAVE];
+    int k_row[SEG_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < SEG_PER_WAVE; ++i) {
+        const int seg = wave * SEG_PER_WAVE + i;
+        k_row[i] = seg * ROWS_PER_SEG + lane / KCH;
+        const int c = (lane % KCH) ^ k_swz<D>(k_row[i]);
+        k_off[i] = (uint32_t)(k_row[i] * p.k_st + c * 8) * 2u;
+    }
+    uint32_t v_off[V_PER_T];
+    int v_row[V_PER_T];
+#pragma unroll
+    for (int j = 0; j < V_PER_T; ++j) {
+        const int u = tid + NT * j;
+        const int dg = u % (D / 4), kg = u / (D / 4);
+        v_row[j] = 4 * kg;
+        v_off[j] = (uint32_t)(4 * kg * p.v_st + 4 * dg) * 2u;
+    }
+    const uint32_t v_st_bytes = (uint32_t)p.v_st * 2u;
     // K tile straight from global memory into LDS (no registers): each lane of a
     // wave writes 16 bytes at lane*16 of the wave's 1 KB segment, so the
     // swizzle is applied by choosing which global chunk each lane fetches.
     auto load_k = [&](int kbase, int slot) __attribute__((always_inline)) {
-        constexpr int ROWS_PER_SEG = 1024 / (D * 2);
-        constexpr int SEG_PER_WAVE = K_BYTES / 1024 / NW;
         unsigned char* Ks = Kbuf + slot * K_BYTES;
+        const char* tb = kbytes + (int64_t)kbase * p.k_st * 2;
+        const bool tail = kbase + KT > p.kv_len;
 #pragma unroll
         for (int i = 0; i < SEG_PER_WAVE; ++i) {
-            const int seg = wave * SEG_PER_WAVE + i;
-            const int r = seg * ROWS_PER_SEG + lane / KCH;
-            const int c = (lane % KCH) ^ k_swz<D>(r);
-            const int key = min(kbase + r, kv_last);
-            __builtin_amdgcn_global_load_lds(kp + (int64_t)key * p.k_st + c * 8,
-                                             (__attribute__((address_space(3))) void*)(Ks + seg * 1024), 16, 0, 0);
+            uint32_t off = k_off[i];
+            if (tail) {
+                const int over = k_row[i] - (kv_last - kbase);
+                if (over > 0) off -= (uint32_t)(over * p.k_st) * 2u;
+            }
+            __builtin_amdgcn_global_load_lds(tb + off, (__attribute__((address_space(3))) void*)(Ks + (wave * SEG_PER_WAVE + i) * 1024),
+                                             16, 0, 0);
         }
     };
     auto load_v = [&](int kbase) __attribute__((always_inline)) {
+        const char* tb = vbytes + (int64_t)kbase * p.v_st * 2;
+        const bool tail = kbase + KT > p.kv_len;
 #pragma unroll
         for (int j = 0; j < V_PER_T; ++j) {
-            const int u = tid + NT * j;
-            const int dg = u % (D / 4), kg = u / (D / 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int key = min(kbase + 4 * kg + r, kv_last);
-                vreg[j][r] = *reinterpret_cast<const u32x2*>(vp + (int64_t)key * p.v_st + 4 * dg);
+                uint32_t off = v_off[j] + (uint32_t)r * v_st_bytes;
+                if (tail) {
+                    const int over = v_row[j] + r - (kv_last - kbase);
+                    if (over > 0) off -= (uint32_t)over * v_st_bytes;
+                }
+                vreg[j][r] = *reinterpret_cast<const u32x2*>(tb + off);
             }
         }
     };
@@ -295,23 +344,24 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
     for (int i = 0; i < MO; ++i) oacc[i][0] = oacc[i][1] = f32x16{};
     float mref[2] = {-INFINITY, -INFINITY};   // reference max per query (raw logit units)
+    float mall[2] = {-INFINITY, -INFINITY};   // running exact max per query
     float lsum[2] = {0.f, 0.f};               // this lane's partial row sums
+    bool grew = false;                        // some row outgrew its reference by > 2^64
     const float c2 = p.scale_log2;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    // masking + row max + (rare) rescale of O for one 32-key half starting at kb0;
-    // returns the exponent offsets
-    auto softmax_max = [&](f32x16 (&s)[2], int kb0, float (&nb)[2]) __attribute__((always_inline)) {
-        if (kb0 + 32 > w_kmin) {
+    // keys at or past `lim` are hidden (-inf) in one 32-key half starting at kb0
+    auto apply_mask = [&](f32x16 (&s)[2], int kb0, const int (&lim)[2]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        for (int r = 0; r < 16; ++r) {
+            const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
 #pragma unroll
-                for (int qb = 0; qb < 2; ++qb)
-                    if (key >= klim[qb]) s[qb][r] = -INFINITY;
-            }
+            for (int qb = 0; qb < 2; ++qb)
+                if (key >= lim[qb]) s[qb][r] = -INFINITY;
         }
-        float mt[2];
+    };
+    // row max and reference update for one 32-key half; returns the exponent offsets
+    auto softmax_max = [&](const f32x16 (&s)[2], float (&nb)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             float ma = max3(s[qb][0], s[qb][1], s[qb][2]);
@@ -321,23 +371,14 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
             ma = max3(ma, s[qb][10], s[qb][11]);
             mb = max3(mb, s[qb][12], s[qb][13]);
             ma = max3(ma, s[qb][14], s[qb][15]);
-            const float m = __builtin_fmaxf(ma, mb);
-            mt[qb] = __builtin_fmaxf(m, swap_halves(m));
+            float m = __builtin_fmaxf(ma, mb);
+            m = __builtin_fmaxf(m, swap_halves(m));
+            // the first finite max becomes the reference; later growth is only recorded
+            grew |= (mref[qb] != -INFINITY) && ((m - mref[qb]) * c2 > kGrowLog2);
+            mref[qb] = (mref[qb] == -INFINITY) ? m : mref[qb];
+            mall[qb] = __builtin_fmaxf(mall[qb], m);
+            nb[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c2;
         }
-        const bool grow = ((mt[0] - mref[0]) * c2 > kRescaleLog2) || ((mt[1] - mref[1]) * c2 > kRescaleLog2);
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                const float mnew = __builtin_fmaxf(mref[qb], mt[qb]);
-                const float alpha = (mref[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mref[qb] - mnew) * c2);
-#pragma unroll
-                for (int i = 0; i < MO; ++i) oacc[i][qb] *= alpha;
-                lsum[qb] *= alpha;
-                mref[qb] = mnew;
-            }
-        }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) nb[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c2;
     };
     // weights of 16-key chunk c (0 or 1) of a half (MFMA k order): 4 bf16 pairs per query block
     auto exp_chunk = [&](const f32x16 (&s)[2], const float (&nb)[2], int c, u32x4 (&w)[2])
@@ -370,45 +411,78 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
         }
     };
 
-    // ---- prologue ---------------------------------------------------------
-    TileEnt e0 = next_tile();
-    TileEnt e1 = next_tile();
-    if (e0.tile >= 0) {
-        load_k(e0.tile * KT, 0);
-        load_v(e0.tile * KT);
-        store_v(0);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K bytes are in LDS
-    __syncthreads();
-
-    // ---- main loop ---------------------------------------------------------
-    int j = 0;
-    while (e0.tile >= 0) {
-        const int slot = j & 1;
-        if (e1.tile >= 0) {
-            load_k(e1.tile * KT, slot ^ 1);
-            load_v(e1.tile * KT);
-        }
-        if (mine(e0)) {
+    // ---- walk the key tiles; a second attempt only if a reference max was outgrown
+    int* flag = reinterpret_cast<int*>(Kbuf);   // used only between walks, when LDS is idle
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        if (attempt == 1) {
+            // restart with the exact row max of the first attempt: no weight exceeds 1
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                f32x16 s[2];
-                float nb[2];
-                qk_half(slot, half, s);
-                softmax_max(s, e0.tile * KT + 32 * half, nb);
-                u32x4 w0[2], w1[2];
-                exp_chunk(s, nb, 0, w0);
-                exp_chunk(s, nb, 1, w1);
-                pv_chunk(slot, 2 * half, w0);
-                pv_chunk(slot, 2 * half + 1, w1);
+            for (int qb = 0; qb < 2; ++qb) {
+                mref[qb] = mall[qb];
+                lsum[qb] = 0.f;
+#pragma unroll
+                for (int i = 0; i < MO; ++i) oacc[i][qb] = f32x16{};
             }
+            reset_walk();
         }
-        if (e1.tile >= 0) store_v(slot ^ 1);
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next K tile is in LDS
+        TileEnt e0 = next_tile();
+        TileEnt e1 = next_tile();
+        if (e0.tile >= 0) {
+            load_k(e0.tile * KT, 0);
+            load_v(e0.tile * KT);
+            store_v(0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K bytes are in LDS
         __syncthreads();
-        e0 = e1;
-        e1 = next_tile();
-        ++j;
+
+        int j = 0;
+        while (e0.tile >= 0) {
+            const int slot = j & 1;
+            if (e1.tile >= 0) {
+                load_k(e1.tile * KT, slot ^ 1);
+                load_v(e1.tile * KT);
+            }
+            // a tile outside this wave's own list is computed fully masked
+            const bool own = mine(e0);
+            const int lim[2] = {own ? klim[0] : -1, own ? klim[1] : -1};
+            const int wlim = own ? w_kmin : -1;
+            const int kb = e0.tile * KT;
+            // the only branches sit on the logits (after QK of each half), never
+            // around the accumulators, so O stays in place in AGPRs
+            const bool need_mask = kb + KT > wlim;
+            f32x16 s0[2], s1[2];
+            float nb0[2], nb1[2];
+            u32x4 w00[2], w01[2], w10[2], w11[2];
+            qk_half(slot, 0, s0);
+            if (need_mask) apply_mask(s0, kb, lim);
+            softmax_max(s0, nb0);
+            qk_half(slot, 1, s1);
+            exp_chunk(s0, nb0, 0, w00);
+            exp_chunk(s0, nb0, 1, w01);
+            if (need_mask) apply_mask(s1, kb + 32, lim);
+            softmax_max(s1, nb1);
+            pv_chunk(slot, 0, w00);
+            pv_chunk(slot, 1, w01);
+            exp_chunk(s1, nb1, 0, w10);
+            exp_chunk(s1, nb1, 1, w11);
+            pv_chunk(slot, 2, w10);
+            pv_chunk(slot, 3, w11);
+            if (e1.tile >= 0) store_v(slot ^ 1);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next K tile is in LDS
+            __syncthreads();
+            e0 = e1;
+            e1 = next_tile();
+            ++j;
+        }
+        if (attempt == 1) break;
+        // the loop ended on a barrier with no load in flight: the K slots are free
+        if (tid == 0) *flag = 0;
+        __syncthreads();
+        if (__builtin_amdgcn_ballot_w64(grew) && lane == 0) *flag = 1;
+        __syncthreads();
+        const int again = *flag;
+        __syncthreads();
+        if (!again) break;
     }
 
     // ---- epilogue --------------------------------------------------------
