@@ -30,14 +30,16 @@
 //    other half of a double-buffered LDS ring (V transposed on the way): one
 //    barrier per tile.
 //  * Softmax in the log2 domain (scale*log2(e) folded into one FMA before
-//    v_exp_f32) against a fixed reference max per row: the max of the row's
-//    first tile.  Later weights may exceed 1 (bounded by 2^64, exact in fp32
-//    and bf16 range), so the accumulators are never rescaled and the loop
-//    body has no control flow around them.  If some row's max ever grows by
-//    more than 64 (log2 units) the workgroup runs the pass a second time
-//    with the exact row max found by the first pass (which then cannot
-//    grow).  Row sums accumulate the bf16-rounded weights with v_dot2 (the
-//    same weights that multiply V).
+//    v_exp_f32) against a fixed reference max per row: the max of the first
+//    tile in which the row sees a key.  Later weights may exceed 1 (fp32 and
+//    bf16 keep the full exponent range), so the accumulators are never
+//    rescaled, the loop body has no control flow around them and, once
+//    every row has its reference, no row max is computed at all.  A row
+//    whose sum ends up above 2^100 (or non-finite) had logits far above its
+//    reference: then the workgroup recomputes, first the exact row maxima
+//    (QK only), then the weights against them (all <= 1).  Row sums
+//    accumulate the bf16-rounded weights with v_dot2 (the same weights that
+//    multiply V).
 //  * Block-sparse: a workgroup's 4 waves cover 4 consecutive 64-row query
 //    tiles; the workgroup walks the merged (union) list of their kept key
 //    tiles and each wave computes only the tiles of its own list.
@@ -63,7 +65,7 @@ constexpr int NT = NW * 64;            // threads per workgroup
 constexpr int QW = 64;                 // query rows per wave
 constexpr int QT = NW * QW;            // query rows per workgroup
 constexpr int KT = 64;                 // keys per tile (= sparse tile width)
-constexpr float kGrowLog2 = 64.0f;     // weight bound 2^64 relative to the reference max
+constexpr float kSumLimit = 0x1p100f;  // a row sum above this triggers the exact recompute
 
 __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
     // The dispatcher places workgroup i on XCD i % 8.  Give each XCD a
@@ -104,6 +106,16 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
 }
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
+
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
+template <bool B>
+struct BoolC {
+    static constexpr bool value = B;
+};
 
 // One entry of the key-tile walk: tile index (-1 = end) and the waves that use it.
 struct TileEnt {
@@ -180,15 +192,24 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
             lend[w] = r < n_qt ? p.row_ptr[r + 1] : 0;
             lhead[w] = lptr[w] < lend[w] ? p.col_idx[lptr[w]] : INT_MAX;
         }
-    } else {
+    }
+    int wg_kmin;   // smallest key limit in the workgroup: tiles below it need no mask
+    {
         int* red = reinterpret_cast<int*>(smem);
-        if (lane == 0) red[wave] = w_kmax;
+        if (lane == 0) {
+            red[wave] = w_kmax;
+            red[NW + wave] = w_kmin;
+        }
         __syncthreads();
-        int m = red[0];
+        int m = red[0], mn = red[NW];
 #pragma unroll
-        for (int i = 1; i < NW; ++i) m = max(m, red[i]);
+        for (int i = 1; i < NW; ++i) {
+            m = max(m, red[i]);
+            mn = min(mn, red[NW + i]);
+        }
         __syncthreads();
-        dense_end = (m + KT - 1) / KT;
+        if constexpr (!SPARSE) dense_end = __builtin_amdgcn_readfirstlane((m + KT - 1) / KT);
+        wg_kmin = __builtin_amdgcn_readfirstlane(mn);
     }
     auto next_tile = [&]() __attribute__((always_inline)) -> TileEnt {
         TileEnt e;
@@ -242,64 +263,57 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
     u32x2 vreg[V_PER_T][4];
 
     // Per-lane byte offsets inside a tile (rows of a 64-key tile; the host
-    // guarantees 64 rows of K and V fit 32-bit offsets).  Interior tiles add
-    // only a uniform 64-bit tile base; the tail tile clamps rows to kv_len-1.
+    // guarantees 64 rows of K and V fit 32-bit offsets).  Every offset is
+    // formed as a non-negative 32-bit value before it is added to a tile's
+    // 64-bit base.  Interior tiles use precomputed offsets; the tail tile
+    // clamps rows to kv_len-1 (those keys are masked later).
     constexpr int ROWS_PER_SEG = 1024 / (D * 2);
     constexpr int SEG_PER_WAVE = K_BYTES / 1024 / NW;
     const char* const kbytes = reinterpret_cast<const char*>(kp);
     const char* const vbytes = reinterpret_cast<const char*>(vp);
-    uint32_t k_off[SEG_PER_WAVE];
-    int k_row[SEG_PER_WAVE];
+    const uint32_t k_st_bytes = (uint32_t)p.k_st * 2u;
+    const uint32_t v_st_bytes = (uint32_t)p.v_st * 2u;
+    uint32_t k_col[SEG_PER_WAVE];   // byte offset of this lane's 16-byte chunk in its row
+    int k_row[SEG_PER_WAVE];        // row of the tile this lane fetches
 #pragma unroll
     for (int i = 0; i < SEG_PER_WAVE; ++i) {
         const int seg = wave * SEG_PER_WAVE + i;
         k_row[i] = seg * ROWS_PER_SEG + lane / KCH;
-        const int c = (lane % KCH) ^ k_swz<D>(k_row[i]);
-        k_off[i] = (uint32_t)(k_row[i] * p.k_st + c * 8) * 2u;
+        k_col[i] = (uint32_t)(((lane % KCH) ^ k_swz<D>(k_row[i])) * 16);
     }
-    uint32_t v_off[V_PER_T];
+    uint32_t v_col[V_PER_T];
     int v_row[V_PER_T];
 #pragma unroll
     for (int j = 0; j < V_PER_T; ++j) {
         const int u = tid + NT * j;
         const int dg = u % (D / 4), kg = u / (D / 4);
         v_row[j] = 4 * kg;
-        v_off[j] = (uint32_t)(4 * kg * p.v_st + 4 * dg) * 2u;
+        v_col[j] = (uint32_t)(8 * dg);
     }
-    const uint32_t v_st_bytes = (uint32_t)p.v_st * 2u;
     // K tile straight from global memory into LDS (no registers): each lane of a
     // wave writes 16 bytes at lane*16 of the wave's 1 KB segment, so the
     // swizzle is applied by choosing which global chunk each lane fetches.
     auto load_k = [&](int kbase, int slot) __attribute__((always_inline)) {
         unsigned char* Ks = Kbuf + slot * K_BYTES;
         const char* tb = kbytes + (int64_t)kbase * p.k_st * 2;
-        const bool tail = kbase + KT > p.kv_len;
+        const int last = min(kv_last - kbase, KT - 1);   // last valid row of this tile
 #pragma unroll
         for (int i = 0; i < SEG_PER_WAVE; ++i) {
-            uint32_t off = k_off[i];
-            if (tail) {
-                const int over = k_row[i] - (kv_last - kbase);
-                if (over > 0) off -= (uint32_t)(over * p.k_st) * 2u;
-            }
+            const uint32_t off = (uint32_t)min(k_row[i], last) * k_st_bytes + k_col[i];
             __builtin_amdgcn_global_load_lds(tb + off, (__attribute__((address_space(3))) void*)(Ks + (wave * SEG_PER_WAVE + i) * 1024),
                                              16, 0, 0);
         }
     };
     auto load_v = [&](int kbase) __attribute__((always_inline)) {
         const char* tb = vbytes + (int64_t)kbase * p.v_st * 2;
-        const bool tail = kbase + KT > p.kv_len;
+        const int last = min(kv_last - kbase, KT - 1);
 #pragma unroll
-        for (int j = 0; j < V_PER_T; ++j) {
+        for (int j = 0; j < V_PER_T; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                uint32_t off = v_off[j] + (uint32_t)r * v_st_bytes;
-                if (tail) {
-                    const int over = v_row[j] + r - (kv_last - kbase);
-                    if (over > 0) off -= (uint32_t)over * v_st_bytes;
-                }
+                const uint32_t off = (uint32_t)min(v_row[j] + r, last) * v_st_bytes + v_col[j];
                 vreg[j][r] = *reinterpret_cast<const u32x2*>(tb + off);
             }
-        }
     };
     auto store_v = [&](int slot) __attribute__((always_inline)) {
         unsigned char* Vs = Vbuf + slot * V_BYTES;
@@ -344,9 +358,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
     for (int i = 0; i < MO; ++i) oacc[i][0] = oacc[i][1] = f32x16{};
     float mref[2] = {-INFINITY, -INFINITY};   // reference max per query (raw logit units)
-    float mall[2] = {-INFINITY, -INFINITY};   // running exact max per query
+    float nb[2] = {0.f, 0.f};                 // -mref * scale * log2(e)
     float lsum[2] = {0.f, 0.f};               // this lane's partial row sums
-    bool grew = false;                        // some row outgrew its reference by > 2^64
+    bool need_ref = true;                     // some row of the wave has no reference yet
     const float c2 = p.scale_log2;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -360,8 +374,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                 if (key >= lim[qb]) s[qb][r] = -INFINITY;
         }
     };
-    // row max and reference update for one 32-key half; returns the exponent offsets
-    auto softmax_max = [&](const f32x16 (&s)[2], float (&nb)[2]) __attribute__((always_inline)) {
+    // row max of one 32-key half (both query blocks), across the lane pair
+    auto half_max = [&](const f32x16 (&s)[2], float (&mt)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             float ma = max3(s[qb][0], s[qb][1], s[qb][2]);
@@ -371,17 +385,23 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
             ma = max3(ma, s[qb][10], s[qb][11]);
             mb = max3(mb, s[qb][12], s[qb][13]);
             ma = max3(ma, s[qb][14], s[qb][15]);
-            float m = __builtin_fmaxf(ma, mb);
-            m = __builtin_fmaxf(m, swap_halves(m));
-            // the first finite max becomes the reference; later growth is only recorded
-            grew |= (mref[qb] != -INFINITY) && ((m - mref[qb]) * c2 > kGrowLog2);
-            mref[qb] = (mref[qb] == -INFINITY) ? m : mref[qb];
-            mall[qb] = __builtin_fmaxf(mall[qb], m);
-            nb[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c2;
+            const float m = __builtin_fmaxf(ma, mb);
+            mt[qb] = __builtin_fmaxf(m, swap_halves(m));
         }
     };
+    // rows without a reference yet take this half's max as their reference
+    auto set_reference = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) {
+        float mt[2];
+        half_max(s, mt);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            mref[qb] = (mref[qb] == -INFINITY) ? mt[qb] : mref[qb];
+            nb[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c2;
+        }
+        need_ref = __builtin_amdgcn_ballot_w64(mref[0] == -INFINITY || mref[1] == -INFINITY) != 0;
+    };
     // weights of 16-key chunk c (0 or 1) of a half (MFMA k order): 4 bf16 pairs per query block
-    auto exp_chunk = [&](const f32x16 (&s)[2], const float (&nb)[2], int c, u32x4 (&w)[2])
+    auto exp_chunk = [&](const f32x16 (&s)[2], int c, u32x4 (&w)[2])
                          __attribute__((always_inline)) {
         const int r0 = 8 * c;
 #pragma unroll
@@ -411,78 +431,140 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
         }
     };
 
-    // ---- walk the key tiles; a second attempt only if a reference max was outgrown
-    int* flag = reinterpret_cast<int*>(Kbuf);   // used only between walks, when LDS is idle
-    for (int attempt = 0; attempt < 2; ++attempt) {
-        if (attempt == 1) {
-            // restart with the exact row max of the first attempt: no weight exceeds 1
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
-                mref[qb] = mall[qb];
-                lsum[qb] = 0.f;
-#pragma unroll
-                for (int i = 0; i < MO; ++i) oacc[i][qb] = f32x16{};
-            }
-            reset_walk();
-        }
+    // ---- walk the key tiles -----------------------------------------------
+    // mode 0: weights against the per-row reference (the fast path)
+    // mode 1: exact row maxima only (QK, no weights); they become the references
+    //
+    // Tiles that every wave owns and that need no mask run a branch-free body
+    // (QK of the second half overlaps the exponentials of the first, the
+    // exponentials of the second overlap the P V^T of the first); the first
+    // tile (which sets the references) and masked or partly owned tiles run a
+    // general body.  The two bodies sit in separate loops, so the
+    // accumulators only flow from one loop into the next.
+    auto walk = [&](auto mode_tag) __attribute__((always_inline)) {
+        constexpr int MODE = decltype(mode_tag)::value;
+        reset_walk();
         TileEnt e0 = next_tile();
         TileEnt e1 = next_tile();
         if (e0.tile >= 0) {
             load_k(e0.tile * KT, 0);
-            load_v(e0.tile * KT);
-            store_v(0);
+            if constexpr (MODE == 0) {
+                load_v(e0.tile * KT);
+                store_v(0);
+            }
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K bytes are in LDS
         __syncthreads();
 
         int j = 0;
-        while (e0.tile >= 0) {
+        auto fast = [&](const TileEnt& e) __attribute__((always_inline)) -> bool {
+            return j > 0 && e.mask == (1 << NW) - 1 && e.tile * KT + KT <= wg_kmin;
+        };
+        auto iterate = [&](auto fast_tag) __attribute__((always_inline)) {
+            constexpr bool FAST = decltype(fast_tag)::value;
             const int slot = j & 1;
             if (e1.tile >= 0) {
                 load_k(e1.tile * KT, slot ^ 1);
-                load_v(e1.tile * KT);
+                if constexpr (MODE == 0) load_v(e1.tile * KT);
             }
-            // a tile outside this wave's own list is computed fully masked
-            const bool own = mine(e0);
-            const int lim[2] = {own ? klim[0] : -1, own ? klim[1] : -1};
-            const int wlim = own ? w_kmin : -1;
             const int kb = e0.tile * KT;
-            // the only branches sit on the logits (after QK of each half), never
-            // around the accumulators, so O stays in place in AGPRs
-            const bool need_mask = kb + KT > wlim;
             f32x16 s0[2], s1[2];
-            float nb0[2], nb1[2];
-            u32x4 w00[2], w01[2], w10[2], w11[2];
-            qk_half(slot, 0, s0);
-            if (need_mask) apply_mask(s0, kb, lim);
-            softmax_max(s0, nb0);
-            qk_half(slot, 1, s1);
-            exp_chunk(s0, nb0, 0, w00);
-            exp_chunk(s0, nb0, 1, w01);
-            if (need_mask) apply_mask(s1, kb + 32, lim);
-            softmax_max(s1, nb1);
-            pv_chunk(slot, 0, w00);
-            pv_chunk(slot, 1, w01);
-            exp_chunk(s1, nb1, 0, w10);
-            exp_chunk(s1, nb1, 1, w11);
-            pv_chunk(slot, 2, w10);
-            pv_chunk(slot, 3, w11);
-            if (e1.tile >= 0) store_v(slot ^ 1);
+            if constexpr (MODE == 0 && FAST) {
+                u32x4 w00[2], w01[2], w10[2], w11[2];
+                qk_half(slot, 0, s0);
+                qk_half(slot, 1, s1);
+                exp_chunk(s0, 0, w00);
+                exp_chunk(s0, 1, w01);
+                pv_chunk(slot, 0, w00);
+                pv_chunk(slot, 1, w01);
+                exp_chunk(s1, 0, w10);
+                exp_chunk(s1, 1, w11);
+                pv_chunk(slot, 2, w10);
+                pv_chunk(slot, 3, w11);
+            } else {
+                // a tile outside this wave's own list is computed fully masked
+                const bool own = mine(e0);
+                const int lim[2] = {own ? klim[0] : -1, own ? klim[1] : -1};
+                const bool need_mask = kb + KT > (own ? w_kmin : -1);
+                if constexpr (MODE == 0) {
+                    u32x4 w00[2], w01[2], w10[2], w11[2];
+                    qk_half(slot, 0, s0);
+                    if (need_mask) apply_mask(s0, kb, lim);
+                    if (need_ref) set_reference(s0);
+                    qk_half(slot, 1, s1);
+                    if (need_mask) apply_mask(s1, kb + 32, lim);
+                    if (need_ref) set_reference(s1);
+                    exp_chunk(s0, 0, w00);
+                    exp_chunk(s0, 1, w01);
+                    exp_chunk(s1, 0, w10);
+                    exp_chunk(s1, 1, w11);
+                    pv_chunk(slot, 0, w00);
+                    pv_chunk(slot, 1, w01);
+                    pv_chunk(slot, 2, w10);
+                    pv_chunk(slot, 3, w11);
+                } else {
+                    float mt[2];
+                    qk_half(slot, 0, s0);
+                    if (need_mask) apply_mask(s0, kb, lim);
+                    half_max(s0, mt);
+                    mref[0] = __builtin_fmaxf(mref[0], mt[0]);
+                    mref[1] = __builtin_fmaxf(mref[1], mt[1]);
+                    qk_half(slot, 1, s1);
+                    if (need_mask) apply_mask(s1, kb + 32, lim);
+                    half_max(s1, mt);
+                    mref[0] = __builtin_fmaxf(mref[0], mt[0]);
+                    mref[1] = __builtin_fmaxf(mref[1], mt[1]);
+                }
+            }
+            if constexpr (MODE == 0) {
+                if (e1.tile >= 0) store_v(slot ^ 1);
+            }
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next K tile is in LDS
             __syncthreads();
             e0 = e1;
             e1 = next_tile();
             ++j;
+        };
+        while (e0.tile >= 0) {
+            if constexpr (MODE == 0) {
+                while (e0.tile >= 0 && fast(e0)) iterate(BoolC<true>{});
+            }
+            while (e0.tile >= 0 && (MODE != 0 || !fast(e0))) iterate(BoolC<false>{});
         }
-        if (attempt == 1) break;
-        // the loop ended on a barrier with no load in flight: the K slots are free
+    };
+
+    walk(IntC<0>{});
+    // a row sum above 2^100 (or inf/nan) means logits far above the row's
+    // reference: recompute against the exact row maxima (rare; workgroup-wide)
+    {
+        bool bad = false;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float ltot = lsum[qb] + swap_halves(lsum[qb]);
+            // a sum out of range, or a row that saw keys only in branch-free
+            // tiles before it had a reference, needs the exact recompute
+            bad |= !(ltot <= kSumLimit) || (mref[qb] == -INFINITY && ltot > 0.f);
+        }
+        int* flag = reinterpret_cast<int*>(Kbuf);   // the walk ended on a barrier: LDS is idle
         if (tid == 0) *flag = 0;
         __syncthreads();
-        if (__builtin_amdgcn_ballot_w64(grew) && lane == 0) *flag = 1;
+        if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) *flag = 1;
         __syncthreads();
         const int again = *flag;
         __syncthreads();
-        if (!again) break;
+        if (again) {
+            mref[0] = mref[1] = -INFINITY;
+            walk(IntC<1>{});
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                nb[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c2;
+                lsum[qb] = 0.f;
+#pragma unroll
+                for (int i = 0; i < MO; ++i) oacc[i][qb] = f32x16{};
+            }
+            need_ref = false;
+            walk(IntC<0>{});
+        }
     }
 
     // ---- epilogue --------------------------------------------------------

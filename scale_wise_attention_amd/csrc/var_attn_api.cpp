@@ -75,6 +75,9 @@ var_status check_layout(const char* name, const var_layout& l, int D, int elem_b
                     (long long)l.batch, (long long)l.head, (long long)l.token, D);
     if (l.batch % m || l.head % m || l.token % m)
         return fail(VAR_ERR_STRIDE, "%s strides must be multiples of %lld elements", name, (long long)m);
+    // the kernels address the rows of one 64-key tile with 32-bit byte offsets
+    if (l.token * elem_bytes * 64 >= ((int64_t)1 << 31))
+        return fail(VAR_ERR_STRIDE, "%s token stride %lld too large", name, (long long)l.token);
     return VAR_OK;
 }
 
