@@ -61,8 +61,8 @@ def _read_traffic():
 
 
 def cpu_baseline(wl, q, k, v, heads):
-    """The oracle (as it stands) on a bounded sample: the dense last step for `heads` (b, h) pairs."""
-    import numpy as np
+    """The oracle (as it stands) on a bounded sample of the same workload: the
+    dense generation (all 13 steps) for `heads` (batch, head) pairs."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -73,19 +73,21 @@ def cpu_baseline(wl, q, k, v, heads):
     off = [0]
     for g in wl.grids:
         off.append(off[-1] + g * g)
-    qn = q[:, :, off[K - 1]:off[K]].float().cpu().numpy()
+    qn = q.float().cpu().numpy()
     kn = k.float().cpu().numpy()
     vn = v.float().cpu().numpy()
     pairs = [(b, h) for b in range(wl.batch) for h in range(wl.heads)][:heads]
-    n, L = off[K] - off[K - 1], off[K]
+    flops = 0.0
     t0 = time.perf_counter()
     for (b, h) in pairs:
-        oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], wl.h, wl.w, K - 1, K)
+        for s in range(K):
+            oracle.attention(qn[b:b + 1, h:h + 1, off[s]:off[s + 1]], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1],
+                             wl.h, wl.w, s, s + 1)
+            flops += 4.0 * wl.head_dim * (off[s + 1] - off[s]) * off[s + 1]
     dt = time.perf_counter() - t0
-    flops = 4.0 * wl.head_dim * n * L * len(pairs)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"dense last step (4096 queries x 10521 keys, D=128) for {len(pairs)} of 32 (batch, head) "
-                      f"pairs, NumPy float64: {dt:.2f} s",
+            "sample": f"dense generation (13 steps, 10521 tokens, D=128) for {len(pairs)} of 32 (batch, head) "
+                      f"pairs, NumPy float64: {flops / 1e9:.1f} GFLOP in {dt:.2f} s",
             "seconds": dt}
 
 
@@ -95,7 +97,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--reps", type=int, default=20, help="repetitions per launch for the per-step timings")
-    ap.add_argument("--cpu-heads", type=int, default=8, help="(b, h) pairs in the oracle's CPU sample")
+    ap.add_argument("--cpu-heads", type=int, default=32, help="(b, h) pairs in the oracle's CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
     args = ap.parse_args()
@@ -227,36 +229,56 @@ def main():
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     value = pass_flops / (ms_per_step * 1e-3) / 1e12
 
-    # ---- per-launch timings (events on the launch stream, median of reps) --
-    def time_launch(fn, reps):
-        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for a, b in es:
-            a.record()
-            fn()
-            b.record()
-        torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in es]
-
+    # ---- per-launch timings -------------------------------------------------
+    # Each launch group is captured `reps` times back to back into one HIP
+    # graph; replaying it between two events on the launch stream gives the
+    # kernel time per launch without host launch latency (as a kernel trace
+    # sees it, plus the small gaps between graph nodes).
     R = args.reps
-    dense_ms = [statistics.median(time_launch(lambda s=s: dense_step(s), R)) for s in range(K)]
-    mask_ms = [statistics.median(time_launch(lambda s=s: mask_step(s), R)) for s in range(K)]
-    sparse_ms = [statistics.median(time_launch(lambda s=s: sparse_step(s), R)) for s in range(K)]
-    scatter_ms = statistics.median(time_launch(scatter_step, R))
-    sparse_full_ms = statistics.median(time_launch(sparse_full_last_step, R))
-    sparse_full_flops = acc.sparse_step_flops(wl, full_rp.cpu().numpy(), full_ci.cpu().numpy(), 4096, off[K])
 
-    def gen_time_ms(fn):
-        for _ in range(3):
+    def graph_of(fn, reps):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
             fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(R):
-            fn()
-        b.record()
+        torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / R
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        torch.cuda.synchronize()
+        return g
 
-    dense_gen_ms = gen_time_ms(lambda: [dense_step(s) for s in range(K)])
+    def time_launch(fn, reps=R, replays=3):
+        if graph is None:       # eager fallback: events around each launch
+            es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in es:
+                a.record()
+                fn()
+                b.record()
+            torch.cuda.synchronize()
+            return statistics.median([a.elapsed_time(b) for a, b in es])
+        g = graph_of(fn, reps)
+        g.replay()
+        torch.cuda.synchronize()
+        vals = []
+        for _ in range(replays):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            vals.append(a.elapsed_time(b) / reps)
+        return statistics.median(vals)
+
+    dense_ms = [time_launch(lambda s=s: dense_step(s)) for s in range(K)]
+    mask_ms = [time_launch(lambda s=s: mask_step(s)) for s in range(K)]
+    sparse_ms = [time_launch(lambda s=s: sparse_step(s)) for s in range(K)]
+    scatter_ms = time_launch(scatter_step)
+    sparse_full_ms = time_launch(sparse_full_last_step)
+    sparse_full_flops = acc.sparse_step_flops(wl, full_rp.cpu().numpy(), full_ci.cpu().numpy(), 4096, off[K])
+    dense_gen_ms = time_launch(lambda: [dense_step(s) for s in range(K)], reps=max(2, R // 4))
 
     def sparse_gen():
         for s in range(K):
@@ -264,7 +286,7 @@ def main():
             sparse_step(s)
         scatter_step()
 
-    sparse_gen_ms = gen_time_ms(sparse_gen)
+    sparse_gen_ms = time_launch(sparse_gen, reps=max(2, R // 4))
 
     # dominant kernel: the dense bf16 attention kernel, averaged over its launches in one step
     avg_launch_ms = sum(dense_ms) / K
