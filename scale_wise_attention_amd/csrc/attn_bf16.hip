@@ -96,8 +96,9 @@ __device__ __forceinline__ int k_swz(int r) {
 // V^T tile: 128-byte rows (64 keys), row = d.
 __device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xffffu) | (b << 16); }
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xffff0000u); }
+// low halves of a and b -> (a.lo, b.lo); high halves -> (a.hi, b.hi): one v_perm_b32 each
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 // round-to-nearest-even pair conversion: one v_cvt_pk_bf16_f32
@@ -172,8 +173,12 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
         klim[qb] = kl;
         const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)pos * p.q_st;
 #pragma unroll
-        for (int ks = 0; ks < SK; ++ks)
+        for (int ks = 0; ks < SK; ++ks) {
             qreg[qb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks + 8 * g));
+            // Q is only ever an MFMA operand: keep it in AGPRs (MFMAs read them
+            // directly), which leaves the VGPRs to the softmax and the loads
+            asm volatile("" : "+a"(qreg[qb][ks]));
+        }
     }
     const int w_kmin = __builtin_amdgcn_readfirstlane(wave_min_i(min(klim[0], klim[1])));
     const int w_kmax = __builtin_amdgcn_readfirstlane(wave_max_i(max(klim[0], klim[1])));
@@ -281,6 +286,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
         k_row[i] = seg * ROWS_PER_SEG + lane / KCH;
         k_col[i] = (uint32_t)(((lane % KCH) ^ k_swz<D>(k_row[i])) * 16);
     }
+    uint32_t k_full[SEG_PER_WAVE];  // offsets of an interior (full) tile
+#pragma unroll
+    for (int i = 0; i < SEG_PER_WAVE; ++i) k_full[i] = (uint32_t)k_row[i] * k_st_bytes + k_col[i];
     uint32_t v_col[V_PER_T];
     int v_row[V_PER_T];
 #pragma unroll
@@ -296,24 +304,39 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
     auto load_k = [&](int kbase, int slot) __attribute__((always_inline)) {
         unsigned char* Ks = Kbuf + slot * K_BYTES;
         const char* tb = kbytes + (int64_t)kbase * p.k_st * 2;
-        const int last = min(kv_last - kbase, KT - 1);   // last valid row of this tile
-#pragma unroll
-        for (int i = 0; i < SEG_PER_WAVE; ++i) {
-            const uint32_t off = (uint32_t)min(k_row[i], last) * k_st_bytes + k_col[i];
+        auto issue = [&](int i, uint32_t off) __attribute__((always_inline)) {
             __builtin_amdgcn_global_load_lds(tb + off, (__attribute__((address_space(3))) void*)(Ks + (wave * SEG_PER_WAVE + i) * 1024),
                                              16, 0, 0);
+        };
+        if (kbase + KT <= p.kv_len) {
+#pragma unroll
+            for (int i = 0; i < SEG_PER_WAVE; ++i) issue(i, k_full[i]);
+        } else {
+            const int last = kv_last - kbase;   // last valid row of this tile (< KT here)
+#pragma unroll
+            for (int i = 0; i < SEG_PER_WAVE; ++i) issue(i, (uint32_t)min(k_row[i], last) * k_st_bytes + k_col[i]);
         }
     };
     auto load_v = [&](int kbase) __attribute__((always_inline)) {
         const char* tb = vbytes + (int64_t)kbase * p.v_st * 2;
-        const int last = min(kv_last - kbase, KT - 1);
+        if (kbase + KT <= p.kv_len) {
 #pragma unroll
-        for (int j = 0; j < V_PER_T; ++j)
+            for (int j = 0; j < V_PER_T; ++j) {
+                const char* rowp = tb + ((uint32_t)v_row[j] * v_st_bytes + v_col[j]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t off = (uint32_t)min(v_row[j] + r, last) * v_st_bytes + v_col[j];
-                vreg[j][r] = *reinterpret_cast<const u32x2*>(tb + off);
+                for (int r = 0; r < 4; ++r)
+                    vreg[j][r] = *reinterpret_cast<const u32x2*>(rowp + (uint32_t)r * v_st_bytes);
             }
+        } else {
+            const int last = kv_last - kbase;
+#pragma unroll
+            for (int j = 0; j < V_PER_T; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t off = (uint32_t)min(v_row[j] + r, last) * v_st_bytes + v_col[j];
+                    vreg[j][r] = *reinterpret_cast<const u32x2*>(tb + off);
+                }
+        }
     };
     auto store_v = [&](int slot) __attribute__((always_inline)) {
         unsigned char* Vs = Vbuf + slot * V_BYTES;
@@ -341,17 +364,26 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
     };
 
     // S^T of one 32-key half: s[qb] holds keys kb0 + 8(r/4) + 4g + (r%4) of query 32qb + n.
-    auto qk_half = [&](int slot, int half, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    // K operands of one 32-key half (all k-steps), then its MFMAs
+    auto k_operands = [&](int slot, int half, bf16x8 (&a)[SK]) __attribute__((always_inline)) {
         const unsigned char* Ks = Kbuf + slot * K_BYTES;
-        s[0] = s[1] = f32x16{};
         const int r = 32 * half + n;
 #pragma unroll
+        for (int ks = 0; ks < SK; ++ks)
+            a[ks] = *reinterpret_cast<const bf16x8*>(Ks + (r * KCH + ((2 * ks + g) ^ k_swz<D>(r))) * 16);
+    };
+    auto qk_mfma = [&](const bf16x8 (&a)[SK], f32x16 (&s)[2]) __attribute__((always_inline)) {
+        s[0] = s[1] = f32x16{};
+#pragma unroll
         for (int ks = 0; ks < SK; ++ks) {
-            const int chunk = 2 * ks + g;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (r * KCH + (chunk ^ k_swz<D>(r))) * 16);
-            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[0][ks], s[0], 0, 0, 0);
-            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[1][ks], s[1], 0, 0, 0);
+            s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qreg[0][ks], s[0], 0, 0, 0);
+            s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qreg[1][ks], s[1], 0, 0, 0);
         }
+    };
+    auto qk_half = [&](int slot, int half, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        bf16x8 a[SK];
+        k_operands(slot, half, a);
+        qk_mfma(a, s);
     };
 
     f32x16 oacc[MO][2];
@@ -417,18 +449,29 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
         }
     };
     // O^T += V^T P^T for the 16-key chunk ks (0..3) of the tile
-    auto pv_chunk = [&](int slot, int ks, const u32x4 (&w)[2]) __attribute__((always_inline)) {
+    // V^T operands of the 16-key chunk ks (all d blocks), then its MFMAs
+    auto v_operands = [&](int slot, int ks, bf16x8 (&a)[MO]) __attribute__((always_inline)) {
         const unsigned char* Vs = Vbuf + slot * V_BYTES;
-        const bf16x8 b0 = __builtin_bit_cast(bf16x8, w[0]);
-        const bf16x8 b1 = __builtin_bit_cast(bf16x8, w[1]);
         const int chunk = 2 * ks + g;
 #pragma unroll
         for (int mb = 0; mb < MO; ++mb) {
             const int d = 32 * mb + n;
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vs + d * 128 + ((chunk ^ v_swz(d)) * 16));
-            oacc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, oacc[mb][0], 0, 0, 0);
-            oacc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, oacc[mb][1], 0, 0, 0);
+            a[mb] = *reinterpret_cast<const bf16x8*>(Vs + d * 128 + ((chunk ^ v_swz(d)) * 16));
         }
+    };
+    auto pv_mfma = [&](const bf16x8 (&a)[MO], const u32x4 (&w)[2]) __attribute__((always_inline)) {
+        const bf16x8 b0 = __builtin_bit_cast(bf16x8, w[0]);
+        const bf16x8 b1 = __builtin_bit_cast(bf16x8, w[1]);
+#pragma unroll
+        for (int mb = 0; mb < MO; ++mb) {
+            oacc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b0, oacc[mb][0], 0, 0, 0);
+            oacc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b1, oacc[mb][1], 0, 0, 0);
+        }
+    };
+    auto pv_chunk = [&](int slot, int ks, const u32x4 (&w)[2]) __attribute__((always_inline)) {
+        bf16x8 a[MO];
+        v_operands(slot, ks, a);
+        pv_mfma(a, w);
     };
 
     // ---- walk the key tiles -----------------------------------------------
@@ -470,17 +513,35 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
             const int kb = e0.tile * KT;
             f32x16 s0[2], s1[2];
             if constexpr (MODE == 0 && FAST) {
+                // explicit phases (scheduling barriers keep every group of LDS
+                // operand reads ahead of the MFMAs that consume it):
+                //   P1 QK(h0)        + K reads of h1
+                //   P2 QK(h1)        || exp(h0) + V reads of chunks 0,1
+                //   P3 PV(chunks 0,1) || exp(h1) + V reads of chunks 2,3
+                //   P4 PV(chunks 2,3) || staging of the next V tile
                 u32x4 w00[2], w01[2], w10[2], w11[2];
-                qk_half(slot, 0, s0);
-                qk_half(slot, 1, s1);
+                bf16x8 ka[SK], kb1[SK], va0[MO], va1[MO], va2[MO], va3[MO];
+                k_operands(slot, 0, ka);
+                __builtin_amdgcn_sched_barrier(0);
+                k_operands(slot, 1, kb1);
+                qk_mfma(ka, s0);
+                __builtin_amdgcn_sched_barrier(0);
+                v_operands(slot, 0, va0);
+                v_operands(slot, 1, va1);
+                qk_mfma(kb1, s1);
                 exp_chunk(s0, 0, w00);
                 exp_chunk(s0, 1, w01);
-                pv_chunk(slot, 0, w00);
-                pv_chunk(slot, 1, w01);
+                __builtin_amdgcn_sched_barrier(0);
+                v_operands(slot, 2, va2);
+                v_operands(slot, 3, va3);
+                pv_mfma(va0, w00);
+                pv_mfma(va1, w01);
                 exp_chunk(s1, 0, w10);
                 exp_chunk(s1, 1, w11);
-                pv_chunk(slot, 2, w10);
-                pv_chunk(slot, 3, w11);
+                __builtin_amdgcn_sched_barrier(0);
+                pv_mfma(va2, w10);
+                pv_mfma(va3, w11);
+                if (e1.tile >= 0) store_v(slot ^ 1);
             } else {
                 // a tile outside this wave's own list is computed fully masked
                 const bool own = mine(e0);
@@ -516,7 +577,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                     mref[1] = __builtin_fmaxf(mref[1], mt[1]);
                 }
             }
-            if constexpr (MODE == 0) {
+            if constexpr (MODE == 0 && !FAST) {
                 if (e1.tile >= 0) store_v(slot ^ 1);
             }
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next K tile is in LDS
