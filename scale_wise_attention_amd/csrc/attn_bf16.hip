@@ -48,6 +48,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <utility>
 
 #include "kernels.h"
 
@@ -93,8 +94,18 @@ __device__ __forceinline__ int k_swz(int r) {
     if constexpr (D == 128) return r & 15;        // 256-byte rows
     else return (r >> 1) & 7;                     // 128-byte rows
 }
-// V^T tile: 128-byte rows (64 keys), row = d.
-__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
+// V^T tile: row d holds 64 keys (128 bytes, 16-byte chunks c = 0..7); rows
+// 2m and 2m+1 share a 256-byte line of 16 slots.  Chunk c of row d goes to slot
+// ((d ^ c) & 1) * 8 + (c ^ H(m)) with H(m) = (m + ((m >> 3) & 1)) & 7, so that
+//  - an operand read (16 lanes: 16 consecutive d, one chunk) and
+//  - a staging write (32 lanes: 8 d of one parity x 2 chunks x two 8-byte halves)
+// each touch every LDS bank once, and the swizzle depends on d & 31 only (the
+// 32-row block of d is a constant offset).
+__device__ __forceinline__ int v_addr(int d, int c) {
+    const int m = d >> 1;
+    const int h = (m + ((m >> 3) & 1)) & 7;
+    return m * 256 + ((((d ^ c) & 1) << 3) | ((c ^ h) & 7)) * 16;
+}
 
 // low halves of a and b -> (a.lo, b.lo); high halves -> (a.hi, b.hi): one v_perm_b32 each
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
@@ -117,6 +128,16 @@ template <bool B>
 struct BoolC {
     static constexpr bool value = B;
 };
+
+// calls f(std::integral_constant<int, I>) for I = 0..N-1 (every index a constant)
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // One entry of the key-tile walk: tile index (-1 = end) and the waves that use it.
 struct TileEnt {
@@ -289,12 +310,25 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
     uint32_t k_full[SEG_PER_WAVE];  // offsets of an interior (full) tile
 #pragma unroll
     for (int i = 0; i < SEG_PER_WAVE; ++i) k_full[i] = (uint32_t)k_row[i] * k_st_bytes + k_col[i];
+    // V staging unit u: keys 4kg..4kg+3 x columns 4dg..4dg+3 (one 8-byte load per
+    // key).  Within the 16-key block kb the 4-key groups g4 = 0..3 are stored in
+    // the order {0, 2, 1, 3} (the order in which a lane's weights come out of
+    // S^T): group g4 goes to chunk 2kb + (g4 & 1), 8-byte half g4 >> 1.  The bits
+    // of u are (from the lowest): half, dg mod 8, chunk parity, then dg / 8 and kb.
+    auto v_unit = [&](int u, int& dg, int& kg, int& chunk, int& half) __attribute__((always_inline)) {
+        const int c0 = (u >> 4) & 1, r = u >> 5;
+        const int kb = r / (D / 32);
+        half = u & 1;
+        dg = 8 * (r % (D / 32)) + ((u >> 1) & 7);
+        kg = 4 * kb + 2 * half + c0;
+        chunk = 2 * kb + c0;
+    };
     uint32_t v_col[V_PER_T];
     int v_row[V_PER_T];
 #pragma unroll
     for (int j = 0; j < V_PER_T; ++j) {
-        const int u = tid + NT * j;
-        const int dg = u % (D / 4), kg = u / (D / 4);
+        int dg, kg, chunk, half;
+        v_unit(tid + NT * j, dg, kg, chunk, half);
         v_row[j] = 4 * kg;
         v_col[j] = (uint32_t)(8 * dg);
     }
@@ -338,29 +372,24 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                 }
         }
     };
-    auto store_v = [&](int slot) __attribute__((always_inline)) {
+    // one 4-key x 1-column piece (row i of the 4x4 block j) of the V^T staging
+    auto store_v_piece = [&](int slot, int j, int i) __attribute__((always_inline)) {
         unsigned char* Vs = Vbuf + slot * V_BYTES;
+        int dg, kg, chunk, half;
+        v_unit(tid + NT * j, dg, kg, chunk, half);
+        const u32x2* a = vreg[j];
+        u32x2 outv;
+        if (i == 0) outv = u32x2{pack_lo(a[0].x, a[1].x), pack_lo(a[2].x, a[3].x)};
+        if (i == 1) outv = u32x2{pack_hi(a[0].x, a[1].x), pack_hi(a[2].x, a[3].x)};
+        if (i == 2) outv = u32x2{pack_lo(a[0].y, a[1].y), pack_lo(a[2].y, a[3].y)};
+        if (i == 3) outv = u32x2{pack_hi(a[0].y, a[1].y), pack_hi(a[2].y, a[3].y)};
+        *reinterpret_cast<u32x2*>(Vs + v_addr(4 * dg + i, chunk) + half * 8) = outv;
+    };
+    auto store_v = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < V_PER_T; ++j) {
-            const int u = tid + NT * j;
-            const int dg = u % (D / 4), kg = u / (D / 4);
-            // keys 4kg..4kg+3 go to position kb*16 + perm(g4)*4, perm = {0, 2, 1, 3}
-            const int kb = kg >> 2, g4 = kg & 3;
-            const int pg = ((g4 & 1) << 1) | (g4 >> 1);
-            const int chunk = 2 * kb + (pg >> 1);
-            const int half = pg & 1;
-            const u32x2* a = vreg[j];
-            u32x2 outv[4];
-            outv[0] = u32x2{pack_lo(a[0].x, a[1].x), pack_lo(a[2].x, a[3].x)};
-            outv[1] = u32x2{pack_hi(a[0].x, a[1].x), pack_hi(a[2].x, a[3].x)};
-            outv[2] = u32x2{pack_lo(a[0].y, a[1].y), pack_lo(a[2].y, a[3].y)};
-            outv[3] = u32x2{pack_hi(a[0].y, a[1].y), pack_hi(a[2].y, a[3].y)};
+        for (int j = 0; j < V_PER_T; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d = 4 * dg + i;
-                *reinterpret_cast<u32x2*>(Vs + d * 128 + ((chunk ^ v_swz(d)) * 16) + half * 8) = outv[i];
-            }
-        }
+            for (int i = 0; i < 4; ++i) store_v_piece(slot, j, i);
     };
 
     // S^T of one 32-key half: s[qb] holds keys kb0 + 8(r/4) + 4g + (r%4) of query 32qb + n.
@@ -432,21 +461,22 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
         }
         need_ref = __builtin_amdgcn_ballot_w64(mref[0] == -INFINITY || mref[1] == -INFINITY) != 0;
     };
-    // weights of 16-key chunk c (0 or 1) of a half (MFMA k order): 4 bf16 pairs per query block
-    auto exp_chunk = [&](const f32x16 (&s)[2], int c, u32x4 (&w)[2])
-                         __attribute__((always_inline)) {
-        const int r0 = 8 * c;
+    // weights of one key pair (pair i of 16-key chunk c of a half, MFMA k
+    // order) of query block qb, packed to bf16; the pair adds to the row sum
+    auto exp_pair = [&](const f32x16 (&s)[2], int c, int qb, int i, u32x4 (&w)[2]) __attribute__((always_inline)) {
+        const int r = 8 * c + 2 * i;
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c2, nb[qb]));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r + 1], c2, nb[qb]));
+        const uint32_t pr = f32x2_to_bf16x2(e0, e1);
+        w[qb][i] = pr;
+        lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr), ones, lsum[qb], false);
+    };
+    // weights of 16-key chunk c (0 or 1) of a half: 4 bf16 pairs per query block
+    auto exp_chunk = [&](const f32x16 (&s)[2], int c, u32x4 (&w)[2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r0 + 2 * i], c2, nb[qb]));
-                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r0 + 2 * i + 1], c2, nb[qb]));
-                const uint32_t pr = f32x2_to_bf16x2(e0, e1);
-                w[qb][i] = pr;
-                lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr), ones, lsum[qb], false);
-            }
-        }
+            for (int i = 0; i < 4; ++i) exp_pair(s, c, qb, i, w);
     };
     // O^T += V^T P^T for the 16-key chunk ks (0..3) of the tile
     // V^T operands of the 16-key chunk ks (all d blocks), then its MFMAs
@@ -456,7 +486,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
         for (int mb = 0; mb < MO; ++mb) {
             const int d = 32 * mb + n;
-            a[mb] = *reinterpret_cast<const bf16x8*>(Vs + d * 128 + ((chunk ^ v_swz(d)) * 16));
+            a[mb] = *reinterpret_cast<const bf16x8*>(Vs + v_addr(d, chunk));
         }
     };
     auto pv_mfma = [&](const bf16x8 (&a)[MO], const u32x4 (&w)[2]) __attribute__((always_inline)) {
@@ -506,42 +536,105 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
         auto iterate = [&](auto fast_tag) __attribute__((always_inline)) {
             constexpr bool FAST = decltype(fast_tag)::value;
             const int slot = j & 1;
-            if (e1.tile >= 0) {
-                load_k(e1.tile * KT, slot ^ 1);
-                if constexpr (MODE == 0) load_v(e1.tile * KT);
+            if (e1.tile >= 0) load_k(e1.tile * KT, slot ^ 1);
+            if constexpr (MODE == 0) {
+                // the branch-free body always stages a V tile into the idle
+                // slot; after the last tile it re-stages its own (never read)
+                if (FAST || e1.tile >= 0) load_v((e1.tile >= 0 ? e1.tile : e0.tile) * KT);
             }
             const int kb = e0.tile * KT;
             f32x16 s0[2], s1[2];
             if constexpr (MODE == 0 && FAST) {
-                // explicit phases (scheduling barriers keep every group of LDS
-                // operand reads ahead of the MFMAs that consume it):
-                //   P1 QK(h0)        + K reads of h1
-                //   P2 QK(h1)        || exp(h0) + V reads of chunks 0,1
-                //   P3 PV(chunks 0,1) || exp(h1) + V reads of chunks 2,3
-                //   P4 PV(chunks 2,3) || staging of the next V tile
-                u32x4 w00[2], w01[2], w10[2], w11[2];
-                bf16x8 ka[SK], kb1[SK], va0[MO], va1[MO], va2[MO], va3[MO];
-                k_operands(slot, 0, ka);
-                __builtin_amdgcn_sched_barrier(0);
-                k_operands(slot, 1, kb1);
-                qk_mfma(ka, s0);
-                __builtin_amdgcn_sched_barrier(0);
-                v_operands(slot, 0, va0);
-                v_operands(slot, 1, va1);
-                qk_mfma(kb1, s1);
-                exp_chunk(s0, 0, w00);
-                exp_chunk(s0, 1, w01);
-                __builtin_amdgcn_sched_barrier(0);
-                v_operands(slot, 2, va2);
-                v_operands(slot, 3, va3);
-                pv_mfma(va0, w00);
-                pv_mfma(va1, w01);
-                exp_chunk(s1, 0, w10);
-                exp_chunk(s1, 1, w11);
-                __builtin_amdgcn_sched_barrier(0);
-                pv_mfma(va2, w10);
-                pv_mfma(va3, w11);
-                if (e1.tile >= 0) store_v(slot ^ 1);
+                // Software-ordered body: slot m issues MFMA m and a fixed share of
+                // independent work, and a scheduling fence closes the slot, so the
+                // single wave of the SIMD keeps its matrix unit fed while it
+                // computes the weights.  MFMAs: QK(h0) | QK(h1) | PV chunks 0..3.
+                // A weight pair passes three stages in three consecutive slots
+                // (scale+shift, exp2, pack+row sum), so no slot waits on its own
+                // results; the pairs of h0 run under QK(h1), those of h1 under the
+                // PV of chunks 0 and 1.  Operand reads run one phase ahead; the
+                // next V tile is staged under the last PV chunk.
+                const unsigned char* Ks = Kbuf + slot * K_BYTES;
+                const unsigned char* Vs = Vbuf + slot * V_BYTES;
+                auto kread = [&](int half, int ks) __attribute__((always_inline)) -> bf16x8 {
+                    const int r = 32 * half + n;
+                    return *reinterpret_cast<const bf16x8*>(Ks + (r * KCH + ((2 * ks + g) ^ k_swz<D>(r))) * 16);
+                };
+                auto vread = [&](int ks, int mb) __attribute__((always_inline)) -> bf16x8 {
+                    return *reinterpret_cast<const bf16x8*>(Vs + v_addr(32 * mb + n, 2 * ks + g));
+                };
+                constexpr int NQ = 2 * SK;                 // QK slots per half
+                constexpr int NP = 2 * MO;                 // PV slots per 16-key chunk
+                constexpr int NSLOT = 2 * NQ + 4 * NP;     // = 64 MFMAs per tile
+                constexpr int PV0 = 2 * NQ;                // first PV slot
+                // first-stage slot of weight pair i (0..15: h0, 16..31: h1)
+                auto sigma = [](int i) constexpr -> int {
+                    return i < 16 ? NQ + (i * NQ) / 16
+                                  : PV0 + 2 + ((i - 16) / 8) * NP + (((i - 16) % 8) * NP) / 8;
+                };
+                u32x4 w[2][2][2];                          // [half][chunk][qb]
+                float xs[32][2], xe[32][2];
+                bf16x8 ka[SK], kb1[SK], va[4][MO];
+#pragma unroll
+                for (int ks = 0; ks < SK; ++ks) ka[ks] = kread(0, ks);
+                s0[0] = s0[1] = s1[0] = s1[1] = f32x16{};
+                static_for<NSLOT>([&](auto mc) __attribute__((always_inline)) {
+                    constexpr int m = decltype(mc)::value;
+                    if constexpr (m < NQ) {
+                        constexpr int ks = m >> 1, qb = m & 1;
+                        s0[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[qb][ks], s0[qb], 0, 0, 0);
+                        if constexpr (qb == 1) kb1[ks] = kread(1, ks);
+                    } else if constexpr (m < 2 * NQ) {
+                        constexpr int t = m - NQ, ks = t >> 1, qb = t & 1;
+                        s1[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb1[ks], qreg[qb][ks], s1[qb], 0, 0, 0);
+                        static_for<2 * MO>([&](auto ec) __attribute__((always_inline)) {
+                            constexpr int e = decltype(ec)::value;
+                            if constexpr (e * NQ / (2 * MO) == t) va[e / MO][e % MO] = vread(e / MO, e % MO);
+                        });
+                    } else {
+                        constexpr int t = m - PV0, c = t / NP, mb = (t % NP) >> 1, qb = t & 1;
+                        oacc[mb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            va[c][mb], __builtin_bit_cast(bf16x8, w[c >> 1][c & 1][qb]), oacc[mb][qb], 0, 0, 0);
+                        if constexpr (c < 2) {
+                            static_for<2 * MO>([&](auto ec) __attribute__((always_inline)) {
+                                constexpr int e = decltype(ec)::value;
+                                if constexpr (e * 2 * NP / (2 * MO) == t) va[2 + e / MO][e % MO] = vread(2 + e / MO, e % MO);
+                            });
+                        }
+                        if constexpr (c == 3) {
+                            static_for<4 * V_PER_T>([&](auto ec) __attribute__((always_inline)) {
+                                constexpr int e = decltype(ec)::value;
+                                if constexpr (e * NP / (4 * V_PER_T) == t - 3 * NP) store_v_piece(slot ^ 1, e >> 2, e & 3);
+                            });
+                        }
+                    }
+                    // weight pipeline: stage 3, stage 2, stage 1 (oldest first)
+                    static_for<32>([&](auto ic) __attribute__((always_inline)) {
+                        constexpr int i = decltype(ic)::value;
+                        constexpr int hf = i >> 4, c = (i >> 3) & 1, qb = (i >> 2) & 1, ii = i & 3;
+                        constexpr int r = 8 * c + 2 * ii;
+                        constexpr int sg = sigma(i);
+                        if constexpr (sg + 2 == m) {
+                            const uint32_t pr = f32x2_to_bf16x2(xe[i][0], xe[i][1]);
+                            w[hf][c][qb][ii] = pr;
+                            lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr), ones, lsum[qb], false);
+                        }
+                        if constexpr (sg + 1 == m) {
+                            xe[i][0] = __builtin_amdgcn_exp2f(xs[i][0]);
+                            xe[i][1] = __builtin_amdgcn_exp2f(xs[i][1]);
+                        }
+                        if constexpr (sg == m) {
+                            if constexpr (hf == 0) {
+                                xs[i][0] = __builtin_fmaf(s0[qb][r], c2, nb[qb]);
+                                xs[i][1] = __builtin_fmaf(s0[qb][r + 1], c2, nb[qb]);
+                            } else {
+                                xs[i][0] = __builtin_fmaf(s1[qb][r], c2, nb[qb]);
+                                xs[i][1] = __builtin_fmaf(s1[qb][r + 1], c2, nb[qb]);
+                            }
+                        }
+                    });
+                    __builtin_amdgcn_sched_barrier(0);
+                });
             } else {
                 // a tile outside this wave's own list is computed fully masked
                 const bool own = mine(e0);
