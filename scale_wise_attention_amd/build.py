@@ -22,8 +22,10 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["attn_bf16.hip", "attn_f32.hip", "tile_mask.hip", "scatter.hip", "var_attn_api.cpp"]
 # The bf16 attention kernels run with the IEEE mode bit off and without NaN
 # semantics (infinities stay honoured: masked logits are -inf): max/min then
-# need no NaN-quieting instructions in the softmax.
-PER_FILE_FLAGS = {"attn_bf16.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+# need no NaN-quieting instructions in the softmax.  Their MFMAs write VGPRs
+# (S and O are read by VALU code); the kernel itself places the MFMA operands
+# that stay resident (Q) or come from LDS (K, V^T) in AGPRs.
+PER_FILE_FLAGS = {"attn_bf16.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

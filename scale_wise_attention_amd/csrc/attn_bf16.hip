@@ -139,6 +139,60 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Slots of the branch-free tile body (one MFMA each): the QK MFMAs of the four
+// 32x32 S^T blocks (half h, query block qb) run chain by chain (slots
+// (2h+qb)*SK .. +SK-1), then the PV MFMAs (chunk C, d block mb, query block qb)
+// at slot 4*SK + C*NP + 2*mb + qb.  Weight pair i (half i >> 4, block
+// (i >> 3) & 1, chunk (i >> 2) & 1, pair i & 3) takes three stages in slots
+// at[i], at[i]+1, at[i]+2: from two slots after its S^T block is complete, and
+// done before the first PV MFMA that reads it.  Pairs are spread evenly over
+// the slots in between (earliest deadline first), at most `cap` first stages
+// per slot.
+template <int D>
+struct WeightSlots {
+    static constexpr int SK = D / 16, NP = D / 16, NS = D / 2;
+    int at[32];
+    static constexpr int release(int i) { return (2 * (i >> 4) + ((i >> 3) & 1) + 1) * SK + 1; }
+    static constexpr int deadline(int i) {   // the stage-3 slot must come before this one
+        return 4 * SK + (2 * (i >> 4) + ((i >> 2) & 1)) * NP + ((i >> 3) & 1);
+    }
+    constexpr WeightSlots() : at{} {
+        const int cap = D == 128 ? 1 : 2;
+        int first = NS, last = 0;
+        bool done[32] = {};
+        for (int i = 0; i < 32; ++i) {
+            first = release(i) < first ? release(i) : first;
+            last = deadline(i) - 3 > last ? deadline(i) - 3 : last;
+        }
+        const int span = last - first + 1;
+        int placed = 0;
+        for (int m = 0; m < NS; ++m) {
+            int k = 0;
+            bool tried[32] = {};
+            while (k < cap) {
+                int best = -1;
+                for (int i = 0; i < 32; ++i)
+                    if (!done[i] && !tried[i] && release(i) <= m && (best < 0 || deadline(i) < deadline(best))) best = i;
+                if (best < 0) break;
+                tried[best] = true;
+                const bool urgent = deadline(best) - 3 - m <= 0;
+                const int quota = ((m - first + 1) * 32 + span - 1) / span;
+                if (urgent || placed < quota) {
+                    at[best] = m;
+                    done[best] = true;
+                    ++placed;
+                    ++k;
+                }
+            }
+        }
+    }
+    constexpr bool valid() const {
+        for (int i = 0; i < 32; ++i)
+            if (at[i] < release(i) || at[i] + 2 >= deadline(i)) return false;
+        return true;
+    }
+};
+
 // One entry of the key-tile walk: tile index (-1 = end) and the waves that use it.
 struct TileEnt {
     int tile;
@@ -548,12 +602,12 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                 // Software-ordered body: slot m issues MFMA m and a fixed share of
                 // independent work, and a scheduling fence closes the slot, so the
                 // single wave of the SIMD keeps its matrix unit fed while it
-                // computes the weights.  MFMAs: QK(h0) | QK(h1) | PV chunks 0..3.
-                // A weight pair passes three stages in three consecutive slots
-                // (scale+shift, exp2, pack+row sum), so no slot waits on its own
-                // results; the pairs of h0 run under QK(h1), those of h1 under the
-                // PV of chunks 0 and 1.  Operand reads run one phase ahead; the
-                // next V tile is staged under the last PV chunk.
+                // computes the weights.  The QK MFMAs run block by block, so the
+                // weights of a 32x32 S^T block start as soon as it is complete;
+                // the weight pairs are spread over the slots (WeightSlots), each
+                // in three stages (scale+shift, exp2, pack+row sum) in three
+                // consecutive slots.  Operand reads run a phase ahead; the next V
+                // tile is staged under the last PV chunk.
                 const unsigned char* Ks = Kbuf + slot * K_BYTES;
                 const unsigned char* Vs = Vbuf + slot * V_BYTES;
                 auto kread = [&](int half, int ks) __attribute__((always_inline)) -> bf16x8 {
@@ -563,68 +617,73 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                 auto vread = [&](int ks, int mb) __attribute__((always_inline)) -> bf16x8 {
                     return *reinterpret_cast<const bf16x8*>(Vs + v_addr(32 * mb + n, 2 * ks + g));
                 };
-                constexpr int NQ = 2 * SK;                 // QK slots per half
-                constexpr int NP = 2 * MO;                 // PV slots per 16-key chunk
-                constexpr int NSLOT = 2 * NQ + 4 * NP;     // = 64 MFMAs per tile
-                constexpr int PV0 = 2 * NQ;                // first PV slot
-                // first-stage slot of weight pair i (0..15: h0, 16..31: h1)
-                auto sigma = [](int i) constexpr -> int {
-                    return i < 16 ? NQ + (i * NQ) / 16
-                                  : PV0 + 2 + ((i - 16) / 8) * NP + (((i - 16) % 8) * NP) / 8;
+                // MFMA operands read from LDS are handed to the MFMA from AGPRs
+                // (the loads then write AGPRs), which leaves the VGPRs to O, S and
+                // the weights
+                auto in_agpr = [](bf16x8 x) __attribute__((always_inline)) -> bf16x8 {
+                    asm("" : "+a"(x));
+                    return x;
                 };
-                u32x4 w[2][2][2];                          // [half][chunk][qb]
-                float xs[32][2], xe[32][2];
+                constexpr int L = 2 * SK;                  // QK slots per half
+                constexpr int NP = 2 * MO;                 // PV slots per 16-key chunk
+                constexpr WeightSlots<D> WS{};
+                static_assert(WS.valid(), "weight pairs scheduled in time");
+                u32x4 w[4][2];                             // [chunk][qb]
+                float xs[32][2];                           // weight-pair stage values
                 bf16x8 ka[SK], kb1[SK], va[4][MO];
 #pragma unroll
                 for (int ks = 0; ks < SK; ++ks) ka[ks] = kread(0, ks);
                 s0[0] = s0[1] = s1[0] = s1[1] = f32x16{};
-                static_for<NSLOT>([&](auto mc) __attribute__((always_inline)) {
+                static_for<4 * L>([&](auto mc) __attribute__((always_inline)) {
                     constexpr int m = decltype(mc)::value;
-                    if constexpr (m < NQ) {
-                        constexpr int ks = m >> 1, qb = m & 1;
-                        s0[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qreg[qb][ks], s0[qb], 0, 0, 0);
-                        if constexpr (qb == 1) kb1[ks] = kread(1, ks);
-                    } else if constexpr (m < 2 * NQ) {
-                        constexpr int t = m - NQ, ks = t >> 1, qb = t & 1;
-                        s1[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb1[ks], qreg[qb][ks], s1[qb], 0, 0, 0);
-                        static_for<2 * MO>([&](auto ec) __attribute__((always_inline)) {
-                            constexpr int e = decltype(ec)::value;
-                            if constexpr (e * NQ / (2 * MO) == t) va[e / MO][e % MO] = vread(e / MO, e % MO);
-                        });
-                    } else {
-                        constexpr int t = m - PV0, c = t / NP, mb = (t % NP) >> 1, qb = t & 1;
-                        oacc[mb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            va[c][mb], __builtin_bit_cast(bf16x8, w[c >> 1][c & 1][qb]), oacc[mb][qb], 0, 0, 0);
-                        if constexpr (c < 2) {
+                    if constexpr (m < 2 * L) {
+                        // QK chains: S^T block (h, qb) in slots (2h+qb)*SK .. +SK-1
+                        constexpr int chain = m / SK, ks = m % SK, h = chain >> 1, qb = chain & 1;
+                        if constexpr (h == 0) s0[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(in_agpr(ka[ks]), qreg[qb][ks], s0[qb], 0, 0, 0);
+                        else s1[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(in_agpr(kb1[ks]), qreg[qb][ks], s1[qb], 0, 0, 0);
+                        // K operands of h1 during QK(h0), V operands of chunks 0, 1 during QK(h1)
+                        if constexpr (m < L && (m & 1) == 1) kb1[m >> 1] = kread(1, m >> 1);
+                        if constexpr (m >= L) {
                             static_for<2 * MO>([&](auto ec) __attribute__((always_inline)) {
                                 constexpr int e = decltype(ec)::value;
-                                if constexpr (e * 2 * NP / (2 * MO) == t) va[2 + e / MO][e % MO] = vread(2 + e / MO, e % MO);
+                                if constexpr ((e * L) / (2 * MO) == m - L) va[e / MO][e % MO] = vread(e / MO, e % MO);
+                            });
+                        }
+                    } else {
+                        // PV chunks 0..3 | V operands of chunks 2, 3 | staging of the next V tile
+                        constexpr int t = m - 2 * L, c = t / NP, mb = (t % NP) >> 1, qb = t & 1;
+                        oacc[mb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            in_agpr(va[c][mb]), __builtin_bit_cast(bf16x8, w[c][qb]), oacc[mb][qb], 0, 0, 0);
+                        if constexpr (t < NP) {
+                            static_for<2 * MO>([&](auto ec) __attribute__((always_inline)) {
+                                constexpr int e = decltype(ec)::value;
+                                if constexpr ((e * NP) / (2 * MO) == t) va[2 + e / MO][e % MO] = vread(2 + e / MO, e % MO);
                             });
                         }
                         if constexpr (c == 3) {
                             static_for<4 * V_PER_T>([&](auto ec) __attribute__((always_inline)) {
                                 constexpr int e = decltype(ec)::value;
-                                if constexpr (e * NP / (4 * V_PER_T) == t - 3 * NP) store_v_piece(slot ^ 1, e >> 2, e & 3);
+                                if constexpr ((e * NP) / (4 * V_PER_T) == t - 3 * NP) store_v_piece(slot ^ 1, e >> 2, e & 3);
                             });
                         }
                     }
                     // weight pipeline: stage 3, stage 2, stage 1 (oldest first)
                     static_for<32>([&](auto ic) __attribute__((always_inline)) {
                         constexpr int i = decltype(ic)::value;
-                        constexpr int hf = i >> 4, c = (i >> 3) & 1, qb = (i >> 2) & 1, ii = i & 3;
+                        constexpr int h = i >> 4, qb = (i >> 3) & 1, c = (i >> 2) & 1, ii = i & 3;
                         constexpr int r = 8 * c + 2 * ii;
-                        constexpr int sg = sigma(i);
-                        if constexpr (sg + 2 == m) {
-                            const uint32_t pr = f32x2_to_bf16x2(xe[i][0], xe[i][1]);
-                            w[hf][c][qb][ii] = pr;
+                        constexpr int at = WS.at[i];
+                        if constexpr (at + 2 == m) {
+                            const uint32_t pr = f32x2_to_bf16x2(xs[i][0], xs[i][1]);
+                            w[2 * h + c][qb][ii] = pr;
                             lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr), ones, lsum[qb], false);
                         }
-                        if constexpr (sg + 1 == m) {
-                            xe[i][0] = __builtin_amdgcn_exp2f(xs[i][0]);
-                            xe[i][1] = __builtin_amdgcn_exp2f(xs[i][1]);
+                        if constexpr (at + 1 == m) {
+                            xs[i][0] = __builtin_amdgcn_exp2f(xs[i][0]);
+                            xs[i][1] = __builtin_amdgcn_exp2f(xs[i][1]);
                         }
-                        if constexpr (sg == m) {
-                            if constexpr (hf == 0) {
+                        if constexpr (at == m) {
+                            if constexpr (h == 0) {
                                 xs[i][0] = __builtin_fmaf(s0[qb][r], c2, nb[qb]);
                                 xs[i][1] = __builtin_fmaf(s0[qb][r + 1], c2, nb[qb]);
                             } else {
