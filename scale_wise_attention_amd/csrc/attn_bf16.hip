@@ -562,11 +562,10 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
     // mode 0: weights against the per-row reference (the fast path)
     // mode 1: exact row maxima only (QK, no weights); they become the references
     //
-    // Tiles that every wave owns and that need no mask run a branch-free body
-    // (QK of the second half overlaps the exponentials of the first, the
-    // exponentials of the second overlap the P V^T of the first); the first
-    // tile (which sets the references) and masked or partly owned tiles run a
-    // general body.  The two bodies sit in separate loops, so the
+    // Tiles that need no mask run a branch-free, software-ordered body (waves
+    // that do not own such a tile in a block-sparse walk take it with zero
+    // weights); the first tile (which sets the references) and masked tiles
+    // run a general body.  The two bodies sit in separate loops, so the
     // accumulators only flow from one loop into the next.
     auto walk = [&](auto mode_tag) __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode_tag)::value;
@@ -585,7 +584,9 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
 
         int j = 0;
         auto fast = [&](const TileEnt& e) __attribute__((always_inline)) -> bool {
-            return j > 0 && e.mask == (1 << NW) - 1 && e.tile * KT + KT <= wg_kmin;
+            // (a tile that only some waves own also runs the branch-free body: the
+            // other waves shift their logits to -inf, so their weights are zero)
+            return j > 0 && e.tile * KT + KT <= wg_kmin;
         };
         auto iterate = [&](auto fast_tag) __attribute__((always_inline)) {
             constexpr bool FAST = decltype(fast_tag)::value;
@@ -628,6 +629,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                 constexpr int NP = 2 * MO;                 // PV slots per 16-key chunk
                 constexpr WeightSlots<D> WS{};
                 static_assert(WS.valid(), "weight pairs scheduled in time");
+                const bool own = mine(e0);
+                const float nbt[2] = {own ? nb[0] : -INFINITY, own ? nb[1] : -INFINITY};
                 u32x4 w[4][2];                             // [chunk][qb]
                 float xs[32][2];                           // weight-pair stage values
                 bf16x8 ka[SK], kb1[SK], va[4][MO];
@@ -684,11 +687,11 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                         }
                         if constexpr (at == m) {
                             if constexpr (h == 0) {
-                                xs[i][0] = __builtin_fmaf(s0[qb][r], c2, nb[qb]);
-                                xs[i][1] = __builtin_fmaf(s0[qb][r + 1], c2, nb[qb]);
+                                xs[i][0] = __builtin_fmaf(s0[qb][r], c2, nbt[qb]);
+                                xs[i][1] = __builtin_fmaf(s0[qb][r + 1], c2, nbt[qb]);
                             } else {
-                                xs[i][0] = __builtin_fmaf(s1[qb][r], c2, nb[qb]);
-                                xs[i][1] = __builtin_fmaf(s1[qb][r + 1], c2, nb[qb]);
+                                xs[i][0] = __builtin_fmaf(s1[qb][r], c2, nbt[qb]);
+                                xs[i][1] = __builtin_fmaf(s1[qb][r + 1], c2, nbt[qb]);
                             }
                         }
                     });
