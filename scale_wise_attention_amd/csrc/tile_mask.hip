@@ -10,17 +10,20 @@
 // i.e. the key lies within R of the query's position mapped into grid j.
 // A tile is kept if it holds one selected pair.
 //
-// Instead of enumerating pairs, each (query row, key tile) test is closed
-// form: the tile's keys of scale j form a row-major interval of grid j (a
-// partial first row, full middle rows, a partial last row: three
-// rectangles), and for a rectangle the window test separates into one test
-// per axis: is there a key row y_k in [y0, y1] with y_k*h_q inside
-// [y_q*h_j - R*h_q, y_q*h_j + R*h_q] (same for columns)?
+// Instead of enumerating pairs, each query row marks the key tiles its
+// windows cover.  For key scale j the window is a rectangle of grid j: the
+// key rows with y_q*h_j - R_y*h_q <= y_k*h_q <= y_q*h_j + R_y*h_q are
+// [ceil((y_q*h_j - R_y*h_q)/h_q), floor((y_q*h_j + R_y*h_q)/h_q)] clipped to
+// the grid (same for columns).  Each rectangle row is a run of consecutive
+// tokens, so it covers a run of key tiles; a rectangle spanning the full grid
+// width is a single run.  The sink scales visible to the row are the token
+// prefix [0, off[min(sink_scales, s_q + 1)]).  Window scales below
+// sink_scales lie inside that prefix and are skipped.
 //
-// Two launches: (1) one workgroup per query tile tests every key tile, and
-// writes its kept columns, compacted in ascending order, at col_idx[r*n_kt]
-// with the count in row_ptr[r+1]; (2) one workgroup turns the counts into
-// offsets and moves every row's list down to its final place.
+// Two launches: (1) one workgroup per query tile ORs its rows' tile runs into
+// a bitmap in LDS and writes the kept columns, in ascending order, at
+// col_idx[r*n_kt] with the count in row_ptr[r+1]; (2) one workgroup turns the
+// counts into offsets and moves every row's list down to its final place.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -28,100 +31,124 @@
 namespace varattn {
 namespace {
 
-// Is there an integer y in [lo, hi] with a <= y*m <= b  (m >= 1, a <= b)?
-// For b - a >= m every long-enough window holds a multiple of m, so the test
-// reduces to interval overlap; a shorter window (radius 0) needs the exact check.
-__device__ __forceinline__ bool axis_hit(int lo, int hi, int a, int b, int m) {
-    if (lo > hi) return false;
-    const int L = max(lo * m, a), H = min(hi * m, b);
-    if (L > H) return false;
-    if (b - a >= m) return true;
-    // window shorter than one step: some multiple of m must lie in [L, H]
-    const int r = ((L % m) + m) % m;
-    return r == 0 || L + (m - r) <= H;
+constexpr int kRowThreads = 256;
+constexpr int kChunkTiles = 8192;              // key tiles per bitmap pass
+constexpr int kChunkWords = kChunkTiles / 32;
+
+__device__ __forceinline__ int floor_div(int a, int m) { return a >= 0 ? a / m : -((m - 1 - a) / m); }
+__device__ __forceinline__ int ceil_div(int a, int m) { return -floor_div(-a, m); }
+
+// Scale, row and column of query row i of the call (q_index gathered and
+// clamped into [0, n_q) so that a bad index cannot read outside the schedule).
+__device__ __forceinline__ void row_coords(const MaskParams& p, int i, int& s, int& y, int& x) {
+    int pos = p.q_index ? p.q_index[i] : i;
+    pos = pos < 0 ? 0 : (pos >= p.n_q ? p.n_q - 1 : pos);
+    const int tok = p.q_first + pos;
+    s = 0;
+    while (s + 1 < p.num_scales && tok >= p.off[s + 1]) ++s;
+    const int local = tok - p.off[s];
+    y = local / p.w[s];
+    x = local - y * p.w[s];
 }
 
-// The keys of one scale inside a key tile are the row-major interval from
-// (y0, x0) to (y1, x1) of a grid with w columns: up to three rectangles
-// (partial first row, full middle rows, partial last row).  Window on key
-// rows: ya <= y_k*hq <= yb; on key columns: xa <= x_k*wq <= xb.
-__device__ __forceinline__ bool seg_hit(int y0, int x0, int y1, int x1, int w, int ya, int yb, int xa, int xb,
-                                        int hq, int wq) {
-    if (y0 == y1) return axis_hit(y0, y0, ya, yb, hq) && axis_hit(x0, x1, xa, xb, wq);
-    if (axis_hit(y0, y0, ya, yb, hq) && axis_hit(x0, w - 1, xa, xb, wq)) return true;
-    if (axis_hit(y1, y1, ya, yb, hq) && axis_hit(0, x1, xa, xb, wq)) return true;
-    return axis_hit(y0 + 1, y1 - 1, ya, yb, hq) && axis_hit(0, w - 1, xa, xb, wq);
+// Set the bits of key tiles [t0, t1] that fall in the chunk [c0, c0 + kChunkTiles).
+__device__ __forceinline__ void mark_tiles(uint32_t* bits, int t0, int t1, int c0) {
+    t0 = max(t0 - c0, 0);
+    t1 = min(t1 - c0, kChunkTiles - 1);
+    if (t0 > t1) return;
+    const int w0 = t0 >> 5, w1 = t1 >> 5;
+    for (int wd = w0; wd <= w1; ++wd) {
+        const int lo = wd == w0 ? (t0 & 31) : 0;
+        const int hi = wd == w1 ? (t1 & 31) : 31;
+        const uint32_t m = (hi == 31 ? 0xffffffffu : ((1u << (hi + 1)) - 1u)) & ~((1u << lo) - 1u);
+        atomicOr(&bits[wd], m);
+    }
 }
 
-constexpr int kQChunk = 256;   // query rows staged in LDS at a time
-
-// One workgroup (256 threads) per query tile; thread = key tile.  The tile's
-// query rows are staged in LDS (scale, y, x) in chunks.  Each thread walks
-// the scales present in its key tile, forms that scale's segment once, and
-// tests every staged query against it with multiplications and compares.
-__global__ __launch_bounds__(256) void mask_rows_kernel(const MaskParams p) {
-    __shared__ int wave_cnt[4];
+// One workgroup per query tile.  Keys are processed in chunks of kChunkTiles
+// tiles (one pass for every workload up to 8192 key tiles).
+__global__ __launch_bounds__(kRowThreads) void mask_rows_kernel(const MaskParams p) {
+    __shared__ uint32_t bits[kChunkWords];
+    __shared__ int wave_cnt[kRowThreads / 64];
     __shared__ int running;
-    __shared__ int qs_l[kQChunk], yq_l[kQChunk], xq_l[kQChunk];
+    __shared__ int sink_end;
     const int r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) running = 0;
     const int i0 = r * p.tile_q;
-    const int i_end = min(i0 + p.tile_q, p.n_rows);
+    const int n_rows = min(p.tile_q, p.n_rows - i0);
+    // window scales: [jw, s_q]; scales below sink_scales are covered by the sink prefix
+    const int jw = max(p.sink_scales, p.local_from_scale);
+    const int nj = max(p.num_scales - jw, 0);
+    if (tid == 0) {
+        running = 0;
+        sink_end = 0;
+    }
+    __syncthreads();
+    if (p.sink_scales > 0) {
+        int se = 0;
+        for (int t = tid; t < n_rows; t += kRowThreads) {
+            int s, y, x;
+            row_coords(p, i0 + t, s, y, x);
+            se = max(se, p.off[min(p.sink_scales, s + 1)]);
+        }
+        if (se > 0) atomicMax(&sink_end, se);
+    }
     int* out = p.col_idx + (int64_t)r * p.n_kt;
-    for (int c0 = 0; c0 < p.n_kt; c0 += 256) {
-        const int c = c0 + tid;
-        const bool active = c < p.n_kt;
-        const int k0 = c * p.tile_k, k1 = min(k0 + p.tile_k, p.kv_len);
-        int j_first = 0;
-        if (active)
-            while (j_first + 1 < p.num_scales && k0 >= p.off[j_first + 1]) ++j_first;
-        bool kept = false;
-        for (int q0 = i0; q0 < i_end; q0 += kQChunk) {
-            const int nq = min(kQChunk, i_end - q0);
-            __syncthreads();
-            for (int t = tid; t < nq; t += 256) {
-                int pos = p.q_index ? p.q_index[q0 + t] : q0 + t;
-                pos = pos < 0 ? 0 : (pos >= p.n_q ? p.n_q - 1 : pos);
-                const int tok = p.q_first + pos;
-                int qs = 0;
-                while (qs + 1 < p.num_scales && tok >= p.off[qs + 1]) ++qs;
-                qs_l[t] = qs;
-                yq_l[t] = (tok - p.off[qs]) / p.w[qs];
-                xq_l[t] = (tok - p.off[qs]) % p.w[qs];
-            }
-            __syncthreads();
-            if (!active || kept) continue;
-            for (int j = j_first; j < p.num_scales && p.off[j] < k1 && !kept; ++j) {
-                const int a = max(k0, p.off[j]) - p.off[j];
-                const int e = min(k1, p.off[j + 1]) - p.off[j];
-                if (a >= e) continue;
-                const bool sink = j < p.sink_scales;
-                if (!sink && j < p.local_from_scale) continue;
-                const int hj = p.h[j], wj = p.w[j];
-                const int y0 = a / wj, x0 = a % wj, y1 = (e - 1) / wj, x1 = (e - 1) % wj;
-                for (int t = 0; t < nq; ++t) {
-                    const int qs = qs_l[t];
-                    if (j > qs) continue;                 // key scale not visible to this query
-                    if (sink) { kept = true; break; }
-                    const int hq = p.h[qs], wq = p.w[qs];
-                    const int yq = yq_l[t], xq = xq_l[t];
-                    const int ya = yq * hj - p.radius_y * hq, yb = yq * hj + p.radius_y * hq;
-                    const int xa = xq * wj - p.radius_x * wq, xb = xq * wj + p.radius_x * wq;
-                    if (seg_hit(y0, x0, y1, x1, wj, ya, yb, xa, xb, hq, wq)) { kept = true; break; }
-                }
+    for (int c0 = 0; c0 < p.n_kt; c0 += kChunkTiles) {
+        for (int wd = tid; wd < kChunkWords; wd += kRowThreads) bits[wd] = 0;
+        __syncthreads();
+        if (tid == 0 && sink_end > 0) mark_tiles(bits, 0, (sink_end - 1) / p.tile_k, c0);
+        const int n_items = n_rows * nj;
+        for (int it = tid; it < n_items; it += kRowThreads) {
+            const int t = it / nj;
+            const int j = jw + (it - t * nj);
+            int s, yq, xq;
+            row_coords(p, i0 + t, s, yq, xq);
+            if (j > s) continue;                   // key scale not visible to this row
+            const int hq = p.h[s], wq = p.w[s], hj = p.h[j], wj = p.w[j];
+            const int ylo = max(ceil_div(yq * hj - p.radius_y * hq, hq), 0);
+            const int yhi = min(floor_div(yq * hj + p.radius_y * hq, hq), hj - 1);
+            const int xlo = max(ceil_div(xq * wj - p.radius_x * wq, wq), 0);
+            const int xhi = min(floor_div(xq * wj + p.radius_x * wq, wq), wj - 1);
+            if (ylo > yhi || xlo > xhi) continue;
+            const int base = p.off[j];
+            if (xlo == 0 && xhi == wj - 1) {
+                mark_tiles(bits, (base + ylo * wj) / p.tile_k, (base + yhi * wj + wj - 1) / p.tile_k, c0);
+            } else {
+                for (int yk = ylo; yk <= yhi; ++yk)
+                    mark_tiles(bits, (base + yk * wj + xlo) / p.tile_k, (base + yk * wj + xhi) / p.tile_k, c0);
             }
         }
-        const uint64_t ballot = __ballot(kept && active);
-        const int before = __popcll(ballot & ((1ull << lane) - 1ull));
-        if (lane == 0) wave_cnt[wave] = __popcll(ballot);
         __syncthreads();
-        int base = running;
-        for (int w = 0; w < wave; ++w) base += wave_cnt[w];
-        if (kept && active) out[base + before] = c;
-        __syncthreads();
-        if (tid == 0) running += wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
-        __syncthreads();
+        // bitmap -> ascending column list (block-wide exclusive scan of popcounts)
+        const int n_words = (min(p.n_kt - c0, kChunkTiles) + 31) >> 5;
+        for (int w0 = 0; w0 < n_words; w0 += kRowThreads) {
+            const int wd = w0 + tid;
+            uint32_t m = wd < n_words ? bits[wd] : 0u;
+            const int cnt = __popc(m);
+            int incl = cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int v = __shfl_up(incl, d);
+                if (lane >= d) incl += v;
+            }
+            if (lane == 63) wave_cnt[wave] = incl;
+            __syncthreads();
+            int at = running + incl - cnt;
+            for (int w = 0; w < wave; ++w) at += wave_cnt[w];
+            while (m) {
+                const int bit = __ffs(m) - 1;
+                out[at++] = c0 + wd * 32 + bit;
+                m &= m - 1u;
+            }
+            __syncthreads();
+            if (tid == 0) {
+                int tot = 0;
+                for (int w = 0; w < kRowThreads / 64; ++w) tot += wave_cnt[w];
+                running += tot;
+            }
+            __syncthreads();
+        }
     }
     if (tid == 0) {
         p.row_ptr[r + 1] = running;
@@ -129,44 +156,87 @@ __global__ __launch_bounds__(256) void mask_rows_kernel(const MaskParams p) {
     }
 }
 
-// One workgroup: counts -> offsets, then move row lists down in row order.
-__global__ __launch_bounds__(1024) void mask_compact_kernel(const MaskParams p) {
+constexpr int kCompactThreads = 1024;
+constexpr int kPtrCap = 8192;                  // row offsets staged in LDS up to this many rows
+constexpr int kMovePerThread = 4;
+
+// One workgroup: counts -> offsets, then move row lists down to their final
+// place.  Entry e of the final list (row r, e in [row_ptr[r], row_ptr[r+1]))
+// is read from r*n_kt + e - row_ptr[r] >= e.  Entries are moved in chunks:
+// all reads of a chunk complete before its writes, and every later chunk
+// reads from positions at or beyond its own entries, past what this chunk
+// writes, so the in-place move is safe.
+__global__ __launch_bounds__(kCompactThreads) void mask_compact_kernel(const MaskParams p) {
     __shared__ int carry;
+    __shared__ int buf[kCompactThreads];
+    __shared__ int ptr_l[kPtrCap + 1];
+    __shared__ int stage[kCompactThreads * kMovePerThread];
     const int tid = threadIdx.x;
-    // inclusive scan of row_ptr[1..n_qt] in chunks of 1024 (Hillis-Steele in LDS)
-    __shared__ int buf[1024];
-    if (tid == 0) carry = 0;
+    const bool staged = p.n_qt <= kPtrCap;
+    if (tid == 0) {
+        carry = 0;
+        ptr_l[0] = 0;
+    }
     __syncthreads();
-    for (int r0 = 0; r0 < p.n_qt; r0 += 1024) {
+    // inclusive scan of row_ptr[1..n_qt] in chunks (Hillis-Steele in LDS)
+    for (int r0 = 0; r0 < p.n_qt; r0 += kCompactThreads) {
         const int r = r0 + tid;
-        int v = r < p.n_qt ? p.row_ptr[r + 1] : 0;
-        buf[tid] = v;
+        buf[tid] = r < p.n_qt ? p.row_ptr[r + 1] : 0;
         __syncthreads();
-        for (int s = 1; s < 1024; s <<= 1) {
+        for (int s = 1; s < kCompactThreads; s <<= 1) {
             const int add = tid >= s ? buf[tid - s] : 0;
             __syncthreads();
             buf[tid] += add;
             __syncthreads();
         }
-        if (r < p.n_qt) p.row_ptr[r + 1] = buf[tid] + carry;
+        if (r < p.n_qt) {
+            p.row_ptr[r + 1] = buf[tid] + carry;
+            if (staged) ptr_l[r + 1] = buf[tid] + carry;
+        }
         __syncthreads();
-        if (tid == 0) carry += buf[1023];
+        if (tid == 0) carry += buf[kCompactThreads - 1];
         __syncthreads();
     }
-    // row_ptr now holds offsets; row r's list sits at r*n_kt, length
-    // row_ptr[r+1]-row_ptr[r], and moves down to row_ptr[r] (<= r*n_kt).
-    for (int r = 1; r < p.n_qt; ++r) {
-        const int dst = p.row_ptr[r];
-        const int cnt = p.row_ptr[r + 1] - dst;
-        const int64_t src = (int64_t)r * p.n_kt;
-        for (int j0 = 0; j0 < cnt; j0 += 1024) {
-            const int j = j0 + tid;
-            int v = 0;
-            if (j < cnt) v = p.col_idx[src + j];
-            __syncthreads();
-            if (j < cnt) p.col_idx[dst + j] = v;
-            __syncthreads();
+    if (!staged) {
+        // very many query tiles: move row by row
+        for (int r = 1; r < p.n_qt; ++r) {
+            const int dst = p.row_ptr[r];
+            const int cnt = p.row_ptr[r + 1] - dst;
+            const int64_t src = (int64_t)r * p.n_kt;
+            for (int j0 = 0; j0 < cnt; j0 += kCompactThreads) {
+                const int j = j0 + tid;
+                if (j < cnt) buf[tid] = p.col_idx[src + j];   // the LDS write waits for the load
+                __syncthreads();
+                if (j < cnt) p.col_idx[dst + j] = buf[tid];
+                __syncthreads();
+            }
         }
+        return;
+    }
+    const int nnz = ptr_l[p.n_qt];
+    for (int e0 = 0; e0 < nnz; e0 += kCompactThreads * kMovePerThread) {
+        // read the chunk into LDS (a load completes before its LDS write), then write it back
+#pragma unroll
+        for (int k = 0; k < kMovePerThread; ++k) {
+            const int e = e0 + k * kCompactThreads + tid;
+            if (e < nnz) {
+                // last row r with ptr_l[r] <= e (then e < ptr_l[r + 1])
+                int lo = 0, hi = p.n_qt - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (ptr_l[mid] <= e) lo = mid;
+                    else hi = mid - 1;
+                }
+                stage[k * kCompactThreads + tid] = p.col_idx[(int64_t)lo * p.n_kt + (e - ptr_l[lo])];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kMovePerThread; ++k) {
+            const int e = e0 + k * kCompactThreads + tid;
+            if (e < nnz) p.col_idx[e] = stage[k * kCompactThreads + tid];
+        }
+        __syncthreads();
     }
 }
 

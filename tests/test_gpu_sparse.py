@@ -72,7 +72,21 @@ def test_mask_1024_pruned_last_step(api):
         _assert_mask_equal(api, wl.h, wl.w, K - 1, K, 64, 64, 7, 7, 2, 2, q_index=sel, what=f"pruned seed {seed}")
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("tk,sink,local", [(1, 7, 7), (1, 13, 13), (3, 2, 9)])
+def test_mask_1024_last_step_many_key_tiles(api, tk, sink, local):
+    # more than 8192 key tiles: the builder's bitmap takes several passes
+    wl = WORKLOADS["var1024_sparse"]
+    K = wl.num_scales
+    _assert_mask_equal(api, wl.h, wl.w, K - 1, K, 256, tk, sink, local, 2, 2, what=f"tile_k {tk} sink {sink}")
+
+
+def test_mask_1024_full_sequence_many_query_tiles(api):
+    # more than 8192 query tiles: the compaction moves row by row
+    wl = WORKLOADS["var1024_sparse"]
+    _assert_mask_equal(api, wl.h, wl.w, 0, wl.num_scales, 1, 64, 7, 7, 2, 2, what="tile_q 1")
+
+
+@pytest.mark.parametrize("seed", range(24))
 def test_mask_random_schedules_and_params(api, seed):
     rng = np.random.default_rng(1000 + seed)
     K = int(rng.integers(1, 7))
