@@ -16,7 +16,8 @@ Sources (web pages on visual-autoregressive next-scale generation):
 * "ARVAR: Accelerating Visual Autoregressive Model via Attention Retrospect",
   Background & Motivation (a whole token grid per scale, KV caching,
   FlashAttention), Key Design 2 (gather of the retained positions) and Key
-  Design 3, Equations (8)-(9) (nearest base + overwrite scatter).
+  Design 3, Equations (8)-(9) (nearest base + overwrite scatter); Key
+  Design 2 also for the attention-guided choice of the retained positions.
 * "LiteVAR: Compressing Visual Autoregressive Modelling with Efficient
   Attention and Quantization", method tags "Attention" and "Softmax".
 
@@ -29,6 +30,8 @@ Modules:
   and its CSR form.                                       (pinned: see tests)
 * ``scatter``    -- nearest-upsampled base overwritten at retained indices.
                                                           (pinned: see tests)
+* ``selection``  -- attention-guided saliency of a small step and the Top-K
+  choice of the retained positions on a larger grid.     (pinned: see tests)
 
 Every function here is pinned by ``-m "not gpu"`` tests against something other
 than itself (brute force, closed forms, invariants, library routines); none is
@@ -39,6 +42,7 @@ from .schedule import offsets, token_coords, scale_of_tokens
 from .attention import attention
 from .tile_mask import tile_mask, mask_to_csr, csr_to_mask
 from .scatter import nearest_source_index, scatter_restore
+from .selection import saliency, selection_scores, select_positions
 
 __all__ = [
     "offsets",
@@ -50,4 +54,7 @@ __all__ = [
     "csr_to_mask",
     "nearest_source_index",
     "scatter_restore",
+    "saliency",
+    "selection_scores",
+    "select_positions",
 ]
