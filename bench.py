@@ -288,6 +288,24 @@ def main():
 
     sparse_gen_ms = time_launch(sparse_gen, reps=max(2, R // 4))
 
+    # attention-guided selection of the retained positions: saliency of the
+    # 32x32 step (3 steps before the last) from its attention's LSE, then
+    # Top-K of the map upsampled to 64x64 (not part of the pass, whose pruned
+    # subset is the workload's seeded one)
+    src = K - 4
+    n_src = off[src + 1] - off[src]
+    _, lse_src = api.var_attn_dense(sched, qsteps[src], k, v, src, src + 1, out=dense_out[src], return_lse=True)
+    sal = torch.empty(B, H, n_src, dtype=torch.float32, device=dev)
+    sel_guided = torch.empty(n_sel, dtype=torch.int32, device=dev)
+    saliency_ms = time_launch(lambda: api.var_attn_saliency(sched, qsteps[src], k, lse_src, src, out=sal))
+    select_ms = time_launch(lambda: api.var_select_topk(sal, wl.grids[src], wl.grids[src], wl.grids[K - 1],
+                                                         wl.grids[K - 1], n_sel, out=sel_guided))
+    saliency_flops = 2.0 * D * B * H * n_src * n_src
+
+    # Branch Halving on the last step: the conditional branch alone (batch 1)
+    bh_out = torch.empty(1, H, 4096, D, dtype=bf, device=dev)
+    bh_ms = time_launch(lambda: api.var_attn_dense(sched, qsteps[K - 1][:1], k[:1], v[:1], K - 1, K, out=bh_out))
+
     # dominant launch: the dense bf16 attention kernel on the last step (4096
     # queries x 10521 keys), which carries 61% of the pass's FLOPs
     last = K - 1
@@ -353,6 +371,19 @@ def main():
             "speedup_last_step_unpruned_vs_dense": round(dense_ms[last] / sparse_full_ms, 3),
             "speedup_last_step_pruned_vs_dense": round(dense_ms[last] / (sparse_last_ms + scatter_ms), 3),
             "speedup_generation_vs_dense": round(dense_gen_ms / sparse_gen_ms, 3),
+        },
+        "guided_selection": {
+            "source_step_grid": f"{wl.grids[src]}x{wl.grids[src]}",
+            "saliency_ms": round(saliency_ms, 4),
+            "saliency_gflop": round(saliency_flops / 1e9, 3),
+            "saliency_tflops": round(saliency_flops / (saliency_ms * 1e-3) / 1e12, 2),
+            "select_topk_ms": round(select_ms, 4),
+            "selected": f"{n_sel} of {wl.grids[K - 1] ** 2}",
+        },
+        "branch_halving": {
+            "last_step_cond_only_ms": round(bh_ms, 4),
+            "last_step_cond_only_tflops": round(dense_flops[last] / 2 / (bh_ms * 1e-3) / 1e12, 2),
+            "speedup_vs_both_branches": round(dense_ms[last] / bh_ms, 3),
         },
         "wall_s_timed": round(wall, 3),
     }

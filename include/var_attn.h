@@ -167,6 +167,53 @@ var_status var_attn_block_sparse(const var_schedule* sched, const var_attn_desc*
                                  int32_t tile_q, int32_t tile_k, void* stream);
 
 /*
+ * Saliency of the positions of one (small) step, the signal of attention-guided
+ * pruning ("ARVAR ...", Key Design 2: the attention of an earlier step of the
+ * same layer is reduced to one score per position of its grid; A Worked
+ * Example: the source step lies M = 3 steps before the pruned one).  The page
+ * leaves the reduction axis, the normalisation and the head aggregation
+ * open; this call takes the self-attention block of the step's attention
+ * weights P (rows normalised over every key the query sees) and returns, per
+ * (batch, head), the mean over the step's queries of each own-scale column:
+ *   saliency[b][h][u] = (1/n_s) * sum_i exp(scale * q_i . k_{off[s]+u} - lse[b][h][i])
+ * for u < n_s = h_s*w_s.
+ *  desc   batch, heads, head_dim (64 or 128), softmax_scale as for
+ *         var_attn_dense; q_scale_end must be q_scale_begin + 1 (= s); bf16
+ *         input only (out_dtype is ignored).
+ *  q, k   as in var_attn_dense for that call (q row j = token off[s] + j).
+ *  lse    device fp32 [B][H][n_s], contiguous: the natural-log LSE that
+ *         var_attn_dense returned for the same call (not re-derived here).
+ *  saliency device fp32 [B][H][n_s], contiguous, written.
+ * Errors: VAR_ERR_RANGE for a range of more than one scale; VAR_ERR_UNSUPPORTED
+ * for f32 input or other head dims.
+ */
+var_status var_attn_saliency(const var_schedule* sched, const var_attn_desc* desc,
+                             const void* q, var_layout q_l, const void* k, var_layout k_l,
+                             const float* lse, float* saliency, void* stream);
+
+/*
+ * Top-K choice of the retained positions of a pruned step ("ARVAR ...", Key
+ * Design 2: the saliency map is interpolated to the current grid and Top-K
+ * gives the indices to gather; Key Design 3 scatters them back).
+ * score(t) for t = (y, x) of the h_dst x w_dst grid is
+ *   S[floor(y*h_src/h_dst) * w_src + floor(x*w_src/w_dst)],
+ *   S[u] = saliency[0][u] + saliency[1][u] + ... (fp32, in map order)
+ * (nearest interpolation, the rule of var_scatter_restore).  The n_keep
+ * positions with the largest score are written to q_index in ascending
+ * order; among equal scores lower positions win.  -0.0 counts as 0; scores
+ * must not be NaN (with NaN the result is still n_keep distinct ascending
+ * positions, in an unspecified choice).
+ *  saliency device fp32 [maps][h_src*w_src] contiguous (e.g. the output of
+ *           var_attn_saliency with maps = B*H); h_src*w_src <= 8192.
+ *  q_index  device int32[n_keep], written; n_keep in [0, h_dst*w_dst]
+ *           (0 launches nothing).  Usable directly as the q_index of the
+ *           attention, mask and scatter calls.
+ * One workgroup; meant for grids of a few thousand positions.
+ */
+var_status var_select_topk(int32_t maps, const float* saliency, int32_t h_src, int32_t w_src,
+                           int32_t h_dst, int32_t w_dst, int32_t n_keep, int32_t* q_index, void* stream);
+
+/*
  * Structural reconstruction of a pruned grid ("ARVAR ...", Key Design 3,
  * Equations (8)-(9)): out = Scatter(Up(base; h_out, w_out), q_index, upd).
  * Up is nearest neighbour with source (floor(y*h_in/h_out), floor(x*w_in/w_out));

@@ -7,8 +7,9 @@ kernels; there is no fallback.  Importing this module raises if the library
 has not been built (``python -m scale_wise_attention_amd.build``).
 
 Functions carry the C names: ``var_attn_dense``, ``var_build_tile_mask``,
-``var_attn_block_sparse``, ``var_scatter_restore`` (plus the host-only helpers
-``var_schedule_extent`` and ``var_tile_mask_dims``).
+``var_attn_block_sparse``, ``var_scatter_restore``, ``var_attn_saliency``,
+``var_select_topk`` (plus the host-only helpers ``var_schedule_extent`` and
+``var_tile_mask_dims``).
 """
 
 import ctypes
@@ -28,7 +29,8 @@ STATUS = {0: "VAR_OK", 1: "VAR_ERR_NULL", 2: "VAR_ERR_SCHEDULE", 3: "VAR_ERR_RAN
 MAX_SCALES = 32
 
 EXPORTED = ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_build_tile_mask",
-            "var_attn_block_sparse", "var_scatter_restore", "var_status_string", "var_last_error")
+            "var_attn_block_sparse", "var_scatter_restore", "var_attn_saliency", "var_select_topk",
+            "var_status_string", "var_last_error")
 
 
 class VarAttnError(RuntimeError):
@@ -75,8 +77,10 @@ def _load():
                                           P, P, i32, P, P, i32, i32, P]
     lib.var_scatter_restore.argtypes = [i32, i32, ctypes.c_int, P, i64, i64, i32, i32, P, i64, i64, P, i32,
                                         P, i64, i64, i32, i32, P, P]
+    lib.var_attn_saliency.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, P, P]
+    lib.var_select_topk.argtypes = [i32, P, i32, i32, i32, i32, i32, P, P]
     for name in ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_build_tile_mask",
-                 "var_attn_block_sparse", "var_scatter_restore"):
+                 "var_attn_block_sparse", "var_scatter_restore", "var_attn_saliency", "var_select_topk"):
         getattr(lib, name).restype = ctypes.c_int
     lib.var_status_string.argtypes = [ctypes.c_int]
     lib.var_status_string.restype = ctypes.c_char_p
@@ -294,4 +298,55 @@ def var_scatter_restore(base, h_in, w_in, upd, q_index, h_out, w_out, out=None, 
                                    u3.stride(1) if u3 is not None else 0, _ptr(q_index), n_sel,
                                    _ptr(o3), o3.stride(0), o3.stride(1), h_out, w_out, _ptr(err_flag),
                                    _stream(base.device)))
+    return out
+
+
+def var_attn_saliency(schedule, q, k, lse, step, softmax_scale=0.0, out=None):
+    """Per-(batch, head) saliency [B, H, n_s] (fp32) of the positions of scale `step`.
+
+    q [B, H, n_s, D] bf16 (the step's queries), k [B, H, >= off[step+1], D] bf16,
+    lse [B, H, n_s] fp32 from var_attn_dense(..., step, step + 1, return_lse=True).
+    """
+    s = _as_schedule(schedule)
+    _, n_s, kv_len = var_schedule_extent(s, step, step + 1)
+    for name, t in (("q", q), ("k", k)):
+        if t.dim() != 4 or not t.is_cuda or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a 4-D bf16 device tensor [batch, head, token, dim]")
+    B, H, _, D = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D or k.device != q.device:
+        raise ValueError("q and k disagree in batch, heads, head_dim or device")
+    if q.shape[2] < n_s or k.shape[2] < kv_len:
+        raise ValueError("q or k hold too few tokens for the step")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n_s) or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError(f"lse must be a contiguous fp32 tensor of shape {(B, H, n_s)} on q's device")
+    if out is None:
+        out = torch.empty((B, H, n_s), dtype=torch.float32, device=q.device)
+    elif (out.dtype != torch.float32 or tuple(out.shape) != (B, H, n_s) or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError(f"out must be a contiguous fp32 tensor of shape {(B, H, n_s)} on q's device")
+    desc = AttnDesc(B, H, D, step, step + 1, float(softmax_scale), VAR_BF16, VAR_F32)
+    _check(LIB.var_attn_saliency(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k), _layout(k),
+                                 _ptr(lse), _ptr(out), _stream(q.device)))
+    return out
+
+
+def var_select_topk(saliency, h_src, w_src, h_dst, w_dst, n_keep, out=None):
+    """Retained positions (int32 [n_keep], ascending) of the h_dst x w_dst grid.
+
+    saliency: fp32 [..., h_src*w_src] contiguous; the leading dims are the maps
+    (e.g. [B, H, n_s] from var_attn_saliency), summed in order.
+    """
+    n_src = h_src * w_src
+    if saliency.dtype != torch.float32 or not saliency.is_contiguous() or not saliency.is_cuda:
+        raise ValueError("saliency must be a contiguous fp32 device tensor")
+    if saliency.shape[-1] != n_src:
+        raise ValueError(f"saliency's last dim must be h_src*w_src = {n_src}")
+    maps = saliency.numel() // n_src
+    if out is None:
+        out = torch.empty(max(0, int(n_keep)), dtype=torch.int32, device=saliency.device)
+    elif out.dtype != torch.int32 or out.numel() < n_keep or not out.is_contiguous() or out.device != saliency.device:
+        raise ValueError("out must be a contiguous int32 tensor with n_keep entries on saliency's device")
+    _check(LIB.var_select_topk(maps, _ptr(saliency), h_src, w_src, h_dst, w_dst, int(n_keep),
+                               _ptr(out) if n_keep > 0 else ctypes.c_void_p(0), _stream(saliency.device)))
     return out

@@ -67,7 +67,35 @@ struct ScatterParams {
 // Launchers: return the hipError_t of the launch.
 hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, bool out_bf16, bool sparse, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int head_dim, bool sparse, hipStream_t s);
+// Saliency of one step's own-scale keys (column means of its attention weights).
+struct SaliencyParams {
+    const void* q;        // bf16 queries of the step, row j = token key_first + j
+    const void* k;        // bf16 key cache
+    const float* lse;     // [B*H][n_s] natural-log LSE of the step's attention rows
+    float* sal;           // [B*H][n_s] output
+    int64_t q_sb, q_sh, q_st;
+    int64_t k_sb, k_sh, k_st;
+    int32_t B, H;
+    int32_t n_s;          // tokens of the step's scale (queries = own-scale keys)
+    int32_t key_first;    // token index of the scale's first key
+    int32_t n_kb;         // 64-key blocks per (b, h)
+    float scale_log2;     // softmax scale * log2(e)
+};
+
+// Largest source grid of the Top-K selection (source scores live in LDS).
+constexpr int kSelectMaxSrc = 8192;
+// Destination grids up to this size keep their keys in LDS during the selection.
+constexpr int kSelectDstCache = 7680;
+
+struct SelectParams {
+    const float* sal;     // [maps][h_src*w_src]
+    int32_t* q_index;     // [n_keep] output, ascending
+    int32_t maps, h_src, w_src, h_dst, w_dst, n_keep;
+};
+
 hipError_t launch_tile_mask(const MaskParams& p, hipStream_t s);
+hipError_t launch_saliency(const SaliencyParams& p, int head_dim, hipStream_t s);
+hipError_t launch_select_topk(const SelectParams& p, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, hipStream_t s);
 

@@ -312,6 +312,76 @@ VAR_EXPORT var_status var_build_tile_mask(const var_schedule* sched, int32_t b, 
     return hip_status(varattn::launch_tile_mask(p, s), "var_build_tile_mask launch");
 }
 
+VAR_EXPORT var_status var_attn_saliency(const var_schedule* sched, const var_attn_desc* d, const void* q,
+                                        var_layout q_l, const void* k, var_layout k_l, const float* lse,
+                                        float* saliency, void* stream) {
+    Offsets off;
+    var_status st = check_schedule(sched, &off);
+    if (st != VAR_OK) return st;
+    if (!d) return fail(VAR_ERR_NULL, "desc is NULL");
+    if ((st = check_range(off, d->q_scale_begin, d->q_scale_end)) != VAR_OK) return st;
+    if (d->q_scale_end != d->q_scale_begin + 1)
+        return fail(VAR_ERR_RANGE, "saliency takes one scale, got [%d, %d)", d->q_scale_begin, d->q_scale_end);
+    if (d->batch < 1 || d->heads < 1 || (int64_t)d->batch * d->heads > (1 << 20))
+        return fail(VAR_ERR_RANGE, "batch=%d heads=%d invalid", d->batch, d->heads);
+    if (d->in_dtype != VAR_BF16 || (d->head_dim != 64 && d->head_dim != 128))
+        return fail(VAR_ERR_UNSUPPORTED, "saliency supports bf16 input with head_dim 64 or 128");
+    if (!(d->softmax_scale >= 0.f) || std::isinf(d->softmax_scale))
+        return fail(VAR_ERR_RANGE, "softmax_scale must be finite and >= 0 (0 = 1/sqrt(D))");
+    if (!q || !k || !lse || !saliency) return fail(VAR_ERR_NULL, "q, k, lse and saliency must be non-NULL");
+    if (!aligned16(q) || !aligned16(k)) return fail(VAR_ERR_STRIDE, "q and k must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(saliency) & 3u))
+        return fail(VAR_ERR_STRIDE, "lse and saliency must be 4-byte aligned");
+    if ((st = check_layout("q", q_l, d->head_dim, 2)) != VAR_OK) return st;
+    if ((st = check_layout("k", k_l, d->head_dim, 2)) != VAR_OK) return st;
+    varattn::SaliencyParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q = q;
+    p.k = k;
+    p.lse = lse;
+    p.sal = saliency;
+    p.q_sb = q_l.batch; p.q_sh = q_l.head; p.q_st = q_l.token;
+    p.k_sb = k_l.batch; p.k_sh = k_l.head; p.k_st = k_l.token;
+    p.B = d->batch;
+    p.H = d->heads;
+    p.key_first = off.off[d->q_scale_begin];
+    p.n_s = off.off[d->q_scale_end] - p.key_first;
+    p.n_kb = (p.n_s + 63) / 64;
+    if ((int64_t)p.B * p.H * p.n_kb >= ((int64_t)1 << 31)) return fail(VAR_ERR_RANGE, "saliency grid too large");
+    const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return hip_status(varattn::launch_saliency(p, d->head_dim, reinterpret_cast<hipStream_t>(stream)),
+                      "var_attn_saliency launch");
+}
+
+VAR_EXPORT var_status var_select_topk(int32_t maps, const float* saliency, int32_t h_src, int32_t w_src,
+                                      int32_t h_dst, int32_t w_dst, int32_t n_keep, int32_t* q_index,
+                                      void* stream) {
+    if (maps < 1 || maps > (1 << 20)) return fail(VAR_ERR_RANGE, "maps=%d outside [1, 2^20]", maps);
+    if (h_src < 1 || w_src < 1 || h_dst < 1 || w_dst < 1 || h_src > 4096 || w_src > 4096 || h_dst > 4096 ||
+        w_dst > 4096)
+        return fail(VAR_ERR_RANGE, "grids %dx%d -> %dx%d outside [1, 4096]", h_src, w_src, h_dst, w_dst);
+    if (h_src * w_src > varattn::kSelectMaxSrc)
+        return fail(VAR_ERR_UNSUPPORTED, "source grid %dx%d above %d positions", h_src, w_src, varattn::kSelectMaxSrc);
+    const int64_t n_dst = (int64_t)h_dst * w_dst;
+    if (n_keep < 0 || n_keep > n_dst)
+        return fail(VAR_ERR_RANGE, "n_keep=%d outside [0, %lld]", n_keep, (long long)n_dst);
+    if (n_keep == 0) return ok();
+    if (!saliency || !q_index) return fail(VAR_ERR_NULL, "saliency and q_index must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(saliency) & 3u) || (reinterpret_cast<uintptr_t>(q_index) & 3u))
+        return fail(VAR_ERR_STRIDE, "saliency and q_index must be 4-byte aligned");
+    varattn::SelectParams p;
+    p.sal = saliency;
+    p.q_index = q_index;
+    p.maps = maps;
+    p.h_src = h_src;
+    p.w_src = w_src;
+    p.h_dst = h_dst;
+    p.w_dst = w_dst;
+    p.n_keep = n_keep;
+    return hip_status(varattn::launch_select_topk(p, reinterpret_cast<hipStream_t>(stream)), "var_select_topk launch");
+}
+
 VAR_EXPORT var_status var_scatter_restore(int32_t maps, int32_t row_elems, var_dtype dtype, const void* base,
                                           int64_t base_map_stride, int64_t base_row_stride, int32_t h_in,
                                           int32_t w_in, const void* upd, int64_t upd_map_stride,

@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_match_header(api):
     declared = _declared()
-    assert len(declared) == 8
+    assert len(declared) == 10
     for name in declared:
         assert hasattr(api.LIB, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True).stdout
@@ -161,3 +161,31 @@ def test_scatter_validation_errors(api):
     assert call(brs=64) == E("VAR_ERR_STRIDE")
     assert call(oms=-1) == E("VAR_ERR_STRIDE")
     assert call(maps=0) == 0   # nothing to do, nothing launched
+
+
+def test_saliency_and_select_validation_errors(api):
+    s = api.make_schedule(W1024, W1024)
+    E = lambda n: _code(api, n)
+    P = ctypes.c_void_p
+    L = api.Layout(2 * 16 * 1024 * 128, 1024 * 128, 128)
+    sal = api.LIB.var_attn_saliency
+
+    def call(desc, q=FAKE, k=FAKE, lse=FAKE, out=FAKE):
+        return sal(ctypes.byref(s), ctypes.byref(desc), P(q), L, P(k), L, P(lse), P(out), P(0))
+
+    assert call(_desc(api, q_scale_begin=9, q_scale_end=11)) == E("VAR_ERR_RANGE")
+    assert call(_desc(api, q_scale_begin=9, q_scale_end=10, in_dtype=api.VAR_F32, head_dim=64)) == E("VAR_ERR_UNSUPPORTED")
+    assert call(_desc(api, q_scale_begin=9, q_scale_end=10, head_dim=96)) == E("VAR_ERR_UNSUPPORTED")
+    assert call(_desc(api, q_scale_begin=9, q_scale_end=10), lse=0) == E("VAR_ERR_NULL")
+    assert call(_desc(api, q_scale_begin=9, q_scale_end=10), out=FAKE + 2) == E("VAR_ERR_STRIDE")
+    assert call(_desc(api, q_scale_begin=9, q_scale_end=10), q=FAKE + 8) == E("VAR_ERR_STRIDE")
+    assert call(_desc(api, q_scale_begin=9, q_scale_end=10, batch=0)) == E("VAR_ERR_RANGE")
+    sel = api.LIB.var_select_topk
+    assert sel(32, P(FAKE), 32, 32, 64, 64, 4097, P(FAKE), P(0)) == E("VAR_ERR_RANGE")
+    assert sel(32, P(FAKE), 32, 32, 64, 64, -1, P(FAKE), P(0)) == E("VAR_ERR_RANGE")
+    assert sel(0, P(FAKE), 32, 32, 64, 64, 10, P(FAKE), P(0)) == E("VAR_ERR_RANGE")
+    assert sel(32, P(FAKE), 0, 32, 64, 64, 10, P(FAKE), P(0)) == E("VAR_ERR_RANGE")
+    assert sel(32, P(FAKE), 91, 91, 128, 128, 10, P(FAKE), P(0)) == E("VAR_ERR_UNSUPPORTED")
+    assert sel(32, P(0), 32, 32, 64, 64, 10, P(FAKE), P(0)) == E("VAR_ERR_NULL")
+    assert sel(32, P(FAKE), 32, 32, 64, 64, 10, P(FAKE + 2), P(0)) == E("VAR_ERR_STRIDE")
+    assert sel(32, P(0), 32, 32, 64, 64, 0, P(0), P(0)) == 0   # nothing to select, nothing launched

@@ -219,3 +219,26 @@ def test_invalid_shapes_raise_before_launch(api):
         api.var_attn_dense(_sched(wl), q, k[:, :, :100], v, 9, 10)         # KV shorter than kv_len
     with pytest.raises(api.VarAttnError):
         api.var_attn_dense(_sched(wl), q, k, v, 9, 11)                     # bad scale range
+
+
+def test_branch_halving_cond_only_call_equals_cond_half(api):
+    """Branch Halving ("ARVAR ...", Key Design 1) at the attention level: the
+    step runs the conditional branch alone (a batch-1 call on batch entry 0)
+    and its output stands for both branches.  Each (batch, head) is computed
+    independently, so the batch-1 result equals the conditional half of the
+    two-branch call bit for bit, dense and block-sparse."""
+    wl = WORKLOADS["var1024_sparse"]
+    q, k, v = make_qkv(wl, 1, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    K = wl.num_scales
+    qs = q[:, :, off[K - 1]:]
+    both = api.var_attn_dense(_sched(wl), qs, k, v, K - 1, K, out_dtype=torch.bfloat16)
+    cond = api.var_attn_dense(_sched(wl), qs[:1], k[:1], v[:1], K - 1, K, out_dtype=torch.bfloat16)
+    assert torch.equal(cond.view(torch.int16), both[:1].view(torch.int16))
+    repeated = cond.expand(2, -1, -1, -1)          # the repeat that restores the two-branch interface
+    assert torch.equal(repeated[1].view(torch.int16), both[0].view(torch.int16))
+    mp = api.mask_params()
+    rp, ci = api.var_build_tile_mask(_sched(wl), K - 1, K, mp)
+    both_s = api.var_attn_block_sparse(_sched(wl), qs, k, v, K - 1, K, rp, ci)
+    cond_s = api.var_attn_block_sparse(_sched(wl), qs[:1], k[:1], v[:1], K - 1, K, rp, ci)
+    assert torch.equal(cond_s, both_s[:1])
