@@ -85,7 +85,7 @@ struct SaliencyParams {
 // Largest source grid of the Top-K selection (source scores live in LDS).
 constexpr int kSelectMaxSrc = 8192;
 // Destination grids up to this size keep their keys in LDS during the selection.
-constexpr int kSelectDstCache = 7680;
+constexpr int kSelectDstCache = 6912;
 
 struct SelectParams {
     const float* sal;     // [maps][h_src*w_src]

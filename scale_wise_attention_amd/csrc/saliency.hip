@@ -25,8 +25,9 @@
 // column block are reduced once at the end, then the 4 waves in order.
 //
 // select_topk_kernel: one workgroup.  The summed source scores live in LDS as
-// order-preserving 32-bit keys; a 4-digit radix select finds the key of the
-// n_keep-th best position, then one ascending sweep with block-wide scans
+// order-preserving 32-bit keys; a 4-digit radix select (histogram, then a
+// block-wide scan over the digits) finds the key of the n_keep-th best
+// position, then one ascending sweep with block-wide scans
 // writes the positions above it and the lowest-numbered ones equal to it.
 #include <hip/hip_runtime.h>
 
@@ -141,6 +142,7 @@ __global__ __launch_bounds__(kSalThreads, 2) void saliency_kernel(const Saliency
 }
 
 constexpr int kSelThreads = 1024;
+constexpr int kSelSubHist = 4;
 
 // order-preserving key of a score: larger float -> larger unsigned; -0 counts as +0
 __device__ __forceinline__ uint32_t score_key(float f) {
@@ -174,7 +176,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wave_tot, int& total)
 __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const SelectParams p) {
     __shared__ uint32_t src_key[kSelectMaxSrc];
     __shared__ uint32_t dst_key[kSelectDstCache];
-    __shared__ int hist[256];
+    __shared__ int hist[256 * kSelSubHist];
     __shared__ int wave_tot[kSelThreads / 64];
     __shared__ uint32_t sh_prefix;
     __shared__ int sh_need;
@@ -211,25 +213,30 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(const SelectPa
         sh_need = p.n_keep;
     }
     __syncthreads();
-    // radix select of the n_keep-th largest key, 8 bits at a time from the top
+    // radix select of the n_keep-th largest key, 8 bits at a time from the top;
+    // 4 sub-histograms (by wave) spread the LDS atomics
     uint32_t mask = 0u;
+    const int sub = (tid >> 6) & (kSelSubHist - 1);
     for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
+        for (int i = tid; i < 256 * kSelSubHist; i += kSelThreads) hist[i] = 0;
         __syncthreads();
         const uint32_t prefix = sh_prefix;
+        const int need = sh_need;
         for (int t = tid; t < n_dst; t += kSelThreads) {
             const uint32_t k = key_of(t);
-            if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
+            if ((k & mask) == prefix) atomicAdd(&hist[sub * 256 + ((k >> shift) & 255u)], 1);
         }
         __syncthreads();
-        if (tid == 0) {
-            int need = sh_need, d = 255;
-            for (; d > 0; --d) {
-                if (hist[d] >= need) break;
-                need -= hist[d];
-            }
-            sh_need = need;                       // still to take among keys with this digit
-            sh_prefix = prefix | ((uint32_t)d << shift);
+        // thread i < 256 holds digit 255 - i; an exclusive scan in that order gives,
+        // per digit, the count of keys with a larger digit
+        int cnt = 0;
+        if (tid < 256)
+            for (int j = 0; j < kSelSubHist; ++j) cnt += hist[j * 256 + 255 - tid];
+        int total;
+        const int larger = block_excl_scan(cnt, wave_tot, total);
+        if (tid < 256 && larger < need && larger + cnt >= need) {
+            sh_need = need - larger;              // still to take among keys with this digit
+            sh_prefix = prefix | ((uint32_t)(255 - tid) << shift);
         }
         mask |= 255u << shift;
         __syncthreads();
