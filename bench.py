@@ -147,12 +147,32 @@ def main():
     full_ci = torch.empty(n_qt_full * n_kt_full, dtype=torch.int32, device=dev)
     full_out = torch.empty(B, H, 4096, D, dtype=bf, device=dev)
 
+    # key splits for launches with fewer work items than compute units (the
+    # middle steps); the split count per step comes from the library's plan
+    for s in range(K):
+        rp, ci, idx = csr[s]
+        api.var_build_tile_mask(sched, s, s + 1, mp, q_index=idx, row_ptr=rp, col_idx=ci)
+    torch.cuda.synchronize()
+    dense_splits, sparse_splits, ws_bytes = [], [], 0
+    for s in range(K):
+        n_d, b_d = api.var_attn_split_plan(sched, s, s + 1, B, H, D)
+        rp_h = csr[s][0].cpu().numpy()
+        rows_s = n_sel if s == K - 1 else off[s + 1] - off[s]
+        hint = max(1, int(round(float(rp_h[-1]) / max(1, rp_h.size - 1))))
+        n_s, b_s = api.var_attn_split_plan(sched, s, s + 1, B, H, D, n_sel=n_sel if s == K - 1 else 0,
+                                           kv_tiles_hint=hint)
+        dense_splits.append(n_d)
+        sparse_splits.append(n_s)
+        ws_bytes = max(ws_bytes, b_d, b_s)
+    workspace = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device=dev)
+
     def sparse_full_last_step():
         api.var_build_tile_mask(sched, K - 1, K, mp, row_ptr=full_rp, col_idx=full_ci)
         api.var_attn_block_sparse(sched, qsteps[K - 1], k, v, K - 1, K, full_rp, full_ci, out=full_out)
 
     def dense_step(s):
-        api.var_attn_dense(sched, qsteps[s], k, v, s, s + 1, out=dense_out[s])
+        api.var_attn_dense(sched, qsteps[s], k, v, s, s + 1, out=dense_out[s], n_splits=dense_splits[s],
+                           workspace=workspace)
 
     def mask_step(s):
         rp, ci, idx = csr[s]
@@ -161,7 +181,8 @@ def main():
     def sparse_step(s):
         rp, ci, idx = csr[s]
         out = pruned_out if s == K - 1 else sparse_out[s]
-        api.var_attn_block_sparse(sched, qsteps[s], k, v, s, s + 1, rp, ci, out=out, q_index=idx)
+        api.var_attn_block_sparse(sched, qsteps[s], k, v, s, s + 1, rp, ci, out=out, q_index=idx,
+                                  n_splits=sparse_splits[s], workspace=workspace)
 
     def scatter_step():
         api.var_scatter_restore(sparse_out[K - 2], wl.grids[K - 2], wl.grids[K - 2], pruned_out, sel_t,
@@ -334,6 +355,7 @@ def main():
                         "step) with the last step pruned to 1638 of 4096 queries and scattered over 48x48",
             "launch": "hipGraph replay of the whole pass" if graph is not None else "eager",
             "pass_gflop": round(pass_flops / 1e9, 3),
+            "key_splits": {"dense": dense_splits, "sparse": sparse_splits},
         },
         "roofline": {
             "bound": "mfma",

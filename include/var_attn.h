@@ -125,6 +125,56 @@ var_status var_attn_dense(const var_schedule* sched, const var_attn_desc* desc,
                           float* lse, const int32_t* q_index, int32_t n_sel, void* stream);
 
 /*
+ * Key-split variants of var_attn_dense and var_attn_block_sparse, for launches
+ * with fewer (batch, head, 256-row query tile) work items than the GPU has
+ * compute units: the middle steps of a generation (the "SparVAR ..." and
+ * "ARVAR ..." pages above: each step attends to every earlier scale, so a
+ * step's key range grows while its query grid is still small).  The result
+ * is the same attention; only the order of the floating-point sums differs.
+ * Each work item is split into n_splits parts, each taking an equal share of
+ * its key tiles (dense) or of each 64-row mask row's kept tiles (sparse);
+ * every part writes its rows' normalised O and LSE in fp32 to the workspace,
+ * and a second launch combines them:
+ *   O = sum_s exp(LSE_s - M) O_s / sum_s exp(LSE_s - M),  LSE = M + log(sum ...),
+ *   M = max_s LSE_s  (a part in which a row sees no key has LSE_s = -inf).
+ *  n_splits  1..8; 1 is exactly var_attn_dense / var_attn_block_sparse (the
+ *            workspace is then not used and may be NULL).  > 1 needs bf16 input.
+ *  workspace device memory of at least n_splits*B*H*rows*(D+1)*4 bytes
+ *            (0 for n_splits = 1), 16-byte aligned, owned by the caller; its
+ *            contents on entry do not matter and on return are unspecified.
+ *            Calls that share a workspace must be ordered on one stream.
+ *  Other arguments as in var_attn_dense / var_attn_block_sparse.
+ * Errors: VAR_ERR_RANGE for n_splits outside 1..8, VAR_ERR_UNSUPPORTED for a
+ * split of f32 input, VAR_ERR_NULL / VAR_ERR_STRIDE / VAR_ERR_CAPACITY for a
+ * missing, misaligned or short workspace.
+ */
+var_status var_attn_dense_split(const var_schedule* sched, const var_attn_desc* desc,
+                                const void* q, var_layout q_l, const void* k, var_layout k_l,
+                                const void* v, var_layout v_l, void* o, var_layout o_l,
+                                float* lse, const int32_t* q_index, int32_t n_sel,
+                                int32_t n_splits, void* workspace, int64_t workspace_bytes, void* stream);
+var_status var_attn_block_sparse_split(const var_schedule* sched, const var_attn_desc* desc,
+                                       const void* q, var_layout q_l, const void* k, var_layout k_l,
+                                       const void* v, var_layout v_l, void* o, var_layout o_l,
+                                       float* lse, const int32_t* q_index, int32_t n_sel,
+                                       const int32_t* row_ptr, const int32_t* col_idx,
+                                       int32_t tile_q, int32_t tile_k, int32_t n_splits,
+                                       void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Split count for a call (host only; reads the current device's compute-unit
+ * count, 256 if it cannot): the count with the smallest modelled time
+ * (rounds of work items over the compute units times key tiles per part, plus
+ * the combining launch and its workspace traffic).  kv_tiles_hint: 64-key
+ * tiles a work item visits (0 = ceil(kv_len / 64), the dense count; pass the
+ * mean kept tiles per mask row for a sparse call).  Writes *n_splits and the
+ * workspace bytes it needs (either pointer may be NULL).  n_sel as in
+ * var_attn_dense (0 = no gather).  f32 input always gives 1 and 0 bytes.
+ */
+var_status var_attn_split_plan(const var_schedule* sched, const var_attn_desc* desc, int32_t n_sel,
+                               int32_t kv_tiles_hint, int32_t* n_splits, int64_t* workspace_bytes);
+
+/*
  * Tile mask of the block-sparse variant ("SparVAR ...", abstract: attention
  * sinks, cross-scale locality through an index map, block-wise sparsity).
  * A (query, key) pair is selected when s(key) <= s(query) and either

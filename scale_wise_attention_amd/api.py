@@ -30,6 +30,7 @@ MAX_SCALES = 32
 
 EXPORTED = ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_build_tile_mask",
             "var_attn_block_sparse", "var_scatter_restore", "var_attn_saliency", "var_select_topk",
+            "var_attn_dense_split", "var_attn_block_sparse_split", "var_attn_split_plan",
             "var_status_string", "var_last_error")
 
 
@@ -79,8 +80,15 @@ def _load():
                                         P, i64, i64, i32, i32, P, P]
     lib.var_attn_saliency.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, P, P]
     lib.var_select_topk.argtypes = [i32, P, i32, i32, i32, i32, i32, P, P]
+    lib.var_attn_dense_split.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, Layout, P, Layout,
+                                         P, P, i32, i32, P, i64, P]
+    lib.var_attn_block_sparse_split.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, Layout, P,
+                                                Layout, P, P, i32, P, P, i32, i32, i32, P, i64, P]
+    lib.var_attn_split_plan.argtypes = [SP, ctypes.POINTER(AttnDesc), i32, i32, ctypes.POINTER(i32),
+                                        ctypes.POINTER(i64)]
     for name in ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_build_tile_mask",
-                 "var_attn_block_sparse", "var_scatter_restore", "var_attn_saliency", "var_select_topk"):
+                 "var_attn_block_sparse", "var_scatter_restore", "var_attn_saliency", "var_select_topk",
+                 "var_attn_dense_split", "var_attn_block_sparse_split", "var_attn_split_plan"):
         getattr(lib, name).restype = ctypes.c_int
     lib.var_status_string.argtypes = [ctypes.c_int]
     lib.var_status_string.restype = ctypes.c_char_p
@@ -190,21 +198,53 @@ def _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype, 
     return s, desc, out, lse, rows
 
 
+def var_attn_split_plan(schedule, q_scale_begin, q_scale_end, batch, heads, head_dim, n_sel=0, kv_tiles_hint=0,
+                        dtype=torch.bfloat16):
+    """(n_splits, workspace_bytes) the library picks for a call of this shape."""
+    s = _as_schedule(schedule)
+    desc = AttnDesc(batch, heads, head_dim, q_scale_begin, q_scale_end, 0.0, _dtype_code(dtype), VAR_F32)
+    a, b = ctypes.c_int32(), ctypes.c_int64()
+    _check(LIB.var_attn_split_plan(ctypes.byref(s), ctypes.byref(desc), int(n_sel), int(kv_tiles_hint),
+                                   ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def split_workspace(n_splits, batch, heads, rows, head_dim, device="cuda"):
+    """A workspace tensor for var_attn_*(..., n_splits=n_splits)."""
+    n = n_splits * batch * heads * rows * (head_dim + 1) if n_splits > 1 else 0
+    return torch.empty(max(1, n), dtype=torch.float32, device=device)
+
+
+def _ws_args(n_splits, workspace):
+    if n_splits == 1 and workspace is None:
+        return ctypes.c_void_p(0), 0
+    if workspace is None:
+        raise ValueError("n_splits > 1 needs a workspace (see split_workspace)")
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
 def var_attn_dense(schedule, q, k, v, q_scale_begin, q_scale_end, out=None, out_dtype=None,
-                   softmax_scale=0.0, q_index=None, return_lse=False):
+                   softmax_scale=0.0, q_index=None, return_lse=False, n_splits=1, workspace=None):
     """Dense block-causal attention of the queries of scales [begin, end).
 
     q [B, H, n_q, D] (row j = token off[begin] + j), k / v [B, H, >= kv_len, D];
     returns out [B, H, rows, D] (and lse [B, H, rows]); rows = len(q_index) or n_q.
+    n_splits > 1 runs the key-split variant in `workspace`.
     """
     s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
                                            softmax_scale, q_index, return_lse)
     n_sel = rows if q_index is not None else 0
     if q_index is not None and n_sel == 0:   # an empty selection has no device pointer: nothing to compute
         return (out, lse) if return_lse else out
-    _check(LIB.var_attn_dense(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k), _layout(k),
-                              _ptr(v), _layout(v), _ptr(out), _layout(out), _ptr(lse), _ptr(q_index), n_sel,
-                              _stream(q.device)))
+    args = (ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k), _layout(k), _ptr(v), _layout(v),
+            _ptr(out), _layout(out), _ptr(lse), _ptr(q_index), n_sel)
+    if n_splits == 1 and workspace is None:
+        _check(LIB.var_attn_dense(*args, _stream(q.device)))
+    else:
+        wp, wb = _ws_args(n_splits, workspace)
+        _check(LIB.var_attn_dense_split(*args, int(n_splits), wp, wb, _stream(q.device)))
     return (out, lse) if return_lse else out
 
 
@@ -248,7 +288,8 @@ def var_build_tile_mask(schedule, q_scale_begin, q_scale_end, params, q_index=No
 
 
 def var_attn_block_sparse(schedule, q, k, v, q_scale_begin, q_scale_end, row_ptr, col_idx, out=None,
-                          out_dtype=None, softmax_scale=0.0, q_index=None, return_lse=False, tile_q=64, tile_k=64):
+                          out_dtype=None, softmax_scale=0.0, q_index=None, return_lse=False, tile_q=64, tile_k=64,
+                          n_splits=1, workspace=None):
     s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
                                            softmax_scale, q_index, return_lse)
     n_sel = rows if q_index is not None else 0
@@ -260,9 +301,13 @@ def var_attn_block_sparse(schedule, q, k, v, q_scale_begin, q_scale_end, row_ptr
             raise ValueError(f"{name} must be a contiguous 1-D int32 tensor on q's device")
     if row_ptr.numel() < n_qt + 1:
         raise ValueError(f"row_ptr needs {n_qt + 1} entries")
-    _check(LIB.var_attn_block_sparse(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k), _layout(k),
-                                     _ptr(v), _layout(v), _ptr(out), _layout(out), _ptr(lse), _ptr(q_index), n_sel,
-                                     _ptr(row_ptr), _ptr(col_idx), tile_q, tile_k, _stream(q.device)))
+    args = (ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k), _layout(k), _ptr(v), _layout(v),
+            _ptr(out), _layout(out), _ptr(lse), _ptr(q_index), n_sel, _ptr(row_ptr), _ptr(col_idx), tile_q, tile_k)
+    if n_splits == 1 and workspace is None:
+        _check(LIB.var_attn_block_sparse(*args, _stream(q.device)))
+    else:
+        wp, wb = _ws_args(n_splits, workspace)
+        _check(LIB.var_attn_block_sparse_split(*args, int(n_splits), wp, wb, _stream(q.device)))
     return (out, lse) if return_lse else out
 
 

@@ -221,7 +221,11 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
     const int g = lane >> 5;      // lane half
     const int n = lane & 31;      // column inside a 32-query block
 
-    const int item = xcd_remap(blockIdx.x, gridDim.x);
+    // work item = (batch, head, query tile, key split); the splits of one query
+    // tile are neighbours, so they run on the same XCD
+    const int item_s = xcd_remap(blockIdx.x, gridDim.x);
+    const int split = p.n_splits > 1 ? item_s % p.n_splits : 0;
+    const int item = p.n_splits > 1 ? item_s / p.n_splits : item_s;
     const int qtile = item % p.n_qtiles;
     const int bh = item / p.n_qtiles;
     const int b = bh / p.H;
@@ -260,16 +264,20 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
 
     // ---- key-tile walk (workgroup-uniform) ------------------------------
     const int n_kt_all = (p.kv_len + KT - 1) / KT;
-    int dense_end = 0;      // dense: tiles [0, dense_end)
+    int dense_begin = 0, dense_end = 0;   // dense: tiles [dense_begin, dense_end)
     int dense_next = 0;
-    int lptr[NW], lend[NW], lhead[NW];   // sparse: one list per wave's query tile
+    int lbeg[NW], lptr[NW], lend[NW], lhead[NW];   // sparse: one list per wave's query tile
     if constexpr (SPARSE) {
         const int n_qt = (p.n_rows + KT - 1) / KT;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const int r = qtile * NW + w;
-            lptr[w] = r < n_qt ? p.row_ptr[r] : 0;
-            lend[w] = r < n_qt ? p.row_ptr[r + 1] : 0;
+            const int b0 = r < n_qt ? p.row_ptr[r] : 0;
+            const int cnt = r < n_qt ? p.row_ptr[r + 1] - b0 : 0;
+            // key split: an equal share of this row's kept tiles (in order; the
+            // host bounds cnt * n_splits below 2^31)
+            lbeg[w] = lptr[w] = p.n_splits > 1 ? b0 + cnt * split / p.n_splits : b0;
+            lend[w] = p.n_splits > 1 ? b0 + cnt * (split + 1) / p.n_splits : b0 + cnt;
             lhead[w] = lptr[w] < lend[w] ? p.col_idx[lptr[w]] : INT_MAX;
         }
     }
@@ -288,7 +296,12 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
             mn = min(mn, red[NW + i]);
         }
         __syncthreads();
-        if constexpr (!SPARSE) dense_end = __builtin_amdgcn_readfirstlane((m + KT - 1) / KT);
+        if constexpr (!SPARSE) {
+            const int n_t = (m + KT - 1) / KT;   // key split: an equal share of the tiles
+            dense_begin = p.n_splits > 1 ? __builtin_amdgcn_readfirstlane(n_t * split / p.n_splits) : 0;
+            dense_end = p.n_splits > 1 ? __builtin_amdgcn_readfirstlane(n_t * (split + 1) / p.n_splits) : n_t;
+            dense_next = dense_begin;
+        }
         wg_kmin = __builtin_amdgcn_readfirstlane(mn);
     }
     auto next_tile = [&]() __attribute__((always_inline)) -> TileEnt {
@@ -324,11 +337,11 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
                 const int r = qtile * NW + w;
-                lptr[w] = r < n_qt ? p.row_ptr[r] : 0;
+                lptr[w] = lbeg[w];
                 lhead[w] = lptr[w] < lend[w] ? p.col_idx[lptr[w]] : INT_MAX;
             }
         } else {
-            dense_next = 0;
+            dense_next = dense_begin;
         }
     };
     auto mine = [&](const TileEnt& e) __attribute__((always_inline)) -> bool {
@@ -564,8 +577,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
     //
     // Tiles that need no mask run a branch-free, software-ordered body (waves
     // that do not own such a tile in a block-sparse walk take it with zero
-    // weights); the first tile (which sets the references) and masked tiles
-    // run a general body.  The two bodies sit in separate loops, so the
+    // weights); tiles that set a wave's references and masked tiles run a
+    // general body.  The two bodies sit in separate loops, so the
     // accumulators only flow from one loop into the next.
     auto walk = [&](auto mode_tag) __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode_tag)::value;
@@ -585,7 +598,15 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
         int j = 0;
         auto fast = [&](const TileEnt& e) __attribute__((always_inline)) -> bool {
             // (a tile that only some waves own also runs the branch-free body: the
-            // other waves shift their logits to -inf, so their weights are zero)
+            // other waves shift their logits to -inf, so their weights are zero.
+            // In a block-sparse walk a wave's first owned tile need not be the
+            // walk's first, so a tile that a wave owns while its rows have no
+            // reference max yet takes the general body, which sets it.  In a
+            // dense walk a row that sees any tile of its key range sees the
+            // range's first tile, so every reference is set at j = 0)
+            if constexpr (SPARSE) {
+                if (need_ref && mine(e)) return false;
+            }
             return j > 0 && e.tile * KT + KT <= wg_kmin;
         };
         auto iterate = [&](auto fast_tag) __attribute__((always_inline)) {
@@ -785,37 +806,98 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
 
     // ---- epilogue --------------------------------------------------------
     unsigned char* ob = reinterpret_cast<unsigned char*>(p.o);
+    const bool partial = p.n_splits > 1;   // write this split's normalised O and LSE (fp32) for the merge
+    const int64_t part_row0 = ((int64_t)split * p.B * p.H + b * p.H + h) * p.n_rows;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const float ltot = lsum[qb] + swap_halves(lsum[qb]);
         const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
         if (!row_valid[qb]) continue;
+        if (partial) {
+            float* po = p.part_o + (part_row0 + my_row[qb]) * D;
 #pragma unroll
-        for (int mb = 0; mb < MO; ++mb) {
+            for (int mb = 0; mb < MO; ++mb)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int d0 = 32 * mb + 8 * a + 4 * g;
-                const float x0 = oacc[mb][qb][4 * a + 0] * inv, x1 = oacc[mb][qb][4 * a + 1] * inv;
-                const float x2 = oacc[mb][qb][4 * a + 2] * inv, x3 = oacc[mb][qb][4 * a + 3] * inv;
-                const int64_t e = b * p.o_sb + h * p.o_sh + (int64_t)my_row[qb] * p.o_st + d0;
-                if constexpr (OUT_BF16) {
-                    *reinterpret_cast<u32x2*>(ob + e * 2) = u32x2{f32x2_to_bf16x2(x0, x1), f32x2_to_bf16x2(x2, x3)};
-                } else {
-                    *reinterpret_cast<float4*>(ob + e * 4) = make_float4(x0, x1, x2, x3);
+                for (int a = 0; a < 4; ++a)
+                    *reinterpret_cast<float4*>(po + 32 * mb + 8 * a + 4 * g) =
+                        make_float4(oacc[mb][qb][4 * a + 0] * inv, oacc[mb][qb][4 * a + 1] * inv,
+                                    oacc[mb][qb][4 * a + 2] * inv, oacc[mb][qb][4 * a + 3] * inv);
+        } else {
+#pragma unroll
+            for (int mb = 0; mb < MO; ++mb) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int d0 = 32 * mb + 8 * a + 4 * g;
+                    const float x0 = oacc[mb][qb][4 * a + 0] * inv, x1 = oacc[mb][qb][4 * a + 1] * inv;
+                    const float x2 = oacc[mb][qb][4 * a + 2] * inv, x3 = oacc[mb][qb][4 * a + 3] * inv;
+                    const int64_t e = b * p.o_sb + h * p.o_sh + (int64_t)my_row[qb] * p.o_st + d0;
+                    if constexpr (OUT_BF16) {
+                        *reinterpret_cast<u32x2*>(ob + e * 2) = u32x2{f32x2_to_bf16x2(x0, x1), f32x2_to_bf16x2(x2, x3)};
+                    } else {
+                        *reinterpret_cast<float4*>(ob + e * 4) = make_float4(x0, x1, x2, x3);
+                    }
                 }
             }
         }
-        if (p.lse && g == 0) {
+        if (g == 0) {
             const float l = ltot > 0.f ? mref[qb] * p.scale + __logf(ltot) : -INFINITY;
-            p.lse[(int64_t)(b * p.H + h) * p.n_rows + my_row[qb]] = l;
+            if (partial) p.part_lse[part_row0 + my_row[qb]] = l;
+            else if (p.lse) p.lse[(int64_t)(b * p.H + h) * p.n_rows + my_row[qb]] = l;
         }
     }
 }
 
+// Combination of the key splits of one launch: per row, O = sum_s w_s O_s /
+// sum_s w_s and LSE = M + log(sum_s w_s) with w_s = exp(LSE_s - M), M the
+// largest LSE_s (a split in which the row sees no key has LSE_s = -inf and
+// weight 0).  One thread per 4 output columns of a row.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, int D) {
+    const int cpr = D / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t total = (int64_t)p.B * p.H * p.n_rows * cpr;
+    if (idx >= total) return;
+    const int c = (int)(idx % cpr);
+    const int64_t rr = idx / cpr;
+    const int row = (int)(rr % p.n_rows);
+    const int bh = (int)(rr / p.n_rows);
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int64_t plane = (int64_t)p.B * p.H * p.n_rows;
+    float m = -INFINITY;
+    for (int s = 0; s < p.n_splits; ++s) m = __builtin_fmaxf(m, p.part_lse[s * plane + rr]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float wsum = 0.f;
+    if (m != -INFINITY) {
+        for (int s = 0; s < p.n_splits; ++s) {
+            const float w = __expf(p.part_lse[s * plane + rr] - m);
+            const float4 o = *reinterpret_cast<const float4*>(p.part_o + (s * plane + rr) * D + 4 * c);
+            acc.x += w * o.x;
+            acc.y += w * o.y;
+            acc.z += w * o.z;
+            acc.w += w * o.w;
+            wsum += w;
+        }
+    }
+    const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+    const int64_t e = b * p.o_sb + h * p.o_sh + (int64_t)row * p.o_st + 4 * c;
+    if constexpr (OUT_BF16) {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(p.o) + e * 2) =
+            u32x2{f32x2_to_bf16x2(acc.x * inv, acc.y * inv), f32x2_to_bf16x2(acc.z * inv, acc.w * inv)};
+    } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<unsigned char*>(p.o) + e * 4) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    if (p.lse && c == 0) p.lse[rr] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+}
+
 template <int D, bool OB, bool SP>
 hipError_t launch_one(const AttnParams& p, hipStream_t s) {
-    const int grid = p.n_qtiles * p.B * p.H;
+    const int grid = p.n_qtiles * p.B * p.H * p.n_splits;
     hipLaunchKernelGGL((attn_bf16_kernel<D, OB, SP>), dim3(grid), dim3(NT), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.n_splits == 1) return e;
+    const int64_t threads = (int64_t)p.B * p.H * p.n_rows * (D / 4);
+    hipLaunchKernelGGL((split_merge_kernel<OB>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p, D);
     return hipGetLastError();
 }
 

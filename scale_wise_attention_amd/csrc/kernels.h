@@ -34,7 +34,17 @@ struct AttnParams {
     float scale;         // softmax scale
     float scale_log2;    // scale * log2(e)
     int32_t scale_end[VAR_MAX_SCALES];  // off[s + 1]
+    // key splits (bf16 kernel): with n_splits > 1 each workgroup takes an equal
+    // share of its key tiles and writes fp32 O and LSE to part_o
+    // [n_splits][B*H][n_rows][D] / part_lse [n_splits][B*H][n_rows]; a merge
+    // launch then writes o and lse
+    int32_t n_splits;
+    float* part_o;
+    float* part_lse;
 };
+
+// Largest key-split count of a launch.
+constexpr int kMaxSplits = 8;
 
 struct MaskParams {
     const int32_t* q_index;   // nullable

@@ -151,7 +151,62 @@ var_status prepare_attn(const var_schedule* sched, const var_attn_desc* d, const
     p->scale = scale;
     p->scale_log2 = scale * 1.4426950408889634f;
     for (int s = 0; s < VAR_MAX_SCALES; ++s) p->scale_end[s] = s < off.num_scales ? off.off[s + 1] : off.off[off.num_scales];
+    p->n_splits = 1;
     return ok();
+}
+
+// Bytes of the split workspace: fp32 O and LSE per split, row and (batch, head).
+int64_t split_workspace_bytes(int32_t splits, int64_t bh, int64_t rows, int32_t D) {
+    return splits > 1 ? (int64_t)splits * bh * rows * (D + 1) * 4 : 0;
+}
+
+// Points the parameter block at a split workspace after checking it.
+var_status attach_splits(varattn::AttnParams* p, const var_attn_desc* d, int32_t splits, void* ws,
+                         int64_t ws_bytes) {
+    if (splits < 1 || splits > varattn::kMaxSplits)
+        return fail(VAR_ERR_RANGE, "n_splits=%d outside [1, %d]", splits, varattn::kMaxSplits);
+    if (splits == 1) return VAR_OK;
+    if (d->in_dtype != VAR_BF16) return fail(VAR_ERR_UNSUPPORTED, "key splits need bf16 input");
+    const int64_t bh = (int64_t)p->B * p->H;
+    const int64_t need = split_workspace_bytes(splits, bh, p->n_rows, d->head_dim);
+    if (!ws) return fail(VAR_ERR_NULL, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) & 15u) return fail(VAR_ERR_STRIDE, "workspace must be 16-byte aligned");
+    if (ws_bytes < need)
+        return fail(VAR_ERR_CAPACITY, "workspace of %lld bytes below the %lld needed", (long long)ws_bytes,
+                    (long long)need);
+    p->n_splits = splits;
+    p->part_o = static_cast<float*>(ws);
+    p->part_lse = p->part_o + (int64_t)splits * bh * p->n_rows * d->head_dim;
+    return VAR_OK;
+}
+
+int device_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        return n;
+    return 256;
+}
+
+// Split count with the smallest modelled time, in units of one 64-key
+// iteration of a workgroup (about 1.8 us on MI355X at the 1024px shapes):
+// waves of workgroups over the compute units times the iterations per split,
+// plus, when split, the merge: a launch (about 3 iterations) and the partial
+// O written and read back (8 bytes per element; about 7 MB per iteration at
+// the bandwidth these small launches reach).
+int32_t choose_splits(int64_t tasks, int64_t tiles, int64_t bh_rows, int32_t D, int n_cu) {
+    auto rounds = [&](int64_t n) { return (n + n_cu - 1) / n_cu; };
+    double best = (double)rounds(tasks) * tiles;
+    int32_t best_s = 1;
+    for (int32_t s = 2; s <= varattn::kMaxSplits && tiles >= 2 * s; ++s) {
+        const double cost = (double)rounds(tasks * s) * ((tiles + s - 1) / s) + 3.0 +
+                            (double)s * bh_rows * D * 8.0 / 7.2e6;
+        if (cost < 0.95 * best) {
+            best = cost;
+            best_s = s;
+        }
+    }
+    return best_s;
 }
 
 }  // namespace
@@ -185,23 +240,68 @@ VAR_EXPORT var_status var_schedule_extent(const var_schedule* sched, int32_t b, 
     return ok();
 }
 
-VAR_EXPORT var_status var_attn_dense(const var_schedule* sched, const var_attn_desc* desc, const void* q,
-                                     var_layout q_l, const void* k, var_layout k_l, const void* v, var_layout v_l,
-                                     void* o, var_layout o_l, float* lse, const int32_t* q_index, int32_t n_sel,
-                                     void* stream) {
+namespace {
+
+var_status dense_impl(const var_schedule* sched, const var_attn_desc* desc, const void* q, var_layout q_l,
+                      const void* k, var_layout k_l, const void* v, var_layout v_l, void* o, var_layout o_l,
+                      float* lse, const int32_t* q_index, int32_t n_sel, int32_t splits, void* ws,
+                      int64_t ws_bytes, void* stream) {
     varattn::AttnParams p;
     bool none = false;
     var_status st = prepare_attn(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, &p, &none);
-    if (st != VAR_OK || none) return st;
+    if (st != VAR_OK) return st;
+    if ((st = attach_splits(&p, desc, none ? 1 : splits, ws, ws_bytes)) != VAR_OK) return st;
+    if (none) return ok();
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (desc->in_dtype == VAR_BF16) {
         const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false);
         p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
+        if ((int64_t)p.n_qtiles * p.B * p.H * p.n_splits >= ((int64_t)1 << 31))
+            return fail(VAR_ERR_RANGE, "launch grid too large");
         return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, desc->out_dtype == VAR_BF16, false, s),
                           "var_attn_dense launch");
     }
     p.n_qtiles = (p.n_rows + varattn::kF32RowsPerTile - 1) / varattn::kF32RowsPerTile;
     return hip_status(varattn::launch_attn_f32(p, desc->head_dim, false, s), "var_attn_dense launch");
+}
+
+var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, const void* q, var_layout q_l,
+                       const void* k, var_layout k_l, const void* v, var_layout v_l, void* o, var_layout o_l,
+                       float* lse, const int32_t* q_index, int32_t n_sel, const int32_t* row_ptr,
+                       const int32_t* col_idx, int32_t tile_q, int32_t tile_k, int32_t splits, void* ws,
+                       int64_t ws_bytes, void* stream) {
+    if (tile_q != 64 || tile_k != 64)
+        return fail(VAR_ERR_UNSUPPORTED, "block-sparse attention supports 64x64 tiles, got %dx%d", tile_q, tile_k);
+    if (!row_ptr || !col_idx) return fail(VAR_ERR_NULL, "row_ptr and col_idx must be non-NULL");
+    varattn::AttnParams p;
+    bool none = false;
+    var_status st = prepare_attn(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, &p, &none);
+    if (st != VAR_OK) return st;
+    if ((st = attach_splits(&p, desc, none ? 1 : splits, ws, ws_bytes)) != VAR_OK) return st;
+    if (none) return ok();
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (desc->in_dtype == VAR_BF16) {
+        // each workgroup covers a whole number of 64-row tiles of the mask
+        const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, true);
+        p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
+        if ((int64_t)p.n_qtiles * p.B * p.H * p.n_splits >= ((int64_t)1 << 31))
+            return fail(VAR_ERR_RANGE, "launch grid too large");
+        return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, desc->out_dtype == VAR_BF16, true, s),
+                          "var_attn_block_sparse launch");
+    }
+    p.n_qtiles = (p.n_rows + varattn::kF32RowsPerTile - 1) / varattn::kF32RowsPerTile;
+    return hip_status(varattn::launch_attn_f32(p, desc->head_dim, true, s), "var_attn_block_sparse launch");
+}
+
+}  // namespace
+
+VAR_EXPORT var_status var_attn_dense(const var_schedule* sched, const var_attn_desc* desc, const void* q,
+                                     var_layout q_l, const void* k, var_layout k_l, const void* v, var_layout v_l,
+                                     void* o, var_layout o_l, float* lse, const int32_t* q_index, int32_t n_sel,
+                                     void* stream) {
+    return dense_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, 1, nullptr, 0, stream);
 }
 
 VAR_EXPORT var_status var_attn_block_sparse(const var_schedule* sched, const var_attn_desc* desc, const void* q,
@@ -210,25 +310,55 @@ VAR_EXPORT var_status var_attn_block_sparse(const var_schedule* sched, const var
                                             const int32_t* q_index, int32_t n_sel, const int32_t* row_ptr,
                                             const int32_t* col_idx, int32_t tile_q, int32_t tile_k,
                                             void* stream) {
-    if (tile_q != 64 || tile_k != 64)
-        return fail(VAR_ERR_UNSUPPORTED, "block-sparse attention supports 64x64 tiles, got %dx%d", tile_q, tile_k);
-    if (!row_ptr || !col_idx) return fail(VAR_ERR_NULL, "row_ptr and col_idx must be non-NULL");
-    varattn::AttnParams p;
-    bool none = false;
-    var_status st = prepare_attn(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, &p, &none);
-    if (st != VAR_OK || none) return st;
-    p.row_ptr = row_ptr;
-    p.col_idx = col_idx;
-    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (desc->in_dtype == VAR_BF16) {
-        // each workgroup covers a whole number of 64-row tiles of the mask
-        const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, true);
-        p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
-        return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, desc->out_dtype == VAR_BF16, true, s),
-                          "var_attn_block_sparse launch");
+    return sparse_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, row_ptr, col_idx, tile_q,
+                       tile_k, 1, nullptr, 0, stream);
+}
+
+VAR_EXPORT var_status var_attn_split_plan(const var_schedule* sched, const var_attn_desc* d, int32_t n_sel,
+                                          int32_t kv_tiles_hint, int32_t* n_splits, int64_t* workspace_bytes) {
+    Offsets off;
+    var_status st = check_schedule(sched, &off);
+    if (st != VAR_OK) return st;
+    if (!d) return fail(VAR_ERR_NULL, "desc is NULL");
+    if ((st = check_range(off, d->q_scale_begin, d->q_scale_end)) != VAR_OK) return st;
+    if (d->batch < 1 || d->heads < 1 || (int64_t)d->batch * d->heads > (1 << 20))
+        return fail(VAR_ERR_RANGE, "batch=%d heads=%d invalid", d->batch, d->heads);
+    if (d->head_dim < 1) return fail(VAR_ERR_RANGE, "head_dim=%d invalid", d->head_dim);
+    const int32_t n_q = off.off[d->q_scale_end] - off.off[d->q_scale_begin];
+    if (n_sel < 0 || n_sel > n_q) return fail(VAR_ERR_INDEX, "n_sel=%d outside [0, n_q=%d]", n_sel, n_q);
+    if (kv_tiles_hint < 0) return fail(VAR_ERR_RANGE, "kv_tiles_hint must be >= 0");
+    const int64_t rows = n_sel > 0 ? n_sel : n_q;
+    const int64_t bh = (int64_t)d->batch * d->heads;
+    int32_t s = 1;
+    if (d->in_dtype == VAR_BF16) {
+        const int rpt = varattn::attn_bf16_rows_per_tile(d->head_dim, false);
+        const int64_t tasks = bh * ((rows + rpt - 1) / rpt);
+        const int64_t tiles = kv_tiles_hint > 0 ? kv_tiles_hint : (off.off[d->q_scale_end] + 63) / 64;
+        s = choose_splits(tasks, tiles, bh * rows, d->head_dim, device_cu_count());
     }
-    p.n_qtiles = (p.n_rows + varattn::kF32RowsPerTile - 1) / varattn::kF32RowsPerTile;
-    return hip_status(varattn::launch_attn_f32(p, desc->head_dim, true, s), "var_attn_block_sparse launch");
+    if (n_splits) *n_splits = s;
+    if (workspace_bytes) *workspace_bytes = split_workspace_bytes(s, bh, rows, d->head_dim);
+    return ok();
+}
+
+VAR_EXPORT var_status var_attn_dense_split(const var_schedule* sched, const var_attn_desc* desc, const void* q,
+                                           var_layout q_l, const void* k, var_layout k_l, const void* v,
+                                           var_layout v_l, void* o, var_layout o_l, float* lse,
+                                           const int32_t* q_index, int32_t n_sel, int32_t n_splits,
+                                           void* workspace, int64_t workspace_bytes, void* stream) {
+    return dense_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, n_splits, workspace,
+                      workspace_bytes, stream);
+}
+
+VAR_EXPORT var_status var_attn_block_sparse_split(const var_schedule* sched, const var_attn_desc* desc,
+                                                  const void* q, var_layout q_l, const void* k, var_layout k_l,
+                                                  const void* v, var_layout v_l, void* o, var_layout o_l,
+                                                  float* lse, const int32_t* q_index, int32_t n_sel,
+                                                  const int32_t* row_ptr, const int32_t* col_idx, int32_t tile_q,
+                                                  int32_t tile_k, int32_t n_splits, void* workspace,
+                                                  int64_t workspace_bytes, void* stream) {
+    return sparse_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, row_ptr, col_idx, tile_q,
+                       tile_k, n_splits, workspace, workspace_bytes, stream);
 }
 
 namespace {

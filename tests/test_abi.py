@@ -26,7 +26,7 @@ def _declared():
 
 def test_exports_match_header(api):
     declared = _declared()
-    assert len(declared) == 10
+    assert len(declared) == 13
     for name in declared:
         assert hasattr(api.LIB, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True).stdout

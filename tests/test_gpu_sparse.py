@@ -254,3 +254,34 @@ def test_pruned_pipeline_end_to_end(api):
     ref = oracle.scatter_restore(base.view(torch.int32).cpu().numpy(), 48, 48, upd.view(torch.int32).cpu().numpy(),
                                  sel, 64, 64)
     assert np.array_equal(out.view(torch.int32).cpu().numpy(), ref)
+
+
+def test_sparse_rows_whose_first_tiles_differ(api):
+    """Caller CSR in which the waves of a workgroup start on different key tiles:
+    a wave's first owned tile comes after the walk's first tile, and a masked
+    tail tile comes later.  Each row's reference max must come from its own
+    first tile."""
+    wl = WORKLOADS["var1024_sparse"]
+    q, k, v = make_qkv(wl, 8, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    s = 11
+    n = off[s + 1] - off[s]
+    n_qt, n_kt = -(-n // 64), -(-off[s + 1] // 64)
+    kept = np.zeros((n_qt, n_kt), dtype=bool)
+    for r in range(n_qt):
+        if r % 2 == 0:
+            kept[r, 0:11] = True
+        else:
+            kept[r, 5 + r % 3:21] = True
+            kept[r, 50] = True
+        kept[r, n_kt - 1] = True          # the masked tail tile
+    rp_h, ci_h = oracle.mask_to_csr(kept)
+    rp, ci = torch.from_numpy(rp_h).cuda(), torch.from_numpy(ci_h).cuda()
+    qs = q[:, :, off[s]:off[s + 1]]
+    o = api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, s, s + 1, rp, ci)
+    rows = np.arange(0, n, 29)
+    qn, kn, vn = _np(qs), _np(k), _np(v)
+    for (b, h) in [(0, 1), (1, 8)]:
+        ref = oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], wl.h, wl.w,
+                               s, s + 1, kept=kept, rows=rows)
+        _check(_np(o[b:b + 1, h:h + 1])[:, :, rows], ref, what=f"first tiles differ b{b} h{h}")
