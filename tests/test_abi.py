@@ -8,6 +8,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "var_attn.h")
@@ -189,3 +190,34 @@ def test_saliency_and_select_validation_errors(api):
     assert sel(32, P(0), 32, 32, 64, 64, 10, P(FAKE), P(0)) == E("VAR_ERR_NULL")
     assert sel(32, P(FAKE), 32, 32, 64, 64, 10, P(FAKE + 2), P(0)) == E("VAR_ERR_STRIDE")
     assert sel(32, P(0), 32, 32, 64, 64, 0, P(0), P(0)) == 0   # nothing to select, nothing launched
+
+
+def test_split_validation_and_plan(api):
+    s = api.make_schedule(W1024, W1024)
+    E = lambda n: _code(api, n)
+    P = ctypes.c_void_p
+    L = api.Layout(2 * 16 * 4096 * 128, 4096 * 128, 128)
+    f = api.LIB.var_attn_dense_split
+
+    def call(desc, splits, ws=FAKE, nbytes=1 << 40):
+        return f(ctypes.byref(s), ctypes.byref(desc), P(FAKE), L, P(FAKE), L, P(FAKE), L, P(FAKE), L, P(0), P(0), 0,
+                 splits, P(ws), nbytes, P(0))
+
+    d = _desc(api)
+    assert call(d, 0) == E("VAR_ERR_RANGE")
+    assert call(d, 9) == E("VAR_ERR_RANGE")
+    assert call(d, 2, ws=0) == E("VAR_ERR_NULL")
+    assert call(d, 2, ws=FAKE + 4) == E("VAR_ERR_STRIDE")
+    need = 2 * 32 * 4096 * 129 * 4
+    assert call(d, 2, nbytes=need - 1) == E("VAR_ERR_CAPACITY")
+    f32 = _desc(api, head_dim=64, in_dtype=api.VAR_F32)
+    assert call(f32, 2) == E("VAR_ERR_UNSUPPORTED")
+    n, nbytes = api.var_attn_split_plan((W1024, W1024), 12, 13, 2, 16, 128)
+    assert n == 1 and nbytes == 0                      # 512 work items already fill 256 compute units
+    n, nbytes = api.var_attn_split_plan((W1024, W1024), 9, 10, 2, 16, 128)
+    assert n > 1 and nbytes == n * 32 * 1024 * 129 * 4  # 128 work items of 40 key tiles
+    assert api.var_attn_split_plan((W1024, W1024), 9, 10, 2, 16, 64, dtype=torch.float32) == (1, 0)
+    sp = api.LIB.var_attn_block_sparse_split
+    r = sp(ctypes.byref(s), ctypes.byref(d), P(FAKE), L, P(FAKE), L, P(FAKE), L, P(FAKE), L, P(0), P(0), 0,
+           P(FAKE), P(FAKE), 64, 64, 9, P(FAKE), 1 << 40, P(0))
+    assert r == E("VAR_ERR_RANGE")
