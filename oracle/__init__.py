@@ -12,7 +12,8 @@ Sources (web pages on visual-autoregressive next-scale generation):
 * "SparVAR: Exploring Sparsity in Visual AutoRegressive Modeling for
   Training-Free Acceleration", abstract: every step attends to all tokens of
   all historical scales; attention sinks; cross-scale locality; an index
-  mapping between scales; a block-wise sparse kernel.
+  mapping between scales; a sparse pattern of later scales predicted from a
+  decision scale; a block-wise sparse kernel.
 * "ARVAR: Accelerating Visual Autoregressive Model via Attention Retrospect",
   Background & Motivation (a whole token grid per scale, KV caching,
   FlashAttention), Key Design 2 (gather of the retained positions) and Key
@@ -32,6 +33,9 @@ Modules:
                                                           (pinned: see tests)
 * ``selection``  -- attention-guided saliency of a small step and the Top-K
   choice of the retained positions on a larger grid.     (pinned: see tests)
+* ``dynamic_sparse`` -- per-head tile pattern of a later step predicted from
+  the attention mass of a decision scale through index mapping.
+                                                          (pinned: see tests)
 
 Every function here is pinned by ``-m "not gpu"`` tests against something other
 than itself (brute force, closed forms, invariants, library routines); none is
