@@ -323,6 +323,26 @@ def main():
                                                          wl.grids[K - 1], n_sel, out=sel_guided))
     saliency_flops = 2.0 * D * B * H * n_src * n_src
 
+    # sparse pattern of the last step predicted per head from the 32x32
+    # decision step: its attention mass (from its LSE), the decision tiles
+    # (tau = 0.5), the index-mapped per-head mask, then the per-head sparse
+    # attention of the last step over all 4096 queries
+    tau = 0.5
+    mass = api.var_attn_block_mass(sched, qsteps[src], k, lse_src, src)
+    kept_d = api.var_decision_tiles(mass, tau)
+    dyn_rp, dyn_ci = api.var_mapped_tile_mask(sched, src, K - 1, kept_d)
+    dyn_out = torch.empty(B, H, 4096, D, dtype=bf, device=dev)
+    mass_ms = time_launch(lambda: api.var_attn_block_mass(sched, qsteps[src], k, lse_src, src, out=mass))
+    decision_ms = time_launch(lambda: api.var_decision_tiles(mass, tau, out=kept_d))
+    dyn_mask_ms = time_launch(lambda: api.var_mapped_tile_mask(sched, src, K - 1, kept_d, row_ptr=dyn_rp,
+                                                               col_idx=dyn_ci))
+    dyn_attn_ms = time_launch(lambda: api.var_attn_block_sparse_heads(sched, qsteps[K - 1], k, v, K - 1, K, dyn_rp,
+                                                                      dyn_ci, out=dyn_out))
+    rp_h, ci_h = dyn_rp.cpu().numpy(), dyn_ci.cpu().numpy()
+    dyn_pairs = sum(acc.sparse_pairs(rp_h[m], ci_h[m], 4096, off[K]) for m in range(B * H))
+    dyn_flops = 4.0 * D * dyn_pairs
+    dyn_kept = float(rp_h[:, -1].sum()) / (B * H * rp_h.shape[1] - B * H) / -(-off[K] // 64)
+
     # Branch Halving on the last step: the conditional branch alone (batch 1)
     bh_out = torch.empty(1, H, 4096, D, dtype=bf, device=dev)
     bh_ms = time_launch(lambda: api.var_attn_dense(sched, qsteps[K - 1][:1], k[:1], v[:1], K - 1, K, out=bh_out))
@@ -401,6 +421,18 @@ def main():
             "saliency_tflops": round(saliency_flops / (saliency_ms * 1e-3) / 1e12, 2),
             "select_topk_ms": round(select_ms, 4),
             "selected": f"{n_sel} of {wl.grids[K - 1] ** 2}",
+        },
+        "decision_scale_sparse": {
+            "decision_step_grid": f"{wl.grids[src]}x{wl.grids[src]}",
+            "tau": tau,
+            "block_mass_ms": round(mass_ms, 4),
+            "decision_ms": round(decision_ms, 4),
+            "mapped_mask_ms": round(dyn_mask_ms, 4),
+            "last_step_attn_ms": round(dyn_attn_ms, 4),
+            "last_step_kept_tile_fraction": round(dyn_kept, 4),
+            "last_step_gflop": round(dyn_flops / 1e9, 3),
+            "last_step_tflops": round(dyn_flops / (dyn_attn_ms * 1e-3) / 1e12, 2),
+            "speedup_last_step_vs_dense": round(dense_ms[last] / (dyn_mask_ms + dyn_attn_ms), 3),
         },
         "branch_halving": {
             "last_step_cond_only_ms": round(bh_ms, 4),

@@ -264,6 +264,66 @@ var_status var_select_topk(int32_t maps, const float* saliency, int32_t h_src, i
                            int32_t h_dst, int32_t w_dst, int32_t n_keep, int32_t* q_index, void* stream);
 
 /*
+ * Sparse pattern of a later step predicted from a decision scale ("SparVAR
+ * ...", abstract: the sparse attention pattern of later high-resolution
+ * scales is predicted dynamically from a sparse decision scale, and made
+ * self-similar to it through an index mapping between scales).  The abstract
+ * fixes no formulas; the three calls below take this reading, with 64x64
+ * tiles throughout:
+ *
+ * var_attn_block_mass: attention mass of the decision step d (one scale,
+ * bf16, head_dim 64 or 128; q, k, desc as for var_attn_dense of that step):
+ *   mass[b][h][r][c] = sum_{i in rows 64r..64r+63} sum_{u in tokens 64c..64c+63, u < off[d+1]}
+ *                      exp(scale * q_i . k_u - lse[b][h][i])
+ * with lse the LSE var_attn_dense returned for the same call (device fp32
+ * [B][H][n_d] contiguous).  mass: device fp32 [B][H][ceil(n_d/64)][ceil(off[d+1]/64)],
+ * contiguous, written.  n_d <= 8192.
+ */
+var_status var_attn_block_mass(const var_schedule* sched, const var_attn_desc* desc,
+                               const void* q, var_layout q_l, const void* k, var_layout k_l,
+                               const float* lse, float* mass, void* stream);
+
+/*
+ * var_decision_tiles: per row (map, r) of mass [maps][n_qt][n_kt] (device fp32),
+ * the key tiles in order of decreasing mass (equal masses: lower c first) are
+ * kept while the mass already kept is below tau * total, the sums in fp32, in
+ * that order, the total in ascending c.  kept: device uint8 [maps][n_qt][n_kt]
+ * (1 = kept), written.  0 <= tau <= 1; n_kt <= 1024; masses must not be NaN.
+ */
+var_status var_decision_tiles(int32_t maps, int32_t n_qt, int32_t n_kt, const float* mass, float tau,
+                              uint8_t* kept, void* stream);
+
+/*
+ * var_mapped_tile_mask: per-map tile mask of step T (queries = scale T, keys
+ * [0, off[T+1])) from kept_d [maps][ceil(n_d/64)][ceil(off[d+1]/64)] of the
+ * decision step d <= T.  A query (y, x) of scale T stands for position
+ * (floor(y*h_d/h_T), floor(x*w_d/w_T)) of scale d; a key of a scale j <= d for
+ * itself; a key (y, x) of a scale j > d for (floor(y*h_d/h_j), floor(x*w_d/w_j))
+ * of scale d.  Tile (R, C) is kept when some query of R and key of C stand
+ * for a kept decision pair.  Output: one CSR per map, row_ptr device int32
+ * [maps][n_qt + 1] and col_idx device int32 [maps][col_stride] (col_stride >=
+ * n_qt * n_kt: the buffer doubles as staging), n_qt = ceil(n_T/64),
+ * n_kt = ceil(off[T+1]/64), lists ascending.  Limits: ceil(n_d/64) and
+ * ceil(off[d+1]/64) <= 1024, n_kt <= 8192.
+ */
+var_status var_mapped_tile_mask(const var_schedule* sched, int32_t decision_scale, int32_t step,
+                                int32_t maps, const uint8_t* kept_d, int32_t* row_ptr, int32_t* col_idx,
+                                int64_t col_stride, void* stream);
+
+/*
+ * var_attn_block_sparse with one CSR per (batch, head) (e.g. from
+ * var_mapped_tile_mask with maps = B*H): map m = b*H + h reads row_ptr
+ * + m*(n_qt + 1) and col_idx + m*col_stride.  bf16 input, 64x64 tiles.
+ * Other arguments as in var_attn_block_sparse.
+ */
+var_status var_attn_block_sparse_heads(const var_schedule* sched, const var_attn_desc* desc,
+                                       const void* q, var_layout q_l, const void* k, var_layout k_l,
+                                       const void* v, var_layout v_l, void* o, var_layout o_l,
+                                       float* lse, const int32_t* q_index, int32_t n_sel,
+                                       const int32_t* row_ptr, const int32_t* col_idx,
+                                       int64_t col_stride, void* stream);
+
+/*
  * Structural reconstruction of a pruned grid ("ARVAR ...", Key Design 3,
  * Equations (8)-(9)): out = Scatter(Up(base; h_out, w_out), q_index, upd).
  * Up is nearest neighbour with source (floor(y*h_in/h_out), floor(x*w_in/w_out));

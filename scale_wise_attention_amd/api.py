@@ -31,6 +31,7 @@ MAX_SCALES = 32
 EXPORTED = ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_build_tile_mask",
             "var_attn_block_sparse", "var_scatter_restore", "var_attn_saliency", "var_select_topk",
             "var_attn_dense_split", "var_attn_block_sparse_split", "var_attn_split_plan",
+            "var_attn_block_mass", "var_decision_tiles", "var_mapped_tile_mask", "var_attn_block_sparse_heads",
             "var_status_string", "var_last_error")
 
 
@@ -86,9 +87,15 @@ def _load():
                                                 Layout, P, P, i32, P, P, i32, i32, i32, P, i64, P]
     lib.var_attn_split_plan.argtypes = [SP, ctypes.POINTER(AttnDesc), i32, i32, ctypes.POINTER(i32),
                                         ctypes.POINTER(i64)]
+    lib.var_attn_block_mass.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, P, P]
+    lib.var_decision_tiles.argtypes = [i32, i32, i32, P, ctypes.c_float, P, P]
+    lib.var_mapped_tile_mask.argtypes = [SP, i32, i32, i32, P, P, P, i64, P]
+    lib.var_attn_block_sparse_heads.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, Layout, P,
+                                                Layout, P, P, i32, P, P, i64, P]
     for name in ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_build_tile_mask",
                  "var_attn_block_sparse", "var_scatter_restore", "var_attn_saliency", "var_select_topk",
-                 "var_attn_dense_split", "var_attn_block_sparse_split", "var_attn_split_plan"):
+                 "var_attn_dense_split", "var_attn_block_sparse_split", "var_attn_split_plan",
+                 "var_attn_block_mass", "var_decision_tiles", "var_mapped_tile_mask", "var_attn_block_sparse_heads"):
         getattr(lib, name).restype = ctypes.c_int
     lib.var_status_string.argtypes = [ctypes.c_int]
     lib.var_status_string.restype = ctypes.c_char_p
@@ -395,3 +402,89 @@ def var_select_topk(saliency, h_src, w_src, h_dst, w_dst, n_keep, out=None):
     _check(LIB.var_select_topk(maps, _ptr(saliency), h_src, w_src, h_dst, w_dst, int(n_keep),
                                _ptr(out) if n_keep > 0 else ctypes.c_void_p(0), _stream(saliency.device)))
     return out
+
+
+def var_attn_block_mass(schedule, q, k, lse, step, softmax_scale=0.0, out=None):
+    """Attention mass [B, H, n_qt, n_kt] (fp32) of the 64x64 tiles of step `step` (the decision scale).
+
+    q [B, H, n_d, D] bf16 (the step's queries), k [B, H, >= off[step+1], D] bf16,
+    lse [B, H, n_d] fp32 from var_attn_dense(..., step, step + 1, return_lse=True).
+    """
+    s = _as_schedule(schedule)
+    _, n_d, L = var_schedule_extent(s, step, step + 1)
+    B, H, _, D = q.shape
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or not q.is_cuda or k.device != q.device:
+        raise ValueError("q and k must be bf16 tensors on one device")
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != D or q.shape[2] < n_d or k.shape[2] < L:
+        raise ValueError("q / k shapes do not fit the step")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, n_d) or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError(f"lse must be a contiguous fp32 tensor of shape {(B, H, n_d)}")
+    shape = (B, H, -(-n_d // 64), -(-L // 64))
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != shape or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous fp32 tensor of shape {shape}")
+    desc = AttnDesc(B, H, D, step, step + 1, float(softmax_scale), VAR_BF16, VAR_F32)
+    _check(LIB.var_attn_block_mass(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k), _layout(k),
+                                   _ptr(lse), _ptr(out), _stream(q.device)))
+    return out
+
+
+def var_decision_tiles(mass, tau, out=None):
+    """kept (uint8, same shape as mass [..., n_qt, n_kt]) of the decision scale."""
+    if mass.dtype != torch.float32 or not mass.is_contiguous() or not mass.is_cuda or mass.dim() < 2:
+        raise ValueError("mass must be a contiguous fp32 device tensor [..., n_qt, n_kt]")
+    n_qt, n_kt = mass.shape[-2], mass.shape[-1]
+    maps = mass.numel() // (n_qt * n_kt)
+    if out is None:
+        out = torch.empty(mass.shape, dtype=torch.uint8, device=mass.device)
+    elif out.shape != mass.shape or out.dtype != torch.uint8 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 tensor shaped like mass")
+    _check(LIB.var_decision_tiles(maps, n_qt, n_kt, _ptr(mass), float(tau), _ptr(out), _stream(mass.device)))
+    return out
+
+
+def var_mapped_tile_mask(schedule, decision_scale, step, kept_d, row_ptr=None, col_idx=None):
+    """Per-map CSR of step `step`: row_ptr int32 [maps, n_qt+1], col_idx int32 [maps, n_qt*n_kt]."""
+    s = _as_schedule(schedule)
+    if kept_d.dtype != torch.uint8 or not kept_d.is_contiguous() or not kept_d.is_cuda or kept_d.dim() < 2:
+        raise ValueError("kept_d must be a contiguous uint8 device tensor [..., n_qt_d, n_kt_d]")
+    _, n_d, L_d = var_schedule_extent(s, decision_scale, decision_scale + 1)
+    _, n_t, L_t = var_schedule_extent(s, step, step + 1)
+    if kept_d.shape[-2:] != (-(-n_d // 64), -(-L_d // 64)):
+        raise ValueError("kept_d's last two dims must be the decision step's tile counts")
+    maps = kept_d.numel() // (kept_d.shape[-2] * kept_d.shape[-1])
+    n_qt, n_kt = -(-n_t // 64), -(-L_t // 64)
+    if row_ptr is None:
+        row_ptr = torch.empty(maps, n_qt + 1, dtype=torch.int32, device=kept_d.device)
+    if col_idx is None:
+        col_idx = torch.empty(maps, n_qt * n_kt, dtype=torch.int32, device=kept_d.device)
+    if (row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32 or tuple(row_ptr.shape) != (maps, n_qt + 1)
+            or col_idx.dim() != 2 or col_idx.shape[0] != maps or not row_ptr.is_contiguous()
+            or not col_idx.is_contiguous()):
+        raise ValueError("row_ptr must be int32 [maps, n_qt+1] and col_idx int32 [maps, >= n_qt*n_kt], contiguous")
+    _check(LIB.var_mapped_tile_mask(ctypes.byref(s), decision_scale, step, maps, _ptr(kept_d), _ptr(row_ptr),
+                                    _ptr(col_idx), col_idx.shape[1], _stream(kept_d.device)))
+    return row_ptr, col_idx
+
+
+def var_attn_block_sparse_heads(schedule, q, k, v, q_scale_begin, q_scale_end, row_ptr, col_idx, out=None,
+                                out_dtype=None, softmax_scale=0.0, q_index=None, return_lse=False):
+    """Block-sparse attention with one CSR per (batch, head): row_ptr [B*H, n_qt+1], col_idx [B*H, stride]."""
+    s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
+                                           softmax_scale, q_index, return_lse)
+    n_sel = rows if q_index is not None else 0
+    if q_index is not None and n_sel == 0:
+        return (out, lse) if return_lse else out
+    B, H = q.shape[0], q.shape[1]
+    n_qt = -(-rows // 64)
+    if (row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32 or tuple(row_ptr.shape) != (B * H, n_qt + 1)
+            or col_idx.dim() != 2 or col_idx.shape[0] != B * H or not row_ptr.is_contiguous()
+            or not col_idx.is_contiguous() or row_ptr.device != q.device or col_idx.device != q.device):
+        raise ValueError("row_ptr must be int32 [B*H, n_qt+1] and col_idx int32 [B*H, stride] on q's device")
+    _check(LIB.var_attn_block_sparse_heads(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k),
+                                           _layout(k), _ptr(v), _layout(v), _ptr(out), _layout(out), _ptr(lse),
+                                           _ptr(q_index), n_sel, _ptr(row_ptr), _ptr(col_idx), col_idx.shape[1],
+                                           _stream(q.device)))
+    return (out, lse) if return_lse else out

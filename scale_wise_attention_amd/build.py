@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libvarattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["attn_bf16.hip", "attn_f32.hip", "tile_mask.hip", "scatter.hip", "saliency.hip", "var_attn_api.cpp"]
+SOURCES = ["attn_bf16.hip", "attn_f32.hip", "tile_mask.hip", "scatter.hip", "saliency.hip", "dynamic_sparse.hip", "var_attn_api.cpp"]
 # The bf16 attention kernels run with the IEEE mode bit off and without NaN
 # semantics (infinities stay honoured: masked logits are -inf): max/min then
 # need no NaN-quieting instructions in the softmax.  Their MFMAs write VGPRs

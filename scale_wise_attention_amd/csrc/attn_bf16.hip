@@ -267,18 +267,20 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
     int dense_begin = 0, dense_end = 0;   // dense: tiles [dense_begin, dense_end)
     int dense_next = 0;
     int lbeg[NW], lptr[NW], lend[NW], lhead[NW];   // sparse: one list per wave's query tile
+    const int32_t* const rowp = p.row_ptr + bh * p.rp_bh_stride;   // this (batch, head)'s CSR
+    const int32_t* const coli = p.col_idx + bh * p.ci_bh_stride;
     if constexpr (SPARSE) {
         const int n_qt = (p.n_rows + KT - 1) / KT;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const int r = qtile * NW + w;
-            const int b0 = r < n_qt ? p.row_ptr[r] : 0;
-            const int cnt = r < n_qt ? p.row_ptr[r + 1] - b0 : 0;
+            const int b0 = r < n_qt ? rowp[r] : 0;
+            const int cnt = r < n_qt ? rowp[r + 1] - b0 : 0;
             // key split: an equal share of this row's kept tiles (in order; the
             // host bounds cnt * n_splits below 2^31)
             lbeg[w] = lptr[w] = p.n_splits > 1 ? b0 + cnt * split / p.n_splits : b0;
             lend[w] = p.n_splits > 1 ? b0 + cnt * (split + 1) / p.n_splits : b0 + cnt;
-            lhead[w] = lptr[w] < lend[w] ? p.col_idx[lptr[w]] : INT_MAX;
+            lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
         }
     }
     int wg_kmin;   // smallest key limit in the workgroup: tiles below it need no mask
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                     if (lhead[w] == c) {
                         e.mask |= 1 << w;
                         ++lptr[w];
-                        lhead[w] = lptr[w] < lend[w] ? p.col_idx[lptr[w]] : INT_MAX;
+                        lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
                     }
                 }
                 // a column outside [0, n_kt) cannot come from the mask builder; clamp so loads stay in bounds
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
             for (int w = 0; w < NW; ++w) {
                 const int r = qtile * NW + w;
                 lptr[w] = lbeg[w];
-                lhead[w] = lptr[w] < lend[w] ? p.col_idx[lptr[w]] : INT_MAX;
+                lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
             }
         } else {
             dense_next = dense_begin;

@@ -41,6 +41,9 @@ struct AttnParams {
     int32_t n_splits;
     float* part_o;
     float* part_lse;
+    // per-(batch, head) CSR (block-sparse): element strides between the maps'
+    // row_ptr / col_idx arrays (0: one CSR shared by every (batch, head))
+    int64_t rp_bh_stride, ci_bh_stride;
 };
 
 // Largest key-split count of a launch.
@@ -58,6 +61,7 @@ struct MaskParams {
     int32_t off[VAR_MAX_SCALES + 1];
     int32_t h[VAR_MAX_SCALES];
     int32_t w[VAR_MAX_SCALES];
+    int64_t rp_map_stride, ci_map_stride;   // per-map CSR strides of the compaction (0: one map)
 };
 
 struct ScatterParams {
@@ -103,7 +107,49 @@ struct SelectParams {
     int32_t maps, h_src, w_src, h_dst, w_dst, n_keep;
 };
 
+// Decision-scale sparse pattern (per-head tile masks predicted by index mapping).
+constexpr int kMassMaxRows = 8192;           // rows of the decision step
+constexpr int kDecisionMaxTiles = 1024;      // key tiles of the decision step
+constexpr int kDecisionMaxRowTiles = 1024;   // row tiles of the decision step
+constexpr int kMappedMaxTiles = 8192;        // key tiles of the predicted step
+
+struct MassParams {
+    const void* q;        // bf16 queries of the decision step (row j = token off[d] + j)
+    const void* k;        // bf16 key cache
+    const float* lse;     // [B*H][n_rows] LSE of the decision step's attention
+    float* mass;          // [B*H][ceil(n_rows/64)][n_kt] output
+    int64_t q_sb, q_sh, q_st;
+    int64_t k_sb, k_sh, k_st;
+    int32_t B, H, n_rows, kv_len, n_kt;
+    float scale_log2;
+};
+
+struct DecisionParams {
+    const float* mass;    // [rows][n_kt]
+    unsigned char* kept;  // [rows][n_kt] output (0 / 1)
+    int32_t n_kt;
+    float tau;
+};
+
+struct MappedParams {
+    const unsigned char* kept_d;   // [maps][n_qt_d][n_kt_d]
+    int32_t* row_ptr;              // [maps] x rp_map_stride
+    int32_t* col_idx;              // [maps] x ci_map_stride
+    int64_t rp_map_stride, ci_map_stride;
+    int32_t d, T;
+    int32_t n_qt, n_kt;            // tiles of step T
+    int32_t n_qt_d, n_kt_d;        // tiles of the decision step
+    int32_t off[VAR_MAX_SCALES + 1];
+    int32_t h[VAR_MAX_SCALES];
+    int32_t w[VAR_MAX_SCALES];
+};
+
 hipError_t launch_tile_mask(const MaskParams& p, hipStream_t s);
+hipError_t launch_block_mass(const MassParams& p, int head_dim, hipStream_t s);
+hipError_t launch_decision(const DecisionParams& p, int rows, hipStream_t s);
+hipError_t launch_mapped_mask(const MappedParams& p, int maps, hipStream_t s);
+// The compaction of launch_tile_mask alone, one workgroup per map.
+hipError_t launch_mask_compact(const MaskParams& p, int maps, hipStream_t s);
 hipError_t launch_saliency(const SaliencyParams& p, int head_dim, hipStream_t s);
 hipError_t launch_select_topk(const SelectParams& p, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);

@@ -160,8 +160,8 @@ constexpr int kCompactThreads = 1024;
 constexpr int kPtrCap = 8192;                  // row offsets staged in LDS up to this many rows
 constexpr int kMovePerThread = 4;
 
-// One workgroup: counts -> offsets, then move row lists down to their final
-// place.  Entry e of the final list (row r, e in [row_ptr[r], row_ptr[r+1]))
+// One workgroup per map: counts -> offsets, then move row lists down to their
+// final place.  Entry e of the final list (row r, e in [row_ptr[r], row_ptr[r+1]))
 // is read from r*n_kt + e - row_ptr[r] >= e.  Entries are moved in chunks:
 // all reads of a chunk complete before its writes, and every later chunk
 // reads from positions at or beyond its own entries, past what this chunk
@@ -172,6 +172,9 @@ __global__ __launch_bounds__(kCompactThreads) void mask_compact_kernel(const Mas
     __shared__ int ptr_l[kPtrCap + 1];
     __shared__ int stage[kCompactThreads * kMovePerThread];
     const int tid = threadIdx.x;
+    // one workgroup per map (per (batch, head) for per-head masks)
+    int32_t* const row_ptr = p.row_ptr + (int64_t)blockIdx.x * p.rp_map_stride;
+    int32_t* const col_idx = p.col_idx + (int64_t)blockIdx.x * p.ci_map_stride;
     const bool staged = p.n_qt <= kPtrCap;
     if (tid == 0) {
         carry = 0;
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(kCompactThreads) void mask_compact_kernel(const Mas
     // inclusive scan of row_ptr[1..n_qt] in chunks (Hillis-Steele in LDS)
     for (int r0 = 0; r0 < p.n_qt; r0 += kCompactThreads) {
         const int r = r0 + tid;
-        buf[tid] = r < p.n_qt ? p.row_ptr[r + 1] : 0;
+        buf[tid] = r < p.n_qt ? row_ptr[r + 1] : 0;
         __syncthreads();
         for (int s = 1; s < kCompactThreads; s <<= 1) {
             const int add = tid >= s ? buf[tid - s] : 0;
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(kCompactThreads) void mask_compact_kernel(const Mas
             __syncthreads();
         }
         if (r < p.n_qt) {
-            p.row_ptr[r + 1] = buf[tid] + carry;
+            row_ptr[r + 1] = buf[tid] + carry;
             if (staged) ptr_l[r + 1] = buf[tid] + carry;
         }
         __syncthreads();
@@ -200,14 +203,14 @@ __global__ __launch_bounds__(kCompactThreads) void mask_compact_kernel(const Mas
     if (!staged) {
         // very many query tiles: move row by row
         for (int r = 1; r < p.n_qt; ++r) {
-            const int dst = p.row_ptr[r];
-            const int cnt = p.row_ptr[r + 1] - dst;
+            const int dst = row_ptr[r];
+            const int cnt = row_ptr[r + 1] - dst;
             const int64_t src = (int64_t)r * p.n_kt;
             for (int j0 = 0; j0 < cnt; j0 += kCompactThreads) {
                 const int j = j0 + tid;
-                if (j < cnt) buf[tid] = p.col_idx[src + j];   // the LDS write waits for the load
+                if (j < cnt) buf[tid] = col_idx[src + j];   // the LDS write waits for the load
                 __syncthreads();
-                if (j < cnt) p.col_idx[dst + j] = buf[tid];
+                if (j < cnt) col_idx[dst + j] = buf[tid];
                 __syncthreads();
             }
         }
@@ -227,14 +230,14 @@ __global__ __launch_bounds__(kCompactThreads) void mask_compact_kernel(const Mas
                     if (ptr_l[mid] <= e) lo = mid;
                     else hi = mid - 1;
                 }
-                stage[k * kCompactThreads + tid] = p.col_idx[(int64_t)lo * p.n_kt + (e - ptr_l[lo])];
+                stage[k * kCompactThreads + tid] = col_idx[(int64_t)lo * p.n_kt + (e - ptr_l[lo])];
             }
         }
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < kMovePerThread; ++k) {
             const int e = e0 + k * kCompactThreads + tid;
-            if (e < nnz) p.col_idx[e] = stage[k * kCompactThreads + tid];
+            if (e < nnz) col_idx[e] = stage[k * kCompactThreads + tid];
         }
         __syncthreads();
     }
@@ -246,6 +249,11 @@ __global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
 
 hipError_t launch_zero_i32(int32_t* p, hipStream_t s) {
     hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_mask_compact(const MaskParams& p, int maps, hipStream_t s) {
+    hipLaunchKernelGGL(mask_compact_kernel, dim3(maps), dim3(1024), 0, s, p);
     return hipGetLastError();
 }
 

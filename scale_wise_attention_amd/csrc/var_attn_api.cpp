@@ -269,7 +269,7 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
                        const void* k, var_layout k_l, const void* v, var_layout v_l, void* o, var_layout o_l,
                        float* lse, const int32_t* q_index, int32_t n_sel, const int32_t* row_ptr,
                        const int32_t* col_idx, int32_t tile_q, int32_t tile_k, int32_t splits, void* ws,
-                       int64_t ws_bytes, void* stream) {
+                       int64_t ws_bytes, void* stream, int64_t col_bh_stride = -1) {
     if (tile_q != 64 || tile_k != 64)
         return fail(VAR_ERR_UNSUPPORTED, "block-sparse attention supports 64x64 tiles, got %dx%d", tile_q, tile_k);
     if (!row_ptr || !col_idx) return fail(VAR_ERR_NULL, "row_ptr and col_idx must be non-NULL");
@@ -281,6 +281,16 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
     if (none) return ok();
     p.row_ptr = row_ptr;
     p.col_idx = col_idx;
+    if (col_bh_stride >= 0) {   // one CSR per (batch, head)
+        if (desc->in_dtype != VAR_BF16) return fail(VAR_ERR_UNSUPPORTED, "per-head CSR needs bf16 input");
+        const int64_t n_qt = (p.n_rows + 63) / 64;
+        const int64_t n_kt = (p.kv_len + 63) / 64;
+        if (col_bh_stride < n_qt * n_kt)
+            return fail(VAR_ERR_CAPACITY, "col_stride=%lld below n_qt*n_kt=%lld", (long long)col_bh_stride,
+                        (long long)(n_qt * n_kt));
+        p.rp_bh_stride = n_qt + 1;
+        p.ci_bh_stride = col_bh_stride;
+    }
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (desc->in_dtype == VAR_BF16) {
         // each workgroup covers a whole number of 64-row tiles of the mask
@@ -312,6 +322,124 @@ VAR_EXPORT var_status var_attn_block_sparse(const var_schedule* sched, const var
                                             void* stream) {
     return sparse_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, row_ptr, col_idx, tile_q,
                        tile_k, 1, nullptr, 0, stream);
+}
+
+VAR_EXPORT var_status var_attn_block_sparse_heads(const var_schedule* sched, const var_attn_desc* desc,
+                                                  const void* q, var_layout q_l, const void* k, var_layout k_l,
+                                                  const void* v, var_layout v_l, void* o, var_layout o_l,
+                                                  float* lse, const int32_t* q_index, int32_t n_sel,
+                                                  const int32_t* row_ptr, const int32_t* col_idx,
+                                                  int64_t col_stride, void* stream) {
+    if (col_stride < 0) return fail(VAR_ERR_RANGE, "col_stride must be >= 0");
+    return sparse_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, row_ptr, col_idx, 64, 64, 1,
+                       nullptr, 0, stream, col_stride);
+}
+
+VAR_EXPORT var_status var_attn_block_mass(const var_schedule* sched, const var_attn_desc* d, const void* q,
+                                          var_layout q_l, const void* k, var_layout k_l, const float* lse,
+                                          float* mass, void* stream) {
+    Offsets off;
+    var_status st = check_schedule(sched, &off);
+    if (st != VAR_OK) return st;
+    if (!d) return fail(VAR_ERR_NULL, "desc is NULL");
+    if ((st = check_range(off, d->q_scale_begin, d->q_scale_end)) != VAR_OK) return st;
+    if (d->q_scale_end != d->q_scale_begin + 1)
+        return fail(VAR_ERR_RANGE, "block mass takes one scale, got [%d, %d)", d->q_scale_begin, d->q_scale_end);
+    if (d->batch < 1 || d->heads < 1 || (int64_t)d->batch * d->heads > (1 << 20))
+        return fail(VAR_ERR_RANGE, "batch=%d heads=%d invalid", d->batch, d->heads);
+    if (d->in_dtype != VAR_BF16 || (d->head_dim != 64 && d->head_dim != 128))
+        return fail(VAR_ERR_UNSUPPORTED, "block mass supports bf16 input with head_dim 64 or 128");
+    if (!(d->softmax_scale >= 0.f) || std::isinf(d->softmax_scale))
+        return fail(VAR_ERR_RANGE, "softmax_scale must be finite and >= 0 (0 = 1/sqrt(D))");
+    const int32_t n = off.off[d->q_scale_end] - off.off[d->q_scale_begin];
+    const int32_t L = off.off[d->q_scale_end];
+    if (n > varattn::kMassMaxRows)
+        return fail(VAR_ERR_UNSUPPORTED, "decision step of %d rows above %d", n, varattn::kMassMaxRows);
+    if (!q || !k || !lse || !mass) return fail(VAR_ERR_NULL, "q, k, lse and mass must be non-NULL");
+    if (!aligned16(q) || !aligned16(k)) return fail(VAR_ERR_STRIDE, "q and k must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(mass) & 3u))
+        return fail(VAR_ERR_STRIDE, "lse and mass must be 4-byte aligned");
+    if ((st = check_layout("q", q_l, d->head_dim, 2)) != VAR_OK) return st;
+    if ((st = check_layout("k", k_l, d->head_dim, 2)) != VAR_OK) return st;
+    varattn::MassParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q = q;
+    p.k = k;
+    p.lse = lse;
+    p.mass = mass;
+    p.q_sb = q_l.batch; p.q_sh = q_l.head; p.q_st = q_l.token;
+    p.k_sb = k_l.batch; p.k_sh = k_l.head; p.k_st = k_l.token;
+    p.B = d->batch;
+    p.H = d->heads;
+    p.n_rows = n;
+    p.kv_len = L;
+    p.n_kt = (L + 63) / 64;
+    if ((int64_t)p.B * p.H * p.n_kt >= ((int64_t)1 << 31)) return fail(VAR_ERR_RANGE, "block mass grid too large");
+    const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return hip_status(varattn::launch_block_mass(p, d->head_dim, reinterpret_cast<hipStream_t>(stream)),
+                      "var_attn_block_mass launch");
+}
+
+VAR_EXPORT var_status var_decision_tiles(int32_t maps, int32_t n_qt, int32_t n_kt, const float* mass, float tau,
+                                         uint8_t* kept, void* stream) {
+    if (maps < 1 || n_qt < 1 || n_kt < 1 || (int64_t)maps * n_qt >= ((int64_t)1 << 31))
+        return fail(VAR_ERR_RANGE, "maps=%d n_qt=%d n_kt=%d invalid", maps, n_qt, n_kt);
+    if (n_kt > varattn::kDecisionMaxTiles)
+        return fail(VAR_ERR_UNSUPPORTED, "n_kt=%d above %d", n_kt, varattn::kDecisionMaxTiles);
+    if (!(tau >= 0.f && tau <= 1.f)) return fail(VAR_ERR_RANGE, "tau must lie in [0, 1]");
+    if (!mass || !kept) return fail(VAR_ERR_NULL, "mass and kept must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(mass) & 3u) return fail(VAR_ERR_STRIDE, "mass must be 4-byte aligned");
+    varattn::DecisionParams p;
+    p.mass = mass;
+    p.kept = kept;
+    p.n_kt = n_kt;
+    p.tau = tau;
+    return hip_status(varattn::launch_decision(p, maps * n_qt, reinterpret_cast<hipStream_t>(stream)),
+                      "var_decision_tiles launch");
+}
+
+VAR_EXPORT var_status var_mapped_tile_mask(const var_schedule* sched, int32_t decision_scale, int32_t step,
+                                           int32_t maps, const uint8_t* kept_d, int32_t* row_ptr, int32_t* col_idx,
+                                           int64_t col_stride, void* stream) {
+    Offsets off;
+    var_status st = check_schedule(sched, &off);
+    if (st != VAR_OK) return st;
+    if (decision_scale < 0 || step < decision_scale || step >= off.num_scales)
+        return fail(VAR_ERR_RANGE, "need 0 <= decision_scale <= step < num_scales, got %d, %d", decision_scale, step);
+    if (maps < 1 || maps > (1 << 20)) return fail(VAR_ERR_RANGE, "maps=%d invalid", maps);
+    const int32_t n_d = off.off[decision_scale + 1] - off.off[decision_scale];
+    const int32_t n_qt_d = (n_d + 63) / 64, n_kt_d = (off.off[decision_scale + 1] + 63) / 64;
+    const int32_t n_t = off.off[step + 1] - off.off[step];
+    const int32_t n_qt = (n_t + 63) / 64, n_kt = (off.off[step + 1] + 63) / 64;
+    if (n_qt_d > varattn::kDecisionMaxRowTiles || n_kt_d > varattn::kDecisionMaxTiles || n_kt > varattn::kMappedMaxTiles)
+        return fail(VAR_ERR_UNSUPPORTED, "decision step %d or step %d too large for the mapped mask", decision_scale,
+                    step);
+    if (col_stride < (int64_t)n_qt * n_kt)
+        return fail(VAR_ERR_CAPACITY, "col_stride=%lld below n_qt*n_kt=%lld", (long long)col_stride,
+                    (long long)n_qt * n_kt);
+    if ((int64_t)maps * n_qt >= ((int64_t)1 << 31)) return fail(VAR_ERR_RANGE, "mapped mask grid too large");
+    if (!kept_d || !row_ptr || !col_idx) return fail(VAR_ERR_NULL, "kept_d, row_ptr and col_idx must be non-NULL");
+    varattn::MappedParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.kept_d = kept_d;
+    p.row_ptr = row_ptr;
+    p.col_idx = col_idx;
+    p.rp_map_stride = n_qt + 1;
+    p.ci_map_stride = col_stride;
+    p.d = decision_scale;
+    p.T = step;
+    p.n_qt = n_qt;
+    p.n_kt = n_kt;
+    p.n_qt_d = n_qt_d;
+    p.n_kt_d = n_kt_d;
+    for (int i = 0; i <= VAR_MAX_SCALES; ++i) p.off[i] = i <= off.num_scales ? off.off[i] : off.off[off.num_scales];
+    for (int i = 0; i < VAR_MAX_SCALES; ++i) {
+        p.h[i] = i < off.num_scales ? sched->h[i] : 1;
+        p.w[i] = i < off.num_scales ? sched->w[i] : 1;
+    }
+    return hip_status(varattn::launch_mapped_mask(p, maps, reinterpret_cast<hipStream_t>(stream)),
+                      "var_mapped_tile_mask launch");
 }
 
 VAR_EXPORT var_status var_attn_split_plan(const var_schedule* sched, const var_attn_desc* d, int32_t n_sel,

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header(api):
     declared = _declared()
-    assert len(declared) == 13
+    assert len(declared) == 17
     for name in declared:
         assert hasattr(api.LIB, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True).stdout
@@ -221,3 +221,33 @@ def test_split_validation_and_plan(api):
     r = sp(ctypes.byref(s), ctypes.byref(d), P(FAKE), L, P(FAKE), L, P(FAKE), L, P(FAKE), L, P(0), P(0), 0,
            P(FAKE), P(FAKE), 64, 64, 9, P(FAKE), 1 << 40, P(0))
     assert r == E("VAR_ERR_RANGE")
+
+
+def test_decision_scale_validation_errors(api):
+    s = api.make_schedule(W1024, W1024)
+    E = lambda n: _code(api, n)
+    P = ctypes.c_void_p
+    L = api.Layout(2 * 16 * 1024 * 128, 1024 * 128, 128)
+    bm = api.LIB.var_attn_block_mass
+    assert bm(ctypes.byref(s), ctypes.byref(_desc(api, q_scale_begin=9, q_scale_end=11)), P(FAKE), L, P(FAKE), L,
+              P(FAKE), P(FAKE), P(0)) == E("VAR_ERR_RANGE")
+    big = api.make_schedule([1, 100], [1, 100])       # 10000 rows > 8192
+    assert bm(ctypes.byref(big), ctypes.byref(_desc(api, q_scale_begin=1, q_scale_end=2)), P(FAKE), L, P(FAKE), L,
+              P(FAKE), P(FAKE), P(0)) == E("VAR_ERR_UNSUPPORTED")
+    assert bm(ctypes.byref(s), ctypes.byref(_desc(api, q_scale_begin=9, q_scale_end=10)), P(FAKE), L, P(FAKE), L,
+              P(0), P(FAKE), P(0)) == E("VAR_ERR_NULL")
+    dt = api.LIB.var_decision_tiles
+    assert dt(32, 16, 40, P(FAKE), ctypes.c_float(1.5), P(FAKE), P(0)) == E("VAR_ERR_RANGE")
+    assert dt(32, 16, 1025, P(FAKE), ctypes.c_float(0.5), P(FAKE), P(0)) == E("VAR_ERR_UNSUPPORTED")
+    assert dt(0, 16, 40, P(FAKE), ctypes.c_float(0.5), P(FAKE), P(0)) == E("VAR_ERR_RANGE")
+    assert dt(32, 16, 40, P(0), ctypes.c_float(0.5), P(FAKE), P(0)) == E("VAR_ERR_NULL")
+    mm = api.LIB.var_mapped_tile_mask
+    assert mm(ctypes.byref(s), 10, 9, 32, P(FAKE), P(FAKE), P(FAKE), 64 * 165, P(0)) == E("VAR_ERR_RANGE")
+    assert mm(ctypes.byref(s), 9, 12, 32, P(FAKE), P(FAKE), P(FAKE), 64 * 165 - 1, P(0)) == E("VAR_ERR_CAPACITY")
+    assert mm(ctypes.byref(s), 9, 12, 32, P(0), P(FAKE), P(FAKE), 64 * 165, P(0)) == E("VAR_ERR_NULL")
+    sh = api.LIB.var_attn_block_sparse_heads
+    L2 = api.Layout(2 * 16 * 4096 * 128, 4096 * 128, 128)
+    assert sh(ctypes.byref(s), ctypes.byref(_desc(api)), P(FAKE), L2, P(FAKE), L2, P(FAKE), L2, P(FAKE), L2, P(0), P(0),
+              0, P(FAKE), P(FAKE), 64 * 165 - 1, P(0)) == E("VAR_ERR_CAPACITY")
+    assert sh(ctypes.byref(s), ctypes.byref(_desc(api)), P(FAKE), L2, P(FAKE), L2, P(FAKE), L2, P(FAKE), L2, P(0), P(0),
+              0, P(FAKE), P(FAKE), -1, P(0)) == E("VAR_ERR_RANGE")
