@@ -117,6 +117,16 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
+// A global-memory pointer every lane holds, moved to SGPRs: loads then take
+// the scalar base + 32-bit lane offset form instead of 64-bit vector adds.
+typedef __attribute__((address_space(1))) const char gchar;
+__device__ __forceinline__ const gchar* uniform_ptr(const gchar* q) {
+    const uint64_t v = reinterpret_cast<uint64_t>(q);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const gchar*>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float max3(float a, float b, float c) { return __builtin_fmaxf(a, __builtin_fmaxf(b, c)); }
 
 template <int V>
@@ -364,8 +374,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
     // clamps rows to kv_len-1 (those keys are masked later).
     constexpr int ROWS_PER_SEG = 1024 / (D * 2);
     constexpr int SEG_PER_WAVE = K_BYTES / 1024 / NW;
-    const char* const kbytes = reinterpret_cast<const char*>(kp);
-    const char* const vbytes = reinterpret_cast<const char*>(vp);
+    const gchar* const kbytes = uniform_ptr((const gchar*)(reinterpret_cast<uintptr_t>(kp)));
+    const gchar* const vbytes = uniform_ptr((const gchar*)(reinterpret_cast<uintptr_t>(vp)));
     const uint32_t k_st_bytes = (uint32_t)p.k_st * 2u;
     const uint32_t v_st_bytes = (uint32_t)p.v_st * 2u;
     uint32_t k_col[SEG_PER_WAVE];   // byte offset of this lane's 16-byte chunk in its row
@@ -401,19 +411,28 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
         v_row[j] = 4 * kg;
         v_col[j] = (uint32_t)(8 * dg);
     }
+    uint32_t v_full[V_PER_T];       // lane offsets of an interior (full) tile
+#pragma unroll
+    for (int j = 0; j < V_PER_T; ++j) v_full[j] = (uint32_t)v_row[j] * v_st_bytes + v_col[j];
+    // a loop-invariant lane offset made opaque at its use, so that the
+    // address is formed there as scalar base + 32-bit offset (one instruction)
+    auto lane_off = [](uint32_t o) __attribute__((always_inline)) -> uint32_t {
+        asm volatile("" : "+v"(o));
+        return o;
+    };
     // K tile straight from global memory into LDS (no registers): each lane of a
     // wave writes 16 bytes at lane*16 of the wave's 1 KB segment, so the
     // swizzle is applied by choosing which global chunk each lane fetches.
     auto load_k = [&](int kbase, int slot) __attribute__((always_inline)) {
         unsigned char* Ks = Kbuf + slot * K_BYTES;
-        const char* tb = kbytes + (int64_t)kbase * p.k_st * 2;
+        const gchar* tb = uniform_ptr(kbytes + (int64_t)kbase * p.k_st * 2);
         auto issue = [&](int i, uint32_t off) __attribute__((always_inline)) {
             __builtin_amdgcn_global_load_lds(tb + off, (__attribute__((address_space(3))) void*)(Ks + (wave * SEG_PER_WAVE + i) * 1024),
                                              16, 0, 0);
         };
         if (kbase + KT <= p.kv_len) {
 #pragma unroll
-            for (int i = 0; i < SEG_PER_WAVE; ++i) issue(i, k_full[i]);
+            for (int i = 0; i < SEG_PER_WAVE; ++i) issue(i, lane_off(k_full[i]));
         } else {
             const int last = kv_last - kbase;   // last valid row of this tile (< KT here)
 #pragma unroll
@@ -421,14 +440,15 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
         }
     };
     auto load_v = [&](int kbase) __attribute__((always_inline)) {
-        const char* tb = vbytes + (int64_t)kbase * p.v_st * 2;
+        const gchar* tb = uniform_ptr(vbytes + (int64_t)kbase * p.v_st * 2);
         if (kbase + KT <= p.kv_len) {
 #pragma unroll
             for (int j = 0; j < V_PER_T; ++j) {
-                const char* rowp = tb + ((uint32_t)v_row[j] * v_st_bytes + v_col[j]);
+                const uint32_t o = lane_off(v_full[j]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    vreg[j][r] = *reinterpret_cast<const u32x2*>(rowp + (uint32_t)r * v_st_bytes);
+                    vreg[j][r] = *reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(
+                        uniform_ptr(tb + (uint32_t)r * v_st_bytes) + o);
             }
         } else {
             const int last = kv_last - kbase;
@@ -437,7 +457,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const uint32_t off = (uint32_t)min(v_row[j] + r, last) * v_st_bytes + v_col[j];
-                    vreg[j][r] = *reinterpret_cast<const u32x2*>(tb + off);
+                    vreg[j][r] = *reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(tb + off);
                 }
         }
     };
