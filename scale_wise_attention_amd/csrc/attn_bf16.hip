@@ -221,9 +221,13 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
     constexpr int SK = D / 16;                 // k-steps of S^T = K Q^T
     constexpr int MO = D / 32;                 // 32-row blocks of O^T
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * K_BYTES + 2 * V_BYTES];
+    // LDS ring of K and V^T tiles: 4 slots (two tiles ahead, pairs of tiles
+    // per barrier) in a dense walk, 2 (one tile ahead) in a block-sparse walk
+    constexpr int RING = SPARSE ? 2 : 4;
+    constexpr int AHEAD = RING / 2;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[RING * K_BYTES + RING * V_BYTES];
     unsigned char* const Kbuf = smem;
-    unsigned char* const Vbuf = smem + 2 * K_BYTES;
+    unsigned char* const Vbuf = smem + RING * K_BYTES;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -605,8 +609,11 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
     auto walk = [&](auto mode_tag) __attribute__((always_inline)) {
         constexpr int MODE = decltype(mode_tag)::value;
         reset_walk();
+        // tile j of the walk lives in ring slot j % RING; at the start of an
+        // iteration tiles j .. j+AHEAD-1 are in LDS
         TileEnt e0 = next_tile();
         TileEnt e1 = next_tile();
+        TileEnt e2 = AHEAD == 2 ? next_tile() : TileEnt{-1, 0};
         if (e0.tile >= 0) {
             load_k(e0.tile * KT, 0);
             if constexpr (MODE == 0) {
@@ -614,11 +621,20 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                 store_v(0);
             }
         }
+        if constexpr (AHEAD == 2) {
+            if (e1.tile >= 0) {
+                load_k(e1.tile * KT, 1);
+                if constexpr (MODE == 0) {
+                    load_v(e1.tile * KT);
+                    store_v(1);
+                }
+            }
+        }
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): K bytes are in LDS
         __syncthreads();
 
         int j = 0;
-        auto fast = [&](const TileEnt& e) __attribute__((always_inline)) -> bool {
+        auto fast = [&](const TileEnt& e, int idx) __attribute__((always_inline)) -> bool {
             // (a tile that only some waves own also runs the branch-free body: the
             // other waves shift their logits to -inf, so their weights are zero.
             // In a block-sparse walk a wave's first owned tile need not be the
@@ -629,18 +645,19 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
             if constexpr (SPARSE) {
                 if (need_ref && mine(e)) return false;
             }
-            return j > 0 && e.tile * KT + KT <= wg_kmin;
+            return idx > 0 && e.tile * KT + KT <= wg_kmin;
         };
-        auto iterate = [&](auto fast_tag) __attribute__((always_inline)) {
+        // One tile: e's K and V^T sit in LDS slot `slot`; the V of tile nv (if
+        // any) is loaded now and staged into slot `vslot`.
+        auto body = [&](auto fast_tag, const TileEnt& e, int slot, const TileEnt& nv, int vslot)
+                        __attribute__((always_inline)) {
             constexpr bool FAST = decltype(fast_tag)::value;
-            const int slot = j & 1;
-            if (e1.tile >= 0) load_k(e1.tile * KT, slot ^ 1);
             if constexpr (MODE == 0) {
                 // the branch-free body always stages a V tile into the idle
-                // slot; after the last tile it re-stages its own (never read)
-                if (FAST || e1.tile >= 0) load_v((e1.tile >= 0 ? e1.tile : e0.tile) * KT);
+                // slot; with no next tile it re-stages its own (never read)
+                if (FAST || nv.tile >= 0) load_v((nv.tile >= 0 ? nv.tile : e.tile) * KT);
             }
-            const int kb = e0.tile * KT;
+            const int kb = e.tile * KT;
             f32x16 s0[2], s1[2];
             if constexpr (MODE == 0 && FAST) {
                 // Software-ordered body: slot m issues MFMA m and a fixed share of
@@ -672,7 +689,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                 constexpr int NP = 2 * MO;                 // PV slots per 16-key chunk
                 constexpr WeightSlots<D> WS{};
                 static_assert(WS.valid(), "weight pairs scheduled in time");
-                const bool own = mine(e0);
+                const bool own = mine(e);
                 const float nbt[2] = {own ? nb[0] : -INFINITY, own ? nb[1] : -INFINITY};
                 u32x4 w[4][2];                             // [chunk][qb]
                 float xs[32][2];                           // weight-pair stage values
@@ -708,8 +725,8 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                         }
                         if constexpr (c == 3) {
                             static_for<4 * V_PER_T>([&](auto ec) __attribute__((always_inline)) {
-                                constexpr int e = decltype(ec)::value;
-                                if constexpr ((e * NP) / (4 * V_PER_T) == t - 3 * NP) store_v_piece(slot ^ 1, e >> 2, e & 3);
+                                constexpr int ev = decltype(ec)::value;
+                                if constexpr ((ev * NP) / (4 * V_PER_T) == t - 3 * NP) store_v_piece(vslot, ev >> 2, ev & 3);
                             });
                         }
                     }
@@ -742,7 +759,7 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                 });
             } else {
                 // a tile outside this wave's own list is computed fully masked
-                const bool own = mine(e0);
+                const bool own = mine(e);
                 const int lim[2] = {own ? klim[0] : -1, own ? klim[1] : -1};
                 const bool need_mask = kb + KT > (own ? w_kmin : -1);
                 if constexpr (MODE == 0) {
@@ -776,19 +793,55 @@ __global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
                 }
             }
             if constexpr (MODE == 0 && !FAST) {
-                if (e1.tile >= 0) store_v(slot ^ 1);
+                if (nv.tile >= 0) store_v(vslot);
             }
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): next K tile is in LDS
+        };
+        // the DMA'd K tiles are in LDS and every wave is past its reads of the
+        // slots that the next loads overwrite
+        auto tile_barrier = [&]() __attribute__((always_inline)) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
             __syncthreads();
+        };
+        // one tile per barrier; the tile AHEAD places on is loaded meanwhile
+        auto single = [&](auto fast_tag) __attribute__((always_inline)) {
+            const TileEnt nx = AHEAD == 2 ? e2 : e1;
+            if (nx.tile >= 0) load_k(nx.tile * KT, (j + AHEAD) % RING);
+            body(fast_tag, e0, j % RING, nx, (j + AHEAD) % RING);
+            tile_barrier();
             e0 = e1;
-            e1 = next_tile();
+            if constexpr (AHEAD == 2) {
+                e1 = e2;
+                e2 = next_tile();
+            } else {
+                e1 = next_tile();
+            }
             ++j;
         };
+        // two branch-free tiles per barrier (dense walks): the two after them are
+        // loaded meanwhile
+        auto pair = [&]() __attribute__((always_inline)) {
+            const TileEnt e3 = next_tile();
+            if (e2.tile >= 0) load_k(e2.tile * KT, (j + 2) & 3);
+            if (e3.tile >= 0) load_k(e3.tile * KT, (j + 3) & 3);
+            body(BoolC<true>{}, e0, j & 3, e2, (j + 2) & 3);
+            body(BoolC<true>{}, e1, (j + 1) & 3, e3, (j + 3) & 3);
+            tile_barrier();
+            e0 = e2;
+            e1 = e3;
+            e2 = next_tile();
+            j += 2;
+        };
         while (e0.tile >= 0) {
-            if constexpr (MODE == 0) {
-                while (e0.tile >= 0 && fast(e0)) iterate(BoolC<true>{});
+            if constexpr (MODE == 0 && !SPARSE) {
+                // (the pair decision is workgroup-uniform in a dense walk)
+                while (e1.tile >= 0 && fast(e0, j) && fast(e1, j + 1)) pair();
+                if (e0.tile >= 0) single(BoolC<false>{});
+            } else {
+                if constexpr (MODE == 0) {
+                    while (e0.tile >= 0 && fast(e0, j)) single(BoolC<true>{});
+                }
+                while (e0.tile >= 0 && (MODE != 0 || !fast(e0, j))) single(BoolC<false>{});
             }
-            while (e0.tile >= 0 && (MODE != 0 || !fast(e0))) iterate(BoolC<false>{});
         }
     };
 
