@@ -23,7 +23,9 @@
 // Two launches: (1) one workgroup per query tile ORs its rows' tile runs into
 // a bitmap in LDS and writes the kept columns, in ascending order, at
 // col_idx[r*n_kt] with the count in row_ptr[r+1]; (2) one workgroup turns the
-// counts into offsets and moves every row's list down to its final place.
+// counts into offsets and moves every row's list down to its final place.  A
+// mask of at most 2 query tiles takes one launch: one workgroup builds the
+// rows in order, each list straight at its final offset.
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -32,6 +34,7 @@ namespace varattn {
 namespace {
 
 constexpr int kRowThreads = 256;
+constexpr int kDirectMaxTiles = 2;     // masks of up to this many query tiles take one launch
 constexpr int kChunkTiles = 8192;              // key tiles per bitmap pass
 constexpr int kChunkWords = kChunkTiles / 32;
 
@@ -65,14 +68,21 @@ __device__ __forceinline__ void mark_tiles(uint32_t* bits, int t0, int t1, int c
     }
 }
 
-// One workgroup per query tile.  Keys are processed in chunks of kChunkTiles
-// tiles (one pass for every workload up to 8192 key tiles).
-__global__ __launch_bounds__(kRowThreads) void mask_rows_kernel(const MaskParams p) {
-    __shared__ uint32_t bits[kChunkWords];
-    __shared__ int wave_cnt[kRowThreads / 64];
-    __shared__ int running;
-    __shared__ int sink_end;
-    const int r = blockIdx.x;
+struct RowShared {
+    uint32_t bits[kChunkWords];
+    int wave_cnt[kRowThreads / 64];
+    int running;
+    int sink_end;
+};
+
+// Kept key tiles of query tile r, written in ascending order at out[0 ..);
+// returns their count (to every thread).  Keys are processed in chunks of
+// kChunkTiles tiles (one pass for every workload up to 8192 key tiles).
+__device__ int build_row(const MaskParams& p, int r, int* out, RowShared& sh) {
+    uint32_t* const bits = sh.bits;
+    int* const wave_cnt = sh.wave_cnt;
+    int& running = sh.running;
+    int& sink_end = sh.sink_end;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int i0 = r * p.tile_q;
     const int n_rows = min(p.tile_q, p.n_rows - i0);
@@ -93,7 +103,6 @@ __global__ __launch_bounds__(kRowThreads) void mask_rows_kernel(const MaskParams
         }
         if (se > 0) atomicMax(&sink_end, se);
     }
-    int* out = p.col_idx + (int64_t)r * p.n_kt;
     for (int c0 = 0; c0 < p.n_kt; c0 += kChunkTiles) {
         for (int wd = tid; wd < kChunkWords; wd += kRowThreads) bits[wd] = 0;
         __syncthreads();
@@ -150,11 +159,36 @@ __global__ __launch_bounds__(kRowThreads) void mask_rows_kernel(const MaskParams
             __syncthreads();
         }
     }
-    if (tid == 0) {
-        p.row_ptr[r + 1] = running;
+    const int cnt = running;
+    __syncthreads();   // every thread has the count before the next row resets it
+    return cnt;
+}
+
+// One workgroup per query tile; lists at col_idx[r * n_kt], counts in
+// row_ptr[r + 1] (moved into place by mask_compact_kernel).
+__global__ __launch_bounds__(kRowThreads) void mask_rows_kernel(const MaskParams p) {
+    __shared__ RowShared sh;
+    const int r = blockIdx.x;
+    const int cnt = build_row(p, r, p.col_idx + (int64_t)r * p.n_kt, sh);
+    if (threadIdx.x == 0) {
+        p.row_ptr[r + 1] = cnt;
         if (r == 0) p.row_ptr[0] = 0;
     }
 }
+
+// A mask of few query tiles in one launch: one workgroup builds the rows in
+// order and writes each list straight to its final place.
+__global__ __launch_bounds__(kRowThreads) void mask_direct_kernel(const MaskParams p) {
+    __shared__ RowShared sh;
+    int base = 0;
+    for (int r = 0; r < p.n_qt; ++r) {
+        const int cnt = build_row(p, r, p.col_idx + base, sh);
+        base += cnt;
+        if (threadIdx.x == 0) p.row_ptr[r + 1] = base;
+    }
+    if (threadIdx.x == 0) p.row_ptr[0] = 0;
+}
+
 
 constexpr int kCompactThreads = 1024;
 constexpr int kPtrCap = 8192;                  // row offsets staged in LDS up to this many rows
@@ -258,7 +292,11 @@ hipError_t launch_mask_compact(const MaskParams& p, int maps, hipStream_t s) {
 }
 
 hipError_t launch_tile_mask(const MaskParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(mask_rows_kernel, dim3(p.n_qt), dim3(256), 0, s, p);
+    if (p.n_qt <= kDirectMaxTiles) {
+        hipLaunchKernelGGL(mask_direct_kernel, dim3(1), dim3(kRowThreads), 0, s, p);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(mask_rows_kernel, dim3(p.n_qt), dim3(kRowThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(mask_compact_kernel, dim3(1), dim3(1024), 0, s, p);
