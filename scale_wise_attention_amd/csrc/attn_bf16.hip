@@ -61,10 +61,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int NW = 4;                  // waves per workgroup
-constexpr int NT = NW * 64;            // threads per workgroup
 constexpr int QW = 64;                 // query rows per wave
-constexpr int QT = NW * QW;            // query rows per workgroup
+// waves per workgroup: 4 for dense attention; 2 for block-sparse attention,
+// whose workgroup walks the union of its waves' kept tiles (two workgroups
+// then share a compute unit)
+template <bool SPARSE>
+constexpr int waves_per_wg() { return SPARSE ? 2 : 4; }
 constexpr int KT = 64;                 // keys per tile (= sparse tile width)
 constexpr float kSumLimit = 0x1p100f;  // a row sum above this triggers the exact recompute
 
@@ -210,7 +212,10 @@ struct TileEnt {
 };
 
 template <int D, bool OUT_BF16, bool SPARSE>
-__global__ __launch_bounds__(NT, 1) void attn_bf16_kernel(const AttnParams p) {
+__global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_bf16_kernel(const AttnParams p) {
+    constexpr int NW = waves_per_wg<SPARSE>();   // waves per workgroup
+    constexpr int NT = NW * 64;                  // threads per workgroup
+    constexpr int QT = NW * QW;                  // query rows per workgroup
     constexpr int KCH = D / 8;                 // 16-byte chunks per K row
     constexpr int K_BYTES = KT * D * 2;
     constexpr int V_BYTES = KT * D * 2;
@@ -968,7 +973,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, in
 template <int D, bool OB, bool SP>
 hipError_t launch_one(const AttnParams& p, hipStream_t s) {
     const int grid = p.n_qtiles * p.B * p.H * p.n_splits;
-    hipLaunchKernelGGL((attn_bf16_kernel<D, OB, SP>), dim3(grid), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, OB, SP>), dim3(grid), dim3(waves_per_wg<SP>() * 64), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_splits == 1) return e;
     const int64_t threads = (int64_t)p.B * p.H * p.n_rows * (D / 4);
@@ -980,8 +985,7 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
 
 int attn_bf16_rows_per_tile(int head_dim, bool sparse) {
     (void)head_dim;
-    (void)sparse;
-    return QT;
+    return (sparse ? waves_per_wg<true>() : waves_per_wg<false>()) * QW;
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int D, bool out_bf16, bool sparse, hipStream_t s) {
