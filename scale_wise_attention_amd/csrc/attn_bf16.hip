@@ -12,8 +12,9 @@
 // attention); q_index fuses the gather of pruned queries ("ARVAR ...", Key
 // Design 2).
 //
-// Design (one workgroup = 4 waves = 256 query rows of one (batch, head); one
-// wave per SIMD):
+// Design (dense: one workgroup = 4 waves = 256 query rows of one (batch,
+// head); block-sparse: 2 waves = 128 rows, two workgroups per compute unit;
+// always one wave per SIMD):
 //  * Each wave owns 64 queries in two 32-query column blocks.  S^T = K Q^T is
 //    computed with v_mfma_f32_32x32x16_bf16 (keys on M, queries on N), so a
 //    lane holds 16 logits of each of its two queries and lane l^32 holds the
@@ -22,13 +23,19 @@
 //  * The same registers, rounded to bf16, are the B operand of
 //    O^T += V^T P^T (d on M, queries on N, keys on K).  The MFMA's k order is
 //    matched by permuting keys inside the V^T tile in LDS, so P never moves
-//    between lanes.  Q stays in registers for the whole key loop.
-//  * Per 64-key tile: S^T = K Q^T, the row max, then the weights of each
-//    16-key chunk are exponentiated and rounded while the matrix core runs
-//    the P V^T MFMAs of the previous chunk.  K and V of the next tile are in
-//    flight (global -> registers) during the whole tile and land in the
-//    other half of a double-buffered LDS ring (V transposed on the way): one
-//    barrier per tile.
+//    between lanes.  Q stays in AGPRs for the whole key loop; the O
+//    accumulators are VGPRs (VGPR-form MFMAs) and the K / V^T operands read
+//    from LDS are handed to the MFMAs from AGPRs.
+//  * Tiles that need no mask run a branch-free body, unrolled at compile
+//    time into one slot per MFMA: the QK chains block by block, then the PV
+//    MFMAs, with the weights of each key pair computed in three stages
+//    (scale+shift, exp2, pack) spread over the slots in between.  K goes
+//    straight from global memory into LDS (global_load_lds); V goes through
+//    registers and is written transposed under the last PV chunk.  A dense
+//    walk keeps a 4-slot LDS ring two tiles ahead and runs these tiles in
+//    pairs, one barrier per pair; a block-sparse walk keeps 2 slots, one
+//    tile ahead, one barrier per tile.  The first tile and masked tiles run
+//    a general body.
 //  * Softmax in the log2 domain (scale*log2(e) folded into one FMA before
 //    v_exp_f32) against a fixed reference max per row: the max of the first
 //    tile in which the row sees a key.  Later weights may exceed 1 (fp32 and
@@ -40,9 +47,12 @@
 //    (QK only), then the weights against them (all <= 1).  Row sums
 //    accumulate the bf16-rounded weights with v_dot2 (the same weights that
 //    multiply V).
-//  * Block-sparse: a workgroup's 4 waves cover 4 consecutive 64-row query
+//  * Block-sparse: a workgroup's 2 waves cover 2 consecutive 64-row query
 //    tiles; the workgroup walks the merged (union) list of their kept key
-//    tiles and each wave computes only the tiles of its own list.
+//    tiles and each wave takes only the tiles of its own list.
+//  * Key splits (n_splits > 1): each workgroup takes an equal share of its
+//    key tiles and writes fp32 partial O and LSE; split_merge_kernel combines
+//    them with log-sum-exp weights.
 //  * Workgroup ids are remapped so the query tiles of one (batch, head) run
 //    on one XCD and share its L2 for K and V.
 #include <hip/hip_runtime.h>
