@@ -343,6 +343,21 @@ def main():
     dyn_flops = 4.0 * D * dyn_pairs
     dyn_kept = float(rp_h[:, -1].sum()) / (B * H * rp_h.shape[1] - B * H) / -(-off[K] // 64)
 
+    # the dense last step with its inputs rotated over 3 independent Q/K/V sets
+    # (about 500 MB of K/V/Q, beyond the 256 MB of last-level cache), so each
+    # launch reads cold data
+    rot = [make_qkv(wl, 10 + i, device=dev) for i in range(3)]
+    rot_out = torch.empty(B, H, 4096, D, dtype=bf, device=dev)
+    rot_i = [0]
+
+    def rotated_last_step():
+        rq, rk, rv = rot[rot_i[0] % 3]
+        rot_i[0] += 1
+        api.var_attn_dense(sched, rq[:, :, off[K - 1]:off[K]], rk, rv, K - 1, K, out=rot_out)
+
+    rot_ms = time_launch(rotated_last_step, reps=max(3, R // 2) // 3 * 3)
+
+
     # Branch Halving on the last step: the conditional branch alone (batch 1)
     bh_out = torch.empty(1, H, 4096, D, dtype=bf, device=dev)
     bh_ms = time_launch(lambda: api.var_attn_dense(sched, qsteps[K - 1][:1], k[:1], v[:1], K - 1, K, out=bh_out))
@@ -397,6 +412,7 @@ def main():
             "last_step_gflop": round(dense_flops[last] / 1e9, 3),
             "last_step_tflops": round(last_tflops, 2),
             "last_step_frac_peak": round(last_tflops / PEAK_BF16_TFLOPS, 4),
+            "last_step_rotated_inputs_ms": round(rot_ms, 4),
         },
         "sparse": {
             "generation_ms": round(sparse_gen_ms, 4),
