@@ -20,7 +20,8 @@ Sources (web pages on visual-autoregressive next-scale generation):
   Design 3, Equations (8)-(9) (nearest base + overwrite scatter); Key
   Design 2 also for the attention-guided choice of the retained positions.
 * "LiteVAR: Compressing Visual Autoregressive Modelling with Efficient
-  Attention and Quantization", method tags "Attention" and "Softmax".
+  Attention and Quantization", method tags "Attention" and "Softmax", and the
+  low-bit quantisation of the data precision.
 
 Modules:
 
@@ -36,6 +37,8 @@ Modules:
 * ``dynamic_sparse`` -- per-head tile pattern of a later step predicted from
   the attention mass of a decision scale through index mapping.
                                                           (pinned: see tests)
+* ``fp8``        -- e4m3 quantisation of queries and keys with one scale per
+  (batch, head).                                          (pinned: see tests)
 
 Every function here is pinned by ``-m "not gpu"`` tests against something other
 than itself (brute force, closed forms, invariants, library routines); none is
