@@ -32,6 +32,7 @@ EXPORTED = ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_
             "var_attn_block_sparse", "var_scatter_restore", "var_attn_saliency", "var_select_topk",
             "var_attn_dense_split", "var_attn_block_sparse_split", "var_attn_split_plan",
             "var_attn_block_mass", "var_decision_tiles", "var_mapped_tile_mask", "var_attn_block_sparse_heads",
+            "var_quantize_e4m3", "var_attn_dense_e4m3", "var_attn_block_sparse_e4m3",
             "var_status_string", "var_last_error")
 
 
@@ -92,10 +93,12 @@ def _load():
     lib.var_mapped_tile_mask.argtypes = [SP, i32, i32, i32, P, P, P, i64, P]
     lib.var_attn_block_sparse_heads.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, Layout, P,
                                                 Layout, P, P, i32, P, P, i64, P]
-    for name in ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_build_tile_mask",
-                 "var_attn_block_sparse", "var_scatter_restore", "var_attn_saliency", "var_select_topk",
-                 "var_attn_dense_split", "var_attn_block_sparse_split", "var_attn_split_plan",
-                 "var_attn_block_mass", "var_decision_tiles", "var_mapped_tile_mask", "var_attn_block_sparse_heads"):
+    lib.var_quantize_e4m3.argtypes = [i32, i32, i32, i32, P, Layout, P, Layout, P, P]
+    lib.var_attn_dense_e4m3.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, P, Layout, P, P, Layout, P,
+                                        Layout, P, P, i32, i32, P, i64, P]
+    lib.var_attn_block_sparse_e4m3.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, P, Layout, P, P, Layout,
+                                               P, Layout, P, P, i32, P, P, i64, P]
+    for name in EXPORTED[:-2]:
         getattr(lib, name).restype = ctypes.c_int
     lib.var_status_string.argtypes = [ctypes.c_int]
     lib.var_status_string.restype = ctypes.c_char_p
@@ -175,7 +178,8 @@ def _check_index(q_index, device):
         raise ValueError("q_index must live on the tensors' device")
 
 
-def _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype, softmax_scale, q_index, want_lse):
+def _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype, softmax_scale, q_index, want_lse,
+                 qk_codes=False):
     s = _as_schedule(schedule)
     _, n_q, kv_len = var_schedule_extent(s, q_scale_begin, q_scale_end)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -184,7 +188,10 @@ def _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype, 
     B, H, _, D = q.shape
     if k.shape[0] != B or v.shape[0] != B or k.shape[1] != H or v.shape[1] != H or k.shape[3] != D or v.shape[3] != D:
         raise ValueError("q, k, v disagree in batch, heads or head_dim")
-    if q.dtype != k.dtype or q.dtype != v.dtype:
+    if qk_codes:
+        if q.dtype != torch.uint8 or k.dtype != torch.uint8 or v.dtype != torch.bfloat16:
+            raise ValueError("e4m3 attention takes uint8 codes for q and k and bf16 v")
+    elif q.dtype != k.dtype or q.dtype != v.dtype:
         raise ValueError("q, k, v must share a dtype")
     if q.device != k.device or q.device != v.device:
         raise ValueError("q, k, v must share a device")
@@ -200,7 +207,7 @@ def _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype, 
     elif tuple(out.shape) != (B, H, rows, D) or out.device != q.device:
         raise ValueError(f"out must have shape {(B, H, rows, D)} on q's device")
     lse = torch.empty((B, H, rows), dtype=torch.float32, device=q.device) if want_lse else None
-    desc = AttnDesc(B, H, D, q_scale_begin, q_scale_end, float(softmax_scale), _dtype_code(q.dtype),
+    desc = AttnDesc(B, H, D, q_scale_begin, q_scale_end, float(softmax_scale), _dtype_code(v.dtype),
                     _dtype_code(out.dtype))
     return s, desc, out, lse, rows
 
@@ -487,4 +494,76 @@ def var_attn_block_sparse_heads(schedule, q, k, v, q_scale_begin, q_scale_end, r
                                            _layout(k), _ptr(v), _layout(v), _ptr(out), _layout(out), _ptr(lse),
                                            _ptr(q_index), n_sel, _ptr(row_ptr), _ptr(col_idx), col_idx.shape[1],
                                            _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+def var_quantize_e4m3(x, codes=None, scale=None):
+    """x bf16 [B, H, T, D] -> (codes uint8 [B, H, T, D], scale fp32 [B, H]); value = e4m3(code) * scale."""
+    if x.dim() != 4 or not x.is_cuda or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 4-D bf16 device tensor [batch, head, token, dim]")
+    B, H, T, D = x.shape
+    if codes is None:
+        codes = torch.empty((B, H, T, D), dtype=torch.uint8, device=x.device)
+    elif tuple(codes.shape) != (B, H, T, D) or codes.dtype != torch.uint8 or codes.device != x.device:
+        raise ValueError(f"codes must be uint8 {(B, H, T, D)} on x's device")
+    if scale is None:
+        scale = torch.empty((B, H), dtype=torch.float32, device=x.device)
+    elif scale.numel() != B * H or scale.dtype != torch.float32 or not scale.is_contiguous() or scale.device != x.device:
+        raise ValueError("scale must be a contiguous fp32 tensor of B*H elements on x's device")
+    _check(LIB.var_quantize_e4m3(B, H, T, D, _ptr(x), _layout(x), _ptr(codes), _layout(codes), _ptr(scale),
+                                 _stream(x.device)))
+    return codes, scale
+
+
+def _scale_arg(t, B, H, dev, name):
+    if t.numel() != B * H or t.dtype != torch.float32 or not t.is_contiguous() or t.device != dev:
+        raise ValueError(f"{name} must be a contiguous fp32 tensor of B*H elements on q's device")
+    return _ptr(t)
+
+
+def var_attn_dense_e4m3(schedule, q, q_scale, k, k_scale, v, q_scale_begin, q_scale_end, out=None, out_dtype=None,
+                        softmax_scale=0.0, q_index=None, return_lse=False, n_splits=1, workspace=None):
+    """var_attn_dense with q and k as e4m3 codes (uint8) and fp32 scales [B, H] (see var_quantize_e4m3)."""
+    s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
+                                           softmax_scale, q_index, return_lse, qk_codes=True)
+    n_sel = rows if q_index is not None else 0
+    if q_index is not None and n_sel == 0:
+        return (out, lse) if return_lse else out
+    B, H = q.shape[0], q.shape[1]
+    wp, wb = _ws_args(n_splits, workspace)
+    _check(LIB.var_attn_dense_e4m3(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q),
+                                   _scale_arg(q_scale, B, H, q.device, "q_scale"), _ptr(k), _layout(k),
+                                   _scale_arg(k_scale, B, H, q.device, "k_scale"), _ptr(v), _layout(v), _ptr(out),
+                                   _layout(out), _ptr(lse), _ptr(q_index), n_sel, int(n_splits), wp, wb,
+                                   _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+def var_attn_block_sparse_e4m3(schedule, q, q_scale, k, k_scale, v, q_scale_begin, q_scale_end, row_ptr, col_idx,
+                               out=None, out_dtype=None, softmax_scale=0.0, q_index=None, return_lse=False):
+    """Block-sparse attention with e4m3 q and k.  row_ptr / col_idx 1-D: one CSR for every (batch, head);
+    2-D [B*H, n_qt+1] / [B*H, stride]: one CSR per (batch, head)."""
+    s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
+                                           softmax_scale, q_index, return_lse, qk_codes=True)
+    n_sel = rows if q_index is not None else 0
+    if q_index is not None and n_sel == 0:
+        return (out, lse) if return_lse else out
+    B, H = q.shape[0], q.shape[1]
+    n_qt = -(-rows // 64)
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous int32 tensor on q's device")
+    if row_ptr.dim() == 1:
+        if row_ptr.numel() < n_qt + 1 or col_idx.dim() != 1:
+            raise ValueError(f"a shared CSR needs row_ptr of {n_qt + 1} entries and a 1-D col_idx")
+        stride = 0
+    else:
+        if tuple(row_ptr.shape) != (B * H, n_qt + 1) or col_idx.dim() != 2 or col_idx.shape[0] != B * H:
+            raise ValueError("per-head CSR: row_ptr int32 [B*H, n_qt+1], col_idx int32 [B*H, stride]")
+        stride = col_idx.shape[1]
+    _check(LIB.var_attn_block_sparse_e4m3(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q),
+                                          _scale_arg(q_scale, B, H, q.device, "q_scale"), _ptr(k), _layout(k),
+                                          _scale_arg(k_scale, B, H, q.device, "k_scale"), _ptr(v), _layout(v),
+                                          _ptr(out), _layout(out), _ptr(lse), _ptr(q_index), n_sel, _ptr(row_ptr),
+                                          _ptr(col_idx), stride, _stream(q.device)))
     return (out, lse) if return_lse else out

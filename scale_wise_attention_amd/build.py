@@ -19,13 +19,14 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libvarattn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["attn_bf16.hip", "attn_f32.hip", "tile_mask.hip", "scatter.hip", "saliency.hip", "dynamic_sparse.hip", "var_attn_api.cpp"]
-# The bf16 attention kernels run with the IEEE mode bit off and without NaN
+SOURCES = ["attn_bf16.hip", "attn_fp8.hip", "attn_f32.hip", "quant_e4m3.hip", "tile_mask.hip", "scatter.hip", "saliency.hip", "dynamic_sparse.hip", "var_attn_api.cpp"]
+# The attention kernels (bf16 and e4m3 q / k) run with the IEEE mode bit off and without NaN
 # semantics (infinities stay honoured: masked logits are -inf): max/min then
 # need no NaN-quieting instructions in the softmax.  Their MFMAs write VGPRs
 # (S and O are read by VALU code); the kernel itself places the MFMA operands
 # that stay resident (Q) or come from LDS (K, V^T) in AGPRs.
-PER_FILE_FLAGS = {"attn_bf16.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+_ATTN_FLAGS = ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]
+PER_FILE_FLAGS = {"attn_bf16.hip": _ATTN_FLAGS, "attn_fp8.hip": _ATTN_FLAGS}
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

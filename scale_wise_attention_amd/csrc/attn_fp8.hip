@@ -1,0 +1,16 @@
+// e4m3 instantiations of the next-scale attention kernel (attn_kernel.h):
+// q and k as e4m3 codes with one scale per (batch, head) (the low-bit data
+// precision of "LiteVAR: Compressing Visual Autoregressive Modelling with
+// Efficient Attention and Quantization"), S^T on the e4m3 matrix cores; the
+// weights and v stay bf16, accumulation fp32, fp32 or bf16 output.
+#include "attn_kernel.h"
+
+namespace varattn {
+
+hipError_t launch_attn_fp8(const AttnParams& p, int D, bool out_bf16, bool sparse, hipStream_t s) {
+    if (D != 128) return hipErrorInvalidValue;   // the host layer admits head_dim 128 only
+    if (sparse) return out_bf16 ? launch_one<128, true, true, true>(p, s) : launch_one<128, false, true, true>(p, s);
+    return out_bf16 ? launch_one<128, true, false, true>(p, s) : launch_one<128, false, false, true>(p, s);
+}
+
+}  // namespace varattn

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header(api):
     declared = _declared()
-    assert len(declared) == 17
+    assert len(declared) == 20
     for name in declared:
         assert hasattr(api.LIB, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True).stdout
@@ -251,3 +251,37 @@ def test_decision_scale_validation_errors(api):
               0, P(FAKE), P(FAKE), 64 * 165 - 1, P(0)) == E("VAR_ERR_CAPACITY")
     assert sh(ctypes.byref(s), ctypes.byref(_desc(api)), P(FAKE), L2, P(FAKE), L2, P(FAKE), L2, P(FAKE), L2, P(0), P(0),
               0, P(FAKE), P(FAKE), -1, P(0)) == E("VAR_ERR_RANGE")
+
+
+def test_e4m3_validation_errors(api):
+    s = api.make_schedule(W1024, W1024)
+    E = lambda n: _code(api, n)
+    P = ctypes.c_void_p
+    L = api.Layout(2 * 16 * 10521 * 128, 10521 * 128, 128)
+    qz = api.LIB.var_quantize_e4m3
+    assert qz(2, 0, 10521, 128, P(FAKE), L, P(FAKE), L, P(FAKE), P(0)) == E("VAR_ERR_RANGE")
+    assert qz(256, 256, 10521, 128, P(FAKE), L, P(FAKE), L, P(FAKE), P(0)) == E("VAR_ERR_RANGE")   # > 65535 maps
+    assert qz(2, 16, 10521, 120, P(FAKE), L, P(FAKE), L, P(FAKE), P(0)) == E("VAR_ERR_UNSUPPORTED")
+    assert qz(2, 16, 10521, 128, P(FAKE), L, P(FAKE), L, P(0), P(0)) == E("VAR_ERR_NULL")
+    assert qz(2, 16, 10521, 128, P(FAKE + 8), L, P(FAKE), L, P(FAKE), P(0)) == E("VAR_ERR_STRIDE")
+    odd = api.Layout(2 * 16 * 10521 * 136, 10521 * 136, 136)   # 136-byte code rows: not a multiple of 16
+    assert qz(2, 16, 10521, 128, P(FAKE), L, P(FAKE), odd, P(FAKE), P(0)) == E("VAR_ERR_STRIDE")
+    dn = api.LIB.var_attn_dense_e4m3
+
+    def dense(desc, qs=FAKE, ks=FAKE, ql=L):
+        return dn(ctypes.byref(s), ctypes.byref(desc), P(FAKE), ql, P(qs), P(FAKE), L, P(ks), P(FAKE), L, P(FAKE), L,
+                  P(0), P(0), 0, 1, P(0), 0, P(0))
+
+    assert dense(_desc(api, head_dim=64)) == E("VAR_ERR_UNSUPPORTED")
+    assert dense(_desc(api, in_dtype=api.VAR_F32, head_dim=64)) == E("VAR_ERR_UNSUPPORTED")
+    assert dense(_desc(api), qs=0) == E("VAR_ERR_NULL")
+    assert dense(_desc(api), ks=0) == E("VAR_ERR_NULL")
+    assert dense(_desc(api), qs=FAKE + 2) == E("VAR_ERR_STRIDE")
+    assert dense(_desc(api), ql=odd) == E("VAR_ERR_STRIDE")
+    sp = api.LIB.var_attn_block_sparse_e4m3
+    assert sp(ctypes.byref(s), ctypes.byref(_desc(api)), P(FAKE), L, P(FAKE), P(FAKE), L, P(FAKE), P(FAKE), L,
+              P(FAKE), L, P(0), P(0), 0, P(FAKE), P(FAKE), -1, P(0)) == E("VAR_ERR_RANGE")
+    assert sp(ctypes.byref(s), ctypes.byref(_desc(api)), P(FAKE), L, P(FAKE), P(FAKE), L, P(FAKE), P(FAKE), L,
+              P(FAKE), L, P(0), P(0), 0, P(FAKE), P(FAKE), 64 * 165 - 1, P(0)) == E("VAR_ERR_CAPACITY")
+    assert sp(ctypes.byref(s), ctypes.byref(_desc(api)), P(FAKE), L, P(FAKE), P(FAKE), L, P(FAKE), P(FAKE), L,
+              P(FAKE), L, P(0), P(0), 0, P(0), P(FAKE), 0, P(0)) == E("VAR_ERR_NULL")

@@ -1,0 +1,239 @@
+"""GPU parity of the e4m3 path: the quantiser bit for bit against the oracle's
+quantize_maps (codes and scales), and attention on e4m3 q / k against the fp64
+oracle on the dequantised values, at the bf16 bars (max-abs 1e-2, mean-abs
+1e-3; LSE within 2.5e-3): the products of codes are exact in the matrix cores,
+so the only rounding left is the bf16 weights' and the fp32 sums'.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.fp8 import dequantize, quantize_maps
+from scale_wise_attention_amd.inputs import WORKLOADS, custom_workload, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from scale_wise_attention_amd import api as _api
+    return _api
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _oracle_quant(x):
+    """x bf16 [B, H, T, D] (any device) -> oracle codes [B, H, T, D] and scales [B, H]."""
+    xn = _np(x)
+    B, H = xn.shape[:2]
+    codes, scale = quantize_maps(xn.reshape((B * H,) + xn.shape[2:]))
+    return codes.reshape(xn.shape), scale.reshape(B, H)
+
+
+def _check_quant(api, x, what):
+    codes, scale = api.var_quantize_e4m3(x)
+    ref_c, ref_s = _oracle_quant(x)
+    got_c, got_s = codes.cpu().numpy(), scale.cpu().numpy()
+    bad = np.count_nonzero(got_c != ref_c)
+    print(f"[quant {what}] shape {tuple(x.shape)} code mismatches {bad}", flush=True)
+    assert bad == 0
+    assert np.array_equal(got_s.view(np.uint32), ref_s.view(np.uint32))
+    return codes, scale, ref_c, ref_s
+
+
+@pytest.mark.parametrize("D,T", [(128, 77), (64, 1), (16, 300), (128, 4096)])
+def test_quantize_matches_oracle(api, D, T):
+    rng = np.random.default_rng(40 + D + T)
+    B, H = 2, 3
+    x = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    x *= np.array([1.0, 1e-3, 40.0, 1.0, 0.0, 1.0], np.float32).reshape(B, H, 1, 1)
+    x[1, 0, 0, 0] = 1e4          # one large value: the rest of the map falls into subnormal codes
+    x[0, 0, :, 1] = -0.0         # negative zeros keep their sign bit
+    _check_quant(api, torch.from_numpy(x).to(torch.bfloat16).cuda(), f"D={D}")
+
+
+def test_quantize_ties_between_codes(api):
+    # bf16 values placed so that x * 448 / amax lands on midpoints between e4m3 codes
+    # (amax = 448 makes inv exactly 1): round half to even must pick the even code
+    pos = np.array([1.0 + i / 8 for i in range(8)], np.float64)
+    mids = np.concatenate([(pos[:-1] + pos[1:]) / 2 * 2.0 ** e for e in range(-6, 8)] +
+                          [(pos[:6] + pos[1:7]) / 2 * 2.0 ** 8] +
+                          [np.arange(1, 16) * 2.0 ** -10])   # subnormal codes and their midpoints
+    x = np.zeros((1, 1, 1, 128), np.float32)
+    flat = x.reshape(-1)
+    flat[: mids.size] = mids
+    flat[mids.size] = 448.0
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(xt.float().numpy().reshape(-1)[: mids.size], mids.astype(np.float32))  # exact in bf16
+    _check_quant(api, xt.cuda(), "ties")
+
+
+def test_quantize_strided_views_and_empty(api):
+    wl = WORKLOADS["var1024"]
+    q, k, _ = make_qkv(wl, 3, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    _check_quant(api, q[:, :, off[10]:off[11]], "q step view")
+    big = torch.zeros((2, 2, 40, 256), dtype=torch.bfloat16, device="cuda")
+    big[..., :128] = k[:, :2, :40]
+    _check_quant(api, big[..., :128], "wide rows")
+    codes, scale = api.var_quantize_e4m3(k[:, :, :0])
+    assert codes.numel() == 0 and bool(torch.all(scale.cpu() == float(np.float32(1 / 448))))
+
+
+def test_quantize_var1024_full_cache_sampled_maps(api):
+    """Full-size K cache (10521 tokens); the maps are independent, so a few are compared in full."""
+    wl = WORKLOADS["var1024"]
+    _, k, _ = make_qkv(wl, 5, device="cuda")
+    codes, scale = api.var_quantize_e4m3(k)
+    for b, h in [(0, 0), (0, 13), (1, 7), (1, 15)]:
+        ref_c, ref_s = quantize_maps(_np(k[b:b + 1, h]))
+        assert np.array_equal(codes[b, h].cpu().numpy(), ref_c[0])
+        assert scale[b, h].item() == ref_s[0]
+
+
+def _quantised(api, q, k):
+    """GPU codes for q and k (checked equal to the oracle's) and the oracle's dequantised fp64 values."""
+    q8, sq, rq, rsq = _check_quant(api, q, "q")
+    k8, sk, rk, rsk = _check_quant(api, k, "k")
+    B, H = q.shape[:2]
+    qd = dequantize(rq.reshape((B * H,) + q.shape[2:]), rsq.reshape(-1)).reshape(q.shape)
+    kd = dequantize(rk.reshape((B * H,) + k.shape[2:]), rsk.reshape(-1)).reshape(k.shape)
+    return q8, sq, k8, sk, qd, kd
+
+
+def _bars(got, ref, what, lse=None, ref_lse=None):
+    err = np.abs(got.astype(np.float64) - ref)
+    print(f"[{what}] max-abs {err.max():.3e} mean-abs {err.mean():.3e}", flush=True)
+    assert err.max() <= 1e-2 and err.mean() <= 1e-3
+    if lse is not None:
+        assert np.max(np.abs(lse - ref_lse)) <= 2.5e-3
+
+
+SMALL = (1, 2, 4, 6, 8, 12, 16, 20)
+
+
+@pytest.mark.parametrize("step", [0, 3, 5, 7])
+def test_dense_e4m3_steps_match_oracle(api, step):
+    wl = custom_workload(SMALL, 2, 2, 128, sink_offset_scales=3)
+    q, k, v = make_qkv(wl, 60 + step, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    qs = q[:, :, off[step]:off[step + 1]].contiguous()
+    kc = k[:, :, :off[step + 1]].contiguous()
+    q8, sq, k8, sk, qd, kd = _quantised(api, qs, kc)
+    o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, step, step + 1, return_lse=True)
+    ref, ref_lse = oracle.attention(qd, kd, _np(v), wl.h, wl.w, step, step + 1, return_lse=True)
+    _bars(_np(o), ref, f"e4m3 dense step {step}", _np(lse), ref_lse)
+
+
+def test_dense_e4m3_gather_splits_bf16_out(api):
+    wl = custom_workload(SMALL, 2, 2, 128)
+    q, k, v = make_qkv(wl, 70, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    s = 7
+    qs = q[:, :, off[s]:off[s + 1]]
+    q8, sq, k8, sk, qd, kd = _quantised(api, qs, k)
+    n = off[s + 1] - off[s]
+    sel = np.sort(np.random.default_rng(71).choice(n, 157, replace=False)).astype(np.int32)
+    idx = torch.from_numpy(sel).cuda()
+    ref, ref_lse = oracle.attention(qd, kd, _np(v), wl.h, wl.w, s, s + 1, q_index=sel, return_lse=True)
+    for splits in (1, 3):
+        ws = api.split_workspace(splits, 2, 2, sel.size, 128) if splits > 1 else None
+        for odt in (torch.float32, torch.bfloat16):
+            o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, s, s + 1, q_index=idx, out_dtype=odt,
+                                             return_lse=True, n_splits=splits, workspace=ws)
+            _bars(_np(o), ref, f"e4m3 gather splits={splits} {odt}", _np(lse), ref_lse)
+
+
+def test_dense_e4m3_multi_scale_call(api):
+    """Queries of several scales in one call: each row sees keys up to the end of its own scale."""
+    wl = custom_workload(SMALL, 1, 2, 128)
+    q, k, v = make_qkv(wl, 72, device="cuda")
+    q8, sq, k8, sk, qd, kd = _quantised(api, q, k)
+    o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, 0, len(SMALL), return_lse=True)
+    ref, ref_lse = oracle.attention(qd, kd, _np(v), wl.h, wl.w, 0, len(SMALL), return_lse=True)
+    _bars(_np(o), ref, "e4m3 all scales", _np(lse), ref_lse)
+
+
+def test_dense_e4m3_var1024_last_step_sampled(api):
+    wl = WORKLOADS["var1024"]
+    q, k, v = make_qkv(wl, 73, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    s = len(wl.grids) - 1
+    qs = q[:, :, off[s]:off[s + 1]]
+    q8, sq = api.var_quantize_e4m3(qs)
+    k8, sk = api.var_quantize_e4m3(k)
+    o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, s, s + 1, return_lse=True)
+    n = off[s + 1] - off[s]
+    rows = np.unique(np.concatenate([np.arange(0, n, 61), [n - 1]]))
+    for b, h in [(0, 3), (1, 12)]:
+        rq, rsq = quantize_maps(_np(qs[b:b + 1, h]))
+        rk, rsk = quantize_maps(_np(k[b:b + 1, h]))
+        assert np.array_equal(q8[b, h].cpu().numpy(), rq[0]) and np.array_equal(k8[b, h].cpu().numpy(), rk[0])
+        qd = dequantize(rq, rsq)[None]
+        kd = dequantize(rk, rsk)[None]
+        ref, ref_lse = oracle.attention(qd, kd, _np(v[b:b + 1, h:h + 1]), wl.h, wl.w, s, s + 1, rows=rows,
+                                        return_lse=True)
+        _bars(_np(o[b:b + 1, h:h + 1])[:, :, rows], ref, f"e4m3 1024 last step b{b} h{h}",
+              _np(lse[b:b + 1, h:h + 1])[:, :, rows], ref_lse)
+        # the quantisation itself, against the exact attention of the bf16 inputs (a coarse check:
+        # e4m3 keeps 3 mantissa bits, so logits move by a few hundredths)
+        exact = oracle.attention(_np(qs[b:b + 1, h:h + 1]), _np(k[b:b + 1, h:h + 1]), _np(v[b:b + 1, h:h + 1]),
+                                 wl.h, wl.w, s, s + 1, rows=rows)
+        qerr = np.abs(_np(o[b:b + 1, h:h + 1])[:, :, rows] - exact)
+        print(f"[e4m3 vs bf16 inputs b{b} h{h}] max-abs {qerr.max():.3e} mean-abs {qerr.mean():.3e}", flush=True)
+        assert qerr.mean() <= 1e-2
+
+
+def test_block_sparse_e4m3_shared_and_per_head(api):
+    wl = custom_workload(SMALL, 2, 2, 128)
+    q, k, v = make_qkv(wl, 74, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    s = 7
+    qs = q[:, :, off[s]:off[s + 1]]
+    q8, sq, k8, sk, qd, kd = _quantised(api, qs, k)
+    mp = api.mask_params(64, 64, 2, 3, 1, 1)
+    rp, ci = api.var_build_tile_mask((wl.h, wl.w), s, s + 1, mp)
+    kept = oracle.tile_mask(wl.h, wl.w, s, s + 1, 64, 64, 2, 3, 1, 1)
+    o, lse = api.var_attn_block_sparse_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, s, s + 1, rp, ci, return_lse=True)
+    ref, ref_lse = oracle.attention(qd, kd, _np(v), wl.h, wl.w, s, s + 1, kept=kept, return_lse=True)
+    _bars(_np(o), ref, "e4m3 sparse shared", _np(lse), ref_lse)
+    # one CSR per (batch, head): random kept tiles per map
+    n_qt, n_kt = -(-(off[s + 1] - off[s]) // 64), -(-off[s + 1] // 64)
+    rng = np.random.default_rng(75)
+    masks = rng.random((4, n_qt, n_kt)) < 0.5
+    rps = np.zeros((4, n_qt + 1), np.int32)
+    cis = np.zeros((4, n_qt * n_kt), np.int32)
+    for m in range(4):
+        cols = [np.nonzero(masks[m, r])[0] for r in range(n_qt)]
+        rps[m, 1:] = np.cumsum([c.size for c in cols])
+        flat = np.concatenate(cols) if rps[m, -1] else np.zeros(0, np.int32)
+        cis[m, : flat.size] = flat
+    o2, lse2 = api.var_attn_block_sparse_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, s, s + 1,
+                                              torch.from_numpy(rps).cuda(), torch.from_numpy(cis).cuda(),
+                                              return_lse=True)
+    vn = _np(v)
+    for m in range(4):
+        b, h = divmod(m, 2)
+        ref, ref_lse = oracle.attention(qd[b:b + 1, h:h + 1], kd[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], wl.h, wl.w,
+                                        s, s + 1, kept=masks[m], return_lse=True)
+        got_lse = _np(lse2[b:b + 1, h:h + 1])
+        finite = np.isfinite(ref_lse)
+        assert np.array_equal(np.isfinite(got_lse), finite)
+        _bars(_np(o2[b:b + 1, h:h + 1]), ref, f"e4m3 sparse per-head map {m}", got_lse[finite], ref_lse[finite])
+
+
+def test_e4m3_rejects_wrong_dtypes(api):
+    wl = custom_workload(SMALL, 1, 1, 128)
+    q, k, v = make_qkv(wl, 76, device="cuda")
+    q8, sq = api.var_quantize_e4m3(q)
+    with pytest.raises(ValueError):
+        api.var_attn_dense_e4m3((wl.h, wl.w), q, sq, q8, sq, v, 7, 8)
+    q64 = torch.zeros((1, 1, q.shape[2], 64), dtype=torch.uint8, device="cuda")
+    v64 = torch.zeros((1, 1, q.shape[2], 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(api.VarAttnError):
+        api.var_attn_dense_e4m3((wl.h, wl.w), q64, sq, q64, sq, v64, 7, 8)
