@@ -6,9 +6,10 @@ and low-bit quantisation keeps its quality.  The record names no format; the
 reading taken is 8-bit floating point e4m3 (the OCP "E4M3FN" layout: 1 sign
 bit, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, largest
 finite value 448, no infinities) for the attention's queries and keys, with
-one scale per (batch, head):
+one scale per group of values (quantize_maps: one group per leading index;
+quantize_tiles: one group per (batch, head, 64-token tile)):
 
-    amax  = max |x| over the map (0 -> 1)
+    amax  = max |x| over the group (0 -> 1)
     inv   = 448 / amax            (float32, correctly rounded)
     code  = e4m3(x * inv)         (the product in float32; round to nearest even)
     scale = amax / 448            (float32; dequantised value = e4m3 value * scale)
@@ -83,3 +84,30 @@ def dequantize(codes, scale):
     codes = np.asarray(codes)
     v = e4m3_decode(codes)
     return v * np.asarray(scale, dtype=np.float64).reshape((-1,) + (1,) * (codes.ndim - 1))
+
+
+def quantize_tiles(x, tile=64):
+    """x [B, H, T, D] -> (codes uint8 [B, H, T, D], scale float32 [B, H, ceil(T / tile)]).
+
+    Tokens [tile*j, tile*(j+1)) of each (batch, head) form group j (the last
+    one may be shorter); each group is quantised as quantize_maps does a map.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    B, H, T, D = x.shape
+    n = -(-T // tile)
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    scale = np.zeros((B, H, n), dtype=np.float32)
+    for j in range(n):
+        part = x[:, :, tile * j: tile * (j + 1)]
+        c, s = quantize_maps(part.reshape((B * H,) + part.shape[2:]))
+        codes[:, :, tile * j: tile * (j + 1)] = c.reshape(part.shape)
+        scale[:, :, j] = s.reshape(B, H)
+    return codes, scale
+
+
+def dequantize_tiles(codes, scale, tile=64):
+    """Dequantised float64 values of quantize_tiles output."""
+    v = e4m3_decode(codes)
+    T = codes.shape[2]
+    s = np.repeat(np.asarray(scale, dtype=np.float64), tile, axis=2)[:, :, :T]
+    return v * s[..., None]

@@ -4,14 +4,15 @@ The encoder is checked against torch's float8_e4m3fn cast (a library
 routine, round to nearest even) on random values, ties, subnormals and the
 largest codes; decoding inverts encoding on every finite code; the map
 scales reproduce amax / 448 and every map's largest magnitude quantises to
-448.
+448; tile groups are independent of each other and a whole-map call on a
+tile-sized tensor agrees with the tiled one.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from oracle.fp8 import E4M3_MAX, dequantize, e4m3_decode, e4m3_encode, quantize_maps
+from oracle.fp8 import E4M3_MAX, dequantize, dequantize_tiles, e4m3_decode, e4m3_encode, quantize_maps, quantize_tiles
 
 
 def _torch_codes(y):
@@ -61,3 +62,27 @@ def test_quantize_maps_scale_and_amax():
     deq = dequantize(codes, scale)
     rel = np.abs(deq[:4] - x[:4]) / np.maximum(np.abs(x[:4]), amax[:4, None, None] * 2.0 ** -9 / 448)
     assert rel.max() <= 2.0 ** -4 + 1e-6          # half a unit of 3 mantissa bits (or of the subnormal step)
+
+
+def test_quantize_tiles_groups_are_independent():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((2, 3, 150, 16)).astype(np.float32)   # tiles of 64, 64 and a ragged 22
+    x[1, 2, 70] = 500.0                                             # a spike only moves tile 1 of map (1, 2)
+    codes, scale = quantize_tiles(x)
+    assert codes.shape == x.shape and scale.shape == (2, 3, 3)
+    for b, h, j in [(0, 0, 0), (1, 2, 1), (1, 2, 2), (0, 1, 2)]:
+        part = x[b, h, 64 * j: 64 * (j + 1)]
+        assert scale[b, h, j] == np.float32(np.abs(part).max() / np.float32(448))
+        c, s = quantize_maps(part[None])
+        assert np.array_equal(codes[b, h, 64 * j: 64 * (j + 1)], c[0]) and s[0] == scale[b, h, j]
+    y = x.copy()
+    y[1, 2, 70] = 0.0
+    c2, s2 = quantize_tiles(y)
+    assert np.array_equal(c2[:, :, :64], codes[:, :, :64]) and np.array_equal(c2[:, :, 128:], codes[:, :, 128:])
+    assert s2[1, 2, 1] < scale[1, 2, 1]
+    # rounding error: half a unit of the 3 mantissa bits for normal codes, half the
+    # subnormal step 2^-9 * scale below 2^-6 * scale
+    deq = dequantize_tiles(codes, scale)
+    sc = np.repeat(scale, 64, axis=2)[:, :, :150, None].astype(np.float64)
+    assert np.all(np.abs(deq - x) <= np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * sc) * (1 + 1e-6))
+    assert np.count_nonzero(np.abs(x[1, 2, 64:128]) < 2.0 ** -6 * sc[1, 2, 64:128]) > 0   # subnormals are exercised
