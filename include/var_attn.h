@@ -327,33 +327,39 @@ var_status var_attn_block_sparse_heads(const var_schedule* sched, const var_attn
  * Low-bit (FP8) attention ("LiteVAR: Compressing Visual Autoregressive
  * Modelling with Efficient Attention and Quantization", abstract: the data
  * precision of a VAR model is redundant and low-bit quantisation keeps its
- * quality).  The record names no format and no operand; these calls take
- * queries and keys as OCP e4m3 codes (1 sign, 4 exponent bits with bias 7,
- * 3 mantissa bits, subnormals, largest finite 448, no infinities; 0x7F and
- * 0xFF are NaN) with one fp32 scale per (batch, head), value = e4m3 value *
- * scale.  The attention weights and v stay bf16.
+ * quality).  The record names no format, operand or granularity; these calls
+ * take queries and keys as OCP e4m3 codes (1 sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits, subnormals, largest finite 448, no infinities; 0x7F and
+ * 0xFF are NaN) with one fp32 scale per (batch, head, 64-token tile), value =
+ * e4m3 value * scale.  The attention weights and v stay bf16.
  *
- * var_quantize_e4m3: for each map m = b*heads + h of x (bf16
- * [batch][heads][tokens][head_dim], layout x_l, finite values):
- *   amax = max |x| over the map (1 if all zero), inv = 448 / amax (fp32,
+ * var_quantize_e4m3: x is bf16 [batch][heads][tokens][head_dim] (layout x_l,
+ * finite values).  Tile j of map m = b*heads + h holds tokens
+ * [64j, min(64j + 64, tokens)); for every tile with 64(j+1) > first_token:
+ *   amax = max |x| over the tile (1 if all zero), inv = 448 / amax (fp32,
  *   correctly rounded), code = e4m3(x * inv) (fp32 product, round to nearest
- *   even, magnitudes above 448 -> 448), scale[m] = amax / 448 (fp32).
+ *   even, magnitudes above 448 -> 448), scale[m*scale_stride + j] = amax / 448.
+ * Tiles before first_token / 64 are left untouched (codes and scales), so a
+ * growing key cache requantises only the tiles its new tokens reach.
  *  codes  device uint8, same shape, layout c_l (strides in bytes, multiples
  *         of 16), written.
- *  scale  device fp32 [batch*heads], written (it also holds the maps' maxima
- *         while the call runs).
- *  head_dim a multiple of 16 in [16, 1024]; batch*heads <= 65535; tokens may
- *  be 0 (x and codes may then be NULL; every scale becomes 1/448).
+ *  scale  device fp32 [batch*heads][scale_stride], scale_stride >=
+ *         ceil(tokens/64), written.
+ *  0 <= first_token <= tokens (= tokens: nothing to do; pointers may then be
+ *  NULL); head_dim a multiple of 16 in [16, 256]; batch*heads <= 65535.
  *
- * var_attn_dense_e4m3: var_attn_dense_split with q and k as e4m3 codes:
- * the logits are softmax_scale * q_scale[m] * k_scale[m] * (q_codes .
- * k_codes) with m = b*heads + h, i.e. attention of the dequantised q and k,
- * the products of codes summed exactly in fp32 by the matrix cores.
+ * var_attn_dense_e4m3: var_attn_dense_split with q and k as e4m3 codes: the
+ * logit of query row pos (of q) and key u is
+ *   softmax_scale * q_scale[m][pos / 64] * k_scale[m][u / 64] * (q_codes . k_codes)
+ * with m = b*heads + h, i.e. attention of the dequantised q and k; the
+ * products of codes are summed exactly in fp32 by the matrix cores.
  *  desc   in_dtype must be VAR_BF16 (the dtype of v); head_dim 128;
  *         out_dtype f32 or bf16.
  *  q, k   device uint8 codes with the shapes of var_attn_dense and layouts
  *         q_l, k_l (strides in bytes, multiples of 16).
- *  q_scale, k_scale  device fp32 [batch*heads] (e.g. from var_quantize_e4m3).
+ *  q_scale device fp32 [B*H][q_scale_stride], q_scale_stride >= ceil(n_q/64);
+ *  k_scale device fp32 [B*H][k_scale_stride], k_scale_stride >= ceil(kv_len/64)
+ *         (e.g. from var_quantize_e4m3 of q and of the key cache); positive.
  *  Other arguments as in var_attn_dense_split.
  * var_attn_block_sparse_e4m3: the block-sparse call (64x64 tiles) with e4m3
  * q and k; col_stride 0 takes one CSR shared by every (batch, head) (as
@@ -361,20 +367,22 @@ var_status var_attn_block_sparse_heads(const var_schedule* sched, const var_attn
  * var_attn_block_sparse_heads.
  * Errors: VAR_ERR_UNSUPPORTED for another head_dim or in_dtype, VAR_ERR_NULL
  * for a missing scale array, VAR_ERR_STRIDE for code strides that are not
- * multiples of 16 bytes; otherwise as the bf16 calls.
+ * multiples of 16 bytes or scale strides below the tile counts; otherwise as
+ * the bf16 calls.
  */
 var_status var_quantize_e4m3(int32_t batch, int32_t heads, int32_t tokens, int32_t head_dim,
-                             const void* x, var_layout x_l, uint8_t* codes, var_layout c_l, float* scale,
-                             void* stream);
+                             const void* x, var_layout x_l, uint8_t* codes, var_layout c_l,
+                             float* scale, int64_t scale_stride, int32_t first_token, void* stream);
 var_status var_attn_dense_e4m3(const var_schedule* sched, const var_attn_desc* desc,
-                               const uint8_t* q, var_layout q_l, const float* q_scale,
-                               const uint8_t* k, var_layout k_l, const float* k_scale,
+                               const uint8_t* q, var_layout q_l, const float* q_scale, int64_t q_scale_stride,
+                               const uint8_t* k, var_layout k_l, const float* k_scale, int64_t k_scale_stride,
                                const void* v, var_layout v_l, void* o, var_layout o_l,
                                float* lse, const int32_t* q_index, int32_t n_sel,
                                int32_t n_splits, void* workspace, int64_t workspace_bytes, void* stream);
 var_status var_attn_block_sparse_e4m3(const var_schedule* sched, const var_attn_desc* desc,
                                       const uint8_t* q, var_layout q_l, const float* q_scale,
-                                      const uint8_t* k, var_layout k_l, const float* k_scale,
+                                      int64_t q_scale_stride, const uint8_t* k, var_layout k_l,
+                                      const float* k_scale, int64_t k_scale_stride,
                                       const void* v, var_layout v_l, void* o, var_layout o_l,
                                       float* lse, const int32_t* q_index, int32_t n_sel,
                                       const int32_t* row_ptr, const int32_t* col_idx,

@@ -93,11 +93,11 @@ def _load():
     lib.var_mapped_tile_mask.argtypes = [SP, i32, i32, i32, P, P, P, i64, P]
     lib.var_attn_block_sparse_heads.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, Layout, P,
                                                 Layout, P, P, i32, P, P, i64, P]
-    lib.var_quantize_e4m3.argtypes = [i32, i32, i32, i32, P, Layout, P, Layout, P, P]
-    lib.var_attn_dense_e4m3.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, P, Layout, P, P, Layout, P,
-                                        Layout, P, P, i32, i32, P, i64, P]
-    lib.var_attn_block_sparse_e4m3.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, P, Layout, P, P, Layout,
-                                               P, Layout, P, P, i32, P, P, i64, P]
+    lib.var_quantize_e4m3.argtypes = [i32, i32, i32, i32, P, Layout, P, Layout, P, i64, i32, P]
+    lib.var_attn_dense_e4m3.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, i64, P, Layout, P, i64, P,
+                                        Layout, P, Layout, P, P, i32, i32, P, i64, P]
+    lib.var_attn_block_sparse_e4m3.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, i64, P, Layout, P, i64,
+                                               P, Layout, P, Layout, P, P, i32, P, P, i64, P]
     for name in EXPORTED[:-2]:
         getattr(lib, name).restype = ctypes.c_int
     lib.var_status_string.argtypes = [ctypes.c_int]
@@ -497,33 +497,42 @@ def var_attn_block_sparse_heads(schedule, q, k, v, q_scale_begin, q_scale_end, r
     return (out, lse) if return_lse else out
 
 
-def var_quantize_e4m3(x, codes=None, scale=None):
-    """x bf16 [B, H, T, D] -> (codes uint8 [B, H, T, D], scale fp32 [B, H]); value = e4m3(code) * scale."""
+def var_quantize_e4m3(x, codes=None, scale=None, first_token=0):
+    """x bf16 [B, H, T, D] -> (codes uint8 [B, H, T, D], scale fp32 [B, H, ceil(T/64)]).
+
+    value = e4m3(code) * scale of its 64-token tile.  With first_token > 0 only
+    the tiles from first_token // 64 on are (re)written into the given
+    codes / scale (the others keep their contents).
+    """
     if x.dim() != 4 or not x.is_cuda or x.dtype != torch.bfloat16:
         raise ValueError("x must be a 4-D bf16 device tensor [batch, head, token, dim]")
     B, H, T, D = x.shape
+    n_t = -(-T // 64)
     if codes is None:
         codes = torch.empty((B, H, T, D), dtype=torch.uint8, device=x.device)
     elif tuple(codes.shape) != (B, H, T, D) or codes.dtype != torch.uint8 or codes.device != x.device:
         raise ValueError(f"codes must be uint8 {(B, H, T, D)} on x's device")
     if scale is None:
-        scale = torch.empty((B, H), dtype=torch.float32, device=x.device)
-    elif scale.numel() != B * H or scale.dtype != torch.float32 or not scale.is_contiguous() or scale.device != x.device:
-        raise ValueError("scale must be a contiguous fp32 tensor of B*H elements on x's device")
-    _check(LIB.var_quantize_e4m3(B, H, T, D, _ptr(x), _layout(x), _ptr(codes), _layout(codes), _ptr(scale),
-                                 _stream(x.device)))
+        scale = torch.empty((B, H, n_t), dtype=torch.float32, device=x.device)
+    elif (scale.dim() != 3 or tuple(scale.shape[:2]) != (B, H) or scale.shape[2] < n_t or scale.dtype != torch.float32
+          or not scale.is_contiguous() or scale.device != x.device):
+        raise ValueError(f"scale must be a contiguous fp32 tensor [B, H, >= {n_t}] on x's device")
+    if T > first_token:
+        _check(LIB.var_quantize_e4m3(B, H, T, D, _ptr(x), _layout(x), _ptr(codes), _layout(codes), _ptr(scale),
+                                     scale.shape[2], int(first_token), _stream(x.device)))
     return codes, scale
 
 
 def _scale_arg(t, B, H, dev, name):
-    if t.numel() != B * H or t.dtype != torch.float32 or not t.is_contiguous() or t.device != dev:
-        raise ValueError(f"{name} must be a contiguous fp32 tensor of B*H elements on q's device")
-    return _ptr(t)
+    if (t.dim() != 3 or tuple(t.shape[:2]) != (B, H) or t.dtype != torch.float32 or not t.is_contiguous()
+            or t.device != dev):
+        raise ValueError(f"{name} must be a contiguous fp32 tensor [B, H, tiles] on q's device")
+    return _ptr(t), t.shape[2]
 
 
 def var_attn_dense_e4m3(schedule, q, q_scale, k, k_scale, v, q_scale_begin, q_scale_end, out=None, out_dtype=None,
                         softmax_scale=0.0, q_index=None, return_lse=False, n_splits=1, workspace=None):
-    """var_attn_dense with q and k as e4m3 codes (uint8) and fp32 scales [B, H] (see var_quantize_e4m3)."""
+    """var_attn_dense with q and k as e4m3 codes (uint8) and fp32 tile scales [B, H, tiles] (var_quantize_e4m3)."""
     s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
                                            softmax_scale, q_index, return_lse, qk_codes=True)
     n_sel = rows if q_index is not None else 0
@@ -532,8 +541,8 @@ def var_attn_dense_e4m3(schedule, q, q_scale, k, k_scale, v, q_scale_begin, q_sc
     B, H = q.shape[0], q.shape[1]
     wp, wb = _ws_args(n_splits, workspace)
     _check(LIB.var_attn_dense_e4m3(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q),
-                                   _scale_arg(q_scale, B, H, q.device, "q_scale"), _ptr(k), _layout(k),
-                                   _scale_arg(k_scale, B, H, q.device, "k_scale"), _ptr(v), _layout(v), _ptr(out),
+                                   *_scale_arg(q_scale, B, H, q.device, "q_scale"), _ptr(k), _layout(k),
+                                   *_scale_arg(k_scale, B, H, q.device, "k_scale"), _ptr(v), _layout(v), _ptr(out),
                                    _layout(out), _ptr(lse), _ptr(q_index), n_sel, int(n_splits), wp, wb,
                                    _stream(q.device)))
     return (out, lse) if return_lse else out
@@ -562,8 +571,8 @@ def var_attn_block_sparse_e4m3(schedule, q, q_scale, k, k_scale, v, q_scale_begi
             raise ValueError("per-head CSR: row_ptr int32 [B*H, n_qt+1], col_idx int32 [B*H, stride]")
         stride = col_idx.shape[1]
     _check(LIB.var_attn_block_sparse_e4m3(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q),
-                                          _scale_arg(q_scale, B, H, q.device, "q_scale"), _ptr(k), _layout(k),
-                                          _scale_arg(k_scale, B, H, q.device, "k_scale"), _ptr(v), _layout(v),
+                                          *_scale_arg(q_scale, B, H, q.device, "q_scale"), _ptr(k), _layout(k),
+                                          *_scale_arg(k_scale, B, H, q.device, "k_scale"), _ptr(v), _layout(v),
                                           _ptr(out), _layout(out), _ptr(lse), _ptr(q_index), n_sel, _ptr(row_ptr),
                                           _ptr(col_idx), stride, _stream(q.device)))
     return (out, lse) if return_lse else out

@@ -223,10 +223,13 @@ struct WeightSlots {
     }
 };
 
-// One entry of the key-tile walk: tile index (-1 = end) and the waves that use it.
+// One entry of the key-tile walk: tile index (-1 = end), the waves that use
+// it and (e4m3 keys) the tile's dequantisation scale, loaded when the entry
+// is made, a few tiles before it is used.
 struct TileEnt {
     int tile;
     int mask;
+    float ks;
 };
 
 // QK8: q and k are e4m3 codes with one scale per (batch, head) and S^T comes
@@ -278,6 +281,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     // ---- this lane's two query rows ------------------------------------
     int my_row[2], klim[2];
     bool row_valid[2];
+    float c2q[2];   // log2-domain logit scale of each of the lane's two queries
     qop qreg[2][SK];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -294,6 +298,9 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                 if (s < p.num_scales && tok < p.scale_end[s]) kl = p.scale_end[s];
         }
         klim[qb] = kl;
+        // scale * log2(e), times the query's tile scale for e4m3 codes
+        c2q[qb] = p.scale_log2;
+        if constexpr (QK8) c2q[qb] *= p.q_scale[bh * p.q_scale_stride + (pos >> 6)];
         const unsigned char* qp = reinterpret_cast<const unsigned char*>(p.q) +
                                   (b * p.q_sb + h * p.q_sh + (int64_t)pos * p.q_st) * EK;
 #pragma unroll
@@ -383,6 +390,10 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
             e.tile = dense_next < dense_end ? dense_next : -1;
             e.mask = (1 << NW) - 1;
             ++dense_next;
+        }
+        e.ks = 1.f;
+        if constexpr (QK8) {
+            if (e.tile >= 0) e.ks = p.k_scale[bh * p.k_scale_stride + e.tile];
         }
         return e;
     };
@@ -562,18 +573,18 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     f32x16 oacc[MO][2];
 #pragma unroll
     for (int i = 0; i < MO; ++i) oacc[i][0] = oacc[i][1] = f32x16{};
-    float mref[2] = {-INFINITY, -INFINITY};   // reference max per query (raw logit units)
-    float nb[2] = {0.f, 0.f};                 // -mref * scale * log2(e)
+    // reference max per query, in the log2 domain (logit * log2(e)): the
+    // logits of key tiles with different scales compare only after scaling
+    float mref[2] = {-INFINITY, -INFINITY};
+    float nb[2] = {0.f, 0.f};                 // -mref
     float lsum[2] = {0.f, 0.f};               // this lane's partial row sums
     bool need_ref = true;                     // some row of the wave has no reference yet
-    // logits are scale * (raw dot product), times q_scale * k_scale of the
-    // (batch, head) for e4m3 codes
-    float c2 = p.scale_log2, lse_scale = p.scale;
-    if constexpr (QK8) {
-        const float sqk = p.q_scale[bh] * p.k_scale[bh];
-        c2 *= sqk;
-        lse_scale *= sqk;
-    }
+    // log2-domain scale of the raw dot products of key tile e: scale *
+    // log2(e), times the query's and the key tile's scales for e4m3 codes
+    auto tile_c2 = [&](const TileEnt& e, float (&c2t)[2]) __attribute__((always_inline)) {
+        c2t[0] = QK8 ? c2q[0] * e.ks : c2q[0];
+        c2t[1] = QK8 ? c2q[1] * e.ks : c2q[1];
+    };
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     // keys at or past `lim` are hidden (-inf) in one 32-key half starting at kb0
@@ -602,32 +613,33 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         }
     };
     // rows without a reference yet take this half's max as their reference
-    auto set_reference = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) {
+    auto set_reference = [&](const f32x16 (&s)[2], const float (&c2t)[2]) __attribute__((always_inline)) {
         float mt[2];
         half_max(s, mt);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            mref[qb] = (mref[qb] == -INFINITY) ? mt[qb] : mref[qb];
-            nb[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c2;
+            mref[qb] = (mref[qb] == -INFINITY) ? mt[qb] * c2t[qb] : mref[qb];
+            nb[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb];
         }
         need_ref = __builtin_amdgcn_ballot_w64(mref[0] == -INFINITY || mref[1] == -INFINITY) != 0;
     };
     // weights of one key pair (pair i of 16-key chunk c of a half, MFMA k
     // order) of query block qb, packed to bf16; the pair adds to the row sum
-    auto exp_pair = [&](const f32x16 (&s)[2], int c, int qb, int i, u32x4 (&w)[2]) __attribute__((always_inline)) {
+    auto exp_pair = [&](const f32x16 (&s)[2], int c, int qb, int i, u32x4 (&w)[2], const float (&c2t)[2])
+                        __attribute__((always_inline)) {
         const int r = 8 * c + 2 * i;
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c2, nb[qb]));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r + 1], c2, nb[qb]));
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c2t[qb], nb[qb]));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r + 1], c2t[qb], nb[qb]));
         const uint32_t pr = f32x2_to_bf16x2(e0, e1);
         w[qb][i] = pr;
         lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr), ones, lsum[qb], false);
     };
     // weights of 16-key chunk c (0 or 1) of a half: 4 bf16 pairs per query block
-    auto exp_chunk = [&](const f32x16 (&s)[2], int c, u32x4 (&w)[2]) __attribute__((always_inline)) {
+    auto exp_chunk = [&](const f32x16 (&s)[2], int c, u32x4 (&w)[2], const float (&c2t)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) exp_pair(s, c, qb, i, w);
+            for (int i = 0; i < 4; ++i) exp_pair(s, c, qb, i, w, c2t);
     };
     // O^T += V^T P^T for the 16-key chunk ks (0..3) of the tile
     // V^T operands of the 16-key chunk ks (all d blocks), then its MFMAs
@@ -671,7 +683,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         // iteration tiles j .. j+AHEAD-1 are in LDS
         TileEnt e0 = next_tile();
         TileEnt e1 = next_tile();
-        TileEnt e2 = AHEAD == 2 ? next_tile() : TileEnt{-1, 0};
+        TileEnt e2 = AHEAD == 2 ? next_tile() : TileEnt{-1, 0, 1.f};
         if (e0.tile >= 0) {
             load_k(e0.tile * KT, 0);
             if constexpr (MODE == 0) {
@@ -717,6 +729,8 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
             }
             const int kb = e.tile * KT;
             f32x16 s0[2], s1[2];
+            float c2t[2];
+            tile_c2(e, c2t);
             if constexpr (MODE == 0 && FAST) {
                 // Software-ordered body: slot m issues MFMA m and a fixed share of
                 // independent work, and a scheduling fence closes the slot, so the
@@ -807,11 +821,11 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                         }
                         if constexpr (at == m) {
                             if constexpr (h == 0) {
-                                xs[i][0] = __builtin_fmaf(s0[qb][r], c2, nbt[qb]);
-                                xs[i][1] = __builtin_fmaf(s0[qb][r + 1], c2, nbt[qb]);
+                                xs[i][0] = __builtin_fmaf(s0[qb][r], c2t[qb], nbt[qb]);
+                                xs[i][1] = __builtin_fmaf(s0[qb][r + 1], c2t[qb], nbt[qb]);
                             } else {
-                                xs[i][0] = __builtin_fmaf(s1[qb][r], c2, nbt[qb]);
-                                xs[i][1] = __builtin_fmaf(s1[qb][r + 1], c2, nbt[qb]);
+                                xs[i][0] = __builtin_fmaf(s1[qb][r], c2t[qb], nbt[qb]);
+                                xs[i][1] = __builtin_fmaf(s1[qb][r + 1], c2t[qb], nbt[qb]);
                             }
                         }
                     });
@@ -826,14 +840,14 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                     u32x4 w00[2], w01[2], w10[2], w11[2];
                     qk_half(slot, 0, s0);
                     if (need_mask) apply_mask(s0, kb, lim);
-                    if (need_ref) set_reference(s0);
+                    if (need_ref) set_reference(s0, c2t);
                     qk_half(slot, 1, s1);
                     if (need_mask) apply_mask(s1, kb + 32, lim);
-                    if (need_ref) set_reference(s1);
-                    exp_chunk(s0, 0, w00);
-                    exp_chunk(s0, 1, w01);
-                    exp_chunk(s1, 0, w10);
-                    exp_chunk(s1, 1, w11);
+                    if (need_ref) set_reference(s1, c2t);
+                    exp_chunk(s0, 0, w00, c2t);
+                    exp_chunk(s0, 1, w01, c2t);
+                    exp_chunk(s1, 0, w10, c2t);
+                    exp_chunk(s1, 1, w11, c2t);
                     pv_chunk(slot, 0, w00);
                     pv_chunk(slot, 1, w01);
                     pv_chunk(slot, 2, w10);
@@ -843,13 +857,13 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                     qk_half(slot, 0, s0);
                     if (need_mask) apply_mask(s0, kb, lim);
                     half_max(s0, mt);
-                    mref[0] = __builtin_fmaxf(mref[0], mt[0]);
-                    mref[1] = __builtin_fmaxf(mref[1], mt[1]);
+                    mref[0] = __builtin_fmaxf(mref[0], mt[0] * c2t[0]);
+                    mref[1] = __builtin_fmaxf(mref[1], mt[1] * c2t[1]);
                     qk_half(slot, 1, s1);
                     if (need_mask) apply_mask(s1, kb + 32, lim);
                     half_max(s1, mt);
-                    mref[0] = __builtin_fmaxf(mref[0], mt[0]);
-                    mref[1] = __builtin_fmaxf(mref[1], mt[1]);
+                    mref[0] = __builtin_fmaxf(mref[0], mt[0] * c2t[0]);
+                    mref[1] = __builtin_fmaxf(mref[1], mt[1] * c2t[1]);
                 }
             }
             if constexpr (MODE == 0 && !FAST) {
@@ -929,7 +943,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
             walk(IntC<1>{});
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
-                nb[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb] * c2;
+                nb[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb];
                 lsum[qb] = 0.f;
 #pragma unroll
                 for (int i = 0; i < MO; ++i) oacc[i][qb] = f32x16{};
@@ -975,7 +989,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
             }
         }
         if (g == 0) {
-            const float l = ltot > 0.f ? mref[qb] * lse_scale + __logf(ltot) : -INFINITY;
+            const float l = ltot > 0.f ? mref[qb] * 0.69314718055994531f + __logf(ltot) : -INFINITY;
             if (partial) p.part_lse[part_row0 + my_row[qb]] = l;
             else if (p.lse) p.lse[(int64_t)(b * p.H + h) * p.n_rows + my_row[qb]] = l;
         }

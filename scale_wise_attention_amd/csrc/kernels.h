@@ -44,9 +44,12 @@ struct AttnParams {
     // per-(batch, head) CSR (block-sparse): element strides between the maps'
     // row_ptr / col_idx arrays (0: one CSR shared by every (batch, head))
     int64_t rp_bh_stride, ci_bh_stride;
-    // e4m3 q / k (launch_attn_fp8 only): dequantisation scales [B*H]
+    // e4m3 q / k (launch_attn_fp8 only): dequantisation scales of 64-token
+    // tiles, q_scale[bh * q_scale_stride + pos / 64] for the query at call
+    // position pos, k_scale[bh * k_scale_stride + key / 64]
     const float* q_scale;
     const float* k_scale;
+    int64_t q_scale_stride, k_scale_stride;
 };
 
 // Largest key-split count of a launch.
@@ -86,16 +89,16 @@ hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, bool out_bf16, bo
 // The same attention with q and k as e4m3 codes (q_scale, k_scale set); v bf16.
 hipError_t launch_attn_fp8(const AttnParams& p, int head_dim, bool out_bf16, bool sparse, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int head_dim, bool sparse, hipStream_t s);
-// e4m3 quantisation with one scale per (batch, head) map; the scale array
-// holds the maps' largest magnitudes (float bits) while the launches run.
+// e4m3 quantisation with one scale per (batch, head, 64-token tile).
 struct QuantParams {
     const void* x;            // bf16 [B][H][tokens][D] (element strides)
     uint8_t* codes;           // e4m3 codes, same shape (element = byte strides)
-    float* scale;             // [B*H] dequantisation scales, written
-    uint32_t* amax_bits;      // the same memory as scale
+    float* scale;             // [B*H][scale_stride] dequantisation scales of the tiles
+    int64_t scale_stride;
     int64_t x_sb, x_sh, x_st;
     int64_t c_sb, c_sh, c_st;
     int32_t H, maps, tokens, D;
+    int32_t tile_first;       // first tile written (tiles tile_first .. ceil(tokens / 64) - 1)
 };
 hipError_t launch_quant_e4m3(const QuantParams& p, hipStream_t s);
 

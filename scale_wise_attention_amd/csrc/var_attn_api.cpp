@@ -242,37 +242,54 @@ VAR_EXPORT var_status var_schedule_extent(const var_schedule* sched, int32_t b, 
 
 namespace {
 
+// Tile scales of e4m3 q and k: q_scale[m][q_stride] covers the call's
+// ceil(n_q / 64) query tiles, k_scale[m][k_stride] its ceil(kv_len / 64) key tiles.
+struct E4m3Scales {
+    const float* q;
+    int64_t q_stride;
+    const float* k;
+    int64_t k_stride;
+};
+
 // Extra checks of a call whose q and k are e4m3 codes (v bf16): head_dim 128,
-// 16-byte strides of the code tensors, both scale arrays present.
-var_status check_e4m3(const var_attn_desc* desc, var_layout q_l, var_layout k_l, const float* q_scale,
-                      const float* k_scale) {
+// 16-byte strides of the code tensors, both scale arrays present and long
+// enough.  p is the filled parameter block (n_q, kv_len known).
+var_status check_e4m3(const var_attn_desc* desc, var_layout q_l, var_layout k_l, const E4m3Scales& sc,
+                      const varattn::AttnParams& p) {
     if (desc->in_dtype != VAR_BF16 || desc->head_dim != 128)
         return fail(VAR_ERR_UNSUPPORTED, "e4m3 q/k need bf16 v (in_dtype) and head_dim 128");
-    if (!q_scale || !k_scale) return fail(VAR_ERR_NULL, "q_scale and k_scale must be non-NULL");
-    if ((reinterpret_cast<uintptr_t>(q_scale) & 3u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u))
+    if (!sc.q || !sc.k) return fail(VAR_ERR_NULL, "q_scale and k_scale must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(sc.q) & 3u) || (reinterpret_cast<uintptr_t>(sc.k) & 3u))
         return fail(VAR_ERR_STRIDE, "q_scale and k_scale must be 4-byte aligned");
+    if (sc.q_stride < (p.n_q + 63) / 64 || sc.k_stride < (p.kv_len + 63) / 64)
+        return fail(VAR_ERR_STRIDE, "scale strides (%lld, %lld) below the tiles of the call (%d, %d)",
+                    (long long)sc.q_stride, (long long)sc.k_stride, (p.n_q + 63) / 64, (p.kv_len + 63) / 64);
     var_status st = check_layout("q", q_l, desc->head_dim, 1);
     if (st != VAR_OK) return st;
     return check_layout("k", k_l, desc->head_dim, 1);
 }
 
+void attach_e4m3(varattn::AttnParams* p, const E4m3Scales& sc) {
+    p->q_scale = sc.q;
+    p->k_scale = sc.k;
+    p->q_scale_stride = sc.q_stride;
+    p->k_scale_stride = sc.k_stride;
+}
+
 var_status dense_impl(const var_schedule* sched, const var_attn_desc* desc, const void* q, var_layout q_l,
                       const void* k, var_layout k_l, const void* v, var_layout v_l, void* o, var_layout o_l,
                       float* lse, const int32_t* q_index, int32_t n_sel, int32_t splits, void* ws,
-                      int64_t ws_bytes, void* stream, const float* q_scale = nullptr,
-                      const float* k_scale = nullptr) {
+                      int64_t ws_bytes, void* stream, const E4m3Scales* e4m3 = nullptr) {
     varattn::AttnParams p;
     bool none = false;
     var_status st = prepare_attn(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, &p, &none);
     if (st != VAR_OK) return st;
-    const bool e4m3 = q_scale || k_scale;
-    if (e4m3 && (st = check_e4m3(desc, q_l, k_l, q_scale, k_scale)) != VAR_OK) return st;
+    if (e4m3 && !none && (st = check_e4m3(desc, q_l, k_l, *e4m3, p)) != VAR_OK) return st;
     if ((st = attach_splits(&p, desc, none ? 1 : splits, ws, ws_bytes)) != VAR_OK) return st;
     if (none) return ok();
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (e4m3) {
-        p.q_scale = q_scale;
-        p.k_scale = k_scale;
+        attach_e4m3(&p, *e4m3);
         const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false);
         p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
         if ((int64_t)p.n_qtiles * p.B * p.H * p.n_splits >= ((int64_t)1 << 31))
@@ -296,8 +313,8 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
                        const void* k, var_layout k_l, const void* v, var_layout v_l, void* o, var_layout o_l,
                        float* lse, const int32_t* q_index, int32_t n_sel, const int32_t* row_ptr,
                        const int32_t* col_idx, int32_t tile_q, int32_t tile_k, int32_t splits, void* ws,
-                       int64_t ws_bytes, void* stream, int64_t col_bh_stride = -1, const float* q_scale = nullptr,
-                       const float* k_scale = nullptr) {
+                       int64_t ws_bytes, void* stream, int64_t col_bh_stride = -1,
+                       const E4m3Scales* e4m3 = nullptr) {
     if (tile_q != 64 || tile_k != 64)
         return fail(VAR_ERR_UNSUPPORTED, "block-sparse attention supports 64x64 tiles, got %dx%d", tile_q, tile_k);
     if (!row_ptr || !col_idx) return fail(VAR_ERR_NULL, "row_ptr and col_idx must be non-NULL");
@@ -305,14 +322,13 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
     bool none = false;
     var_status st = prepare_attn(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, &p, &none);
     if (st != VAR_OK) return st;
-    const bool e4m3 = q_scale || k_scale;
-    if (e4m3 && (st = check_e4m3(desc, q_l, k_l, q_scale, k_scale)) != VAR_OK) return st;
+    if (e4m3 && !none && (st = check_e4m3(desc, q_l, k_l, *e4m3, p)) != VAR_OK) return st;
     if ((st = attach_splits(&p, desc, none ? 1 : splits, ws, ws_bytes)) != VAR_OK) return st;
     if (none) return ok();
     p.row_ptr = row_ptr;
     p.col_idx = col_idx;
     if (col_bh_stride >= 0) {   // one CSR per (batch, head)
-        if (desc->in_dtype != VAR_BF16) return fail(VAR_ERR_UNSUPPORTED, "per-head CSR needs bf16 input");
+        if (desc->in_dtype != VAR_BF16) return fail(VAR_ERR_UNSUPPORTED, "per-head CSR needs bf16 v");
         const int64_t n_qt = (p.n_rows + 63) / 64;
         const int64_t n_kt = (p.kv_len + 63) / 64;
         if (col_bh_stride < n_qt * n_kt)
@@ -329,8 +345,7 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
         if ((int64_t)p.n_qtiles * p.B * p.H * p.n_splits >= ((int64_t)1 << 31))
             return fail(VAR_ERR_RANGE, "launch grid too large");
         if (e4m3) {
-            p.q_scale = q_scale;
-            p.k_scale = k_scale;
+            attach_e4m3(&p, *e4m3);
             return hip_status(varattn::launch_attn_fp8(p, desc->head_dim, desc->out_dtype == VAR_BF16, true, s),
                               "var_attn_block_sparse_e4m3 launch");
         }
@@ -372,42 +387,47 @@ VAR_EXPORT var_status var_attn_block_sparse_heads(const var_schedule* sched, con
 }
 
 VAR_EXPORT var_status var_attn_dense_e4m3(const var_schedule* sched, const var_attn_desc* desc, const uint8_t* q,
-                                          var_layout q_l, const float* q_scale, const uint8_t* k, var_layout k_l,
-                                          const float* k_scale, const void* v, var_layout v_l, void* o,
+                                          var_layout q_l, const float* q_scale, int64_t q_scale_stride,
+                                          const uint8_t* k, var_layout k_l, const float* k_scale,
+                                          int64_t k_scale_stride, const void* v, var_layout v_l, void* o,
                                           var_layout o_l, float* lse, const int32_t* q_index, int32_t n_sel,
                                           int32_t n_splits, void* workspace, int64_t workspace_bytes,
                                           void* stream) {
-    if (!desc) return fail(VAR_ERR_NULL, "desc is NULL");
-    if (!q_scale || !k_scale) return fail(VAR_ERR_NULL, "q_scale and k_scale must be non-NULL");
+    const E4m3Scales sc{q_scale, q_scale_stride, k_scale, k_scale_stride};
     return dense_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, n_splits, workspace,
-                      workspace_bytes, stream, q_scale, k_scale);
+                      workspace_bytes, stream, &sc);
 }
 
 VAR_EXPORT var_status var_attn_block_sparse_e4m3(const var_schedule* sched, const var_attn_desc* desc,
                                                  const uint8_t* q, var_layout q_l, const float* q_scale,
-                                                 const uint8_t* k, var_layout k_l, const float* k_scale,
-                                                 const void* v, var_layout v_l, void* o, var_layout o_l, float* lse,
+                                                 int64_t q_scale_stride, const uint8_t* k, var_layout k_l,
+                                                 const float* k_scale, int64_t k_scale_stride, const void* v,
+                                                 var_layout v_l, void* o, var_layout o_l, float* lse,
                                                  const int32_t* q_index, int32_t n_sel, const int32_t* row_ptr,
                                                  const int32_t* col_idx, int64_t col_stride, void* stream) {
-    if (!desc) return fail(VAR_ERR_NULL, "desc is NULL");
-    if (!q_scale || !k_scale) return fail(VAR_ERR_NULL, "q_scale and k_scale must be non-NULL");
     if (col_stride < 0) return fail(VAR_ERR_RANGE, "col_stride must be >= 0");
+    const E4m3Scales sc{q_scale, q_scale_stride, k_scale, k_scale_stride};
     return sparse_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, row_ptr, col_idx, 64, 64, 1,
-                       nullptr, 0, stream, col_stride > 0 ? col_stride : -1, q_scale, k_scale);
+                       nullptr, 0, stream, col_stride > 0 ? col_stride : -1, &sc);
 }
 
 VAR_EXPORT var_status var_quantize_e4m3(int32_t batch, int32_t heads, int32_t tokens, int32_t head_dim,
                                         const void* x, var_layout x_l, uint8_t* codes, var_layout c_l, float* scale,
-                                        void* stream) {
+                                        int64_t scale_stride, int32_t first_token, void* stream) {
     if (batch < 1 || heads < 1 || (int64_t)batch * heads > 65535)
         return fail(VAR_ERR_RANGE, "batch=%d heads=%d invalid (at most 65535 maps)", batch, heads);
     if (tokens < 0 || tokens >= (1 << 24)) return fail(VAR_ERR_RANGE, "tokens=%d outside [0, 2^24)", tokens);
-    if (head_dim < 8 || head_dim > 1024 || head_dim % 16)
-        return fail(VAR_ERR_UNSUPPORTED, "head_dim=%d must be a multiple of 16 in [16, 1024]", head_dim);
-    if (!scale) return fail(VAR_ERR_NULL, "scale must be non-NULL");
-    if (tokens > 0 && (!x || !codes)) return fail(VAR_ERR_NULL, "x and codes must be non-NULL");
+    if (first_token < 0 || first_token > tokens)
+        return fail(VAR_ERR_RANGE, "first_token=%d outside [0, tokens=%d]", first_token, tokens);
+    if (head_dim < 16 || head_dim > 256 || head_dim % 16)
+        return fail(VAR_ERR_UNSUPPORTED, "head_dim=%d must be a multiple of 16 in [16, 256]", head_dim);
+    const int32_t n_tiles = (tokens + 63) / 64;
+    if (first_token == tokens) return ok();   // no tile to write
+    if (!x || !codes || !scale) return fail(VAR_ERR_NULL, "x, codes and scale must be non-NULL");
     if (!aligned16(x) || !aligned16(codes)) return fail(VAR_ERR_STRIDE, "x and codes must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(scale) & 3u) return fail(VAR_ERR_STRIDE, "scale must be 4-byte aligned");
+    if (scale_stride < n_tiles)
+        return fail(VAR_ERR_STRIDE, "scale_stride=%lld below the %d tiles", (long long)scale_stride, n_tiles);
     var_status st = check_layout("x", x_l, head_dim, 2);
     if (st != VAR_OK) return st;
     if ((st = check_layout("codes", c_l, head_dim, 1)) != VAR_OK) return st;
@@ -416,13 +436,14 @@ VAR_EXPORT var_status var_quantize_e4m3(int32_t batch, int32_t heads, int32_t to
     p.x = x;
     p.codes = codes;
     p.scale = scale;
-    p.amax_bits = reinterpret_cast<uint32_t*>(scale);
+    p.scale_stride = scale_stride;
     p.x_sb = x_l.batch; p.x_sh = x_l.head; p.x_st = x_l.token;
     p.c_sb = c_l.batch; p.c_sh = c_l.head; p.c_st = c_l.token;
     p.H = heads;
     p.maps = batch * heads;
     p.tokens = tokens;
     p.D = head_dim;
+    p.tile_first = first_token / 64;
     return hip_status(varattn::launch_quant_e4m3(p, reinterpret_cast<hipStream_t>(stream)),
                       "var_quantize_e4m3 launch");
 }

@@ -258,19 +258,29 @@ def test_e4m3_validation_errors(api):
     E = lambda n: _code(api, n)
     P = ctypes.c_void_p
     L = api.Layout(2 * 16 * 10521 * 128, 10521 * 128, 128)
+    NT = 165                       # 64-token tiles of 10521 keys
     qz = api.LIB.var_quantize_e4m3
-    assert qz(2, 0, 10521, 128, P(FAKE), L, P(FAKE), L, P(FAKE), P(0)) == E("VAR_ERR_RANGE")
-    assert qz(256, 256, 10521, 128, P(FAKE), L, P(FAKE), L, P(FAKE), P(0)) == E("VAR_ERR_RANGE")   # > 65535 maps
-    assert qz(2, 16, 10521, 120, P(FAKE), L, P(FAKE), L, P(FAKE), P(0)) == E("VAR_ERR_UNSUPPORTED")
-    assert qz(2, 16, 10521, 128, P(FAKE), L, P(FAKE), L, P(0), P(0)) == E("VAR_ERR_NULL")
-    assert qz(2, 16, 10521, 128, P(FAKE + 8), L, P(FAKE), L, P(FAKE), P(0)) == E("VAR_ERR_STRIDE")
+
+    def quant(b=2, h=16, t=10521, d=128, x=FAKE, xl=L, c=FAKE, cl=L, sc=FAKE, stride=NT, first=0):
+        return qz(b, h, t, d, P(x), xl, P(c), cl, P(sc), stride, first, P(0))
+
+    assert quant(h=0) == E("VAR_ERR_RANGE")
+    assert quant(b=256, h=256) == E("VAR_ERR_RANGE")                 # > 65535 maps
+    assert quant(first=10522) == E("VAR_ERR_RANGE")
+    assert quant(first=-1) == E("VAR_ERR_RANGE")
+    assert quant(d=120) == E("VAR_ERR_UNSUPPORTED")
+    assert quant(d=512) == E("VAR_ERR_UNSUPPORTED")
+    assert quant(sc=0) == E("VAR_ERR_NULL")
+    assert quant(x=FAKE + 8) == E("VAR_ERR_STRIDE")
+    assert quant(stride=NT - 1) == E("VAR_ERR_STRIDE")
     odd = api.Layout(2 * 16 * 10521 * 136, 10521 * 136, 136)   # 136-byte code rows: not a multiple of 16
-    assert qz(2, 16, 10521, 128, P(FAKE), L, P(FAKE), odd, P(FAKE), P(0)) == E("VAR_ERR_STRIDE")
+    assert quant(cl=odd) == E("VAR_ERR_STRIDE")
+    assert quant(first=10521, x=0, c=0, sc=0) == E("VAR_OK")     # no tile to write: nothing is touched
     dn = api.LIB.var_attn_dense_e4m3
 
-    def dense(desc, qs=FAKE, ks=FAKE, ql=L):
-        return dn(ctypes.byref(s), ctypes.byref(desc), P(FAKE), ql, P(qs), P(FAKE), L, P(ks), P(FAKE), L, P(FAKE), L,
-                  P(0), P(0), 0, 1, P(0), 0, P(0))
+    def dense(desc, qs=FAKE, ks=FAKE, ql=L, qst=64, kst=NT):
+        return dn(ctypes.byref(s), ctypes.byref(desc), P(FAKE), ql, P(qs), qst, P(FAKE), L, P(ks), kst, P(FAKE), L,
+                  P(FAKE), L, P(0), P(0), 0, 1, P(0), 0, P(0))
 
     assert dense(_desc(api, head_dim=64)) == E("VAR_ERR_UNSUPPORTED")
     assert dense(_desc(api, in_dtype=api.VAR_F32, head_dim=64)) == E("VAR_ERR_UNSUPPORTED")
@@ -278,10 +288,14 @@ def test_e4m3_validation_errors(api):
     assert dense(_desc(api), ks=0) == E("VAR_ERR_NULL")
     assert dense(_desc(api), qs=FAKE + 2) == E("VAR_ERR_STRIDE")
     assert dense(_desc(api), ql=odd) == E("VAR_ERR_STRIDE")
+    assert dense(_desc(api), qst=63) == E("VAR_ERR_STRIDE")          # 4096 queries need 64 tile scales
+    assert dense(_desc(api), kst=NT - 1) == E("VAR_ERR_STRIDE")
     sp = api.LIB.var_attn_block_sparse_e4m3
-    assert sp(ctypes.byref(s), ctypes.byref(_desc(api)), P(FAKE), L, P(FAKE), P(FAKE), L, P(FAKE), P(FAKE), L,
-              P(FAKE), L, P(0), P(0), 0, P(FAKE), P(FAKE), -1, P(0)) == E("VAR_ERR_RANGE")
-    assert sp(ctypes.byref(s), ctypes.byref(_desc(api)), P(FAKE), L, P(FAKE), P(FAKE), L, P(FAKE), P(FAKE), L,
-              P(FAKE), L, P(0), P(0), 0, P(FAKE), P(FAKE), 64 * 165 - 1, P(0)) == E("VAR_ERR_CAPACITY")
-    assert sp(ctypes.byref(s), ctypes.byref(_desc(api)), P(FAKE), L, P(FAKE), P(FAKE), L, P(FAKE), P(FAKE), L,
-              P(FAKE), L, P(0), P(0), 0, P(0), P(FAKE), 0, P(0)) == E("VAR_ERR_NULL")
+
+    def sparse(rp=FAKE, stride=0):
+        return sp(ctypes.byref(s), ctypes.byref(_desc(api)), P(FAKE), L, P(FAKE), 64, P(FAKE), L, P(FAKE), NT,
+                  P(FAKE), L, P(FAKE), L, P(0), P(0), 0, P(rp), P(FAKE), stride, P(0))
+
+    assert sparse(stride=-1) == E("VAR_ERR_RANGE")
+    assert sparse(stride=64 * 165 - 1) == E("VAR_ERR_CAPACITY")
+    assert sparse(rp=0) == E("VAR_ERR_NULL")
