@@ -362,6 +362,29 @@ def main():
     bh_out = torch.empty(1, H, 4096, D, dtype=bf, device=dev)
     bh_ms = time_launch(lambda: api.var_attn_dense(sched, qsteps[K - 1][:1], k[:1], v[:1], K - 1, K, out=bh_out))
 
+    # FP8 (e4m3) logits: each step quantises the key tiles its new tokens
+    # reach (64-token tile scales), then runs the attention, which quantises
+    # its queries per 64 rows on load and runs QK on the e4m3 matrix cores
+    # (weights and V bf16)
+    k8 = torch.empty(B, H, off[K], D, dtype=torch.uint8, device=dev)
+    sk8 = torch.empty(B, H, -(-off[K] // 64), dtype=torch.float32, device=dev)
+    f8_out = [torch.empty(B, H, off[s + 1] - off[s], D, dtype=bf, device=dev) for s in range(K)]
+
+    def f8_quant(s):
+        api.var_quantize_e4m3(k[:, :, :off[s + 1]], codes=k8[:, :, :off[s + 1]], scale=sk8, first_token=off[s])
+
+    def f8_attn(s):
+        api.var_attn_dense_e4m3(sched, qsteps[s], k8, sk8, v, s, s + 1, out=f8_out[s], n_splits=dense_splits[s],
+                                workspace=workspace)
+
+    for s in range(K):
+        f8_quant(s)
+    f8_quant_ms = [time_launch(lambda s=s: f8_quant(s)) for s in range(K)]
+    f8_attn_ms = [time_launch(lambda s=s: f8_attn(s)) for s in range(K)]
+    f8_quant_last_ms, f8_attn_last_ms = f8_quant_ms[K - 1], f8_attn_ms[K - 1]
+    f8_gen_ms = time_launch(lambda: [(f8_quant(s), f8_attn(s)) for s in range(K)], reps=max(2, R // 4))
+    f8_quant_bytes = B * H * D * (off[K] - off[K - 1] // 64 * 64) * 3
+
     # dominant launch: the dense bf16 attention kernel on the last step (4096
     # queries x 10521 keys), which carries 61% of the pass's FLOPs
     last = K - 1
@@ -454,6 +477,20 @@ def main():
             "last_step_cond_only_ms": round(bh_ms, 4),
             "last_step_cond_only_tflops": round(dense_flops[last] / 2 / (bh_ms * 1e-3) / 1e12, 2),
             "speedup_vs_both_branches": round(dense_ms[last] / bh_ms, 3),
+        },
+        "fp8_qk": {
+            "format": "e4m3 q and k, one fp32 scale per 64-token tile (keys: of the cache, quantised as "
+                      "they arrive; queries: 64 rows of the call, quantised in the attention kernel); "
+                      "weights and v bf16",
+            "last_step_key_quantize_ms": round(f8_quant_last_ms, 4),
+            "last_step_key_quantize_gbps": round(f8_quant_bytes / (f8_quant_last_ms * 1e-3) / 1e9, 1),
+            "last_step_attn_ms": round(f8_attn_last_ms, 4),
+            "last_step_attn_tflops": round(dense_flops[last] / (f8_attn_last_ms * 1e-3) / 1e12, 2),
+            "speedup_last_step_attn_vs_bf16": round(dense_ms[last] / f8_attn_last_ms, 3),
+            "per_step_key_quantize_ms": [round(x, 4) for x in f8_quant_ms],
+            "per_step_attn_ms": [round(x, 4) for x in f8_attn_ms],
+            "generation_ms": round(f8_gen_ms, 4),
+            "speedup_generation_vs_bf16_dense": round(dense_gen_ms / f8_gen_ms, 3),
         },
         "wall_s_timed": round(wall, 3),
     }

@@ -328,10 +328,10 @@ var_status var_attn_block_sparse_heads(const var_schedule* sched, const var_attn
  * Modelling with Efficient Attention and Quantization", abstract: the data
  * precision of a VAR model is redundant and low-bit quantisation keeps its
  * quality).  The record names no format, operand or granularity; these calls
- * take queries and keys as OCP e4m3 codes (1 sign, 4 exponent bits with bias
- * 7, 3 mantissa bits, subnormals, largest finite 448, no infinities; 0x7F and
- * 0xFF are NaN) with one fp32 scale per (batch, head, 64-token tile), value =
- * e4m3 value * scale.  The attention weights and v stay bf16.
+ * compute the logits from queries and keys in OCP e4m3 (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits, subnormals, largest finite 448, no
+ * infinities; 0x7F and 0xFF are NaN) with one fp32 scale per 64-token tile,
+ * value = e4m3 value * scale.  The attention weights and v stay bf16.
  *
  * var_quantize_e4m3: x is bf16 [batch][heads][tokens][head_dim] (layout x_l,
  * finite values).  Tile j of map m = b*heads + h holds tokens
@@ -348,40 +348,42 @@ var_status var_attn_block_sparse_heads(const var_schedule* sched, const var_attn
  *  0 <= first_token <= tokens (= tokens: nothing to do; pointers may then be
  *  NULL); head_dim a multiple of 16 in [16, 256]; batch*heads <= 65535.
  *
- * var_attn_dense_e4m3: var_attn_dense_split with q and k as e4m3 codes: the
- * logit of query row pos (of q) and key u is
- *   softmax_scale * q_scale[m][pos / 64] * k_scale[m][u / 64] * (q_codes . k_codes)
- * with m = b*heads + h, i.e. attention of the dequantised q and k; the
- * products of codes are summed exactly in fp32 by the matrix cores.
- *  desc   in_dtype must be VAR_BF16 (the dtype of v); head_dim 128;
+ * var_attn_dense_e4m3: var_attn_dense_split with the logits taken from e4m3
+ * queries and keys.  k is e4m3 codes with tile scales (e.g. from
+ * var_quantize_e4m3 of the key cache); q is bf16 and is quantised inside the
+ * call, rows [64j, 64j + 64) of the call (after the q_index gather) forming
+ * one group with the rule of var_quantize_e4m3.  With qs the scale of the
+ * group of output row i and m = b*heads + h, the logit of row i and key u is
+ *   softmax_scale * qs * k_scale[m*k_scale_stride + u/64] * (q_codes . k_codes),
+ * i.e. attention of the dequantised queries and keys; the products of codes
+ * are summed exactly in fp32 by the matrix cores.
+ *  desc   in_dtype must be VAR_BF16 (the dtype of q and v); head_dim 128;
  *         out_dtype f32 or bf16.
- *  q, k   device uint8 codes with the shapes of var_attn_dense and layouts
- *         q_l, k_l (strides in bytes, multiples of 16).
- *  q_scale device fp32 [B*H][q_scale_stride], q_scale_stride >= ceil(n_q/64);
- *  k_scale device fp32 [B*H][k_scale_stride], k_scale_stride >= ceil(kv_len/64)
- *         (e.g. from var_quantize_e4m3 of q and of the key cache); positive.
+ *  k      device uint8 codes [B][H][>= kv_len][128], layout k_l (strides in
+ *         bytes, multiples of 16).
+ *  k_scale device fp32 [B*H][k_scale_stride], k_scale_stride >= ceil(kv_len/64),
+ *         positive.
  *  Other arguments as in var_attn_dense_split.
- * var_attn_block_sparse_e4m3: the block-sparse call (64x64 tiles) with e4m3
- * q and k; col_stride 0 takes one CSR shared by every (batch, head) (as
- * var_attn_block_sparse), col_stride > 0 one CSR per (batch, head) as in
+ * var_attn_block_sparse_e4m3: the block-sparse call (64x64 tiles) with the
+ * same e4m3 logits; col_stride 0 takes one CSR shared by every (batch, head)
+ * (as var_attn_block_sparse), col_stride > 0 one CSR per (batch, head) as in
  * var_attn_block_sparse_heads.
  * Errors: VAR_ERR_UNSUPPORTED for another head_dim or in_dtype, VAR_ERR_NULL
- * for a missing scale array, VAR_ERR_STRIDE for code strides that are not
- * multiples of 16 bytes or scale strides below the tile counts; otherwise as
+ * for a missing k_scale, VAR_ERR_STRIDE for code strides that are not
+ * multiples of 16 bytes or a scale stride below the key tiles; otherwise as
  * the bf16 calls.
  */
 var_status var_quantize_e4m3(int32_t batch, int32_t heads, int32_t tokens, int32_t head_dim,
                              const void* x, var_layout x_l, uint8_t* codes, var_layout c_l,
                              float* scale, int64_t scale_stride, int32_t first_token, void* stream);
 var_status var_attn_dense_e4m3(const var_schedule* sched, const var_attn_desc* desc,
-                               const uint8_t* q, var_layout q_l, const float* q_scale, int64_t q_scale_stride,
-                               const uint8_t* k, var_layout k_l, const float* k_scale, int64_t k_scale_stride,
+                               const void* q, var_layout q_l, const uint8_t* k, var_layout k_l,
+                               const float* k_scale, int64_t k_scale_stride,
                                const void* v, var_layout v_l, void* o, var_layout o_l,
                                float* lse, const int32_t* q_index, int32_t n_sel,
                                int32_t n_splits, void* workspace, int64_t workspace_bytes, void* stream);
 var_status var_attn_block_sparse_e4m3(const var_schedule* sched, const var_attn_desc* desc,
-                                      const uint8_t* q, var_layout q_l, const float* q_scale,
-                                      int64_t q_scale_stride, const uint8_t* k, var_layout k_l,
+                                      const void* q, var_layout q_l, const uint8_t* k, var_layout k_l,
                                       const float* k_scale, int64_t k_scale_stride,
                                       const void* v, var_layout v_l, void* o, var_layout o_l,
                                       float* lse, const int32_t* q_index, int32_t n_sel,

@@ -94,9 +94,9 @@ def _load():
     lib.var_attn_block_sparse_heads.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, Layout, P,
                                                 Layout, P, P, i32, P, P, i64, P]
     lib.var_quantize_e4m3.argtypes = [i32, i32, i32, i32, P, Layout, P, Layout, P, i64, i32, P]
-    lib.var_attn_dense_e4m3.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, i64, P, Layout, P, i64, P,
+    lib.var_attn_dense_e4m3.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, i64, P,
                                         Layout, P, Layout, P, P, i32, i32, P, i64, P]
-    lib.var_attn_block_sparse_e4m3.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, i64, P, Layout, P, i64,
+    lib.var_attn_block_sparse_e4m3.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, i64,
                                                P, Layout, P, Layout, P, P, i32, P, P, i64, P]
     for name in EXPORTED[:-2]:
         getattr(lib, name).restype = ctypes.c_int
@@ -189,8 +189,8 @@ def _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype, 
     if k.shape[0] != B or v.shape[0] != B or k.shape[1] != H or v.shape[1] != H or k.shape[3] != D or v.shape[3] != D:
         raise ValueError("q, k, v disagree in batch, heads or head_dim")
     if qk_codes:
-        if q.dtype != torch.uint8 or k.dtype != torch.uint8 or v.dtype != torch.bfloat16:
-            raise ValueError("e4m3 attention takes uint8 codes for q and k and bf16 v")
+        if q.dtype != torch.bfloat16 or k.dtype != torch.uint8 or v.dtype != torch.bfloat16:
+            raise ValueError("e4m3 attention takes bf16 q and v and uint8 codes for k")
     elif q.dtype != k.dtype or q.dtype != v.dtype:
         raise ValueError("q, k, v must share a dtype")
     if q.device != k.device or q.device != v.device:
@@ -530,9 +530,10 @@ def _scale_arg(t, B, H, dev, name):
     return _ptr(t), t.shape[2]
 
 
-def var_attn_dense_e4m3(schedule, q, q_scale, k, k_scale, v, q_scale_begin, q_scale_end, out=None, out_dtype=None,
+def var_attn_dense_e4m3(schedule, q, k, k_scale, v, q_scale_begin, q_scale_end, out=None, out_dtype=None,
                         softmax_scale=0.0, q_index=None, return_lse=False, n_splits=1, workspace=None):
-    """var_attn_dense with q and k as e4m3 codes (uint8) and fp32 tile scales [B, H, tiles] (var_quantize_e4m3)."""
+    """var_attn_dense with e4m3 logits: k as e4m3 codes (uint8) with tile scales [B, H, tiles]
+    (var_quantize_e4m3); q bf16, quantised in the call per 64 output rows."""
     s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
                                            softmax_scale, q_index, return_lse, qk_codes=True)
     n_sel = rows if q_index is not None else 0
@@ -540,18 +541,17 @@ def var_attn_dense_e4m3(schedule, q, q_scale, k, k_scale, v, q_scale_begin, q_sc
         return (out, lse) if return_lse else out
     B, H = q.shape[0], q.shape[1]
     wp, wb = _ws_args(n_splits, workspace)
-    _check(LIB.var_attn_dense_e4m3(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q),
-                                   *_scale_arg(q_scale, B, H, q.device, "q_scale"), _ptr(k), _layout(k),
+    _check(LIB.var_attn_dense_e4m3(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k), _layout(k),
                                    *_scale_arg(k_scale, B, H, q.device, "k_scale"), _ptr(v), _layout(v), _ptr(out),
                                    _layout(out), _ptr(lse), _ptr(q_index), n_sel, int(n_splits), wp, wb,
                                    _stream(q.device)))
     return (out, lse) if return_lse else out
 
 
-def var_attn_block_sparse_e4m3(schedule, q, q_scale, k, k_scale, v, q_scale_begin, q_scale_end, row_ptr, col_idx,
+def var_attn_block_sparse_e4m3(schedule, q, k, k_scale, v, q_scale_begin, q_scale_end, row_ptr, col_idx,
                                out=None, out_dtype=None, softmax_scale=0.0, q_index=None, return_lse=False):
-    """Block-sparse attention with e4m3 q and k.  row_ptr / col_idx 1-D: one CSR for every (batch, head);
-    2-D [B*H, n_qt+1] / [B*H, stride]: one CSR per (batch, head)."""
+    """Block-sparse attention with e4m3 logits (as var_attn_dense_e4m3).  row_ptr / col_idx 1-D: one CSR
+    for every (batch, head); 2-D [B*H, n_qt+1] / [B*H, stride]: one CSR per (batch, head)."""
     s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
                                            softmax_scale, q_index, return_lse, qk_codes=True)
     n_sel = rows if q_index is not None else 0
@@ -570,9 +570,8 @@ def var_attn_block_sparse_e4m3(schedule, q, q_scale, k, k_scale, v, q_scale_begi
         if tuple(row_ptr.shape) != (B * H, n_qt + 1) or col_idx.dim() != 2 or col_idx.shape[0] != B * H:
             raise ValueError("per-head CSR: row_ptr int32 [B*H, n_qt+1], col_idx int32 [B*H, stride]")
         stride = col_idx.shape[1]
-    _check(LIB.var_attn_block_sparse_e4m3(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q),
-                                          *_scale_arg(q_scale, B, H, q.device, "q_scale"), _ptr(k), _layout(k),
-                                          *_scale_arg(k_scale, B, H, q.device, "k_scale"), _ptr(v), _layout(v),
-                                          _ptr(out), _layout(out), _ptr(lse), _ptr(q_index), n_sel, _ptr(row_ptr),
-                                          _ptr(col_idx), stride, _stream(q.device)))
+    _check(LIB.var_attn_block_sparse_e4m3(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k),
+                                          _layout(k), *_scale_arg(k_scale, B, H, q.device, "k_scale"), _ptr(v),
+                                          _layout(v), _ptr(out), _layout(out), _ptr(lse), _ptr(q_index), n_sel,
+                                          _ptr(row_ptr), _ptr(col_idx), stride, _stream(q.device)))
     return (out, lse) if return_lse else out

@@ -26,7 +26,9 @@ SOURCES = ["attn_bf16.hip", "attn_fp8.hip", "attn_f32.hip", "quant_e4m3.hip", "t
 # (S and O are read by VALU code); the kernel itself places the MFMA operands
 # that stay resident (Q) or come from LDS (K, V^T) in AGPRs.
 _ATTN_FLAGS = ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]
-PER_FILE_FLAGS = {"attn_bf16.hip": _ATTN_FLAGS, "attn_fp8.hip": _ATTN_FLAGS}
+# (the quantiser shares the e4m3 conversion with the attention kernel that
+# quantises its queries, so it is built in the same floating-point mode)
+PER_FILE_FLAGS = {"attn_bf16.hip": _ATTN_FLAGS, "attn_fp8.hip": _ATTN_FLAGS, "quant_e4m3.hip": _ATTN_FLAGS}
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -63,6 +63,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "e4m3.h"
 #include "kernels.h"
 
 namespace varattn {
@@ -239,7 +240,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     constexpr int NW = waves_per_wg<SPARSE>();   // waves per workgroup
     constexpr int NT = NW * 64;                  // threads per workgroup
     constexpr int QT = NW * QW;                  // query rows per workgroup
-    constexpr int EK = QK8 ? 1 : 2;            // bytes per q / k element
+    constexpr int EK = QK8 ? 1 : 2;            // bytes per k element (q is always bf16)
     constexpr int ROWB = D * EK;               // bytes per K row
     constexpr int KCH = ROWB / 16;             // 16-byte chunks per K row
     constexpr int K_BYTES = KT * ROWB;
@@ -283,6 +284,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     bool row_valid[2];
     float c2q[2];   // log2-domain logit scale of each of the lane's two queries
     qop qreg[2][SK];
+    uint32_t qraw[2][QK8 ? SK : 1][4][4];   // e4m3 path: the lane's bf16 query values
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         my_row[qb] = qtile * QT + wave * QW + 32 * qb + n;
@@ -298,25 +300,55 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                 if (s < p.num_scales && tok < p.scale_end[s]) kl = p.scale_end[s];
         }
         klim[qb] = kl;
-        // scale * log2(e), times the query's tile scale for e4m3 codes
         c2q[qb] = p.scale_log2;
-        if constexpr (QK8) c2q[qb] *= p.q_scale[bh * p.q_scale_stride + (pos >> 6)];
         const unsigned char* qp = reinterpret_cast<const unsigned char*>(p.q) +
-                                  (b * p.q_sb + h * p.q_sh + (int64_t)pos * p.q_st) * EK;
+                                  (b * p.q_sb + h * p.q_sh + (int64_t)pos * p.q_st) * 2;
 #pragma unroll
         for (int ks = 0; ks < SK; ++ks) {
             // lane half g holds k = 8g..8g+7 of the bf16 step (16 deep) or
             // 32g..32g+31 of the e4m3 step (64 deep)
             if constexpr (QK8) {
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(qp + 64 * ks + 32 * g);
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(qp + 64 * ks + 32 * g + 16);
-                qreg[qb][ks] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 t = *reinterpret_cast<const u32x4*>(qp + 2 * (64 * ks + 32 * g + 8 * c));
+                    qraw[qb][ks][c][0] = t.x, qraw[qb][ks][c][1] = t.y, qraw[qb][ks][c][2] = t.z, qraw[qb][ks][c][3] = t.w;
+                }
             } else {
                 qreg[qb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * ks + 16 * g));
+                // Q is only ever an MFMA operand: keep it in AGPRs (MFMAs read
+                // them directly), which leaves the VGPRs to the softmax and the loads
+                asm volatile("" : "+a"(qreg[qb][ks]));
             }
-            // Q is only ever an MFMA operand: keep it in AGPRs (MFMAs read them
-            // directly), which leaves the VGPRs to the softmax and the loads
-            asm volatile("" : "+a"(qreg[qb][ks]));
+        }
+    }
+    if constexpr (QK8) {
+        // The wave's 64 rows are one 64-row tile of the call: quantise it to
+        // e4m3 with one scale (amax / 448; rows past n_rows repeat the last
+        // row and leave the maximum unchanged), in the operand layout.
+        uint32_t mx = 0u;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int ks = 0; ks < SK; ++ks)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) mx = max(mx, bf16x8_absmax_bits(qraw[qb][ks][c]));
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, m));
+        const float amax = mx ? __uint_as_float(mx) : 1.0f;
+        const float inv = __fdiv_rn(448.0f, amax);
+        const float sq = __fdiv_rn(amax, 448.0f);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            c2q[qb] = p.scale_log2 * sq;
+#pragma unroll
+            for (int ks = 0; ks < SK; ++ks) {
+                uint32_t cw[8];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bf16x8_to_e4m3(qraw[qb][ks][c], inv, cw[2 * c], cw[2 * c + 1]);
+                qreg[qb][ks] = i32x8{(int)cw[0], (int)cw[1], (int)cw[2], (int)cw[3],
+                                     (int)cw[4], (int)cw[5], (int)cw[6], (int)cw[7]};
+                asm volatile("" : "+a"(qreg[qb][ks]));
+            }
         }
     }
     const int w_kmin = __builtin_amdgcn_readfirstlane(wave_min_i(min(klim[0], klim[1])));

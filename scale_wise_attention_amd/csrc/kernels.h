@@ -44,12 +44,10 @@ struct AttnParams {
     // per-(batch, head) CSR (block-sparse): element strides between the maps'
     // row_ptr / col_idx arrays (0: one CSR shared by every (batch, head))
     int64_t rp_bh_stride, ci_bh_stride;
-    // e4m3 q / k (launch_attn_fp8 only): dequantisation scales of 64-token
-    // tiles, q_scale[bh * q_scale_stride + pos / 64] for the query at call
-    // position pos, k_scale[bh * k_scale_stride + key / 64]
-    const float* q_scale;
+    // e4m3 keys (launch_attn_fp8 only): dequantisation scale of key tile
+    // key / 64 at k_scale[bh * k_scale_stride + key / 64]
     const float* k_scale;
-    int64_t q_scale_stride, k_scale_stride;
+    int64_t k_scale_stride;
 };
 
 // Largest key-split count of a launch.
@@ -86,7 +84,8 @@ struct ScatterParams {
 
 // Launchers: return the hipError_t of the launch.
 hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, bool out_bf16, bool sparse, hipStream_t s);
-// The same attention with q and k as e4m3 codes (q_scale, k_scale set); v bf16.
+// The same attention with k as e4m3 codes (k_scale set) and q quantised to
+// e4m3 in the kernel, one scale per 64-row tile of the call; v bf16.
 hipError_t launch_attn_fp8(const AttnParams& p, int head_dim, bool out_bf16, bool sparse, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int head_dim, bool sparse, hipStream_t s);
 // e4m3 quantisation with one scale per (batch, head, 64-token tile).

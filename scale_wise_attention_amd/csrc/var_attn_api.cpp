@@ -242,49 +242,42 @@ VAR_EXPORT var_status var_schedule_extent(const var_schedule* sched, int32_t b, 
 
 namespace {
 
-// Tile scales of e4m3 q and k: q_scale[m][q_stride] covers the call's
-// ceil(n_q / 64) query tiles, k_scale[m][k_stride] its ceil(kv_len / 64) key tiles.
-struct E4m3Scales {
-    const float* q;
-    int64_t q_stride;
-    const float* k;
-    int64_t k_stride;
+// Tile scales of e4m3 keys: k_scale[m][k_stride] covers the call's
+// ceil(kv_len / 64) key tiles.
+struct E4m3Keys {
+    const float* scale;
+    int64_t stride;
 };
 
-// Extra checks of a call whose q and k are e4m3 codes (v bf16): head_dim 128,
-// 16-byte strides of the code tensors, both scale arrays present and long
-// enough.  p is the filled parameter block (n_q, kv_len known).
-var_status check_e4m3(const var_attn_desc* desc, var_layout q_l, var_layout k_l, const E4m3Scales& sc,
+// Extra checks of a call whose k is e4m3 codes (q and v bf16): head_dim 128,
+// 16-byte strides of the code tensor, a scale array present and long enough.
+// p is the filled parameter block (kv_len known).
+var_status check_e4m3(const var_attn_desc* desc, var_layout k_l, const E4m3Keys& kc,
                       const varattn::AttnParams& p) {
     if (desc->in_dtype != VAR_BF16 || desc->head_dim != 128)
-        return fail(VAR_ERR_UNSUPPORTED, "e4m3 q/k need bf16 v (in_dtype) and head_dim 128");
-    if (!sc.q || !sc.k) return fail(VAR_ERR_NULL, "q_scale and k_scale must be non-NULL");
-    if ((reinterpret_cast<uintptr_t>(sc.q) & 3u) || (reinterpret_cast<uintptr_t>(sc.k) & 3u))
-        return fail(VAR_ERR_STRIDE, "q_scale and k_scale must be 4-byte aligned");
-    if (sc.q_stride < (p.n_q + 63) / 64 || sc.k_stride < (p.kv_len + 63) / 64)
-        return fail(VAR_ERR_STRIDE, "scale strides (%lld, %lld) below the tiles of the call (%d, %d)",
-                    (long long)sc.q_stride, (long long)sc.k_stride, (p.n_q + 63) / 64, (p.kv_len + 63) / 64);
-    var_status st = check_layout("q", q_l, desc->head_dim, 1);
-    if (st != VAR_OK) return st;
+        return fail(VAR_ERR_UNSUPPORTED, "e4m3 keys need bf16 q and v (in_dtype) and head_dim 128");
+    if (!kc.scale) return fail(VAR_ERR_NULL, "k_scale must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(kc.scale) & 3u) return fail(VAR_ERR_STRIDE, "k_scale must be 4-byte aligned");
+    if (kc.stride < (p.kv_len + 63) / 64)
+        return fail(VAR_ERR_STRIDE, "k_scale_stride=%lld below the %d key tiles of the call", (long long)kc.stride,
+                    (p.kv_len + 63) / 64);
     return check_layout("k", k_l, desc->head_dim, 1);
 }
 
-void attach_e4m3(varattn::AttnParams* p, const E4m3Scales& sc) {
-    p->q_scale = sc.q;
-    p->k_scale = sc.k;
-    p->q_scale_stride = sc.q_stride;
-    p->k_scale_stride = sc.k_stride;
+void attach_e4m3(varattn::AttnParams* p, const E4m3Keys& kc) {
+    p->k_scale = kc.scale;
+    p->k_scale_stride = kc.stride;
 }
 
 var_status dense_impl(const var_schedule* sched, const var_attn_desc* desc, const void* q, var_layout q_l,
                       const void* k, var_layout k_l, const void* v, var_layout v_l, void* o, var_layout o_l,
                       float* lse, const int32_t* q_index, int32_t n_sel, int32_t splits, void* ws,
-                      int64_t ws_bytes, void* stream, const E4m3Scales* e4m3 = nullptr) {
+                      int64_t ws_bytes, void* stream, const E4m3Keys* e4m3 = nullptr) {
     varattn::AttnParams p;
     bool none = false;
     var_status st = prepare_attn(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, &p, &none);
     if (st != VAR_OK) return st;
-    if (e4m3 && !none && (st = check_e4m3(desc, q_l, k_l, *e4m3, p)) != VAR_OK) return st;
+    if (e4m3 && !none && (st = check_e4m3(desc, k_l, *e4m3, p)) != VAR_OK) return st;
     if ((st = attach_splits(&p, desc, none ? 1 : splits, ws, ws_bytes)) != VAR_OK) return st;
     if (none) return ok();
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -314,7 +307,7 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
                        float* lse, const int32_t* q_index, int32_t n_sel, const int32_t* row_ptr,
                        const int32_t* col_idx, int32_t tile_q, int32_t tile_k, int32_t splits, void* ws,
                        int64_t ws_bytes, void* stream, int64_t col_bh_stride = -1,
-                       const E4m3Scales* e4m3 = nullptr) {
+                       const E4m3Keys* e4m3 = nullptr) {
     if (tile_q != 64 || tile_k != 64)
         return fail(VAR_ERR_UNSUPPORTED, "block-sparse attention supports 64x64 tiles, got %dx%d", tile_q, tile_k);
     if (!row_ptr || !col_idx) return fail(VAR_ERR_NULL, "row_ptr and col_idx must be non-NULL");
@@ -322,7 +315,7 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
     bool none = false;
     var_status st = prepare_attn(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, &p, &none);
     if (st != VAR_OK) return st;
-    if (e4m3 && !none && (st = check_e4m3(desc, q_l, k_l, *e4m3, p)) != VAR_OK) return st;
+    if (e4m3 && !none && (st = check_e4m3(desc, k_l, *e4m3, p)) != VAR_OK) return st;
     if ((st = attach_splits(&p, desc, none ? 1 : splits, ws, ws_bytes)) != VAR_OK) return st;
     if (none) return ok();
     p.row_ptr = row_ptr;
@@ -386,29 +379,27 @@ VAR_EXPORT var_status var_attn_block_sparse_heads(const var_schedule* sched, con
                        nullptr, 0, stream, col_stride);
 }
 
-VAR_EXPORT var_status var_attn_dense_e4m3(const var_schedule* sched, const var_attn_desc* desc, const uint8_t* q,
-                                          var_layout q_l, const float* q_scale, int64_t q_scale_stride,
-                                          const uint8_t* k, var_layout k_l, const float* k_scale,
+VAR_EXPORT var_status var_attn_dense_e4m3(const var_schedule* sched, const var_attn_desc* desc, const void* q,
+                                          var_layout q_l, const uint8_t* k, var_layout k_l, const float* k_scale,
                                           int64_t k_scale_stride, const void* v, var_layout v_l, void* o,
                                           var_layout o_l, float* lse, const int32_t* q_index, int32_t n_sel,
                                           int32_t n_splits, void* workspace, int64_t workspace_bytes,
                                           void* stream) {
-    const E4m3Scales sc{q_scale, q_scale_stride, k_scale, k_scale_stride};
+    const E4m3Keys kc{k_scale, k_scale_stride};
     return dense_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, n_splits, workspace,
-                      workspace_bytes, stream, &sc);
+                      workspace_bytes, stream, &kc);
 }
 
 VAR_EXPORT var_status var_attn_block_sparse_e4m3(const var_schedule* sched, const var_attn_desc* desc,
-                                                 const uint8_t* q, var_layout q_l, const float* q_scale,
-                                                 int64_t q_scale_stride, const uint8_t* k, var_layout k_l,
+                                                 const void* q, var_layout q_l, const uint8_t* k, var_layout k_l,
                                                  const float* k_scale, int64_t k_scale_stride, const void* v,
                                                  var_layout v_l, void* o, var_layout o_l, float* lse,
                                                  const int32_t* q_index, int32_t n_sel, const int32_t* row_ptr,
                                                  const int32_t* col_idx, int64_t col_stride, void* stream) {
     if (col_stride < 0) return fail(VAR_ERR_RANGE, "col_stride must be >= 0");
-    const E4m3Scales sc{q_scale, q_scale_stride, k_scale, k_scale_stride};
+    const E4m3Keys kc{k_scale, k_scale_stride};
     return sparse_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, row_ptr, col_idx, 64, 64, 1,
-                       nullptr, 0, stream, col_stride > 0 ? col_stride : -1, &sc);
+                       nullptr, 0, stream, col_stride > 0 ? col_stride : -1, &kc);
 }
 
 VAR_EXPORT var_status var_quantize_e4m3(int32_t batch, int32_t heads, int32_t tokens, int32_t head_dim,

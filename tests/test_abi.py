@@ -277,24 +277,23 @@ def test_e4m3_validation_errors(api):
     assert quant(cl=odd) == E("VAR_ERR_STRIDE")
     assert quant(first=10521, x=0, c=0, sc=0) == E("VAR_OK")     # no tile to write: nothing is touched
     dn = api.LIB.var_attn_dense_e4m3
+    Lq = api.Layout(2 * 16 * 4096 * 128, 4096 * 128, 128)
 
-    def dense(desc, qs=FAKE, ks=FAKE, ql=L, qst=64, kst=NT):
-        return dn(ctypes.byref(s), ctypes.byref(desc), P(FAKE), ql, P(qs), qst, P(FAKE), L, P(ks), kst, P(FAKE), L,
-                  P(FAKE), L, P(0), P(0), 0, 1, P(0), 0, P(0))
+    def dense(desc, ks=FAKE, kl=L, kst=NT):
+        return dn(ctypes.byref(s), ctypes.byref(desc), P(FAKE), Lq, P(FAKE), kl, P(ks), kst, P(FAKE), L,
+                  P(FAKE), Lq, P(0), P(0), 0, 1, P(0), 0, P(0))
 
     assert dense(_desc(api, head_dim=64)) == E("VAR_ERR_UNSUPPORTED")
     assert dense(_desc(api, in_dtype=api.VAR_F32, head_dim=64)) == E("VAR_ERR_UNSUPPORTED")
-    assert dense(_desc(api), qs=0) == E("VAR_ERR_NULL")
     assert dense(_desc(api), ks=0) == E("VAR_ERR_NULL")
-    assert dense(_desc(api), qs=FAKE + 2) == E("VAR_ERR_STRIDE")
-    assert dense(_desc(api), ql=odd) == E("VAR_ERR_STRIDE")
-    assert dense(_desc(api), qst=63) == E("VAR_ERR_STRIDE")          # 4096 queries need 64 tile scales
+    assert dense(_desc(api), ks=FAKE + 2) == E("VAR_ERR_STRIDE")
+    assert dense(_desc(api), kl=odd) == E("VAR_ERR_STRIDE")
     assert dense(_desc(api), kst=NT - 1) == E("VAR_ERR_STRIDE")
     sp = api.LIB.var_attn_block_sparse_e4m3
 
     def sparse(rp=FAKE, stride=0):
-        return sp(ctypes.byref(s), ctypes.byref(_desc(api)), P(FAKE), L, P(FAKE), 64, P(FAKE), L, P(FAKE), NT,
-                  P(FAKE), L, P(FAKE), L, P(0), P(0), 0, P(rp), P(FAKE), stride, P(0))
+        return sp(ctypes.byref(s), ctypes.byref(_desc(api)), P(FAKE), Lq, P(FAKE), L, P(FAKE), NT,
+                  P(FAKE), L, P(FAKE), Lq, P(0), P(0), 0, P(rp), P(FAKE), stride, P(0))
 
     assert sparse(stride=-1) == E("VAR_ERR_RANGE")
     assert sparse(stride=64 * 165 - 1) == E("VAR_ERR_CAPACITY")

@@ -1,9 +1,10 @@
 """GPU parity of the e4m3 path: the quantiser bit for bit against the oracle's
-quantize_tiles (codes and the scales of 64-token tiles), and attention on
-e4m3 q / k against the fp64 oracle on the dequantised values, at the bf16
-bars (max-abs 1e-2, mean-abs 1e-3; LSE within 2.5e-3): the products of codes
-are exact in the matrix cores, so the only rounding left is the bf16
-weights' and the fp32 sums'.
+quantize_tiles (codes and the scales of 64-token tiles), and attention with
+e4m3 logits against the fp64 oracle on the dequantised values (keys
+quantised per 64-token tile of the cache, queries per 64 output rows of the
+call), at the bf16 bars (max-abs 1e-2, mean-abs 1e-3; LSE within 2.5e-3):
+the products of codes are exact in the matrix cores, so the only rounding
+left is the bf16 weights' and the fp32 sums'.
 """
 
 import numpy as np
@@ -116,11 +117,20 @@ def test_quantize_growing_cache_touches_only_new_tiles(api):
     assert np.array_equal(scale.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
 
 
-def _quantised(api, q, k):
-    """GPU codes for q and k (checked equal to the oracle's) and the oracle's dequantised fp64 values."""
-    q8, sq, rq, rsq = _check_quant(api, q, "q")
+def _quantised(api, q, k, sel=None):
+    """GPU codes of k (checked equal to the oracle's) with the oracle's dequantised keys, and the
+    oracle's dequantised queries: the call's rows (q, or q[:, :, sel]) in groups of 64, placed back
+    at their positions of q."""
     k8, sk, rk, rsk = _check_quant(api, k, "k")
-    return q8, sq, k8, sk, dequantize_tiles(rq, rsq), dequantize_tiles(rk, rsk)
+    qn = _np(q)
+    rows = qn if sel is None else qn[:, :, sel]
+    qd_rows = dequantize_tiles(*quantize_tiles(rows))
+    qd = np.zeros(qn.shape)
+    if sel is None:
+        qd = qd_rows
+    else:
+        qd[:, :, sel] = qd_rows
+    return k8, sk, qd, dequantize_tiles(rk, rsk)
 
 
 # LSE bar when one weight dominates a row: the row sum adds bf16-rounded
@@ -147,8 +157,8 @@ def test_dense_e4m3_steps_match_oracle(api, step):
     off = oracle.offsets(wl.h, wl.w)
     qs = q[:, :, off[step]:off[step + 1]].contiguous()
     kc = k[:, :, :off[step + 1]].contiguous()
-    q8, sq, k8, sk, qd, kd = _quantised(api, qs, kc)
-    o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, step, step + 1, return_lse=True)
+    k8, sk, qd, kd = _quantised(api, qs, kc)
+    o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), qs, k8, sk, v, step, step + 1, return_lse=True)
     ref, ref_lse = oracle.attention(qd, kd, _np(v), wl.h, wl.w, step, step + 1, return_lse=True)
     _bars(_np(o), ref, f"e4m3 dense step {step}", _np(lse), ref_lse)
 
@@ -159,15 +169,15 @@ def test_dense_e4m3_gather_splits_bf16_out(api):
     off = oracle.offsets(wl.h, wl.w)
     s = 7
     qs = q[:, :, off[s]:off[s + 1]]
-    q8, sq, k8, sk, qd, kd = _quantised(api, qs, k)
     n = off[s + 1] - off[s]
-    sel = np.sort(np.random.default_rng(71).choice(n, 157, replace=False)).astype(np.int32)
+    sel = np.random.default_rng(71).choice(n, 157, replace=False).astype(np.int32)   # any order
+    k8, sk, qd, kd = _quantised(api, qs, k, sel)
     idx = torch.from_numpy(sel).cuda()
     ref, ref_lse = oracle.attention(qd, kd, _np(v), wl.h, wl.w, s, s + 1, q_index=sel, return_lse=True)
     for splits in (1, 3):
         ws = api.split_workspace(splits, 2, 2, sel.size, 128) if splits > 1 else None
         for odt in (torch.float32, torch.bfloat16):
-            o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, s, s + 1, q_index=idx, out_dtype=odt,
+            o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), qs, k8, sk, v, s, s + 1, q_index=idx, out_dtype=odt,
                                              return_lse=True, n_splits=splits, workspace=ws)
             _bars(_np(o), ref, f"e4m3 gather splits={splits} {odt}", _np(lse), ref_lse)
 
@@ -187,11 +197,11 @@ def test_dense_e4m3_tile_scales_differ(api):
     n = off[s + 1] - off[s]
     qf = torch.from_numpy(np.repeat(2.0 ** rng.integers(-2, 2, -(-n // 64)), 64)[:n])
     qs = (q[:, :, off[s]:off[s + 1]].float() * qf.to("cuda", torch.float32)[None, None, :, None]).to(torch.bfloat16)
-    q8, sq, k8, sk, qd, kd = _quantised(api, qs, k)
+    k8, sk, qd, kd = _quantised(api, qs, k)
     ref, ref_lse = oracle.attention(qd, kd, _np(v), wl.h, wl.w, s, s + 1, return_lse=True)
     for splits in (1, 4):
         ws = api.split_workspace(splits, 2, 2, n, 128) if splits > 1 else None
-        o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, s, s + 1, return_lse=True,
+        o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), qs, k8, sk, v, s, s + 1, return_lse=True,
                                          n_splits=splits, workspace=ws)
         _bars(_np(o), ref, f"e4m3 tile scales differ splits={splits}", _np(lse), ref_lse, lse_bar=LSE_PEAKED)
 
@@ -200,8 +210,8 @@ def test_dense_e4m3_multi_scale_call(api):
     """Queries of several scales in one call: each row sees keys up to the end of its own scale."""
     wl = custom_workload(SMALL, 1, 2, 128)
     q, k, v = make_qkv(wl, 72, device="cuda")
-    q8, sq, k8, sk, qd, kd = _quantised(api, q, k)
-    o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, 0, len(SMALL), return_lse=True)
+    k8, sk, qd, kd = _quantised(api, q, k)
+    o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), q, k8, sk, v, 0, len(SMALL), return_lse=True)
     ref, ref_lse = oracle.attention(qd, kd, _np(v), wl.h, wl.w, 0, len(SMALL), return_lse=True)
     _bars(_np(o), ref, "e4m3 all scales", _np(lse), ref_lse)
 
@@ -212,15 +222,14 @@ def test_dense_e4m3_var1024_last_step_sampled(api):
     off = oracle.offsets(wl.h, wl.w)
     s = len(wl.grids) - 1
     qs = q[:, :, off[s]:off[s + 1]]
-    q8, sq = api.var_quantize_e4m3(qs)
     k8, sk = api.var_quantize_e4m3(k)
-    o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, s, s + 1, return_lse=True)
+    o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), qs, k8, sk, v, s, s + 1, return_lse=True)
     n = off[s + 1] - off[s]
     rows = np.unique(np.concatenate([np.arange(0, n, 61), [n - 1]]))
     for b, h in [(0, 3), (1, 12)]:
         rq, rsq = quantize_tiles(_np(qs[b:b + 1, h:h + 1]))
         rk, rsk = quantize_tiles(_np(k[b:b + 1, h:h + 1]))
-        assert np.array_equal(q8[b, h].cpu().numpy(), rq[0, 0]) and np.array_equal(k8[b, h].cpu().numpy(), rk[0, 0])
+        assert np.array_equal(k8[b, h].cpu().numpy(), rk[0, 0])
         qd = dequantize_tiles(rq, rsq)
         kd = dequantize_tiles(rk, rsk)
         ref, ref_lse = oracle.attention(qd, kd, _np(v[b:b + 1, h:h + 1]), wl.h, wl.w, s, s + 1, rows=rows,
@@ -242,11 +251,11 @@ def test_block_sparse_e4m3_shared_and_per_head(api):
     off = oracle.offsets(wl.h, wl.w)
     s = 7
     qs = q[:, :, off[s]:off[s + 1]]
-    q8, sq, k8, sk, qd, kd = _quantised(api, qs, k)
+    k8, sk, qd, kd = _quantised(api, qs, k)
     mp = api.mask_params(64, 64, 2, 3, 1, 1)
     rp, ci = api.var_build_tile_mask((wl.h, wl.w), s, s + 1, mp)
     kept = oracle.tile_mask(wl.h, wl.w, s, s + 1, 64, 64, 2, 3, 1, 1)
-    o, lse = api.var_attn_block_sparse_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, s, s + 1, rp, ci, return_lse=True)
+    o, lse = api.var_attn_block_sparse_e4m3((wl.h, wl.w), qs, k8, sk, v, s, s + 1, rp, ci, return_lse=True)
     ref, ref_lse = oracle.attention(qd, kd, _np(v), wl.h, wl.w, s, s + 1, kept=kept, return_lse=True)
     _bars(_np(o), ref, "e4m3 sparse shared", _np(lse), ref_lse)
     # one CSR per (batch, head): random kept tiles per map
@@ -260,7 +269,7 @@ def test_block_sparse_e4m3_shared_and_per_head(api):
         rps[m, 1:] = np.cumsum([c.size for c in cols])
         flat = np.concatenate(cols) if rps[m, -1] else np.zeros(0, np.int32)
         cis[m, : flat.size] = flat
-    o2, lse2 = api.var_attn_block_sparse_e4m3((wl.h, wl.w), q8, sq, k8, sk, v, s, s + 1,
+    o2, lse2 = api.var_attn_block_sparse_e4m3((wl.h, wl.w), qs, k8, sk, v, s, s + 1,
                                               torch.from_numpy(rps).cuda(), torch.from_numpy(cis).cuda(),
                                               return_lse=True)
     vn = _np(v)
@@ -277,10 +286,10 @@ def test_block_sparse_e4m3_shared_and_per_head(api):
 def test_e4m3_rejects_wrong_dtypes(api):
     wl = custom_workload(SMALL, 1, 1, 128)
     q, k, v = make_qkv(wl, 76, device="cuda")
-    q8, sq = api.var_quantize_e4m3(q)
+    k8, sk = api.var_quantize_e4m3(k)
     with pytest.raises(ValueError):
-        api.var_attn_dense_e4m3((wl.h, wl.w), q, sq, q8, sq, v, 7, 8)
-    q64 = torch.zeros((1, 1, q.shape[2], 64), dtype=torch.uint8, device="cuda")
+        api.var_attn_dense_e4m3((wl.h, wl.w), q, k, sk, v, 7, 8)          # bf16 keys
+    k64 = torch.zeros((1, 1, q.shape[2], 64), dtype=torch.uint8, device="cuda")
     v64 = torch.zeros((1, 1, q.shape[2], 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(api.VarAttnError):
-        api.var_attn_dense_e4m3((wl.h, wl.w), q64, sq, q64, sq, v64, 7, 8)
+        api.var_attn_dense_e4m3((wl.h, wl.w), v64, k64, sk, v64, 7, 8)    # head_dim 64
