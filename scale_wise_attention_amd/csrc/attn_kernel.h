@@ -1,4 +1,5 @@
-// Block-causal next-scale attention, bf16 in / fp32 accumulate, for gfx950.
+// Block-causal next-scale attention for gfx950: bf16 (or e4m3 q / k, QK8)
+// in, fp32 accumulate.
 //
 // For every query row of the call: O = softmax(scale * q K^T) V over the keys
 // the row may see, i.e. all keys of its own and earlier scales ("SparVAR:
@@ -55,6 +56,13 @@
 //    them with log-sum-exp weights.
 //  * Workgroup ids are remapped so the query tiles of one (batch, head) run
 //    on one XCD and share its L2 for K and V.
+//  * QK8 (e4m3 logits, the low-bit data precision of "LiteVAR: Compressing
+//    Visual Autoregressive Modelling with Efficient Attention and
+//    Quantization"): K arrives as e4m3 codes with one scale per 64-key tile;
+//    each wave quantises its 64 bf16 query rows (one group, one scale) on
+//    load; S^T comes from v_mfma_f32_32x32x64_f8f6f4 (2 MFMAs per 32x32
+//    block), and the tile's log2-domain factor is the product of the two
+//    scales.  Weights, V and the rest are as above.
 #pragma once
 
 #include <hip/hip_runtime.h>
