@@ -111,6 +111,7 @@ def main():
               "see the sharding paragraph of the design notes)", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     from scale_wise_attention_amd import api
     from scale_wise_attention_amd import accounting as acc
@@ -170,6 +171,19 @@ def main():
         ws_bytes = max(ws_bytes, b_d, b_s)
     workspace = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device=dev)
 
+    # A step below the sink scale count sees keys of sink scales only, so its
+    # mask keeps every visible tile and the step is dense attention: the
+    # sparse generation runs the dense kernel there and builds no mask.
+    # (Checked here on the masks themselves.)
+    full_mask = []
+    for s in range(K):
+        rp_h, ci_h = csr[s][0].cpu().numpy(), csr[s][1].cpu().numpy()
+        n_kt_s = -(-off[s + 1] // 64)
+        full = bool(rp_h[-1] == (rp_h.size - 1) * n_kt_s and
+                    np.array_equal(ci_h[: rp_h[-1]], np.tile(np.arange(n_kt_s), rp_h.size - 1)))
+        assert full == (s < wl.sink_scales and csr[s][2] is None), f"step {s}: full mask {full}"
+        full_mask.append(full)
+
     def sparse_full_last_step():
         api.var_build_tile_mask(sched, K - 1, K, mp, row_ptr=full_rp, col_idx=full_ci)
         api.var_attn_block_sparse(sched, qsteps[K - 1], k, v, K - 1, K, full_rp, full_ci, out=full_out)
@@ -188,6 +202,14 @@ def main():
         api.var_attn_block_sparse(sched, qsteps[s], k, v, s, s + 1, rp, ci, out=out, q_index=idx,
                                   n_splits=sparse_splits[s], workspace=workspace)
 
+    def sparse_gen_step(s):
+        if full_mask[s]:
+            api.var_attn_dense(sched, qsteps[s], k, v, s, s + 1, out=sparse_out[s], n_splits=dense_splits[s],
+                               workspace=workspace)
+        else:
+            mask_step(s)
+            sparse_step(s)
+
     def scatter_step():
         api.var_scatter_restore(sparse_out[K - 2], wl.grids[K - 2], wl.grids[K - 2], pruned_out, sel_t,
                                 wl.grids[K - 1], wl.grids[K - 1], out=restored)
@@ -196,8 +218,7 @@ def main():
         for s in range(K):
             dense_step(s)
         for s in range(K):
-            mask_step(s)
-            sparse_step(s)
+            sparse_gen_step(s)
         scatter_step()
 
     # ---- algorithmic work ---------------------------------------------------
@@ -307,8 +328,7 @@ def main():
 
     def sparse_gen():
         for s in range(K):
-            mask_step(s)
-            sparse_step(s)
+            sparse_gen_step(s)
         scatter_step()
 
     sparse_gen_ms = time_launch(sparse_gen, reps=max(2, R // 4))
@@ -461,6 +481,7 @@ def main():
             "generation_tflops": round(sum(sparse_flops) / (sparse_gen_ms * 1e-3) / 1e12, 2),
             "per_step_attn_ms": [round(x, 4) for x in sparse_ms],
             "per_step_mask_ms": [round(x, 4) for x in mask_ms],
+            "full_mask_steps_run_dense": [s for s in range(K) if full_mask[s]],
             "last_step_pruned_attn_ms": round(sparse_ms[last], 4),
             "last_step_pruned_gflop": round(sparse_flops[last] / 1e9, 3),
             "scatter_ms": round(scatter_ms, 4),

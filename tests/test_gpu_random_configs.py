@@ -99,3 +99,52 @@ def test_random_sparse_calls(api, seed):
     kept = oracle.tile_mask(h, w, b, e, 64, 64, sink, local, ry, rx, q_index=sel)
     ref = oracle.attention(_np(qs), _np(k), _np(v), h, w, b, e, q_index=sel, kept=kept)
     _check(_np(o), ref, f"sparse seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_e4m3_calls(api, seed):
+    """e4m3 logits (head_dim 128) over random schedules, gathers, splits and masks: keys quantised by
+    the tile quantiser, queries in the call per 64 output rows; the oracle gets the same groups."""
+    from oracle.fp8 import dequantize_tiles, quantize_tiles
+    c = _case(300 + seed)
+    h, w, B, H, b, e, sel, splits = c["h"], c["w"], c["B"], c["H"], c["b"], c["e"], c["sel"], c["splits"]
+    rng = c["rng"]
+    sparse = bool(rng.random() < 0.4)
+    if sparse:
+        b, splits = e - 1, 1
+    off = oracle.offsets(h, w)
+    n_q = off[e] - off[b]
+    sel = None if sel is None or sel.max() >= n_q else rng.permutation(sel)   # gathers in any order
+    print(f"[e4m3 seed {seed}] grids {h}x{w} B={B} H={H} scales [{b},{e}) sel={None if sel is None else sel.size}"
+          f" splits={splits} sparse={sparse} bf16out={c['out_bf16']}", flush=True)
+    wl = custom_workload([1], B, H, 128)
+    q, k, v = make_qkv(wl, 90 + seed, device="cuda", grids_hw=list(zip(h, w)))
+    qs = q[:, :, off[b]:off[e]]
+    k8, sk = api.var_quantize_e4m3(k)
+    rk, rsk = quantize_tiles(_np(k))
+    assert np.array_equal(k8.cpu().numpy(), rk)
+    qn = _np(qs)
+    rows_q = qn if sel is None else qn[:, :, sel]
+    qd = np.zeros(qn.shape)
+    if sel is None:
+        qd = dequantize_tiles(*quantize_tiles(rows_q))
+    else:
+        qd[:, :, sel] = dequantize_tiles(*quantize_tiles(rows_q))
+    kd = dequantize_tiles(rk, rsk)
+    idx = None if sel is None else torch.from_numpy(sel.astype(np.int32)).cuda()
+    rows = n_q if sel is None else sel.size
+    odt = torch.bfloat16 if c["out_bf16"] else torch.float32
+    kept = None
+    if sparse:
+        K = len(h)
+        sink, local = int(rng.integers(0, K + 1)), int(rng.integers(0, K + 1))
+        ry, rx = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+        rp, ci = api.var_build_tile_mask((h, w), b, e, api.mask_params(64, 64, sink, local, ry, rx), q_index=idx)
+        kept = oracle.tile_mask(h, w, b, e, 64, 64, sink, local, ry, rx, q_index=sel)
+        o = api.var_attn_block_sparse_e4m3((h, w), qs, k8, sk, v, b, e, rp, ci, q_index=idx, out_dtype=odt)
+    else:
+        ws = api.split_workspace(splits, B, H, rows, 128) if splits > 1 else None
+        o = api.var_attn_dense_e4m3((h, w), qs, k8, sk, v, b, e, q_index=idx, out_dtype=odt, n_splits=splits,
+                                    workspace=ws)
+    ref = oracle.attention(qd, kd, _np(v), h, w, b, e, q_index=sel, kept=kept)
+    _check(_np(o), ref, f"e4m3 seed {seed}")
