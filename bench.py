@@ -427,6 +427,31 @@ def main():
     # dominant launch: the dense bf16 attention kernel on the last step (4096
     # queries x 10521 keys), which carries 61% of the pass's FLOPs
     last = K - 1
+    # its spread over single launches (events around each launch)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(40)]
+    for a, b_ in ev:
+        a.record()
+        dense_step(last)
+        b_.record()
+    torch.cuda.synchronize()
+    single_us = sorted(a.elapsed_time(b_) * 1e3 for a, b_ in ev)
+    # attainable bf16 matrix-core rate on this device: a large plain GEMM
+    # (hipBLASLt through torch.matmul, contiguous operands)
+    ga = torch.randn(8192, 8192, device=dev).to(bf)
+    gb = torch.randn(8192, 8192, device=dev).to(bf)
+    gc = torch.empty(8192, 8192, device=dev, dtype=bf)
+    for _ in range(3):
+        torch.matmul(ga, gb, out=gc)       # (eager: the library call stays out of graphs)
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for _ in range(10):
+        torch.matmul(ga, gb, out=gc)
+    g1.record()
+    torch.cuda.synchronize()
+    gemm_ms = g0.elapsed_time(g1) / 10
+    gemm_tflops = 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12
+    del ga, gb, gc
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
     last_tflops = dense_flops[last] / (dense_ms[last] * 1e-3) / 1e12
     achieved = last_tflops
     traffic = _read_traffic()
@@ -465,6 +490,12 @@ def main():
             "avg_launch_us": round(dense_ms[last] * 1e3, 2),
             "algorithmic_gflop_per_launch": round(dense_flops[last] / 1e9, 3),
             "algorithmic_hbm_bytes_per_launch": acc.dense_step_bytes(wl, last),
+            "single_launch_us_p10_p50_p90": [round(single_us[len(single_us) // 10], 1),
+                                             round(statistics.median(single_us), 1),
+                                             round(single_us[(9 * len(single_us)) // 10], 1)],
+            "peak_basis": f"{n_cu} CUs x 2.4 GHz x 4096 bf16 flop/clk",
+            "bf16_gemm_8192_tflops": round(gemm_tflops, 1),
+            "frac_of_gemm": round(achieved / gemm_tflops, 4),
         },
         "dense": {
             "generation_ms": round(dense_gen_ms, 4),
