@@ -406,6 +406,11 @@ def main():
     f8_quant_ms = [time_launch(lambda s=s: f8_quant(s)) for s in range(K)]
     f8_attn_ms = [time_launch(lambda s=s: f8_attn(s)) for s in range(K)]
     f8_quant_last_ms, f8_attn_last_ms = f8_quant_ms[K - 1], f8_attn_ms[K - 1]
+    bf_sparse_attn_ms = time_launch(lambda: api.var_attn_block_sparse(sched, qsteps[K - 1], k, v, K - 1, K, full_rp,
+                                                                      full_ci, out=full_out))
+    f8_sparse_out = torch.empty(B, H, 4096, D, dtype=bf, device=dev)
+    f8_sparse_ms = time_launch(lambda: api.var_attn_block_sparse_e4m3(sched, qsteps[K - 1], k8, sk8, v, K - 1, K,
+                                                                      full_rp, full_ci, out=f8_sparse_out))
     f8_gen_all_ms = time_launch(lambda: [(f8_quant(s), f8_attn(s)) for s in range(K)], reps=max(2, R // 4))
     # mixed generation: bf16 while a step's attention is a few microseconds
     # (there the key quantisation launch costs more than e4m3 saves), e4m3
@@ -558,6 +563,8 @@ def main():
             "last_step_attn_ms": round(f8_attn_last_ms, 4),
             "last_step_attn_tflops": round(dense_flops[last] / (f8_attn_last_ms * 1e-3) / 1e12, 2),
             "speedup_last_step_attn_vs_bf16": round(dense_ms[last] / f8_attn_last_ms, 3),
+            "last_step_sparse_attn_ms": round(f8_sparse_ms, 4),
+            "speedup_last_step_sparse_attn_vs_bf16_sparse": round(bf_sparse_attn_ms / f8_sparse_ms, 3),
             "per_step_key_quantize_ms": [round(x, 4) for x in f8_quant_ms],
             "per_step_attn_ms": [round(x, 4) for x in f8_attn_ms],
             "generation_all_steps_e4m3_ms": round(f8_gen_all_ms, 4),
