@@ -355,8 +355,12 @@ var_status var_attn_block_sparse_heads(const var_schedule* sched, const var_attn
  * one group with the rule of var_quantize_e4m3.  With qs the scale of the
  * group of output row i and m = b*heads + h, the logit of row i and key u is
  *   softmax_scale * qs * k_scale[m*k_scale_stride + u/64] * (q_codes . k_codes),
- * i.e. attention of the dequantised queries and keys; the products of codes
- * are summed exactly in fp32 by the matrix cores.
+ * i.e. attention of the dequantised queries and keys.  The e4m3 matrix
+ * instruction sums the 64 products of a k-step with a relative error of up
+ * to about 2^-12 of the sum of their magnitudes (measured on gfx950; not an
+ * exact fp32 sum), so a logit can move by about 2^-12 * softmax_scale * qs *
+ * ks * sum_d |q_d k_d|: around 3e-4 at softmax_scale = 1/sqrt(128) on unit
+ * data, below the bf16 rounding of the weights.
  *  desc   in_dtype must be VAR_BF16 (the dtype of q and v); head_dim 128;
  *         out_dtype f32 or bf16.
  *  k      device uint8 codes [B][H][>= kv_len][128], layout k_l (strides in

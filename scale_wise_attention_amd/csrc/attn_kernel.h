@@ -323,136 +323,9 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                 }
             } else {
                 qreg[qb][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * ks + 16 * g));
-                // Q is only ever an MFMA operand: keep it in AGPRs (MFMAs read
-                // them directly), which leaves the VGPRs to the softmax and the loads
-                asm volatile("" : "+a"(qreg[qb][ks]));
             }
         }
     }
-    if constexpr (QK8) {
-        // The wave's 64 rows are one 64-row tile of the call: quantise it to
-        // e4m3 with one scale (amax / 448; rows past n_rows repeat the last
-        // row and leave the maximum unchanged), in the operand layout.
-        uint32_t mx = 0u;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int ks = 0; ks < SK; ++ks)
-#pragma unroll
-                for (int c = 0; c < 4; ++c) mx = max(mx, bf16x8_absmax_bits(qraw[qb][ks][c]));
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, m));
-        const float amax = mx ? __uint_as_float(mx) : 1.0f;
-        const float inv = __fdiv_rn(448.0f, amax);
-        const float sq = __fdiv_rn(amax, 448.0f);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            c2q[qb] = p.scale_log2 * sq;
-#pragma unroll
-            for (int ks = 0; ks < SK; ++ks) {
-                uint32_t cw[8];
-#pragma unroll
-                for (int c = 0; c < 4; ++c) bf16x8_to_e4m3(qraw[qb][ks][c], inv, cw[2 * c], cw[2 * c + 1]);
-                qreg[qb][ks] = i32x8{(int)cw[0], (int)cw[1], (int)cw[2], (int)cw[3],
-                                     (int)cw[4], (int)cw[5], (int)cw[6], (int)cw[7]};
-                asm volatile("" : "+a"(qreg[qb][ks]));
-            }
-        }
-    }
-    const int w_kmin = __builtin_amdgcn_readfirstlane(wave_min_i(min(klim[0], klim[1])));
-    const int w_kmax = __builtin_amdgcn_readfirstlane(wave_max_i(max(klim[0], klim[1])));
-
-    // ---- key-tile walk (workgroup-uniform) ------------------------------
-    const int n_kt_all = (p.kv_len + KT - 1) / KT;
-    int dense_begin = 0, dense_end = 0;   // dense: tiles [dense_begin, dense_end)
-    int dense_next = 0;
-    int lbeg[NW], lptr[NW], lend[NW], lhead[NW];   // sparse: one list per wave's query tile
-    const int32_t* const rowp = p.row_ptr + bh * p.rp_bh_stride;   // this (batch, head)'s CSR
-    const int32_t* const coli = p.col_idx + bh * p.ci_bh_stride;
-    if constexpr (SPARSE) {
-        const int n_qt = (p.n_rows + KT - 1) / KT;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const int r = qtile * NW + w;
-            const int b0 = r < n_qt ? rowp[r] : 0;
-            const int cnt = r < n_qt ? rowp[r + 1] - b0 : 0;
-            // key split: an equal share of this row's kept tiles (in order; the
-            // host bounds cnt * n_splits below 2^31)
-            lbeg[w] = lptr[w] = p.n_splits > 1 ? b0 + cnt * split / p.n_splits : b0;
-            lend[w] = p.n_splits > 1 ? b0 + cnt * (split + 1) / p.n_splits : b0 + cnt;
-            lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
-        }
-    }
-    int wg_kmin;   // smallest key limit in the workgroup: tiles below it need no mask
-    {
-        int* red = reinterpret_cast<int*>(smem);
-        if (lane == 0) {
-            red[wave] = w_kmax;
-            red[NW + wave] = w_kmin;
-        }
-        __syncthreads();
-        int m = red[0], mn = red[NW];
-#pragma unroll
-        for (int i = 1; i < NW; ++i) {
-            m = max(m, red[i]);
-            mn = min(mn, red[NW + i]);
-        }
-        __syncthreads();
-        if constexpr (!SPARSE) {
-            const int n_t = (m + KT - 1) / KT;   // key split: an equal share of the tiles
-            dense_begin = p.n_splits > 1 ? __builtin_amdgcn_readfirstlane(n_t * split / p.n_splits) : 0;
-            dense_end = p.n_splits > 1 ? __builtin_amdgcn_readfirstlane(n_t * (split + 1) / p.n_splits) : n_t;
-            dense_next = dense_begin;
-        }
-        wg_kmin = __builtin_amdgcn_readfirstlane(mn);
-    }
-    auto next_tile = [&]() __attribute__((always_inline)) -> TileEnt {
-        TileEnt e;
-        if constexpr (SPARSE) {
-            int c = INT_MAX;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) c = min(c, lhead[w]);
-            e.tile = -1;
-            e.mask = 0;
-            if (c != INT_MAX) {
-#pragma unroll
-                for (int w = 0; w < NW; ++w) {
-                    if (lhead[w] == c) {
-                        e.mask |= 1 << w;
-                        ++lptr[w];
-                        lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
-                    }
-                }
-                // a column outside [0, n_kt) cannot come from the mask builder; clamp so loads stay in bounds
-                e.tile = min(max(c, 0), n_kt_all - 1);
-            }
-        } else {
-            e.tile = dense_next < dense_end ? dense_next : -1;
-            e.mask = (1 << NW) - 1;
-            ++dense_next;
-        }
-        e.ks = 1.f;
-        if constexpr (QK8) {
-            if (e.tile >= 0) e.ks = p.k_scale[bh * p.k_scale_stride + e.tile];
-        }
-        return e;
-    };
-    auto reset_walk = [&]() __attribute__((always_inline)) {
-        if constexpr (SPARSE) {
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                lptr[w] = lbeg[w];
-                lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
-            }
-        } else {
-            dense_next = dense_begin;
-        }
-    };
-    auto mine = [&](const TileEnt& e) __attribute__((always_inline)) -> bool {
-        if constexpr (SPARSE) return e.tile >= 0 && ((e.mask >> wave) & 1);
-        else return e.tile >= 0 && e.tile * KT < w_kmax;
-    };
-
     const unsigned char* kp = reinterpret_cast<const unsigned char*>(p.k) + (b * p.k_sb + h * p.k_sh) * EK;
     const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + h * p.v_sh;
     const int kv_last = p.kv_len - 1;
@@ -571,6 +444,151 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         for (int j = 0; j < V_PER_T; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) store_v_piece(slot, j, i);
+    };
+
+    // The first key tile of an unsplit dense walk is tile 0 (keys [0, 64),
+    // always present): its K DMA and V loads are issued now, so that their
+    // latency overlaps the Q loads' (a small step is little more than these
+    // two round trips).  The walk's prologue then skips them.
+    bool first_tile_preloaded = false;
+    if constexpr (!SPARSE) {
+        if (p.n_splits == 1) {
+            load_k(0, 0);
+            load_v(0);
+            first_tile_preloaded = true;
+        }
+    }
+    if constexpr (QK8) {
+        // The wave's 64 rows are one 64-row tile of the call: quantise it to
+        // e4m3 with one scale (amax / 448; rows past n_rows repeat the last
+        // row and leave the maximum unchanged), in the operand layout.
+        uint32_t mx = 0u;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int ks = 0; ks < SK; ++ks)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) mx = max(mx, bf16x8_absmax_bits(qraw[qb][ks][c]));
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, m));
+        const float amax = mx ? __uint_as_float(mx) : 1.0f;
+        const float inv = __fdiv_rn(448.0f, amax);
+        const float sq = __fdiv_rn(amax, 448.0f);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            c2q[qb] = p.scale_log2 * sq;
+#pragma unroll
+            for (int ks = 0; ks < SK; ++ks) {
+                uint32_t cw[8];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) bf16x8_to_e4m3(qraw[qb][ks][c], inv, cw[2 * c], cw[2 * c + 1]);
+                qreg[qb][ks] = i32x8{(int)cw[0], (int)cw[1], (int)cw[2], (int)cw[3],
+                                     (int)cw[4], (int)cw[5], (int)cw[6], (int)cw[7]};
+                asm volatile("" : "+a"(qreg[qb][ks]));
+            }
+        }
+    } else {
+        // Q is only ever an MFMA operand: keep it in AGPRs (MFMAs read them
+        // directly), which leaves the VGPRs to the softmax and the loads
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int ks = 0; ks < SK; ++ks) asm volatile("" : "+a"(qreg[qb][ks]));
+    }
+    const int w_kmin = __builtin_amdgcn_readfirstlane(wave_min_i(min(klim[0], klim[1])));
+    const int w_kmax = __builtin_amdgcn_readfirstlane(wave_max_i(max(klim[0], klim[1])));
+
+    // ---- key-tile walk (workgroup-uniform) ------------------------------
+    const int n_kt_all = (p.kv_len + KT - 1) / KT;
+    int dense_begin = 0, dense_end = 0;   // dense: tiles [dense_begin, dense_end)
+    int dense_next = 0;
+    int lbeg[NW], lptr[NW], lend[NW], lhead[NW];   // sparse: one list per wave's query tile
+    const int32_t* const rowp = p.row_ptr + bh * p.rp_bh_stride;   // this (batch, head)'s CSR
+    const int32_t* const coli = p.col_idx + bh * p.ci_bh_stride;
+    if constexpr (SPARSE) {
+        const int n_qt = (p.n_rows + KT - 1) / KT;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const int r = qtile * NW + w;
+            const int b0 = r < n_qt ? rowp[r] : 0;
+            const int cnt = r < n_qt ? rowp[r + 1] - b0 : 0;
+            // key split: an equal share of this row's kept tiles (in order; the
+            // host bounds cnt * n_splits below 2^31)
+            lbeg[w] = lptr[w] = p.n_splits > 1 ? b0 + cnt * split / p.n_splits : b0;
+            lend[w] = p.n_splits > 1 ? b0 + cnt * (split + 1) / p.n_splits : b0 + cnt;
+            lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
+        }
+    }
+    // workgroup reductions in LDS words of their own (a K DMA may be in flight)
+    __shared__ int wg_words[3 * NW];
+    int wg_kmin;   // smallest key limit in the workgroup: tiles below it need no mask
+    {
+        int* red = wg_words;
+        if (lane == 0) {
+            red[wave] = w_kmax;
+            red[NW + wave] = w_kmin;
+        }
+        __syncthreads();
+        int m = red[0], mn = red[NW];
+#pragma unroll
+        for (int i = 1; i < NW; ++i) {
+            m = max(m, red[i]);
+            mn = min(mn, red[NW + i]);
+        }
+        __syncthreads();
+        if constexpr (!SPARSE) {
+            const int n_t = (m + KT - 1) / KT;   // key split: an equal share of the tiles
+            dense_begin = p.n_splits > 1 ? __builtin_amdgcn_readfirstlane(n_t * split / p.n_splits) : 0;
+            dense_end = p.n_splits > 1 ? __builtin_amdgcn_readfirstlane(n_t * (split + 1) / p.n_splits) : n_t;
+            dense_next = dense_begin;
+        }
+        wg_kmin = __builtin_amdgcn_readfirstlane(mn);
+    }
+    auto next_tile = [&]() __attribute__((always_inline)) -> TileEnt {
+        TileEnt e;
+        if constexpr (SPARSE) {
+            int c = INT_MAX;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) c = min(c, lhead[w]);
+            e.tile = -1;
+            e.mask = 0;
+            if (c != INT_MAX) {
+#pragma unroll
+                for (int w = 0; w < NW; ++w) {
+                    if (lhead[w] == c) {
+                        e.mask |= 1 << w;
+                        ++lptr[w];
+                        lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
+                    }
+                }
+                // a column outside [0, n_kt) cannot come from the mask builder; clamp so loads stay in bounds
+                e.tile = min(max(c, 0), n_kt_all - 1);
+            }
+        } else {
+            e.tile = dense_next < dense_end ? dense_next : -1;
+            e.mask = (1 << NW) - 1;
+            ++dense_next;
+        }
+        e.ks = 1.f;
+        if constexpr (QK8) {
+            if (e.tile >= 0) e.ks = p.k_scale[bh * p.k_scale_stride + e.tile];
+        }
+        return e;
+    };
+    auto reset_walk = [&]() __attribute__((always_inline)) {
+        if constexpr (SPARSE) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                lptr[w] = lbeg[w];
+                lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
+            }
+        } else {
+            dense_next = dense_begin;
+        }
+    };
+    auto mine = [&](const TileEnt& e) __attribute__((always_inline)) -> bool {
+        if constexpr (SPARSE) return e.tile >= 0 && ((e.mask >> wave) & 1);
+        else return e.tile >= 0 && e.tile * KT < w_kmax;
     };
 
     // S^T of one 32-key half: s[qb] holds keys kb0 + 8(r/4) + 4g + (r%4) of query 32qb + n.
@@ -724,10 +742,12 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         TileEnt e0 = next_tile();
         TileEnt e1 = next_tile();
         TileEnt e2 = AHEAD == 2 ? next_tile() : TileEnt{-1, 0, 1.f};
+        const bool pre = first_tile_preloaded && e0.tile == 0;
+        first_tile_preloaded = false;
         if (e0.tile >= 0) {
-            load_k(e0.tile * KT, 0);
+            if (!pre) load_k(e0.tile * KT, 0);
             if constexpr (MODE == 0) {
-                load_v(e0.tile * KT);
+                if (!pre) load_v(e0.tile * KT);
                 store_v(0);
             }
         }
@@ -971,13 +991,15 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
             // tiles before it had a reference, needs the exact recompute
             bad |= !(ltot <= kSumLimit) || (mref[qb] == -INFINITY && ltot > 0.f);
         }
-        int* flag = reinterpret_cast<int*>(Kbuf);   // the walk ended on a barrier: LDS is idle
-        if (tid == 0) *flag = 0;
+        // one flag per wave, in words no walk overwrites: one barrier
+        int* flags = wg_words + 2 * NW;
+        const bool wave_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+        if (lane == 0) flags[wave] = wave_bad ? 1 : 0;
         __syncthreads();
-        if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) *flag = 1;
-        __syncthreads();
-        const int again = *flag;
-        __syncthreads();
+        int again = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) again |= flags[w];
+        again = __builtin_amdgcn_readfirstlane(again);
         if (again) {
             mref[0] = mref[1] = -INFINITY;
             walk(IntC<1>{});
