@@ -201,7 +201,7 @@ int32_t choose_splits(int64_t tasks, int64_t tiles, int64_t bh_rows, int32_t D, 
     for (int32_t s = 2; s <= varattn::kMaxSplits && tiles >= 2 * s; ++s) {
         const double cost = (double)rounds(tasks * s) * ((tiles + s - 1) / s) + 3.0 +
                             (double)s * bh_rows * D * 8.0 / 7.2e6;
-        if (cost < 0.95 * best) {
+        if (cost < 0.97 * best) {   // a split must win by 3% (the model's noise)
             best = cost;
             best_s = s;
         }
