@@ -1,8 +1,9 @@
 // e4m3 instantiations of the next-scale attention kernel (attn_kernel.h):
-// q and k as e4m3 codes with one scale per (batch, head) (the low-bit data
-// precision of "LiteVAR: Compressing Visual Autoregressive Modelling with
-// Efficient Attention and Quantization"), S^T on the e4m3 matrix cores; the
-// weights and v stay bf16, accumulation fp32, fp32 or bf16 output.
+// logits from e4m3 queries and keys (the low-bit data precision of "LiteVAR:
+// Compressing Visual Autoregressive Modelling with Efficient Attention and
+// Quantization"): keys as codes with one scale per 64-token tile, queries
+// quantised in the kernel per 64 rows of the call, S^T on the e4m3 matrix
+// cores; the weights and v stay bf16, accumulation fp32, fp32 or bf16 output.
 #include "attn_kernel.h"
 
 namespace varattn {

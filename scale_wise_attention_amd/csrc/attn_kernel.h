@@ -241,8 +241,9 @@ struct TileEnt {
     float ks;
 };
 
-// QK8: q and k are e4m3 codes with one scale per (batch, head) and S^T comes
-// from v_mfma_f32_32x32x64_f8f6f4 (64 keys deep per k-step); V stays bf16.
+// QK8: k is e4m3 codes with one scale per 64-key tile, each wave quantises
+// its 64 bf16 query rows to e4m3 (one scale), and S^T comes from
+// v_mfma_f32_32x32x64_f8f6f4 (64 deep per k-step); V stays bf16.
 template <int D, bool OUT_BF16, bool SPARSE, bool QK8>
 __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(const AttnParams p) {
     constexpr int NW = waves_per_wg<SPARSE>();   // waves per workgroup
