@@ -519,6 +519,11 @@ def main():
             "generation_ms": round(dense_gen_ms, 4),
             "generation_tflops": round(sum(dense_flops) / (dense_gen_ms * 1e-3) / 1e12, 2),
             "per_step_ms": [round(x, 4) for x in dense_ms],
+            # the small steps are bound by latency (launch, two memory round
+            # trips, one tile), far below both the HBM and the MFMA roofs
+            "per_step_algorithmic_mb": [round(acc.dense_step_bytes(wl, s_) / 1e6, 3) for s_ in range(K)],
+            "per_step_gbps": [round(acc.dense_step_bytes(wl, s_) / (dense_ms[s_] * 1e-3) / 1e9, 1) for s_ in range(K)],
+            "per_step_tflops": [round(dense_flops[s_] / (dense_ms[s_] * 1e-3) / 1e12, 2) for s_ in range(K)],
             "last_step_ms": round(dense_ms[last], 4),
             "last_step_gflop": round(dense_flops[last] / 1e9, 3),
             "last_step_tflops": round(last_tflops, 2),
