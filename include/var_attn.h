@@ -126,15 +126,18 @@ var_status var_attn_dense(const var_schedule* sched, const var_attn_desc* desc,
 
 /*
  * Key-split variants of var_attn_dense and var_attn_block_sparse, for launches
- * with fewer (batch, head, 256-row query tile) work items than the GPU has
- * compute units: the middle steps of a generation (the "SparVAR ..." and
+ * whose (batch, head, query tile) work items leave compute units idle in
+ * their last round: the middle steps of a generation (the "SparVAR ..." and
  * "ARVAR ..." pages above: each step attends to every earlier scale, so a
  * step's key range grows while its query grid is still small).  The result
  * is the same attention; only the order of the floating-point sums differs.
- * Each work item is split into n_splits parts, each taking an equal share of
- * its key tiles (dense) or of each 64-row mask row's kept tiles (sparse);
- * every part writes its rows' normalised O and LSE in fp32 to the workspace,
- * and a second launch combines them:
+ * The work items that fill whole rounds of the device's resident workgroups
+ * (compute units times workgroups per unit) run unsplit; each remaining item
+ * (every item, when there are fewer than one round's worth) is split into
+ * n_splits parts, each taking an equal share of its key tiles (dense) or of
+ * each 64-row mask row's kept tiles (sparse); every part writes its rows'
+ * normalised O and LSE in fp32 to the workspace, and a second launch combines
+ * them:
  *   O = sum_s exp(LSE_s - M) O_s / sum_s exp(LSE_s - M),  LSE = M + log(sum ...),
  *   M = max_s LSE_s  (a part in which a row sees no key has LSE_s = -inf).
  *  n_splits  1..8; 1 is exactly var_attn_dense / var_attn_block_sparse (the
@@ -164,8 +167,9 @@ var_status var_attn_block_sparse_split(const var_schedule* sched, const var_attn
 /*
  * Split count for a call (host only; reads the current device's compute-unit
  * count, 256 if it cannot): the count with the smallest modelled time
- * (rounds of work items over the compute units times key tiles per part, plus
- * the combining launch and its workspace traffic).  kv_tiles_hint: 64-key
+ * (the unsplit rounds, then rounds of parts over the resident workgroups
+ * times key tiles per part, plus the combining launch and its workspace
+ * traffic).  kv_tiles_hint: 64-key
  * tiles a work item visits (0 = ceil(kv_len / 64), the dense count; pass the
  * mean kept tiles per mask row for a sparse call).  Writes *n_splits and the
  * workspace bytes it needs (either pointer may be NULL).  n_sel as in

@@ -8,6 +8,11 @@
 
 namespace varattn {
 
+int attn_fp8_resident_wgs(bool out_bf16, bool sparse) {
+    if (sparse) return out_bf16 ? resident_wgs<128, true, true, true>() : resident_wgs<128, false, true, true>();
+    return out_bf16 ? resident_wgs<128, true, false, true>() : resident_wgs<128, false, false, true>();
+}
+
 hipError_t launch_attn_fp8(const AttnParams& p, int D, bool out_bf16, bool sparse, hipStream_t s) {
     if (D != 128) return hipErrorInvalidValue;   // the host layer admits head_dim 128 only
     if (sparse) return out_bf16 ? launch_one<128, true, true, true>(p, s) : launch_one<128, false, true, true>(p, s);

@@ -51,9 +51,11 @@
 //  * Block-sparse: a workgroup's 2 waves cover 2 consecutive 64-row query
 //    tiles; the workgroup walks the merged (union) list of their kept key
 //    tiles and each wave takes only the tiles of its own list.
-//  * Key splits (n_splits > 1): each workgroup takes an equal share of its
-//    key tiles and writes fp32 partial O and LSE; split_merge_kernel combines
-//    them with log-sum-exp weights.
+//  * Key splits (n_splits > 1): the work items that fill whole rounds of the
+//    device's resident workgroups run unsplit; each remaining item runs as
+//    n_splits workgroups, each with an equal share of its key tiles, which
+//    write fp32 partial O and LSE; split_merge_kernel combines them with
+//    log-sum-exp weights.
 //  * Workgroup ids are remapped so the query tiles of one (batch, head) run
 //    on one XCD and share its L2 for K and V.
 //  * QK8 (e4m3 logits, the low-bit data precision of "LiteVAR: Compressing
@@ -93,12 +95,29 @@ constexpr int waves_per_wg() { return SPARSE ? 2 : 4; }
 constexpr int KT = 64;                 // keys per tile (= sparse tile width)
 constexpr float kSumLimit = 0x1p100f;  // a row sum above this triggers the exact recompute
 
-__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
-    // The dispatcher places workgroup i on XCD i % 8.  Give each XCD a
-    // contiguous range of work items so neighbours share an L2.
-    const int q = nwg >> 3, r = nwg & 7;
+// Work of workgroup wg (of nwg): work item `item`, key split `split`, and
+// whether the item runs whole.  Items below split_from run whole; every later
+// item runs as `splits` pieces (pieces of one item are consecutive).  The
+// dispatcher places workgroup i on XCD i % 8 and starts an XCD's workgroups in
+// order, so each XCD takes an equal share of the whole items first and then an
+// equal share of the pieces, each share a contiguous range: neighbouring items
+// belong to one (batch, head) and share its K and V in that XCD's L2.
+__device__ __forceinline__ void decode_work(int wg, int nwg, int split_from, int splits, int& item, int& split,
+                                            bool& whole) {
     const int x = wg & 7, j = wg >> 3;
-    return x * q + (x < r ? x : r) + j;
+    const int fq = split_from >> 3, fr = split_from & 7;
+    const int n_whole = fq + (x < fr ? 1 : 0);   // whole items on this XCD
+    if (j < n_whole) {
+        item = x * fq + min(x, fr) + j;
+        split = 0;
+        whole = true;
+        return;
+    }
+    const int q = nwg >> 3, r = nwg & 7;
+    const int piece = x * (q - fq) + min(x, r) - min(x, fr) + (j - n_whole);
+    item = split_from + piece / splits;
+    split = piece - (piece / splits) * splits;
+    whole = false;
 }
 
 __device__ __forceinline__ int wave_min_i(int v) {
@@ -278,11 +297,11 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     const int g = lane >> 5;      // lane half
     const int n = lane & 31;      // column inside a 32-query block
 
-    // work item = (batch, head, query tile, key split); the splits of one query
-    // tile are neighbours, so they run on the same XCD
-    const int item_s = xcd_remap(blockIdx.x, gridDim.x);
-    const int split = p.n_splits > 1 ? item_s % p.n_splits : 0;
-    const int item = p.n_splits > 1 ? item_s / p.n_splits : item_s;
+    // work item = (batch, head, query tile), whole or one of its key splits
+    int item, split;
+    bool whole;
+    decode_work(blockIdx.x, gridDim.x, p.split_from, p.n_splits, item, split, whole);
+    const int n_sp = whole ? 1 : p.n_splits;
     const int qtile = item % p.n_qtiles;
     const int bh = item / p.n_qtiles;
     const int b = bh / p.H;
@@ -453,7 +472,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     // two round trips).  The walk's prologue then skips them.
     bool first_tile_preloaded = false;
     if constexpr (!SPARSE) {
-        if (p.n_splits == 1) {
+        if (whole) {
             load_k(0, 0);
             load_v(0);
             first_tile_preloaded = true;
@@ -515,8 +534,8 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
             const int cnt = r < n_qt ? rowp[r + 1] - b0 : 0;
             // key split: an equal share of this row's kept tiles (in order; the
             // host bounds cnt * n_splits below 2^31)
-            lbeg[w] = lptr[w] = p.n_splits > 1 ? b0 + cnt * split / p.n_splits : b0;
-            lend[w] = p.n_splits > 1 ? b0 + cnt * (split + 1) / p.n_splits : b0 + cnt;
+            lbeg[w] = lptr[w] = n_sp > 1 ? b0 + cnt * split / n_sp : b0;
+            lend[w] = n_sp > 1 ? b0 + cnt * (split + 1) / n_sp : b0 + cnt;
             lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
         }
     }
@@ -539,8 +558,8 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         __syncthreads();
         if constexpr (!SPARSE) {
             const int n_t = (m + KT - 1) / KT;   // key split: an equal share of the tiles
-            dense_begin = p.n_splits > 1 ? __builtin_amdgcn_readfirstlane(n_t * split / p.n_splits) : 0;
-            dense_end = p.n_splits > 1 ? __builtin_amdgcn_readfirstlane(n_t * (split + 1) / p.n_splits) : n_t;
+            dense_begin = n_sp > 1 ? __builtin_amdgcn_readfirstlane(n_t * split / n_sp) : 0;
+            dense_end = n_sp > 1 ? __builtin_amdgcn_readfirstlane(n_t * (split + 1) / n_sp) : n_t;
             dense_next = dense_begin;
         }
         wg_kmin = __builtin_amdgcn_readfirstlane(mn);
@@ -1018,7 +1037,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
 
     // ---- epilogue --------------------------------------------------------
     unsigned char* ob = reinterpret_cast<unsigned char*>(p.o);
-    const bool partial = p.n_splits > 1;   // write this split's normalised O and LSE (fp32) for the merge
+    const bool partial = !whole;   // write this split's normalised O and LSE (fp32) for the merge
     const int64_t part_row0 = ((int64_t)split * p.B * p.H + b * p.H + h) * p.n_rows;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -1059,21 +1078,26 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     }
 }
 
-// Combination of the key splits of one launch: per row, O = sum_s w_s O_s /
-// sum_s w_s and LSE = M + log(sum_s w_s) with w_s = exp(LSE_s - M), M the
-// largest LSE_s (a split in which the row sees no key has LSE_s = -inf and
-// weight 0).  One thread per 4 output columns of a row.
+// Combination of the key splits of one launch: per row of a split item, O =
+// sum_s w_s O_s / sum_s w_s and LSE = M + log(sum_s w_s) with w_s =
+// exp(LSE_s - M), M the largest LSE_s (a split in which the row sees no key
+// has LSE_s = -inf and weight 0).  One thread per 4 output columns of a row;
+// the threads cover items [split_from, items) only, rows_per_item rows each.
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, int D) {
+__global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, int D, int rows_per_item) {
     const int cpr = D / 4;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)p.B * p.H * p.n_rows * cpr;
-    if (idx >= total) return;
+    const int64_t items = (int64_t)p.n_qtiles * p.B * p.H;
+    if (idx >= (items - p.split_from) * rows_per_item * cpr) return;
     const int c = (int)(idx % cpr);
-    const int64_t rr = idx / cpr;
-    const int row = (int)(rr % p.n_rows);
-    const int bh = (int)(rr / p.n_rows);
+    const int64_t t = idx / cpr;
+    const int item = p.split_from + (int)(t / rows_per_item);
+    const int qtile = item % p.n_qtiles;
+    const int bh = item / p.n_qtiles;
+    const int row = qtile * rows_per_item + (int)(t % rows_per_item);
+    if (row >= p.n_rows) return;
     const int b = bh / p.H, h = bh - b * p.H;
+    const int64_t rr = (int64_t)bh * p.n_rows + row;
     const int64_t plane = (int64_t)p.B * p.H * p.n_rows;
     float m = -INFINITY;
     for (int s = 0; s < p.n_splits; ++s) m = __builtin_fmaxf(m, p.part_lse[s * plane + rr]);
@@ -1102,14 +1126,33 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, in
     if (p.lse && c == 0) p.lse[rr] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
 }
 
+// Workgroups of one instantiation that a compute unit holds at once (1 when
+// the runtime cannot say).
+template <int D, bool OB, bool SP, bool QK8>
+int resident_wgs() {
+    static const int n = [] {
+        int k = 0;
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &k, attn_kernel<D, OB, SP, QK8>, waves_per_wg<SP>() * 64, 0);
+        if (e != hipSuccess) (void)hipGetLastError();
+        return e == hipSuccess && k > 0 ? k : 1;
+    }();
+    return n;
+}
+
+// The host bounds split_from + (items - split_from) * n_splits below 2^31 and
+// sets split_from = items when n_splits == 1.
 template <int D, bool OB, bool SP, bool QK8>
 hipError_t launch_one(const AttnParams& p, hipStream_t s) {
-    const int grid = p.n_qtiles * p.B * p.H * p.n_splits;
+    const int items = p.n_qtiles * p.B * p.H;
+    const int grid = p.split_from + (items - p.split_from) * p.n_splits;
     hipLaunchKernelGGL((attn_kernel<D, OB, SP, QK8>), dim3(grid), dim3(waves_per_wg<SP>() * 64), 0, s, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.n_splits == 1) return e;
-    const int64_t threads = (int64_t)p.B * p.H * p.n_rows * (D / 4);
-    hipLaunchKernelGGL((split_merge_kernel<OB>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p, D);
+    if (e != hipSuccess || p.split_from == items) return e;
+    constexpr int QT = waves_per_wg<SP>() * QW;
+    const int64_t threads = (int64_t)(items - p.split_from) * QT * (D / 4);
+    hipLaunchKernelGGL((split_merge_kernel<OB>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p, D,
+                       QT);
     return hipGetLastError();
 }
 

@@ -34,11 +34,14 @@ struct AttnParams {
     float scale;         // softmax scale
     float scale_log2;    // scale * log2(e)
     int32_t scale_end[VAR_MAX_SCALES];  // off[s + 1]
-    // key splits (bf16 kernel): with n_splits > 1 each workgroup takes an equal
-    // share of its key tiles and writes fp32 O and LSE to part_o
+    // key splits (bf16 kernel): work items (batch, head, query tile), numbered
+    // bh * n_qtiles + tile, below split_from run whole; with n_splits > 1 each
+    // later item runs as n_splits workgroups, each taking an equal share of
+    // its key tiles and writing fp32 O and LSE to part_o
     // [n_splits][B*H][n_rows][D] / part_lse [n_splits][B*H][n_rows]; a merge
-    // launch then writes o and lse
+    // launch then writes their o and lse.  n_splits == 1: split_from = items.
     int32_t n_splits;
+    int32_t split_from;
     float* part_o;
     float* part_lse;
     // per-(batch, head) CSR (block-sparse): element strides between the maps'
@@ -177,6 +180,10 @@ hipError_t launch_zero_i32(int32_t* p, hipStream_t s);
 
 // Query-tile height of the bf16 kernels (rows per workgroup).
 int attn_bf16_rows_per_tile(int head_dim, bool sparse);
+// Workgroups of the bf16 / e4m3 attention kernel that one compute unit holds
+// at once (from the runtime's occupancy query; 1 when it cannot say).
+int attn_bf16_resident_wgs(int head_dim, bool out_bf16, bool sparse);
+int attn_fp8_resident_wgs(bool out_bf16, bool sparse);
 constexpr int kF32RowsPerTile = 64;
 
 }  // namespace varattn

@@ -188,19 +188,40 @@ int device_cu_count() {
     return 256;
 }
 
+// Items of a key-split launch: those that fill whole rounds of the device's
+// resident workgroups run unsplit (split_from); only the remaining partial
+// round is split (every item when there are fewer than one round's worth).
+// Checks that the launch grid stays below 2^31.
+var_status set_split_items(varattn::AttnParams* p, int resident_per_cu) {
+    const int64_t items = (int64_t)p->n_qtiles * p->B * p->H;
+    int64_t from = items;
+    if (p->n_splits > 1) {
+        const int64_t cap = (int64_t)device_cu_count() * resident_per_cu;
+        from = items / cap * cap;
+    }
+    if (from + (items - from) * p->n_splits >= ((int64_t)1 << 31)) return fail(VAR_ERR_RANGE, "launch grid too large");
+    p->split_from = (int32_t)from;
+    return VAR_OK;
+}
+
 // Split count with the smallest modelled time, in units of one 64-key
-// iteration of a workgroup (about 1.8 us on MI355X at the 1024px shapes):
-// waves of workgroups over the compute units times the iterations per split,
-// plus, when split, the merge: a launch (about 3 iterations) and the partial
-// O written and read back (8 bytes per element; about 7 MB per iteration at
-// the bandwidth these small launches reach).
-int32_t choose_splits(int64_t tasks, int64_t tiles, int64_t bh_rows, int32_t D, int n_cu) {
-    auto rounds = [&](int64_t n) { return (n + n_cu - 1) / n_cu; };
+// iteration of a workgroup (about 1.8 us on MI355X at the 1024px shapes).
+// The items that fill whole rounds of the `cap` resident workgroups run
+// unsplit, a round taking `tiles` iterations; the rest, split s ways, take
+// their rounds of ceil(tiles / s) iterations, plus the merge: a launch (about
+// 3 iterations) and the split items' partial O written and read back (8 bytes
+// per element; about 7 MB per iteration at the bandwidth these small launches
+// reach).
+int32_t choose_splits(int64_t tasks, int64_t tiles, int64_t bh_rows, int32_t D, int64_t cap) {
+    auto rounds = [&](int64_t n) { return (n + cap - 1) / cap; };
+    const int64_t whole = tasks / cap * cap, rest = tasks - whole;
     double best = (double)rounds(tasks) * tiles;
     int32_t best_s = 1;
+    if (rest == 0) return 1;
+    const double rest_rows = (double)bh_rows * rest / tasks;
     for (int32_t s = 2; s <= varattn::kMaxSplits && tiles >= 2 * s; ++s) {
-        const double cost = (double)rounds(tasks * s) * ((tiles + s - 1) / s) + 3.0 +
-                            (double)s * bh_rows * D * 8.0 / 7.2e6;
+        const double cost = (double)(whole / cap) * tiles + (double)rounds(rest * s) * ((tiles + s - 1) / s) + 3.0 +
+                            (double)s * rest_rows * D * 8.0 / 7.2e6;
         if (cost < 0.97 * best) {   // a split must win by 3% (the model's noise)
             best = cost;
             best_s = s;
@@ -285,16 +306,17 @@ var_status dense_impl(const var_schedule* sched, const var_attn_desc* desc, cons
         attach_e4m3(&p, *e4m3);
         const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false);
         p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
-        if ((int64_t)p.n_qtiles * p.B * p.H * p.n_splits >= ((int64_t)1 << 31))
-            return fail(VAR_ERR_RANGE, "launch grid too large");
+        if ((st = set_split_items(&p, varattn::attn_fp8_resident_wgs(desc->out_dtype == VAR_BF16, false))) != VAR_OK)
+            return st;
         return hip_status(varattn::launch_attn_fp8(p, desc->head_dim, desc->out_dtype == VAR_BF16, false, s),
                           "var_attn_dense_e4m3 launch");
     }
     if (desc->in_dtype == VAR_BF16) {
         const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false);
         p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
-        if ((int64_t)p.n_qtiles * p.B * p.H * p.n_splits >= ((int64_t)1 << 31))
-            return fail(VAR_ERR_RANGE, "launch grid too large");
+        const bool ob = desc->out_dtype == VAR_BF16;
+        if ((st = set_split_items(&p, varattn::attn_bf16_resident_wgs(desc->head_dim, ob, false))) != VAR_OK)
+            return st;
         return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, desc->out_dtype == VAR_BF16, false, s),
                           "var_attn_dense launch");
     }
@@ -335,8 +357,10 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
         // each workgroup covers a whole number of 64-row tiles of the mask
         const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, true);
         p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
-        if ((int64_t)p.n_qtiles * p.B * p.H * p.n_splits >= ((int64_t)1 << 31))
-            return fail(VAR_ERR_RANGE, "launch grid too large");
+        const bool ob = desc->out_dtype == VAR_BF16;
+        const int resident = e4m3 ? varattn::attn_fp8_resident_wgs(ob, true)
+                                  : varattn::attn_bf16_resident_wgs(desc->head_dim, ob, true);
+        if ((st = set_split_items(&p, resident)) != VAR_OK) return st;
         if (e4m3) {
             attach_e4m3(&p, *e4m3);
             return hip_status(varattn::launch_attn_fp8(p, desc->head_dim, desc->out_dtype == VAR_BF16, true, s),
@@ -566,7 +590,9 @@ VAR_EXPORT var_status var_attn_split_plan(const var_schedule* sched, const var_a
         const int rpt = varattn::attn_bf16_rows_per_tile(d->head_dim, false);
         const int64_t tasks = bh * ((rows + rpt - 1) / rpt);
         const int64_t tiles = kv_tiles_hint > 0 ? kv_tiles_hint : (off.off[d->q_scale_end] + 63) / 64;
-        s = choose_splits(tasks, tiles, bh * rows, d->head_dim, device_cu_count());
+        const int64_t cap =
+            (int64_t)device_cu_count() * varattn::attn_bf16_resident_wgs(d->head_dim, d->out_dtype == VAR_BF16, false);
+        s = choose_splits(tasks, tiles, bh * rows, d->head_dim, cap);
     }
     if (n_splits) *n_splits = s;
     if (workspace_bytes) *workspace_bytes = split_workspace_bytes(s, bh, rows, d->head_dim);

@@ -49,7 +49,9 @@ def test_dense_split_steps_match_oracle(api, step, splits):
                                 workspace=_ws(api, splits, q, n))
     rows = np.unique(np.concatenate([np.arange(0, n, max(1, n // 61)), [n - 1]]))
     qn, kn, vn = _np(qs), _np(k), _np(v)
-    for (b, h) in [(0, 0), (1, 9)]:
+    # (1, 12) and (1, 15): at step 11 (288 work items) the items past the
+    # device's first round run split, the earlier ones whole
+    for (b, h) in [(0, 0), (1, 9), (1, 12), (1, 15)]:
         ref, ref_lse = oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1],
                                         wl.h, wl.w, step, step + 1, rows=rows, return_lse=True)
         _check(_np(o[b:b + 1, h:h + 1])[:, :, rows], ref, f"dense step {step} x{splits} b{b} h{h}")
@@ -70,6 +72,38 @@ def test_dense_split_bf16_output_matches_unsplit(api):
         d = (got - base).abs()
         print(f"[split vs unsplit] max {float(d.max()):.3e} mean {float(d.mean()):.3e}", flush=True)
         assert float(d.max()) <= 1e-2 and float(d.mean()) <= 1e-3
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_dense_whole_and_split_items(api, out_dtype):
+    """The 48x48 step: 9 query tiles x 32 (batch, head) = 288 work items, more
+    than one round of a 256-CU device.  The items of the whole rounds run
+    unsplit and write O directly; the rest run as 8 key splits and are merged.
+    The workspace starts as NaN, so a merge over a whole item's rows, or a
+    whole item's partial read back, shows as NaN.  Every row is compared with
+    the unsplit launch, and rows of every (batch, head) with the oracle."""
+    wl = WORKLOADS["var1024"]
+    q, k, v = make_qkv(wl, 8, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    s = 11
+    n = off[s + 1] - off[s]
+    qs = q[:, :, off[s]:off[s + 1]]
+    base, base_lse = api.var_attn_dense((wl.h, wl.w), qs, k, v, s, s + 1, out_dtype=out_dtype, return_lse=True)
+    ws = _ws(api, 8, q, n).fill_(float("nan"))
+    for rep in range(2):      # a second call over the first one's workspace
+        o, lse = api.var_attn_dense((wl.h, wl.w), qs, k, v, s, s + 1, out_dtype=out_dtype, return_lse=True,
+                                    n_splits=8, workspace=ws)
+        assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+        d = (o.float() - base.float()).abs()
+        print(f"[whole+split vs unsplit {out_dtype} call {rep}] max {float(d.max()):.3e} "
+              f"mean {float(d.mean()):.3e}", flush=True)
+        assert float(d.max()) <= 1e-2 and float(d.mean()) <= 1e-3
+        assert float((lse - base_lse).abs().max()) <= 2.5e-3
+    rows = np.unique(np.concatenate([np.arange(3, n, 97), [n - 1]]))
+    qn, kn, vn = _np(qs), _np(k), _np(v)
+    ref, ref_lse = oracle.attention(qn, kn, vn, wl.h, wl.w, s, s + 1, rows=rows, return_lse=True)
+    _check(_np(o)[:, :, rows], ref, f"whole+split x8 {out_dtype}")
+    assert np.max(np.abs(_np(lse)[:, :, rows] - ref_lse)) <= 2.5e-3
 
 
 def test_full_sequence_split_rows_with_empty_parts(api):
