@@ -171,7 +171,9 @@ var_status var_attn_block_sparse_split(const var_schedule* sched, const var_attn
  * times key tiles per part, plus the combining launch and its workspace
  * traffic).  kv_tiles_hint: 64-key
  * tiles a work item visits (0 = ceil(kv_len / 64), the dense count; pass the
- * mean kept tiles per mask row for a sparse call).  Writes *n_splits and the
+ * mean kept tiles per mask row for a sparse call; the model still counts the
+ * dense kernel's work items, 256 query rows each, one workgroup per compute
+ * unit, so for sparse calls it is a rougher guide).  Writes *n_splits and the
  * workspace bytes it needs (either pointer may be NULL).  n_sel as in
  * var_attn_dense (0 = no gather).  f32 input always gives 1 and 0 bytes.
  */
