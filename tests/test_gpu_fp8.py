@@ -246,6 +246,39 @@ def test_dense_e4m3_var1024_last_step_sampled(api):
         assert qerr.mean() <= 1e-2
 
 
+def test_dense_e4m3_whole_and_split_items(api):
+    """The 1024px 48x48 step (288 work items) with 6 key splits: on a 256-CU
+    device the items of the first round run whole and the rest split.  Every
+    row is compared with the unsplit launch (the workspace starts as NaN),
+    and rows of heads on both sides of the boundary with the oracle."""
+    wl = WORKLOADS["var1024"]
+    q, k, v = make_qkv(wl, 74, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    s = 11
+    n = off[s + 1] - off[s]
+    qs = q[:, :, off[s]:off[s + 1]]
+    kc = k[:, :, :off[s + 1]]
+    k8, sk = api.var_quantize_e4m3(kc)
+    base, base_lse = api.var_attn_dense_e4m3((wl.h, wl.w), qs, k8, sk, v, s, s + 1, return_lse=True)
+    ws = api.split_workspace(6, 2, 16, n, 128).fill_(float("nan"))
+    o, lse = api.var_attn_dense_e4m3((wl.h, wl.w), qs, k8, sk, v, s, s + 1, return_lse=True, n_splits=6,
+                                     workspace=ws)
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    d = (o.float() - base.float()).abs()
+    print(f"[e4m3 whole+split vs unsplit] max {float(d.max()):.3e} mean {float(d.mean()):.3e}", flush=True)
+    assert float(d.max()) <= 1e-2 and float(d.mean()) <= 1e-3
+    assert float((lse - base_lse).abs().max()) <= 2.5e-3
+    rows = np.unique(np.concatenate([np.arange(5, n, 71), [n - 1]]))
+    for b, h in [(0, 1), (1, 12), (1, 15)]:
+        rq, rsq = quantize_tiles(_np(qs[b:b + 1, h:h + 1]))
+        rk, rsk = quantize_tiles(_np(kc[b:b + 1, h:h + 1]))
+        ref, ref_lse = oracle.attention(dequantize_tiles(rq, rsq), dequantize_tiles(rk, rsk),
+                                        _np(v[b:b + 1, h:h + 1]), wl.h, wl.w, s, s + 1, rows=rows,
+                                        return_lse=True)
+        _bars(_np(o[b:b + 1, h:h + 1])[:, :, rows], ref, f"e4m3 48x48 x6 b{b} h{h}",
+              _np(lse[b:b + 1, h:h + 1])[:, :, rows], ref_lse)
+
+
 def test_block_sparse_e4m3_shared_and_per_head(api):
     wl = custom_workload(SMALL, 2, 2, 128)
     q, k, v = make_qkv(wl, 74, device="cuda")
