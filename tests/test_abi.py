@@ -217,6 +217,9 @@ def test_split_validation_and_plan(api):
     n, nbytes = api.var_attn_split_plan((W1024, W1024), 9, 10, 2, 16, 128)
     assert n > 1 and nbytes == n * 32 * 1024 * 129 * 4  # 128 work items of 40 key tiles
     assert api.var_attn_split_plan((W1024, W1024), 9, 10, 2, 16, 64, dtype=torch.float32) == (1, 0)
+    # 288 work items: one whole round of 256 plus 32 items of 101 key tiles that the split spreads
+    n, nbytes = api.var_attn_split_plan((W1024, W1024), 11, 12, 2, 16, 128)
+    assert n >= 4 and nbytes == n * 32 * 2304 * 129 * 4
     sp = api.LIB.var_attn_block_sparse_split
     r = sp(ctypes.byref(s), ctypes.byref(d), P(FAKE), L, P(FAKE), L, P(FAKE), L, P(FAKE), L, P(0), P(0), 0,
            P(FAKE), P(FAKE), 64, 64, 9, P(FAKE), 1 << 40, P(0))
