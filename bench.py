@@ -10,7 +10,9 @@ B=2 (CFG cond + uncond), H=16, D=128, bf16 in, fp32 accumulate, bf16 out):
      7 sink scales, window radius 2) is built on the device and the sparse
      kernel walks it; the last step keeps a seeded 40 % subset of its 4096
      queries (fused gather), and its outputs are scattered over the
-     nearest-upsampled 48x48 output of the previous step.
+     nearest-upsampled 48x48 output of the previous step.  The masks depend
+     on positions only, so they are built on a second stream from the start
+     of the sparse generation, overlapping its steps.
 
 The pass is captured once into a HIP graph and replayed (launch overhead of
 the 13+28 launches off the host); every kernel of the pass runs in every
@@ -210,6 +212,32 @@ def main():
             mask_step(s)
             sparse_step(s)
 
+    # The masks depend on positions (and, for the last step, the retained
+    # index list) only, so the sparse generation builds them on a second
+    # stream (default priority) from its start, in step order, while the
+    # steps run; each sparse step waits for its own mask.  The fork from the
+    # launch stream also orders them after every earlier use of the CSR
+    # buffers.
+    mask_stream = torch.cuda.Stream()
+
+    def sparse_gen_steps_overlapped():
+        main = torch.cuda.current_stream()
+        mask_stream.wait_stream(main)
+        ready = {}
+        with torch.cuda.stream(mask_stream):
+            for s in range(K):
+                if not full_mask[s]:
+                    mask_step(s)
+                    ready[s] = torch.cuda.Event()
+                    ready[s].record(mask_stream)
+        for s in range(K):
+            if full_mask[s]:
+                api.var_attn_dense(sched, qsteps[s], k, v, s, s + 1, out=sparse_out[s], n_splits=dense_splits[s],
+                                   workspace=workspace)
+            else:
+                main.wait_event(ready[s])
+                sparse_step(s)
+
     def scatter_step():
         api.var_scatter_restore(sparse_out[K - 2], wl.grids[K - 2], wl.grids[K - 2], pruned_out, sel_t,
                                 wl.grids[K - 1], wl.grids[K - 1], out=restored)
@@ -217,13 +245,25 @@ def main():
     def run_pass():
         for s in range(K):
             dense_step(s)
-        for s in range(K):
-            sparse_gen_step(s)
+        sparse_gen_steps_overlapped()
         scatter_step()
 
     # ---- algorithmic work ---------------------------------------------------
+    # (the sparse outputs of the pass, with its masks on the second stream,
+    # must equal those of the same steps with each mask built inline)
+    for s in range(K):
+        sparse_gen_step(s)
+    torch.cuda.synchronize()
+    inline_outs = [t.clone() for t in sparse_out] + [pruned_out.clone()]
     run_pass()
     torch.cuda.synchronize()
+
+    def check_sparse_outputs(what):
+        same = all(torch.equal(a, b) for a, b in zip(inline_outs, list(sparse_out) + [pruned_out]))
+        if not same:
+            raise RuntimeError(f"bench.py: sparse outputs of the {what} differ from the inline-mask steps")
+
+    check_sparse_outputs("eager pass")
     dense_flops = [acc.dense_step_flops(wl, s) for s in range(K)]
     sparse_flops = []
     for s in range(K):
@@ -273,6 +313,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    check_sparse_outputs("timed passes")
     value = pass_flops / (ms_per_step * 1e-3) / 1e12
 
     # ---- per-launch timings -------------------------------------------------
@@ -327,11 +368,18 @@ def main():
     dense_gen_ms = time_launch(lambda: [dense_step(s) for s in range(K)], reps=max(2, R // 4))
 
     def sparse_gen():
+        sparse_gen_steps_overlapped()
+        scatter_step()
+
+    sparse_gen_ms = time_launch(sparse_gen, reps=max(2, R // 4))
+
+    # the same with each mask built on the launch stream right before its step
+    def sparse_gen_inline_masks():
         for s in range(K):
             sparse_gen_step(s)
         scatter_step()
 
-    sparse_gen_ms = time_launch(sparse_gen, reps=max(2, R // 4))
+    sparse_gen_inline_ms = time_launch(sparse_gen_inline_masks, reps=max(2, R // 4))
 
     # the same with the masks built beforehand: they depend on positions only,
     # so a model builds them once per step for all its layers
@@ -491,8 +539,9 @@ def main():
         "config": {
             "workload": "1024px VAR generation: grids 1,2,4,6,8,12,16,20,24,32,40,48,64 (10521 tokens), "
                         "B=2 (CFG), H=16, D=128, bf16 in / fp32 accumulate / bf16 out; dense block-causal "
-                        "(13 launches) + block-sparse (64x64 tiles, 7 sink scales, radius 2; mask built per "
-                        "step) with the last step pruned to 1638 of 4096 queries and scattered over 48x48",
+                        "(13 launches) + block-sparse (64x64 tiles, 7 sink scales, radius 2; masks built per "
+                        "step on a second stream, overlapping the steps) with the last step pruned to 1638 of "
+                        "4096 queries and scattered over 48x48",
             "launch": "hipGraph replay of the whole pass" if graph is not None else "eager",
             "pass_gflop": round(pass_flops / 1e9, 3),
             "key_splits": {"dense": dense_splits, "sparse": sparse_splits},
@@ -536,6 +585,7 @@ def main():
             "per_step_attn_ms": [round(x, 4) for x in sparse_ms],
             "per_step_mask_ms": [round(x, 4) for x in mask_ms],
             "full_mask_steps_run_dense": [s for s in range(K) if full_mask[s]],
+            "generation_masks_inline_ms": round(sparse_gen_inline_ms, 4),
             "generation_masks_prebuilt_ms": round(sparse_gen_pre_ms, 4),
             "last_step_pruned_attn_ms": round(sparse_ms[last], 4),
             "last_step_pruned_gflop": round(sparse_flops[last] / 1e9, 3),
