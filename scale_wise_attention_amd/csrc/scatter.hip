@@ -4,10 +4,11 @@
 // with source (floor(y*h_in/h_out), floor(x*w_in/w_out)); Scatter overwrites.
 //
 // One pass over the output grid: every output row picks its single source —
-// the update row i if it is retained (found by binary search in the
-// ascending index list), else the upsampled base row — so each output byte is
-// written exactly once and no inverse map or second pass is needed.  Copies
-// are 16 bytes per lane when rows, strides and pointers allow it (else 4 or 2).
+// the update row i if it is retained (marked per group of rows after one
+// wave-wide search of the ascending index list), else the upsampled base
+// row — so each output byte is written exactly once and no inverse map or
+// second pass is needed.  Copies are 16 bytes per lane when rows, strides and
+// pointers allow it (else 4 or 2).
 #include <hip/hip_runtime.h>
 
 #include "kernels.h"
@@ -15,25 +16,42 @@
 namespace varattn {
 namespace {
 
-// Index of t in the ascending list, or -1.
-__device__ __forceinline__ int find_index(const int32_t* __restrict__ idx, int n, int t) {
+constexpr int kThreads = 256;
+
+// First position of the ascending index list holding a value >= t (n if
+// none), by one wave: each round probes 64 evenly spaced positions of the
+// remaining range [lo, hi] and keeps the gap between the last probe below t
+// and the next, so a list of n entries takes about log64(n) rounds of one
+// load each (3 for n <= 2^18).  Every round shrinks the range, also for a
+// list that is not ascending (the result is then some position in [0, n]).
+__device__ __forceinline__ int wave_lower_bound(const int32_t* __restrict__ idx, int n, int t, int lane) {
     int lo = 0, hi = n;
     while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (idx[mid] < t) lo = mid + 1; else hi = mid;
+        const int step = (hi - lo + 63) >> 6;
+        const int pos = lo + lane * step;
+        const bool below = pos < hi && idx[pos] < t;
+        const int c = __popcll(__ballot(below));
+        const int nlo = c > 0 ? lo + (c - 1) * step + 1 : lo;
+        hi = min(hi, lo + c * step);
+        lo = nlo;
     }
-    return (lo < n && idx[lo] == t) ? lo : -1;
+    return lo;
 }
 
+// A workgroup copies groups of `rows_per_group` consecutive output rows of one
+// map (as many rows as 256 lanes cover, at least one), one unit per lane per
+// pass.  Per group, wave 0 finds the group's first retained position with one
+// wave-wide search and marks the group's retained rows in LDS.
 template <int UNIT>
-__global__ __launch_bounds__(256) void scatter_kernel(const ScatterParams p) {
+__global__ __launch_bounds__(kThreads) void scatter_kernel(const ScatterParams p, int rows_per_group) {
     const int n_out = p.h_out * p.w_out;
     const int per_row = p.row_bytes / UNIT;   // the host picks UNIT dividing rows, strides, pointers
-    const int64_t total = (int64_t)p.maps * n_out * per_row;
+    const int groups_per_map = (n_out + rows_per_group - 1) / rows_per_group;
+    const int64_t groups = (int64_t)p.maps * groups_per_map;
+    const int tid = threadIdx.x;
     // index checks (once, by the first threads of the grid)
     if (p.err_flag) {
-        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < p.n_sel;
-             i += (int64_t)gridDim.x * blockDim.x) {
+        for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < p.n_sel; i += (int64_t)gridDim.x * kThreads) {
             const int v = p.q_index[i];
             int bad = 0;
             if (v < 0 || v >= n_out) bad |= 1;
@@ -41,43 +59,68 @@ __global__ __launch_bounds__(256) void scatter_kernel(const ScatterParams p) {
             if (bad) atomicOr(p.err_flag, bad);
         }
     }
-    for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < total;
-         it += (int64_t)gridDim.x * blockDim.x) {
-        const int chunk = (int)(it % per_row);
-        const int64_t rowlin = it / per_row;
-        const int t = (int)(rowlin % n_out);
-        const int m = (int)(rowlin / n_out);
-        const int i = find_index(p.q_index, p.n_sel, t);
-        const unsigned char* src;
-        if (i >= 0) {
-            src = p.upd + m * p.upd_map_stride + i * p.upd_row_stride;
-        } else {
-            const int y = t / p.w_out, x = t - y * p.w_out;
-            const int ys = (int)(((int64_t)y * p.h_in) / p.h_out);
-            const int xs = (int)(((int64_t)x * p.w_in) / p.w_out);
-            src = p.base + m * p.base_map_stride + (int64_t)(ys * p.w_in + xs) * p.base_row_stride;
+    __shared__ int src_of[kThreads];   // update row of each row of the group, or -1
+    for (int64_t gi = blockIdx.x; gi < groups; gi += gridDim.x) {
+        const int m = (int)(gi / groups_per_map);
+        const int t0 = (int)(gi - (int64_t)m * groups_per_map) * rows_per_group;
+        const int rows = min(rows_per_group, n_out - t0);
+        if (tid < 64) {
+            for (int r = tid; r < rows; r += 64) src_of[r] = -1;
+            if (p.n_sel > 0) {
+                // an ascending list holds the group's retained rows in [first, first + rows);
+                // with a list that breaks the contract the rows are unspecified but every
+                // access stays in bounds
+                const int first = wave_lower_bound(p.q_index, p.n_sel, t0, tid);
+                for (int r = tid; r < rows; r += 64) {
+                    const int k = first + r;
+                    if (k < p.n_sel) {
+                        const int v = p.q_index[k];
+                        if (v >= t0 && v < t0 + rows) src_of[v - t0] = k;
+                    }
+                }
+            }
         }
-        unsigned char* dst = p.out + m * p.out_map_stride + (int64_t)t * p.out_row_stride;
-        if constexpr (UNIT == 16) {
-            *reinterpret_cast<uint4*>(dst + chunk * 16) = *reinterpret_cast<const uint4*>(src + chunk * 16);
-        } else if constexpr (UNIT == 4) {
-            *reinterpret_cast<uint32_t*>(dst + chunk * 4) = *reinterpret_cast<const uint32_t*>(src + chunk * 4);
-        } else {
-            *reinterpret_cast<uint16_t*>(dst + chunk * 2) = *reinterpret_cast<const uint16_t*>(src + chunk * 2);
+        __syncthreads();
+        const int64_t work = (int64_t)rows * per_row;
+        for (int64_t w = tid; w < work; w += kThreads) {
+            const int r = (int)(w / per_row);
+            const int64_t chunk = w - (int64_t)r * per_row;
+            const int t = t0 + r;
+            const int i = src_of[r];
+            const unsigned char* src;
+            if (i >= 0) {
+                src = p.upd + m * p.upd_map_stride + (int64_t)i * p.upd_row_stride;
+            } else {
+                const int y = t / p.w_out, x = t - y * p.w_out;
+                const int ys = (int)(((int64_t)y * p.h_in) / p.h_out);
+                const int xs = (int)(((int64_t)x * p.w_in) / p.w_out);
+                src = p.base + m * p.base_map_stride + (int64_t)(ys * p.w_in + xs) * p.base_row_stride;
+            }
+            unsigned char* dst = p.out + m * p.out_map_stride + (int64_t)t * p.out_row_stride;
+            if constexpr (UNIT == 16) {
+                *reinterpret_cast<uint4*>(dst + chunk * 16) = *reinterpret_cast<const uint4*>(src + chunk * 16);
+            } else if constexpr (UNIT == 4) {
+                *reinterpret_cast<uint32_t*>(dst + chunk * 4) = *reinterpret_cast<const uint32_t*>(src + chunk * 4);
+            } else {
+                *reinterpret_cast<uint16_t*>(dst + chunk * 2) = *reinterpret_cast<const uint16_t*>(src + chunk * 2);
+            }
         }
+        __syncthreads();   // the group's marks are read before the next group resets them
     }
 }
 
 }  // namespace
 
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s) {
-    const int64_t total = (int64_t)p.maps * p.h_out * p.w_out * (p.row_bytes / p.unit);
-    int64_t blocks = (total + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
+    const int per_row = p.row_bytes / p.unit;
+    const int rows_per_group = per_row >= kThreads ? 1 : kThreads / per_row;
+    const int64_t n_out = (int64_t)p.h_out * p.w_out;
+    const int64_t groups = (int64_t)p.maps * ((n_out + rows_per_group - 1) / rows_per_group);
+    int64_t blocks = groups < 65536 ? groups : 65536;
     if (blocks < 1) blocks = 1;
-    if (p.unit == 16) hipLaunchKernelGGL(scatter_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, s, p);
-    else if (p.unit == 4) hipLaunchKernelGGL(scatter_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(scatter_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    if (p.unit == 16) hipLaunchKernelGGL(scatter_kernel<16>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, rows_per_group);
+    else if (p.unit == 4) hipLaunchKernelGGL(scatter_kernel<4>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, rows_per_group);
+    else hipLaunchKernelGGL(scatter_kernel<2>, dim3((unsigned)blocks), dim3(kThreads), 0, s, p, rows_per_group);
     return hipGetLastError();
 }
 
