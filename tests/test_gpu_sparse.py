@@ -209,6 +209,19 @@ def test_scatter_restore_bit_exact(api, dtype):
     assert int(flag.item()) == 0
 
 
+def test_scatter_more_row_groups_than_workgroups(api):
+    """260 maps x 256 row groups of 16 rows: more groups than the launch's 65536
+    workgroups, so workgroups take a second group (and reset its marks)."""
+    maps, E = 260, 128
+    base = torch.from_numpy(normal_tensor((maps, 48 * 48, E), 3)).to(torch.bfloat16).cuda()
+    sel = pruned_index(4096, 0.4, 1)
+    upd = torch.from_numpy(normal_tensor((maps, sel.size, E), 4)).to(torch.bfloat16).cuda()
+    out = api.var_scatter_restore(base, 48, 48, upd, torch.from_numpy(sel).cuda(), 64, 64)
+    ref = oracle.scatter_restore(base.view(torch.int16).cpu().numpy(), 48, 48, upd.view(torch.int16).cpu().numpy(),
+                                 sel, 64, 64)
+    assert np.array_equal(out.view(torch.int16).cpu().numpy(), ref)
+
+
 def test_scatter_edge_cases(api):
     # no index: pure nearest upsampling; odd row widths take the 2-byte path
     for (hi, wi, ho, wo, E) in [(48, 48, 64, 64, 64), (3, 5, 7, 9, 3), (4, 4, 4, 4, 8), (7, 3, 5, 2, 5)]:
