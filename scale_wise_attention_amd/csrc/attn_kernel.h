@@ -104,20 +104,17 @@ constexpr float kSumLimit = 0x1p100f;  // a row sum above this triggers the exac
 // belong to one (batch, head) and share its K and V in that XCD's L2.
 __device__ __forceinline__ void decode_work(int wg, int nwg, int split_from, int splits, int& item, int& split,
                                             bool& whole) {
+    // (branch-free, results in scalar registers: the values are uniform)
     const int x = wg & 7, j = wg >> 3;
     const int fq = split_from >> 3, fr = split_from & 7;
     const int n_whole = fq + (x < fr ? 1 : 0);   // whole items on this XCD
-    if (j < n_whole) {
-        item = x * fq + min(x, fr) + j;
-        split = 0;
-        whole = true;
-        return;
-    }
     const int q = nwg >> 3, r = nwg & 7;
-    const int piece = x * (q - fq) + min(x, r) - min(x, fr) + (j - n_whole);
-    item = split_from + piece / splits;
-    split = piece - (piece / splits) * splits;
-    whole = false;
+    const bool w = j < n_whole;
+    const int piece = max(x * (q - fq) + min(x, r) - min(x, fr) + (j - n_whole), 0);
+    const int pdiv = piece / splits;
+    item = __builtin_amdgcn_readfirstlane(w ? x * fq + min(x, fr) + j : split_from + pdiv);
+    split = __builtin_amdgcn_readfirstlane(w ? 0 : piece - pdiv * splits);
+    whole = w;
 }
 
 __device__ __forceinline__ int wave_min_i(int v) {
@@ -301,7 +298,10 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     int item, split;
     bool whole;
     decode_work(blockIdx.x, gridDim.x, p.split_from, p.n_splits, item, split, whole);
-    const int n_sp = whole ? 1 : p.n_splits;
+    // this workgroup's share count (1: the whole item).  The later tests use
+    // this integer, not the flag: a flag kept for them cost the key loop
+    // about a dozen registers (moved through AGPRs every tile).
+    const int n_sp = __builtin_amdgcn_readfirstlane(whole ? 1 : p.n_splits);
     const int qtile = item % p.n_qtiles;
     const int bh = item / p.n_qtiles;
     const int b = bh / p.H;
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     // two round trips).  The walk's prologue then skips them.
     bool first_tile_preloaded = false;
     if constexpr (!SPARSE) {
-        if (whole) {
+        if (n_sp == 1) {
             load_k(0, 0);
             load_v(0);
             first_tile_preloaded = true;
@@ -1037,7 +1037,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
 
     // ---- epilogue --------------------------------------------------------
     unsigned char* ob = reinterpret_cast<unsigned char*>(p.o);
-    const bool partial = !whole;   // write this split's normalised O and LSE (fp32) for the merge
+    const bool partial = n_sp > 1;   // write this split's normalised O and LSE (fp32) for the merge
     const int64_t part_row0 = ((int64_t)split * p.B * p.H + b * p.H + h) * p.n_rows;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
