@@ -523,8 +523,12 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     int dense_begin = 0, dense_end = 0;   // dense: tiles [dense_begin, dense_end)
     int dense_next = 0;
     int lbeg[NW], lptr[NW], lend[NW], lhead[NW];   // sparse: one list per wave's query tile
-    const int32_t* const rowp = p.row_ptr + bh * p.rp_bh_stride;   // this (batch, head)'s CSR
-    const int32_t* const coli = p.col_idx + bh * p.ci_bh_stride;
+    // this (batch, head)'s CSR, read through the constant address space: the
+    // launch never writes it and every read is workgroup-uniform, so the
+    // reads go through the scalar path into scalar registers
+    typedef const __attribute__((address_space(4))) int32_t* csr_ptr;
+    const csr_ptr rowp = (csr_ptr)(p.row_ptr + bh * p.rp_bh_stride);
+    const csr_ptr coli = (csr_ptr)(p.col_idx + bh * p.ci_bh_stride);
     if constexpr (SPARSE) {
         const int n_qt = (p.n_rows + KT - 1) / KT;
 #pragma unroll
@@ -591,7 +595,9 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         }
         e.ks = 1.f;
         if constexpr (QK8) {
-            if (e.tile >= 0) e.ks = p.k_scale[bh * p.k_scale_stride + e.tile];
+            // (uniform and never written by the launch: a scalar load, as for the CSR)
+            typedef const __attribute__((address_space(4))) float* scale_ptr;
+            if (e.tile >= 0) e.ks = ((scale_ptr)p.k_scale)[bh * p.k_scale_stride + e.tile];
         }
         return e;
     };
