@@ -208,12 +208,19 @@ var_status var_build_tile_mask(const var_schedule* sched, int32_t q_scale_begin,
 
 /*
  * Block-sparse next-scale attention: var_attn_dense restricted to the kept
- * tiles of a CSR tile mask (as produced by var_build_tile_mask; any CSR with
- * in-range columns is accepted).  Inside a kept tile every block-causally
- * visible pair is attended.  tile_q = tile_k = 64 only.  Arguments as in
- * var_attn_dense; row_ptr / col_idx are device arrays with n_qt + 1 and
- * row_ptr[n_qt] entries.  A row whose kept tiles hold no visible key gets
- * O = 0 and LSE = -inf.
+ * tiles of a CSR tile mask (as produced by var_build_tile_mask).  Inside a
+ * kept tile every block-causally visible pair is attended.  tile_q = tile_k
+ * = 64 only.  Arguments as in var_attn_dense; row_ptr / col_idx are device
+ * arrays with n_qt + 1 and row_ptr[n_qt] entries.  A row whose kept tiles
+ * hold no visible key gets O = 0 and LSE = -inf.
+ * CSR contract (the caller's; the arrays are on the device and not checked
+ * on the host): row_ptr[0] = 0, row_ptr non-decreasing, row_ptr[n_qt] at most
+ * the capacity of col_idx; each row's columns strictly ascending, in
+ * [0, n_kt).  Within that contract each listed tile is attended once.  With
+ * row_ptr inside the contract, any column values keep every access in
+ * bounds: a column outside [0, n_kt) is clamped into it, a column repeated
+ * right after itself counts once, and any other repeat (out of order) counts
+ * its tile again.
  */
 var_status var_attn_block_sparse(const var_schedule* sched, const var_attn_desc* desc,
                                  const void* q, var_layout q_l, const void* k, var_layout k_l,
@@ -362,11 +369,12 @@ var_status var_attn_block_sparse_heads(const var_schedule* sched, const var_attn
  * group of output row i and m = b*heads + h, the logit of row i and key u is
  *   softmax_scale * qs * k_scale[m*k_scale_stride + u/64] * (q_codes . k_codes),
  * i.e. attention of the dequantised queries and keys.  The e4m3 matrix
- * instruction sums the 64 products of a k-step with a relative error of up
- * to about 2^-12 of the sum of their magnitudes (measured on gfx950; not an
- * exact fp32 sum), so a logit can move by about 2^-12 * softmax_scale * qs *
- * ks * sum_d |q_d k_d|: around 3e-4 at softmax_scale = 1/sqrt(128) on unit
- * data, below the bf16 rounding of the weights.
+ * instruction does not round its sums like fp32: its error reached 2^-11.8
+ * of the sum of the product magnitudes for codes spread over the whole e4m3
+ * range (the worst case measured on gfx950; 2^-14.6 for normally distributed
+ * codes), so a logit can move by up to 2^-11.8 * softmax_scale * qs * ks *
+ * sum_d |q_d k_d|: around 2e-3 at softmax_scale = 1/sqrt(128) on unit data
+ * in the worst case, about 3e-4 typically.
  *  desc   in_dtype must be VAR_BF16 (the dtype of q and v); head_dim 128;
  *         out_dtype f32 or bf16.
  *  k      device uint8 codes [B][H][>= kv_len][128], layout k_l (strides in

@@ -61,6 +61,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
         n_tiles = (wmax + 63) / 64;
     }
     for (int it = 0; it < n_tiles; ++it) {
+        // (a column repeated right after itself is visited once; the list is uniform)
+        if (SPARSE && it > 0 && p.col_idx[list_begin + it] == p.col_idx[list_begin + it - 1]) continue;
         const int tbase = SPARSE ? min(max(p.col_idx[list_begin + it], 0), (p.kv_len - 1) / 64) * 64 : it * 64;
         for (int half = 0; half < 2; ++half) {
             const int kbase = tbase + half * KH;

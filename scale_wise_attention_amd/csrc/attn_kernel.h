@@ -538,8 +538,12 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
             const int cnt = r < n_qt ? rowp[r + 1] - b0 : 0;
             // key split: an equal share of this row's kept tiles (in order; the
             // host bounds cnt * n_splits below 2^31)
-            lbeg[w] = lptr[w] = n_sp > 1 ? b0 + cnt * split / n_sp : b0;
+            lbeg[w] = n_sp > 1 ? b0 + cnt * split / n_sp : b0;
             lend[w] = n_sp > 1 ? b0 + cnt * (split + 1) / n_sp : b0 + cnt;
+            // a share that starts inside a run of one repeated column leaves
+            // the run to the share that holds its first entry
+            while (lbeg[w] > b0 && lbeg[w] < lend[w] && coli[lbeg[w]] == coli[lbeg[w] - 1]) ++lbeg[w];
+            lptr[w] = lbeg[w];
             lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
         }
     }
@@ -581,8 +585,11 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                 for (int w = 0; w < NW; ++w) {
                     if (lhead[w] == c) {
                         e.mask |= 1 << w;
-                        ++lptr[w];
-                        lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
+                        // (a column repeated right after itself is taken once)
+                        do {
+                            ++lptr[w];
+                            lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
+                        } while (lhead[w] == c);
                     }
                 }
                 // a column outside [0, n_kt) cannot come from the mask builder; clamp so loads stay in bounds
@@ -1007,15 +1014,27 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
 
     walk(IntC<0>{});
     // a row sum above 2^100 (or inf/nan) means logits far above the row's
-    // reference: recompute against the exact row maxima (rare; workgroup-wide)
+    // reference: recompute against the exact row maxima (rare; workgroup-wide).
+    // So does an accumulator that is no longer finite (weights up to 2^100
+    // times large values of v).  The tests look at exponent bits: the kernel
+    // is built without NaN semantics, so float comparisons cannot see a NaN.
     {
         bool bad = false;
+        uint32_t obits = 0u;   // largest |O| bit pattern of the lane
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int mb = 0; mb < MO; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) obits = max(obits, __float_as_uint(oacc[mb][qb][r]) & 0x7fffffffu);
+        bad |= obits >= 0x7f800000u;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const float ltot = lsum[qb] + swap_halves(lsum[qb]);
             // a sum out of range, or a row that saw keys only in branch-free
             // tiles before it had a reference, needs the exact recompute
-            bad |= !(ltot <= kSumLimit) || (mref[qb] == -INFINITY && ltot > 0.f);
+            bad |= (__float_as_uint(ltot) & 0x7fffffffu) > __float_as_uint(kSumLimit) ||
+                   (mref[qb] == -INFINITY && ltot > 0.f);
         }
         // one flag per wave, in words no walk overwrites: one barrier
         int* flags = wg_words + 2 * NW;

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+from _oracle_heads import attention_all_heads
 from scale_wise_attention_amd.inputs import WORKLOADS, make_qkv, pruned_index, normal_tensor
 
 pytestmark = pytest.mark.gpu
@@ -115,16 +116,35 @@ def test_mask_capacity_error(api):
     assert e.value.status_name == "VAR_ERR_CAPACITY"
 
 
-def _sparse_vs_oracle(api, wl, q, k, v, s, sel=None, rows=None, heads=None, what=""):
+def _sparse_vs_oracle(api, wl, q, k, v, s, sel=None, rows=None, heads=None, what="", out_dtype=None,
+                      planned_splits=False):
+    """Block-sparse step s (mask built by the library) against the oracle with the
+    oracle's own mask.  Without `heads` and `rows`: every (batch, head) and row.
+    planned_splits: the key splits the library plans for the call (as the
+    benchmark launches it), over a NaN-filled workspace."""
     off = oracle.offsets(wl.h, wl.w)
     qs = q[:, :, off[s]:off[s + 1]]
     idx = None if sel is None else torch.from_numpy(sel).cuda()
     mp = api.mask_params(64, 64, wl.sink_scales, wl.local_from_scale, wl.radius, wl.radius)
     rp, ci = api.var_build_tile_mask((wl.h, wl.w), s, s + 1, mp, q_index=idx)
-    o = api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, s, s + 1, rp, ci, q_index=idx)
+    n_splits, ws = 1, None
+    if planned_splits:
+        rp_h = rp.cpu().numpy()
+        hint = max(1, int(round(float(rp_h[-1]) / max(1, rp_h.size - 1))))
+        B, H, D = q.shape[0], q.shape[1], q.shape[3]
+        n_splits, ws_bytes = api.var_attn_split_plan((wl.h, wl.w), s, s + 1, B, H, D,
+                                                     n_sel=0 if sel is None else sel.size, kv_tiles_hint=hint)
+        if n_splits > 1:
+            ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda").fill_(float("nan"))
+    o = api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, s, s + 1, rp, ci, q_index=idx, out_dtype=out_dtype,
+                                  n_splits=n_splits, workspace=ws)
     kept = oracle.tile_mask(wl.h, wl.w, s, s + 1, 64, 64, wl.sink_scales, wl.local_from_scale, wl.radius,
                             wl.radius, q_index=sel)
     on, qn, kn, vn = _np(o), _np(qs), _np(k), _np(v)
+    if heads is None and rows is None:
+        ref = attention_all_heads(qn, kn, vn, wl.h, wl.w, s, s + 1, q_index=sel, kept=kept)
+        _check(on, ref, what=f"{what}, {n_splits} key splits, all (b, h), all rows")
+        return o
     heads = heads or [(b, h) for b in range(q.shape[0]) for h in range(q.shape[1])]
     for (b, h) in heads:
         ref = oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], wl.h, wl.w,
@@ -135,25 +155,32 @@ def _sparse_vs_oracle(api, wl, q, k, v, s, sel=None, rows=None, heads=None, what
 
 
 def test_sparse_1024_last_step_full_size(api):
+    """The unpruned block-sparse last step (4096 queries x 10521 keys, 1932 of 10560 tiles)
+    as the benchmark launches it (bf16 output): every (batch, head) and row."""
     wl = WORKLOADS["var1024_sparse"]
     q, k, v = make_qkv(wl, 0, device="cuda")
-    rows = np.unique(np.concatenate([np.arange(0, 4096, 37), [63, 64, 127, 128, 4095]]))
-    _sparse_vs_oracle(api, wl, q, k, v, wl.num_scales - 1, rows=rows,
-                      heads=[(0, 0), (0, 9), (1, 4), (1, 15)], what="sparse last step")
+    _sparse_vs_oracle(api, wl, q, k, v, wl.num_scales - 1, what="sparse last step", out_dtype=torch.bfloat16,
+                      planned_splits=True)
 
 
 def test_sparse_1024_pruned_last_step(api):
+    """The pruned last step (1638 of 4096 queries gathered, block-sparse) as benchmarked:
+    every (batch, head) and row."""
     wl = WORKLOADS["var1024_sparse"]
     q, k, v = make_qkv(wl, 1, device="cuda")
     sel = pruned_index(4096, 0.4, 1)
-    _sparse_vs_oracle(api, wl, q, k, v, wl.num_scales - 1, sel=sel, heads=[(0, 2), (1, 11)], what="sparse pruned")
+    _sparse_vs_oracle(api, wl, q, k, v, wl.num_scales - 1, sel=sel, what="sparse pruned",
+                      out_dtype=torch.bfloat16, planned_splits=True)
 
 
-def test_sparse_1024_middle_steps_one_head(api):
+def test_sparse_1024_middle_steps(api):
+    """The sparse steps with a partial mask (20x20 .. 48x48) as benchmarked: every (batch,
+    head) and row."""
     wl = WORKLOADS["var1024_sparse"]
     q, k, v = make_qkv(wl, 2, device="cuda")
-    for s in (6, 8, 10, 11):
-        _sparse_vs_oracle(api, wl, q, k, v, s, heads=[(1, 1)], what=f"sparse step {s}")
+    for s in range(wl.sink_scales, wl.num_scales - 1):
+        _sparse_vs_oracle(api, wl, q, k, v, s, what=f"sparse step {s}", out_dtype=torch.bfloat16,
+                          planned_splits=True)
 
 
 def test_sparse_all_tiles_kept_equals_dense(api):
@@ -190,6 +217,71 @@ def test_sparse_empty_rows_give_zero_and_neg_inf_lse(api):
     ci = torch.zeros(1, dtype=torch.int32, device="cuda")
     o, lse = api.var_attn_block_sparse((wl.h, wl.w), q[:, :, 424:], k, v, s, s + 1, rp, ci, return_lse=True)
     assert torch.count_nonzero(o) == 0 and bool(torch.isneginf(lse).all())
+
+
+def _csr_with_repeats(kept, seed):
+    """CSR of `kept` with some columns repeated right after themselves (the same kept set)."""
+    rng = np.random.default_rng(seed)
+    cols = []
+    for r in range(kept.shape[0]):
+        row = []
+        for c in np.nonzero(kept[r])[0]:
+            row += [int(c)] * int(rng.integers(1, 4))
+        cols.append(row)
+    rp = np.concatenate([[0], np.cumsum([len(c) for c in cols])]).astype(np.int32)
+    ci = np.array(sum(cols, []) or [0], dtype=np.int32)
+    assert rp[-1] > int(kept.sum()), "some column is repeated"
+    return torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda()
+
+
+@pytest.mark.parametrize("wl_name,in_f32", [("var256", False), ("var512", False), ("tiny_fp32", True)])
+def test_sparse_caller_csr_with_repeated_columns(api, wl_name, in_f32):
+    """A caller's CSR listing a kept tile several times in a row attends it once: equal to the
+    call with the unique list (bit for bit) and to the oracle with the kept set."""
+    wl = WORKLOADS[wl_name]
+    q, k, v = make_qkv(wl, 9, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    s = wl.num_scales - 1
+    qs = q[:, :, off[s]:off[s + 1]]
+    n_qt, n_kt = -(-(off[s + 1] - off[s]) // 64), -(-off[s + 1] // 64)
+    kept = np.random.default_rng(10).random((n_qt, n_kt)) < 0.6
+    kept[:, 0] = True
+    rp_u, ci_u = (torch.from_numpy(a).cuda() for a in oracle.mask_to_csr(kept))
+    rp_r, ci_r = _csr_with_repeats(kept, 11)
+    o_u, l_u = api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, s, s + 1, rp_u, ci_u, return_lse=True)
+    o_r, l_r = api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, s, s + 1, rp_r, ci_r, return_lse=True)
+    assert torch.equal(o_u, o_r) and torch.equal(l_u, l_r)
+    ref = oracle.attention(_np(qs), _np(k), _np(v), wl.h, wl.w, s, s + 1, kept=kept)
+    if in_f32:
+        _check(_np(o_r), ref, 1e-5, 1e-5, f"{wl_name} repeated columns")
+    else:
+        _check(_np(o_r), ref, what=f"{wl_name} repeated columns")
+
+
+def test_sparse_e4m3_and_split_with_repeated_columns(api):
+    """The same on the e4m3 and key-split paths (head_dim 128)."""
+    from scale_wise_attention_amd.inputs import custom_workload
+    wl = custom_workload((1, 2, 4, 6, 8, 12, 16, 20), 2, 2, 128)
+    q, k, v = make_qkv(wl, 12, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    s = 7
+    qs = q[:, :, off[s]:off[s + 1]]
+    n_qt, n_kt = -(-(off[s + 1] - off[s]) // 64), -(-off[s + 1] // 64)
+    kept = np.random.default_rng(13).random((n_qt, n_kt)) < 0.5
+    kept[:, 0] = True
+    rp_u, ci_u = (torch.from_numpy(a).cuda() for a in oracle.mask_to_csr(kept))
+    rp_r, ci_r = _csr_with_repeats(kept, 14)
+    k8, sk = api.var_quantize_e4m3(k)
+    a = api.var_attn_block_sparse_e4m3((wl.h, wl.w), qs, k8, sk, v, s, s + 1, rp_u, ci_u)
+    b = api.var_attn_block_sparse_e4m3((wl.h, wl.w), qs, k8, sk, v, s, s + 1, rp_r, ci_r)
+    assert torch.equal(a, b)
+    n = off[s + 1] - off[s]
+    ws = api.split_workspace(3, 2, 2, n, 128)
+    a = api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, s, s + 1, rp_u, ci_u, n_splits=3, workspace=ws)
+    b = api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, s, s + 1, rp_r, ci_r, n_splits=3, workspace=ws)
+    ref = oracle.attention(_np(qs), _np(k), _np(v), wl.h, wl.w, s, s + 1, kept=kept)
+    _check(_np(b), ref, what="split x3 repeated columns")
+    _check(_np(a), ref, what="split x3 unique columns")
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])

@@ -42,6 +42,45 @@ def test_hand_derived_1024_last_step_row0():
     assert list(np.nonzero(got[0])[0]) == expect
 
 
+def test_hand_derived_1024_last_step_row63():
+    expect = [int(a) for a in _read_rows("tile_mask_1024_row63.txt")[0].split()]
+    wl = WORKLOADS["var1024_sparse"]
+    K = wl.num_scales
+    # the last query tile: the 64 positions of grid row 63
+    got = oracle.tile_mask(wl.h, wl.w, K - 1, K, 64, 64, 7, 7, 2, 2, q_index=np.arange(4032, 4096))
+    assert list(np.nonzero(got[0])[0]) == expect
+
+
+def test_1024_generation_mask_figures():
+    """Figures of the 1024px sparse workload's masks from an independent pair-by-pair
+    enumeration written for the workload description (not from the pages, which print
+    none), under the same readings (literal index map compared by cross-multiplication,
+    tiles aligned at the call's first row and at key token 0, real visible pairs only).
+    They pin the window rule on far rows and on every step, not only row 0 and the total."""
+    from scale_wise_attention_amd import accounting as acc
+    wl = WORKLOADS["var1024_sparse"]
+    K = wl.num_scales
+    off = oracle.offsets(wl.h, wl.w)
+    kept_total = {7: (80, 105), 8: (136, 216), 9: (284, 640), 10: (525, 1625), 11: (915, 3636),
+                  12: (1932, 10560)}
+    pairs = 0
+    for s in range(K):
+        kept = oracle.tile_mask(wl.h, wl.w, s, s + 1, 64, 64, 7, 7, 2, 2)
+        if s < 7:
+            assert kept.all(), f"step {s}: steps of sink scales only keep every tile"
+        else:
+            assert (int(kept.sum()), kept.size) == kept_total[s], f"step {s}"
+        rp, ci = oracle.mask_to_csr(kept)
+        pairs += acc.sparse_pairs(rp, ci, off[s + 1] - off[s], off[s + 1])
+        if s == K - 1:
+            nnz = np.diff(rp)
+            assert (int(nnz.min()), int(nnz.max())) == (24, 33)
+            assert int(ci.sum()) == 95_967
+            assert int(sum((r + 1) * int(ci[rp[r]:rp[r + 1]].sum()) for r in range(rp.size - 1))) == 3_349_961
+    # computed (visible, kept) pairs of the whole sparse generation: 23.3 % of the dense 68,484,681
+    assert pairs == 15_977_033
+
+
 @pytest.mark.parametrize("R", [0, 1, 2])
 def test_single_scale_tile1_is_chebyshev_neighbourhood(R):
     h, w = [5], [6]
