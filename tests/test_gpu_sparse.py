@@ -225,8 +225,8 @@ def _csr_with_repeats(kept, seed):
     cols = []
     for r in range(kept.shape[0]):
         row = []
-        for c in np.nonzero(kept[r])[0]:
-            row += [int(c)] * int(rng.integers(1, 4))
+        for j, c in enumerate(np.nonzero(kept[r])[0]):
+            row += [int(c)] * int(rng.integers(2 if j == 0 else 1, 4))   # each row's first column repeated
         cols.append(row)
     rp = np.concatenate([[0], np.cumsum([len(c) for c in cols])]).astype(np.int32)
     ci = np.array(sum(cols, []) or [0], dtype=np.int32)
