@@ -37,6 +37,7 @@ METRIC = "effective attn TFLOP/s + ms/step at 1024px (dense & block-sparse), % M
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk (the published 2.5 PFLOP/s)
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dense_attn_1024_traffic.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "dense_attn_1024_counters.txt")
 # the sources of the dense bf16 attention kernel: its template and the bf16 instantiations
 KERNEL_SRCS = [os.path.join(ROOT, "scale_wise_attention_amd", "csrc", f) for f in ("attn_kernel.h", "attn_bf16.hip")]
 
@@ -49,21 +50,82 @@ def _kernel_hash():
     return h.hexdigest()[:16]
 
 
-def _read_traffic():
-    """HBM bytes of the dense last-step launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+def _profile_field(path, key):
+    """A `key = value` field of a committed rocprofv3 summary, if that summary was taken
+    on the current kernel source; else None."""
     try:
         fields = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for ln in f:
                 if "=" in ln and not ln.startswith("#"):
                     a, b = ln.split("=", 1)
                     fields[a.strip()] = b.strip()
         if fields.get("kernel_source_sha256_16") != _kernel_hash():
             return None
-        return float(fields["last_step_hbm_bytes"])
+        return float(fields[key])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def _read_traffic():
+    """HBM bytes of the dense last-step launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)."""
+    return _profile_field(TRAFFIC_FILE, "last_step_hbm_bytes")
+
+
+def device_peak(api):
+    """(compute units, peak engine clock in GHz) the device reports, and the bf16 MFMA
+    peak they give at 4096 flop per clock per compute unit."""
+    n_cu, khz = api.var_device_info()
+    ghz = khz / 1e6
+    return n_cu, ghz, (n_cu * ghz * 1e9 * 4096 / 1e12 if ghz > 0 else None)
+
+
+def step_roof(flops, nbytes, ms, peak_tflops):
+    """Binding roof of a launch (bf16 MFMA or HBM) and the fraction of it reached:
+    roof time = max(flops / MFMA peak, bytes / HBM bandwidth), fraction = roof time / time."""
+    t_mfma = flops / (peak_tflops * 1e12)
+    t_hbm = nbytes / (HBM_GBPS * 1e9)
+    return ("mfma" if t_mfma >= t_hbm else "hbm"), max(t_mfma, t_hbm) / (ms * 1e-3)
+
+
+def small_config(name, time_launch, api, acc, torch, dev):
+    """Per-step times of one dense generation of a smaller workload (the library's split
+    plan per step, bf16 out), each step against its binding roof."""
+    from scale_wise_attention_amd.inputs import WORKLOADS, make_qkv
+    wl = WORKLOADS[name]
+    K = wl.num_scales
+    B, H, D = wl.batch, wl.heads, wl.head_dim
+    sched = api.make_schedule(wl.h, wl.w)
+    q, k, v = make_qkv(wl, 0, device=dev)
+    off = [0]
+    for g in wl.grids:
+        off.append(off[-1] + g * g)
+    plans = [api.var_attn_split_plan(sched, s, s + 1, B, H, D) for s in range(K)]
+    ws = torch.empty(max(1, max(b for _, b in plans) // 4), dtype=torch.float32, device=dev)
+    outs = [torch.empty(B, H, off[s + 1] - off[s], D, dtype=torch.bfloat16, device=dev) for s in range(K)]
+
+    def step(s):
+        api.var_attn_dense(sched, q[:, :, off[s]:off[s + 1]], k, v, s, s + 1, out=outs[s], n_splits=plans[s][0],
+                           workspace=ws)
+
+    ms = [time_launch(lambda s=s: step(s)) for s in range(K)]
+    gen_ms = time_launch(lambda: [step(s) for s in range(K)])
+    flops = [acc.dense_step_flops(wl, s) for s in range(K)]
+    nbytes = [acc.dense_step_bytes(wl, s) for s in range(K)]
+    roofs = [step_roof(flops[s], nbytes[s], ms[s], PEAK_BF16_TFLOPS) for s in range(K)]
+    return {
+        "workload": f"grids {','.join(map(str, wl.grids))} ({wl.tokens} tokens), B={B}, H={H}, D={D}, bf16 in / "
+                    f"bf16 out, dense block-causal, one launch per step",
+        "generation_ms": round(gen_ms, 4),
+        "generation_gflop": round(sum(flops) / 1e9, 3),
+        "per_step_ms": [round(x, 4) for x in ms],
+        "per_step_algorithmic_mb": [round(b / 1e6, 3) for b in nbytes],
+        "per_step_gbps": [round(nbytes[s] / (ms[s] * 1e-3) / 1e9, 1) for s in range(K)],
+        "per_step_tflops": [round(flops[s] / (ms[s] * 1e-3) / 1e12, 2) for s in range(K)],
+        "per_step_bound": [r[0] for r in roofs],
+        "per_step_frac": [round(r[1], 4) for r in roofs],
+        "key_splits": [p[0] for p in plans],
+    }
 
 
 def cpu_baseline(wl, q, k, v, heads):
@@ -198,8 +260,14 @@ def main():
         rp, ci, idx = csr[s]
         api.var_build_tile_mask(sched, s, s + 1, mp, q_index=idx, row_ptr=rp, col_idx=ci)
 
-    def sparse_step(s):
+    def sparse_step(s, in_place=False):
+        # in_place (the pruned last step): each retained row goes straight to its
+        # place in the 64x64 grid `restored` (the scatter fused into the epilogue)
         rp, ci, idx = csr[s]
+        if s == K - 1 and in_place:
+            api.var_attn_block_sparse(sched, qsteps[s], k, v, s, s + 1, rp, ci, out=restored, q_index=idx,
+                                      n_splits=sparse_splits[s], workspace=workspace, out_at_index=True)
+            return
         out = pruned_out if s == K - 1 else sparse_out[s]
         api.var_attn_block_sparse(sched, qsteps[s], k, v, s, s + 1, rp, ci, out=out, q_index=idx,
                                   n_splits=sparse_splits[s], workspace=workspace)
@@ -218,7 +286,17 @@ def main():
     # steps run; each sparse step waits for its own mask.  The fork from the
     # launch stream also orders them after every earlier use of the CSR
     # buffers.
+    # The reconstruction of the pruned last step is split in two disjoint halves:
+    # the attention writes the retained rows in place, and the base-only
+    # scatter fills the other rows from the upsampled 48x48 output, right
+    # after the 48x48 step (the two touch disjoint rows, so no order is needed
+    # between them; measured, running them on two streams side by side was
+    # slower than one after the other).
     mask_stream = torch.cuda.Stream()
+
+    def base_scatter():
+        api.var_scatter_restore(sparse_out[K - 2], wl.grids[K - 2], wl.grids[K - 2], None, sel_t,
+                                wl.grids[K - 1], wl.grids[K - 1], out=restored)
 
     def sparse_gen_steps_overlapped():
         main = torch.cuda.current_stream()
@@ -236,9 +314,12 @@ def main():
                                    workspace=workspace)
             else:
                 main.wait_event(ready[s])
-                sparse_step(s)
+                sparse_step(s, in_place=True)
+            if s == K - 2:
+                base_scatter()
 
     def scatter_step():
+        # the separate reconstruction from the gathered rows (the reference path)
         api.var_scatter_restore(sparse_out[K - 2], wl.grids[K - 2], wl.grids[K - 2], pruned_out, sel_t,
                                 wl.grids[K - 1], wl.grids[K - 1], out=restored)
 
@@ -246,20 +327,24 @@ def main():
         for s in range(K):
             dense_step(s)
         sparse_gen_steps_overlapped()
-        scatter_step()
 
     # ---- algorithmic work ---------------------------------------------------
     # (the sparse outputs of the pass, with its masks on the second stream,
     # must equal those of the same steps with each mask built inline)
     for s in range(K):
         sparse_gen_step(s)
+    scatter_step()
     torch.cuda.synchronize()
-    inline_outs = [t.clone() for t in sparse_out] + [pruned_out.clone()]
+    inline_outs = [t.clone() for t in sparse_out] + [restored.clone()]
+    restored.fill_(float("nan"))
     run_pass()
     torch.cuda.synchronize()
 
     def check_sparse_outputs(what):
-        same = all(torch.equal(a, b) for a, b in zip(inline_outs, list(sparse_out) + [pruned_out]))
+        # (the restored grid, bit for bit: rows written in place + base-only scatter
+        # against gathered rows + the separate scatter)
+        same = all(torch.equal(a.view(torch.int16), b.view(torch.int16))
+                   for a, b in zip(inline_outs, list(sparse_out) + [restored]))
         if not same:
             raise RuntimeError(f"bench.py: sparse outputs of the {what} differ from the inline-mask steps")
 
@@ -363,21 +448,27 @@ def main():
     mask_ms = [time_launch(lambda s=s: mask_step(s)) for s in range(K)]
     sparse_ms = [time_launch(lambda s=s: sparse_step(s)) for s in range(K)]
     scatter_ms = time_launch(scatter_step)
+    base_scatter_ms = time_launch(base_scatter)
+    pruned_in_place_ms = time_launch(lambda: sparse_step(K - 1, in_place=True))
+
+    # the last step's attention writing in place after the base-only scatter:
+    # the reconstruction's cost on the critical path
+    def pruned_with_reconstruction():
+        base_scatter()
+        sparse_step(K - 1, in_place=True)
+
+    pruned_recon_ms = time_launch(pruned_with_reconstruction)
     sparse_full_ms = time_launch(sparse_full_last_step)
     sparse_full_flops = acc.sparse_step_flops(wl, full_rp.cpu().numpy(), full_ci.cpu().numpy(), 4096, off[K])
     dense_gen_ms = time_launch(lambda: [dense_step(s) for s in range(K)], reps=max(2, R // 4))
 
-    def sparse_gen():
-        sparse_gen_steps_overlapped()
-        scatter_step()
-
-    sparse_gen_ms = time_launch(sparse_gen, reps=max(2, R // 4))
+    sparse_gen_ms = time_launch(sparse_gen_steps_overlapped, reps=max(2, R // 4))
 
     # the same with each mask built on the launch stream right before its step
     def sparse_gen_inline_masks():
         for s in range(K):
             sparse_gen_step(s)
-        scatter_step()
+        scatter_step()     # (one stream throughout: the separate reconstruction)
 
     sparse_gen_inline_ms = time_launch(sparse_gen_inline_masks, reps=max(2, R // 4))
 
@@ -389,8 +480,8 @@ def main():
                 api.var_attn_dense(sched, qsteps[s], k, v, s, s + 1, out=sparse_out[s], n_splits=dense_splits[s],
                                    workspace=workspace)
             else:
-                sparse_step(s)
-        scatter_step()
+                sparse_step(s, in_place=True)
+        base_scatter()
 
     sparse_gen_pre_ms = time_launch(sparse_gen_prebuilt_masks, reps=max(2, R // 4))
 
@@ -517,8 +608,14 @@ def main():
     gemm_ms = g0.elapsed_time(g1) / 10
     gemm_tflops = 2.0 * 8192 ** 3 / (gemm_ms * 1e-3) / 1e12
     del ga, gb, gc
-    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    n_cu, max_ghz, peak_device = device_peak(api)
     last_tflops = dense_flops[last] / (dense_ms[last] * 1e-3) / 1e12
+    dense_roofs = [step_roof(dense_flops[s_], acc.dense_step_bytes(wl, s_), dense_ms[s_], PEAK_BF16_TFLOPS)
+                   for s_ in range(K)]
+    sparse_roofs = [step_roof(sparse_flops[s_], acc.dense_step_bytes(wl, s_, rows=n_sel if s_ == K - 1 else None),
+                              sparse_ms[s_], PEAK_BF16_TFLOPS) for s_ in range(K)]
+    clock_ghz = _profile_field(COUNTERS_FILE, "clock_ghz")
+    small = {name: small_config(name, time_launch, api, acc, torch, dev) for name in ("var256", "var512")}
     achieved = last_tflops
     traffic = _read_traffic()
     sparse_last_ms = mask_ms[last] + sparse_ms[last]
@@ -560,7 +657,14 @@ def main():
             "single_launch_us_p10_p50_p90": [round(single_us[len(single_us) // 10], 1),
                                              round(statistics.median(single_us), 1),
                                              round(single_us[(9 * len(single_us)) // 10], 1)],
-            "peak_basis": f"{n_cu} CUs x 2.4 GHz x 4096 bf16 flop/clk",
+            "peak_basis": "published MI355X dense bf16 MFMA peak (256 CUs x 2.4 GHz x 4096 flop/clk)",
+            "device_cus": n_cu,
+            "device_max_clock_ghz": round(max_ghz, 3) if max_ghz else None,
+            "device_peak_tflops": round(peak_device, 1) if peak_device else None,
+            "frac_of_device_peak": round(achieved / peak_device, 4) if peak_device else None,
+            "clock_ghz_during_launch": clock_ghz,
+            "clock_source": "rocprofv3 GRBM_GUI_ACTIVE per XCD / kernel time of this launch, from the committed "
+                            "counter summary of the same kernel source (null if the source changed since)",
             "bf16_gemm_8192_tflops": round(gemm_tflops, 1),
             "frac_of_gemm": round(achieved / gemm_tflops, 4),
         },
@@ -573,6 +677,8 @@ def main():
             "per_step_algorithmic_mb": [round(acc.dense_step_bytes(wl, s_) / 1e6, 3) for s_ in range(K)],
             "per_step_gbps": [round(acc.dense_step_bytes(wl, s_) / (dense_ms[s_] * 1e-3) / 1e9, 1) for s_ in range(K)],
             "per_step_tflops": [round(dense_flops[s_] / (dense_ms[s_] * 1e-3) / 1e12, 2) for s_ in range(K)],
+            "per_step_bound": [r[0] for r in dense_roofs],
+            "per_step_frac": [round(r[1], 4) for r in dense_roofs],
             "last_step_ms": round(dense_ms[last], 4),
             "last_step_gflop": round(dense_flops[last] / 1e9, 3),
             "last_step_tflops": round(last_tflops, 2),
@@ -583,6 +689,8 @@ def main():
             "generation_ms": round(sparse_gen_ms, 4),
             "generation_tflops": round(sum(sparse_flops) / (sparse_gen_ms * 1e-3) / 1e12, 2),
             "per_step_attn_ms": [round(x, 4) for x in sparse_ms],
+            "per_step_bound": [r[0] for r in sparse_roofs],
+            "per_step_frac": [round(r[1], 4) for r in sparse_roofs],
             "per_step_mask_ms": [round(x, 4) for x in mask_ms],
             "full_mask_steps_run_dense": [s for s in range(K) if full_mask[s]],
             "generation_masks_inline_ms": round(sparse_gen_inline_ms, 4),
@@ -591,13 +699,22 @@ def main():
             "last_step_pruned_gflop": round(sparse_flops[last] / 1e9, 3),
             "scatter_ms": round(scatter_ms, 4),
             "scatter_gbps": round(acc.scatter_bytes(B * H, D * 2, n_sel, 4096) / (scatter_ms * 1e-3) / 1e9, 1),
+            "reconstruction_fused": {
+                "pruned_attn_rows_in_place_ms": round(pruned_in_place_ms, 4),
+                "base_only_scatter_ms": round(base_scatter_ms, 4),
+                "base_only_scatter_gbps": round(acc.scatter_bytes(B * H, D * 2, 0, 4096 - n_sel) /
+                                                (base_scatter_ms * 1e-3) / 1e9, 1),
+                "pruned_attn_plus_reconstruction_ms": round(pruned_recon_ms, 4),
+                "reconstruction_cost_on_critical_path_ms": round(pruned_recon_ms - sparse_ms[last], 4),
+            },
             "last_step_unpruned_ms": round(sparse_full_ms, 4),
             "last_step_unpruned_gflop": round(sparse_full_flops / 1e9, 3),
             "last_step_unpruned_tflops": round(sparse_full_flops / (sparse_full_ms * 1e-3) / 1e12, 2),
             "speedup_last_step_unpruned_vs_dense": round(dense_ms[last] / sparse_full_ms, 3),
-            "speedup_last_step_pruned_vs_dense": round(dense_ms[last] / (sparse_last_ms + scatter_ms), 3),
+            "speedup_last_step_pruned_vs_dense": round(dense_ms[last] / (mask_ms[last] + pruned_recon_ms), 3),
             "speedup_generation_vs_dense": round(dense_gen_ms / sparse_gen_ms, 3),
         },
+        "smaller_configs": small,
         "guided_selection": {
             "source_step_grid": f"{wl.grids[src]}x{wl.grids[src]}",
             "saliency_ms": round(saliency_ms, 4),

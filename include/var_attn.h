@@ -81,6 +81,10 @@ typedef struct var_attn_desc {
     float softmax_scale;    /* 0 => 1/sqrt(head_dim)                               */
     var_dtype in_dtype;     /* dtype of q, k, v                                    */
     var_dtype out_dtype;    /* dtype of o (bf16 in: f32 or bf16; f32 in: f32)      */
+    int32_t out_at_index;   /* 0: output row i is row i of o.  1 (needs q_index):  */
+                            /* output row i is written to row q_index[i] of o,     */
+                            /* which then holds n_q rows; other rows of o are left */
+                            /* untouched (lse stays in call order)                 */
 } var_attn_desc;
 
 typedef struct var_mask_params {
@@ -119,6 +123,13 @@ var_status var_schedule_extent(const var_schedule* sched, int32_t q_scale_begin,
  * Alignment: q, k, v, o 16-byte aligned; token/head/batch strides multiples
  * of 8 elements (bf16) or 4 elements (f32).
  */
+/*
+ * With desc->out_at_index = 1 a pruned call writes its rows straight to their
+ * places in the full output grid (the scatter of "ARVAR ...", Key Design 3,
+ * Equation (9), fused into the attention epilogue); var_scatter_restore with
+ * upd = NULL then fills the other rows from the upsampled base (Equation (8)),
+ * and the two calls touch disjoint rows.
+ */
 var_status var_attn_dense(const var_schedule* sched, const var_attn_desc* desc,
                           const void* q, var_layout q_l, const void* k, var_layout k_l,
                           const void* v, var_layout v_l, void* o, var_layout o_l,
@@ -142,10 +153,14 @@ var_status var_attn_dense(const var_schedule* sched, const var_attn_desc* desc,
  *   M = max_s LSE_s  (a part in which a row sees no key has LSE_s = -inf).
  *  n_splits  1..8; 1 is exactly var_attn_dense / var_attn_block_sparse (the
  *            workspace is then not used and may be NULL).  > 1 needs bf16 input.
- *  workspace device memory of at least n_splits*B*H*rows*(D+1)*4 bytes
- *            (0 for n_splits = 1), 16-byte aligned, owned by the caller; its
- *            contents on entry do not matter and on return are unspecified.
- *            Calls that share a workspace must be ordered on one stream.
+ *  workspace device memory, 16-byte aligned, owned by the caller, of
+ *            n_splits*P*(D+1)*4 bytes, P the rows of the split work items:
+ *            the (batch, head, row) rows, in that order, from the first row
+ *            of the first split item on (P depends on the device's compute
+ *            units; var_attn_split_plan reports the bytes, and
+ *            n_splits*B*H*rows*(D+1)*4 is always enough).  Its contents on
+ *            entry do not matter and on return are unspecified.  Calls that
+ *            share a workspace must be ordered on one stream.
  *  Other arguments as in var_attn_dense / var_attn_block_sparse.
  * Errors: VAR_ERR_RANGE for n_splits outside 1..8, VAR_ERR_UNSUPPORTED for a
  * split of f32 input, VAR_ERR_NULL / VAR_ERR_STRIDE / VAR_ERR_CAPACITY for a
@@ -174,7 +189,8 @@ var_status var_attn_block_sparse_split(const var_schedule* sched, const var_attn
  * mean kept tiles per mask row for a sparse call; the model still counts the
  * dense kernel's work items, 256 query rows each, one workgroup per compute
  * unit, so for sparse calls it is a rougher guide).  Writes *n_splits and the
- * workspace bytes it needs (either pointer may be NULL).  n_sel as in
+ * workspace bytes a dense or block-sparse call with that count needs on this
+ * device (either pointer may be NULL).  n_sel as in
  * var_attn_dense (0 = no gather).  f32 input always gives 1 and 0 bytes.
  */
 var_status var_attn_split_plan(const var_schedule* sched, const var_attn_desc* desc, int32_t n_sel,
@@ -423,6 +439,10 @@ var_status var_attn_block_sparse_e4m3(const var_schedule* sched, const var_attn_
  * the kernel ORs in 1 for an out-of-range index and 2 for a non-ascending
  * (duplicate or unsorted) pair; rows are then unspecified but every access
  * stays in bounds.
+ * upd = NULL with n_sel > 0: the rows q_index[i] of out are left untouched
+ * (written by an attention call with out_at_index = 1) and only the other
+ * rows are filled from the upsampled base; the two calls may then run in
+ * either order or concurrently.
  */
 var_status var_scatter_restore(int32_t maps, int32_t row_elems, var_dtype dtype,
                                const void* base, int64_t base_map_stride, int64_t base_row_stride,
@@ -431,6 +451,14 @@ var_status var_scatter_restore(int32_t maps, int32_t row_elems, var_dtype dtype,
                                const int32_t* q_index, int32_t n_sel,
                                void* out, int64_t out_map_stride, int64_t out_row_stride,
                                int32_t h_out, int32_t w_out, int32_t* err_flag, void* stream);
+
+/*
+ * Compute units and peak engine clock (kHz) of the calling thread's current
+ * device, as the key-split plan sees them (read once per device from the
+ * device properties).  Either pointer may be NULL.  VAR_ERR_HIP when there is
+ * no device.
+ */
+var_status var_device_info(int32_t* compute_units, int32_t* max_clock_khz);
 
 /* Static name of a status code. */
 const char* var_status_string(var_status s);

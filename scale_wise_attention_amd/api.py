@@ -32,7 +32,7 @@ EXPORTED = ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_
             "var_attn_block_sparse", "var_scatter_restore", "var_attn_saliency", "var_select_topk",
             "var_attn_dense_split", "var_attn_block_sparse_split", "var_attn_split_plan",
             "var_attn_block_mass", "var_decision_tiles", "var_mapped_tile_mask", "var_attn_block_sparse_heads",
-            "var_quantize_e4m3", "var_attn_dense_e4m3", "var_attn_block_sparse_e4m3",
+            "var_quantize_e4m3", "var_attn_dense_e4m3", "var_attn_block_sparse_e4m3", "var_device_info",
             "var_status_string", "var_last_error")
 
 
@@ -55,7 +55,8 @@ class Layout(ctypes.Structure):
 class AttnDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("q_scale_begin", ctypes.c_int32), ("q_scale_end", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int)]
+                ("softmax_scale", ctypes.c_float), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("out_at_index", ctypes.c_int32)]
 
 
 class MaskParams(ctypes.Structure):
@@ -98,6 +99,7 @@ def _load():
                                         Layout, P, Layout, P, P, i32, i32, P, i64, P]
     lib.var_attn_block_sparse_e4m3.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, i64,
                                                P, Layout, P, Layout, P, P, i32, P, P, i64, P]
+    lib.var_device_info.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32)]
     for name in EXPORTED[:-2]:
         getattr(lib, name).restype = ctypes.c_int
     lib.var_status_string.argtypes = [ctypes.c_int]
@@ -179,7 +181,7 @@ def _check_index(q_index, device):
 
 
 def _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype, softmax_scale, q_index, want_lse,
-                 qk_codes=False):
+                 qk_codes=False, out_at_index=False):
     s = _as_schedule(schedule)
     _, n_q, kv_len = var_schedule_extent(s, q_scale_begin, q_scale_end)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -201,15 +203,25 @@ def _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype, 
         raise ValueError(f"k/v hold fewer than kv_len={kv_len} tokens")
     _check_index(q_index, q.device)
     rows = n_q if q_index is None else int(q_index.numel())
+    if out_at_index and q_index is None:
+        raise ValueError("out_at_index needs q_index")
+    out_rows = n_q if out_at_index else rows      # out_at_index: row i goes to row q_index[i] of the full grid
     if out is None:
         odt = out_dtype if out_dtype is not None else torch.float32
-        out = torch.empty((B, H, rows, D), dtype=odt, device=q.device)
-    elif tuple(out.shape) != (B, H, rows, D) or out.device != q.device:
-        raise ValueError(f"out must have shape {(B, H, rows, D)} on q's device")
+        out = torch.empty((B, H, out_rows, D), dtype=odt, device=q.device)
+    elif tuple(out.shape) != (B, H, out_rows, D) or out.device != q.device:
+        raise ValueError(f"out must have shape {(B, H, out_rows, D)} on q's device")
     lse = torch.empty((B, H, rows), dtype=torch.float32, device=q.device) if want_lse else None
     desc = AttnDesc(B, H, D, q_scale_begin, q_scale_end, float(softmax_scale), _dtype_code(v.dtype),
-                    _dtype_code(out.dtype))
+                    _dtype_code(out.dtype), 1 if out_at_index else 0)
     return s, desc, out, lse, rows
+
+
+def var_device_info():
+    """(compute units, peak engine clock in kHz) of the current device, as the library reads them."""
+    a, b = ctypes.c_int32(), ctypes.c_int32()
+    _check(LIB.var_device_info(ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
 
 
 def var_attn_split_plan(schedule, q_scale_begin, q_scale_end, batch, heads, head_dim, n_sel=0, kv_tiles_hint=0,
@@ -240,15 +252,16 @@ def _ws_args(n_splits, workspace):
 
 
 def var_attn_dense(schedule, q, k, v, q_scale_begin, q_scale_end, out=None, out_dtype=None,
-                   softmax_scale=0.0, q_index=None, return_lse=False, n_splits=1, workspace=None):
+                   softmax_scale=0.0, q_index=None, return_lse=False, n_splits=1, workspace=None, out_at_index=False):
     """Dense block-causal attention of the queries of scales [begin, end).
 
     q [B, H, n_q, D] (row j = token off[begin] + j), k / v [B, H, >= kv_len, D];
     returns out [B, H, rows, D] (and lse [B, H, rows]); rows = len(q_index) or n_q.
-    n_splits > 1 runs the key-split variant in `workspace`.
+    n_splits > 1 runs the key-split variant in `workspace`.  out_at_index: output row i is
+    written to row q_index[i] of out [B, H, n_q, D] (other rows untouched).
     """
     s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
-                                           softmax_scale, q_index, return_lse)
+                                           softmax_scale, q_index, return_lse, out_at_index=out_at_index)
     n_sel = rows if q_index is not None else 0
     if q_index is not None and n_sel == 0:   # an empty selection has no device pointer: nothing to compute
         return (out, lse) if return_lse else out
@@ -303,9 +316,9 @@ def var_build_tile_mask(schedule, q_scale_begin, q_scale_end, params, q_index=No
 
 def var_attn_block_sparse(schedule, q, k, v, q_scale_begin, q_scale_end, row_ptr, col_idx, out=None,
                           out_dtype=None, softmax_scale=0.0, q_index=None, return_lse=False, tile_q=64, tile_k=64,
-                          n_splits=1, workspace=None):
+                          n_splits=1, workspace=None, out_at_index=False):
     s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
-                                           softmax_scale, q_index, return_lse)
+                                           softmax_scale, q_index, return_lse, out_at_index=out_at_index)
     n_sel = rows if q_index is not None else 0
     if q_index is not None and n_sel == 0:
         return (out, lse) if return_lse else out
@@ -477,10 +490,10 @@ def var_mapped_tile_mask(schedule, decision_scale, step, kept_d, row_ptr=None, c
 
 
 def var_attn_block_sparse_heads(schedule, q, k, v, q_scale_begin, q_scale_end, row_ptr, col_idx, out=None,
-                                out_dtype=None, softmax_scale=0.0, q_index=None, return_lse=False):
+                                out_dtype=None, softmax_scale=0.0, q_index=None, return_lse=False, out_at_index=False):
     """Block-sparse attention with one CSR per (batch, head): row_ptr [B*H, n_qt+1], col_idx [B*H, stride]."""
     s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
-                                           softmax_scale, q_index, return_lse)
+                                           softmax_scale, q_index, return_lse, out_at_index=out_at_index)
     n_sel = rows if q_index is not None else 0
     if q_index is not None and n_sel == 0:
         return (out, lse) if return_lse else out
@@ -531,11 +544,11 @@ def _scale_arg(t, B, H, dev, name):
 
 
 def var_attn_dense_e4m3(schedule, q, k, k_scale, v, q_scale_begin, q_scale_end, out=None, out_dtype=None,
-                        softmax_scale=0.0, q_index=None, return_lse=False, n_splits=1, workspace=None):
+                        softmax_scale=0.0, q_index=None, return_lse=False, n_splits=1, workspace=None, out_at_index=False):
     """var_attn_dense with e4m3 logits: k as e4m3 codes (uint8) with tile scales [B, H, tiles]
     (var_quantize_e4m3); q bf16, quantised in the call per 64 output rows."""
     s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
-                                           softmax_scale, q_index, return_lse, qk_codes=True)
+                                           softmax_scale, q_index, return_lse, qk_codes=True, out_at_index=out_at_index)
     n_sel = rows if q_index is not None else 0
     if q_index is not None and n_sel == 0:
         return (out, lse) if return_lse else out
@@ -549,11 +562,11 @@ def var_attn_dense_e4m3(schedule, q, k, k_scale, v, q_scale_begin, q_scale_end, 
 
 
 def var_attn_block_sparse_e4m3(schedule, q, k, k_scale, v, q_scale_begin, q_scale_end, row_ptr, col_idx,
-                               out=None, out_dtype=None, softmax_scale=0.0, q_index=None, return_lse=False):
+                               out=None, out_dtype=None, softmax_scale=0.0, q_index=None, return_lse=False, out_at_index=False):
     """Block-sparse attention with e4m3 logits (as var_attn_dense_e4m3).  row_ptr / col_idx 1-D: one CSR
     for every (batch, head); 2-D [B*H, n_qt+1] / [B*H, stride]: one CSR per (batch, head)."""
     s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
-                                           softmax_scale, q_index, return_lse, qk_codes=True)
+                                           softmax_scale, q_index, return_lse, qk_codes=True, out_at_index=out_at_index)
     n_sel = rows if q_index is not None else 0
     if q_index is not None and n_sel == 0:
         return (out, lse) if return_lse else out

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const AttnParams p) {
     }
     if (row_valid) {
         const float inv = l > 0.f ? 1.0f / l : 0.f;
-        float* op = reinterpret_cast<float*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)my_row * p.o_st;
+        float* op = reinterpret_cast<float*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)out_row_of(p, my_row) * p.o_st;
 #pragma unroll
         for (int d = 0; d < D; d += 4)
             *reinterpret_cast<float4*>(op + d) = make_float4(o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv);

@@ -1063,7 +1063,9 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     // ---- epilogue --------------------------------------------------------
     unsigned char* ob = reinterpret_cast<unsigned char*>(p.o);
     const bool partial = n_sp > 1;   // write this split's normalised O and LSE (fp32) for the merge
-    const int64_t part_row0 = ((int64_t)split * p.B * p.H + b * p.H + h) * p.n_rows;
+    // partial rows are numbered over the split items only: (b, h, row) flattened,
+    // from the first row of item split_from (part_first), part_rows per split
+    const int64_t part_row0 = (int64_t)split * p.part_rows + (int64_t)(b * p.H + h) * p.n_rows - p.part_first;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
         const float ltot = lsum[qb] + swap_halves(lsum[qb]);
@@ -1079,6 +1081,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                         make_float4(oacc[mb][qb][4 * a + 0] * inv, oacc[mb][qb][4 * a + 1] * inv,
                                     oacc[mb][qb][4 * a + 2] * inv, oacc[mb][qb][4 * a + 3] * inv);
         } else {
+            const int orow = out_row_of(p, my_row[qb]);
 #pragma unroll
             for (int mb = 0; mb < MO; ++mb) {
 #pragma unroll
@@ -1086,7 +1089,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                     const int d0 = 32 * mb + 8 * a + 4 * g;
                     const float x0 = oacc[mb][qb][4 * a + 0] * inv, x1 = oacc[mb][qb][4 * a + 1] * inv;
                     const float x2 = oacc[mb][qb][4 * a + 2] * inv, x3 = oacc[mb][qb][4 * a + 3] * inv;
-                    const int64_t e = b * p.o_sb + h * p.o_sh + (int64_t)my_row[qb] * p.o_st + d0;
+                    const int64_t e = b * p.o_sb + h * p.o_sh + (int64_t)orow * p.o_st + d0;
                     if constexpr (OUT_BF16) {
                         *reinterpret_cast<u32x2*>(ob + e * 2) = u32x2{f32x2_to_bf16x2(x0, x1), f32x2_to_bf16x2(x2, x3)};
                     } else {
@@ -1123,15 +1126,16 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, in
     if (row >= p.n_rows) return;
     const int b = bh / p.H, h = bh - b * p.H;
     const int64_t rr = (int64_t)bh * p.n_rows + row;
-    const int64_t plane = (int64_t)p.B * p.H * p.n_rows;
+    const int64_t plane = p.part_rows;
     float m = -INFINITY;
-    for (int s = 0; s < p.n_splits; ++s) m = __builtin_fmaxf(m, p.part_lse[s * plane + rr]);
+    const int64_t pr = rr - p.part_first;   // this row among the split items' rows
+    for (int s = 0; s < p.n_splits; ++s) m = __builtin_fmaxf(m, p.part_lse[s * plane + pr]);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float wsum = 0.f;
     if (m != -INFINITY) {
         for (int s = 0; s < p.n_splits; ++s) {
-            const float w = __expf(p.part_lse[s * plane + rr] - m);
-            const float4 o = *reinterpret_cast<const float4*>(p.part_o + (s * plane + rr) * D + 4 * c);
+            const float w = __expf(p.part_lse[s * plane + pr] - m);
+            const float4 o = *reinterpret_cast<const float4*>(p.part_o + (s * plane + pr) * D + 4 * c);
             acc.x += w * o.x;
             acc.y += w * o.y;
             acc.z += w * o.z;
@@ -1140,7 +1144,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, in
         }
     }
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    const int64_t e = b * p.o_sb + h * p.o_sh + (int64_t)row * p.o_st + 4 * c;
+    const int64_t e = b * p.o_sb + h * p.o_sh + (int64_t)out_row_of(p, row) * p.o_st + 4 * c;
     if constexpr (OUT_BF16) {
         *reinterpret_cast<u32x2*>(reinterpret_cast<unsigned char*>(p.o) + e * 2) =
             u32x2{f32x2_to_bf16x2(acc.x * inv, acc.y * inv), f32x2_to_bf16x2(acc.z * inv, acc.w * inv)};

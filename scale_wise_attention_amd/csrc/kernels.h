@@ -31,19 +31,24 @@ struct AttnParams {
     int32_t n_qtiles;    // query tiles per (b, h) of this launch
     int32_t num_scales;
     int32_t step_mode;   // every query lies in the last scale => key limit is kv_len
+    int32_t out_at_index;   // output row i goes to row q_index[i] of o
     float scale;         // softmax scale
     float scale_log2;    // scale * log2(e)
     int32_t scale_end[VAR_MAX_SCALES];  // off[s + 1]
     // key splits (bf16 kernel): work items (batch, head, query tile), numbered
     // bh * n_qtiles + tile, below split_from run whole; with n_splits > 1 each
     // later item runs as n_splits workgroups, each taking an equal share of
-    // its key tiles and writing fp32 O and LSE to part_o
-    // [n_splits][B*H][n_rows][D] / part_lse [n_splits][B*H][n_rows]; a merge
-    // launch then writes their o and lse.  n_splits == 1: split_from = items.
+    // its key tiles and writing fp32 O and LSE to part_o [n_splits][part_rows][D]
+    // / part_lse [n_splits][part_rows]; a merge launch then writes their o and
+    // lse.  The split items' rows are those of the flattened (b*H + h)*n_rows +
+    // row numbering from part_first on (item split_from's first row), so
+    // part_rows = B*H*n_rows - part_first.  n_splits == 1: split_from = items.
     int32_t n_splits;
     int32_t split_from;
     float* part_o;
     float* part_lse;
+    int64_t part_first;
+    int64_t part_rows;
     // per-(batch, head) CSR (block-sparse): element strides between the maps'
     // row_ptr / col_idx arrays (0: one CSR shared by every (batch, head))
     int64_t rp_bh_stride, ci_bh_stride;
@@ -52,6 +57,14 @@ struct AttnParams {
     const float* k_scale;
     int64_t k_scale_stride;
 };
+
+// Row of o that output row `row` of an attention call is written to: itself,
+// or (out_at_index) its gathered position, clamped like the gather.
+__device__ __forceinline__ int out_row_of(const AttnParams& p, int row) {
+    if (!p.out_at_index) return row;
+    const int pos = p.q_index[row];
+    return pos < 0 ? 0 : (pos >= p.n_q ? p.n_q - 1 : pos);
+}
 
 // Largest key-split count of a launch.
 constexpr int kMaxSplits = 8;

@@ -7,7 +7,8 @@
 // the update row i if it is retained (marked per group of rows after one
 // wave-wide search of the ascending index list), else the upsampled base
 // row — so each output byte is written exactly once and no inverse map or
-// second pass is needed.  Copies are 16 bytes per lane when rows, strides and
+// second pass is needed.  Without update rows (upd NULL) the retained rows
+// are skipped: the attention call wrote them in place.  Copies are 16 bytes per lane when rows, strides and
 // pointers allow it (else 4 or 2).
 #include <hip/hip_runtime.h>
 
@@ -89,6 +90,7 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const ScatterParams p
             const int i = src_of[r];
             const unsigned char* src;
             if (i >= 0) {
+                if (!p.upd) continue;   // a retained row written by the attention call itself
                 src = p.upd + m * p.upd_map_stride + (int64_t)i * p.upd_row_stride;
             } else {
                 const int y = t / p.w_out, x = t - y * p.w_out;

@@ -4,6 +4,7 @@
 // HIP runtime, derives the schedule offsets, fills the kernel's parameter
 // block and enqueues the kernel(s) on the caller's stream.  Nothing is
 // allocated, nothing is cached between calls.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -119,6 +120,9 @@ var_status prepare_attn(const var_schedule* sched, const var_attn_desc* d, const
     } else if (n_sel != 0) {
         return fail(VAR_ERR_INDEX, "n_sel=%d given without q_index", n_sel);
     }
+    if (d->out_at_index != 0 && d->out_at_index != 1)
+        return fail(VAR_ERR_RANGE, "out_at_index must be 0 or 1");
+    if (d->out_at_index && !q_index) return fail(VAR_ERR_INDEX, "out_at_index needs q_index");
     if (rows == 0) {   // nothing to compute; o and lse may be empty (NULL) tensors
         *nothing_to_do = true;
         return ok();
@@ -147,6 +151,7 @@ var_status prepare_attn(const var_schedule* sched, const var_attn_desc* d, const
     p->kv_len = off.off[d->q_scale_end];
     p->num_scales = d->q_scale_end;   // scales beyond the call's last are never visible
     p->step_mode = (d->q_scale_end - d->q_scale_begin == 1) ? 1 : 0;
+    p->out_at_index = d->out_at_index;
     const float scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->head_dim);
     p->scale = scale;
     p->scale_log2 = scale * 1.4426950408889634f;
@@ -155,49 +160,98 @@ var_status prepare_attn(const var_schedule* sched, const var_attn_desc* d, const
     return ok();
 }
 
-// Bytes of the split workspace: fp32 O and LSE per split, row and (batch, head).
-int64_t split_workspace_bytes(int32_t splits, int64_t bh, int64_t rows, int32_t D) {
-    return splits > 1 ? (int64_t)splits * bh * rows * (D + 1) * 4 : 0;
+// Split items and partial rows of a launch with `items` work items of `rpt`
+// rows (bh maps of `rows` rows each) on `cap` resident workgroups: the items
+// that fill whole rounds run unsplit (split_from = items / cap * cap); the
+// partial rows are those of the split items, numbered in the flattened
+// (map, row) order from the first row of item split_from on.
+struct SplitRows {
+    int64_t split_from, part_first, part_rows;
+};
+SplitRows split_rows(int64_t bh, int64_t rows, int64_t rpt, int64_t cap) {
+    const int64_t n_qt = (rows + rpt - 1) / rpt, items = bh * n_qt;
+    SplitRows r;
+    r.split_from = items / cap * cap;
+    r.part_first = r.split_from >= items ? bh * rows : (r.split_from / n_qt) * rows + (r.split_from % n_qt) * rpt;
+    r.part_rows = bh * rows - r.part_first;
+    return r;
 }
 
-// Points the parameter block at a split workspace after checking it.
-var_status attach_splits(varattn::AttnParams* p, const var_attn_desc* d, int32_t splits, void* ws,
-                         int64_t ws_bytes) {
+// Bytes of the split workspace the kernels use: fp32 O and LSE per split and
+// partial row.
+int64_t split_need_bytes(int32_t splits, int64_t part_rows, int32_t D) {
+    return splits > 1 ? (int64_t)splits * part_rows * (D + 1) * 4 : 0;
+}
+
+// Records a split request after its basic checks; the workspace size is
+// checked by set_split_items once the split items are known.
+var_status attach_splits(varattn::AttnParams* p, const var_attn_desc* d, int32_t splits, void* ws) {
     if (splits < 1 || splits > varattn::kMaxSplits)
         return fail(VAR_ERR_RANGE, "n_splits=%d outside [1, %d]", splits, varattn::kMaxSplits);
     if (splits == 1) return VAR_OK;
     if (d->in_dtype != VAR_BF16) return fail(VAR_ERR_UNSUPPORTED, "key splits need bf16 input");
-    const int64_t bh = (int64_t)p->B * p->H;
-    const int64_t need = split_workspace_bytes(splits, bh, p->n_rows, d->head_dim);
     if (!ws) return fail(VAR_ERR_NULL, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(ws) & 15u) return fail(VAR_ERR_STRIDE, "workspace must be 16-byte aligned");
-    if (ws_bytes < need)
-        return fail(VAR_ERR_CAPACITY, "workspace of %lld bytes below the %lld needed", (long long)ws_bytes,
-                    (long long)need);
     p->n_splits = splits;
     p->part_o = static_cast<float*>(ws);
-    p->part_lse = p->part_o + (int64_t)splits * bh * p->n_rows * d->head_dim;
     return VAR_OK;
 }
 
+// Compute units and peak engine clock (kHz) of the current device, read once
+// per device.  From the device properties record (its layout is versioned in
+// the HIP ABI), not from hipDeviceGetAttribute, whose attribute numbers differ
+// between HIP runtime releases (the process may run on another release of the
+// runtime than these headers describe).  {0, 0} when there is no device.
+struct DeviceInfo {
+    int cus, clock_khz;
+};
+DeviceInfo device_info() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<long long> cache[kMaxDevices];   // cus << 32 | clock_khz, 0 = not read yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return {0, 0};
+    }
+    if (dev < kMaxDevices) {
+        const long long c = cache[dev].load(std::memory_order_relaxed);
+        if (c) return {(int)(c >> 32), (int)(c & 0xffffffff)};
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return {0, 0};
+    }
+    const DeviceInfo r{prop.multiProcessorCount, prop.clockRate};
+    if (dev < kMaxDevices && r.cus > 0)
+        cache[dev].store(((long long)r.cus << 32) | (unsigned)r.clock_khz, std::memory_order_relaxed);
+    return r;
+}
+
 int device_cu_count() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-        return n;
-    return 256;
+    const int n = device_info().cus;
+    return n > 0 ? n : 256;
 }
 
 // Items of a key-split launch: those that fill whole rounds of the device's
 // resident workgroups run unsplit (split_from); only the remaining partial
 // round is split (every item when there are fewer than one round's worth).
-// Checks that the launch grid stays below 2^31.
-var_status set_split_items(varattn::AttnParams* p, int resident_per_cu) {
+// Checks that the launch grid stays below 2^31 and that the workspace holds
+// the split items' partial rows, and points part_o / part_lse into it.
+var_status set_split_items(varattn::AttnParams* p, int resident_per_cu, int rpt, int D, int64_t ws_bytes) {
     const int64_t items = (int64_t)p->n_qtiles * p->B * p->H;
     int64_t from = items;
     if (p->n_splits > 1) {
-        const int64_t cap = (int64_t)device_cu_count() * resident_per_cu;
-        from = items / cap * cap;
+        const SplitRows r = split_rows((int64_t)p->B * p->H, p->n_rows, rpt,
+                                       (int64_t)device_cu_count() * resident_per_cu);
+        from = r.split_from;
+        const int64_t need = split_need_bytes(p->n_splits, r.part_rows, D);
+        if (ws_bytes < need)
+            return fail(VAR_ERR_CAPACITY, "workspace of %lld bytes below the %lld needed", (long long)ws_bytes,
+                        (long long)need);
+        p->part_first = r.part_first;
+        p->part_rows = r.part_rows;
+        p->part_lse = p->part_o + p->n_splits * r.part_rows * D;
     }
     if (from + (items - from) * p->n_splits >= ((int64_t)1 << 31)) return fail(VAR_ERR_RANGE, "launch grid too large");
     p->split_from = (int32_t)from;
@@ -249,6 +303,14 @@ VAR_EXPORT const char* var_status_string(var_status s) {
 
 VAR_EXPORT const char* var_last_error(void) { return g_last_error; }
 
+VAR_EXPORT var_status var_device_info(int32_t* compute_units, int32_t* max_clock_khz) {
+    const DeviceInfo d = device_info();
+    if (d.cus <= 0) return fail(VAR_ERR_HIP, "no current HIP device");
+    if (compute_units) *compute_units = d.cus;
+    if (max_clock_khz) *max_clock_khz = d.clock_khz;
+    return ok();
+}
+
 VAR_EXPORT var_status var_schedule_extent(const var_schedule* sched, int32_t b, int32_t e, int64_t* first_token,
                                           int64_t* n_q, int64_t* kv_len) {
     Offsets off;
@@ -299,14 +361,15 @@ var_status dense_impl(const var_schedule* sched, const var_attn_desc* desc, cons
     var_status st = prepare_attn(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, &p, &none);
     if (st != VAR_OK) return st;
     if (e4m3 && !none && (st = check_e4m3(desc, k_l, *e4m3, p)) != VAR_OK) return st;
-    if ((st = attach_splits(&p, desc, none ? 1 : splits, ws, ws_bytes)) != VAR_OK) return st;
+    if ((st = attach_splits(&p, desc, none ? 1 : splits, ws)) != VAR_OK) return st;
     if (none) return ok();
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (e4m3) {
         attach_e4m3(&p, *e4m3);
         const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false);
         p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
-        if ((st = set_split_items(&p, varattn::attn_fp8_resident_wgs(desc->out_dtype == VAR_BF16, false))) != VAR_OK)
+        if ((st = set_split_items(&p, varattn::attn_fp8_resident_wgs(desc->out_dtype == VAR_BF16, false), rpt,
+                                  desc->head_dim, ws_bytes)) != VAR_OK)
             return st;
         return hip_status(varattn::launch_attn_fp8(p, desc->head_dim, desc->out_dtype == VAR_BF16, false, s),
                           "var_attn_dense_e4m3 launch");
@@ -315,7 +378,8 @@ var_status dense_impl(const var_schedule* sched, const var_attn_desc* desc, cons
         const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false);
         p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
         const bool ob = desc->out_dtype == VAR_BF16;
-        if ((st = set_split_items(&p, varattn::attn_bf16_resident_wgs(desc->head_dim, ob, false))) != VAR_OK)
+        if ((st = set_split_items(&p, varattn::attn_bf16_resident_wgs(desc->head_dim, ob, false), rpt,
+                                  desc->head_dim, ws_bytes)) != VAR_OK)
             return st;
         return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, desc->out_dtype == VAR_BF16, false, s),
                           "var_attn_dense launch");
@@ -338,7 +402,7 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
     var_status st = prepare_attn(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, &p, &none);
     if (st != VAR_OK) return st;
     if (e4m3 && !none && (st = check_e4m3(desc, k_l, *e4m3, p)) != VAR_OK) return st;
-    if ((st = attach_splits(&p, desc, none ? 1 : splits, ws, ws_bytes)) != VAR_OK) return st;
+    if ((st = attach_splits(&p, desc, none ? 1 : splits, ws)) != VAR_OK) return st;
     if (none) return ok();
     p.row_ptr = row_ptr;
     p.col_idx = col_idx;
@@ -360,7 +424,7 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
         const bool ob = desc->out_dtype == VAR_BF16;
         const int resident = e4m3 ? varattn::attn_fp8_resident_wgs(ob, true)
                                   : varattn::attn_bf16_resident_wgs(desc->head_dim, ob, true);
-        if ((st = set_split_items(&p, resident)) != VAR_OK) return st;
+        if ((st = set_split_items(&p, resident, rpt, desc->head_dim, ws_bytes)) != VAR_OK) return st;
         if (e4m3) {
             attach_e4m3(&p, *e4m3);
             return hip_status(varattn::launch_attn_fp8(p, desc->head_dim, desc->out_dtype == VAR_BF16, true, s),
@@ -595,7 +659,18 @@ VAR_EXPORT var_status var_attn_split_plan(const var_schedule* sched, const var_a
         s = choose_splits(tasks, tiles, bh * rows, d->head_dim, cap);
     }
     if (n_splits) *n_splits = s;
-    if (workspace_bytes) *workspace_bytes = split_workspace_bytes(s, bh, rows, d->head_dim);
+    if (workspace_bytes) {
+        *workspace_bytes = 0;
+        if (s > 1) {   // enough for a dense or a block-sparse call (their work items differ)
+            for (const bool sp : {false, true}) {
+                const int rpt = varattn::attn_bf16_rows_per_tile(d->head_dim, sp);
+                const int64_t cap = (int64_t)device_cu_count() *
+                                    varattn::attn_bf16_resident_wgs(d->head_dim, d->out_dtype == VAR_BF16, sp);
+                const int64_t need = split_need_bytes(s, split_rows(bh, rows, rpt, cap).part_rows, d->head_dim);
+                *workspace_bytes = need > *workspace_bytes ? need : *workspace_bytes;
+            }
+        }
+    }
     return ok();
 }
 
@@ -783,14 +858,14 @@ VAR_EXPORT var_status var_scatter_restore(int32_t maps, int32_t row_elems, var_d
         return fail(VAR_ERR_RANGE, "grid sizes invalid");
     if (n_sel < 0 || (int64_t)n_sel > (int64_t)h_out * w_out)
         return fail(VAR_ERR_INDEX, "n_sel=%d outside [0, h_out*w_out]", n_sel);
-    if (!base || !out || (n_sel > 0 && (!upd || !q_index)))
-        return fail(VAR_ERR_NULL, "base, out (and upd, q_index when n_sel > 0) must be non-NULL");
+    if (!base || !out || (n_sel > 0 && !q_index))
+        return fail(VAR_ERR_NULL, "base, out (and q_index when n_sel > 0) must be non-NULL");
     const int eb = dtype == VAR_BF16 ? 2 : 4;
     const int64_t strides[6] = {base_map_stride, base_row_stride, upd_map_stride, upd_row_stride, out_map_stride,
                                 out_row_stride};
     for (int i = 0; i < 6; ++i)
         if (strides[i] < 0) return fail(VAR_ERR_STRIDE, "strides must be non-negative");
-    if (base_row_stride < row_elems || out_row_stride < row_elems || (n_sel > 0 && upd_row_stride < row_elems))
+    if (base_row_stride < row_elems || out_row_stride < row_elems || (n_sel > 0 && upd && upd_row_stride < row_elems))
         return fail(VAR_ERR_STRIDE, "row strides must be >= row_elems");
     if (maps == 0) return ok();
     varattn::ScatterParams p;

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header(api):
     declared = _declared()
-    assert len(declared) == 20
+    assert len(declared) == 21
     for name in declared:
         assert hasattr(api.LIB, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True).stdout
@@ -208,8 +208,13 @@ def test_split_validation_and_plan(api):
     assert call(d, 9) == E("VAR_ERR_RANGE")
     assert call(d, 2, ws=0) == E("VAR_ERR_NULL")
     assert call(d, 2, ws=FAKE + 4) == E("VAR_ERR_STRIDE")
-    need = 2 * 32 * 4096 * 129 * 4
-    assert call(d, 2, nbytes=need - 1) == E("VAR_ERR_CAPACITY")
+    # the 48x48 step: 288 work items of 256 rows; on 256 compute units (the count the
+    # library assumes without a device) items 256..287 run split: rows from
+    # (b, h) = 28, row 1024 on, 8192 of them, fp32 O and LSE for each of 2 parts
+    d48 = _desc(api, q_scale_begin=11, q_scale_end=12)
+    need = 2 * (32 * 2304 - (28 * 2304 + 4 * 256)) * 129 * 4
+    assert need == 2 * 8192 * 129 * 4
+    assert call(d48, 2, nbytes=need - 1) == E("VAR_ERR_CAPACITY")
     f32 = _desc(api, head_dim=64, in_dtype=api.VAR_F32)
     assert call(f32, 2) == E("VAR_ERR_UNSUPPORTED")
     n, nbytes = api.var_attn_split_plan((W1024, W1024), 12, 13, 2, 16, 128)
@@ -219,7 +224,7 @@ def test_split_validation_and_plan(api):
     assert api.var_attn_split_plan((W1024, W1024), 9, 10, 2, 16, 64, dtype=torch.float32) == (1, 0)
     # 288 work items: one whole round of 256 plus 32 items of 101 key tiles that the split spreads
     n, nbytes = api.var_attn_split_plan((W1024, W1024), 11, 12, 2, 16, 128)
-    assert n >= 4 and nbytes == n * 32 * 2304 * 129 * 4
+    assert n >= 4 and nbytes == n * 8192 * 129 * 4         # only the 32 split items' rows
     sp = api.LIB.var_attn_block_sparse_split
     r = sp(ctypes.byref(s), ctypes.byref(d), P(FAKE), L, P(FAKE), L, P(FAKE), L, P(FAKE), L, P(0), P(0), 0,
            P(FAKE), P(FAKE), 64, 64, 9, P(FAKE), 1 << 40, P(0))
@@ -301,3 +306,20 @@ def test_e4m3_validation_errors(api):
     assert sparse(stride=-1) == E("VAR_ERR_RANGE")
     assert sparse(stride=64 * 165 - 1) == E("VAR_ERR_CAPACITY")
     assert sparse(rp=0) == E("VAR_ERR_NULL")
+
+
+def test_out_at_index_needs_q_index(api):
+    """out_at_index = 1 without a q_index, or another value, is rejected before any HIP call."""
+    s = api.make_schedule(W1024, W1024)
+    assert _dense(api, s, _desc(api, out_at_index=1)) == _code(api, "VAR_ERR_INDEX")
+    assert _dense(api, s, _desc(api, out_at_index=2), q_index=FAKE, n_sel=16) == _code(api, "VAR_ERR_RANGE")
+
+
+def test_device_info_without_a_device(api):
+    """No HIP device here: the query reports VAR_ERR_HIP instead of a made-up count."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present (the GPU tests check the values)")
+    with pytest.raises(api.VarAttnError) as e:
+        api.var_device_info()
+    assert e.value.status_name == "VAR_ERR_HIP"

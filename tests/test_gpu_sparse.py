@@ -314,6 +314,40 @@ def test_scatter_more_row_groups_than_workgroups(api):
     assert np.array_equal(out.view(torch.int16).cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("path", ["short list", "long list"])
+def test_scatter_paths_full_and_base_only(api, path):
+    """A short index list (1638 of 64x64) and a long one (20000 of 160x160, 42 maps x
+    1600 row groups, more than the launch's 65536 workgroups).  Full scatter bit-exact
+    against the oracle; base-only (upd NULL) leaves the retained rows untouched and
+    writes every other row as the oracle."""
+    if path == "short list":
+        maps, E, hi, ho, n_sel, seed = 32, 128, 48, 64, 1638, 5
+    else:
+        maps, E, hi, ho, n_sel, seed = 42, 128, 100, 160, 20000, 6
+    base = torch.from_numpy(normal_tensor((maps, hi * hi, E), seed)).to(torch.bfloat16).cuda()
+    sel = np.sort(np.random.default_rng(seed).choice(ho * ho, n_sel, replace=False)).astype(np.int32)
+    upd = torch.from_numpy(normal_tensor((maps, n_sel, E), seed + 1)).to(torch.bfloat16).cuda()
+    idx = torch.from_numpy(sel).cuda()
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = api.var_scatter_restore(base, hi, hi, upd, idx, ho, ho, err_flag=flag)
+    ref = oracle.scatter_restore(base.view(torch.int16).cpu().numpy(), hi, hi, upd.view(torch.int16).cpu().numpy(),
+                                 sel, ho, ho)
+    assert np.array_equal(out.view(torch.int16).cpu().numpy(), ref) and int(flag.item()) == 0
+    sentinel = torch.full_like(out, float("nan"))
+    api.var_scatter_restore(base, hi, hi, None, idx, ho, ho, out=sentinel)
+    got = sentinel.view(torch.int16).cpu().numpy()
+    keep = np.ones(ho * ho, bool)
+    keep[sel] = False
+    assert np.array_equal(got[:, keep], ref[:, keep])
+    assert np.array_equal(got[:, sel], np.full_like(got[:, sel], torch.tensor(float("nan"), dtype=torch.bfloat16)
+                                                     .view(torch.int16).item()))
+    bad = idx.clone()
+    bad[5] = bad[4]
+    flag.zero_()
+    api.var_scatter_restore(base, hi, hi, upd, bad, ho, ho, err_flag=flag)
+    assert int(flag.item()) & 2
+
+
 def test_scatter_edge_cases(api):
     # no index: pure nearest upsampling; odd row widths take the 2-byte path
     for (hi, wi, ho, wo, E) in [(48, 48, 64, 64, 64), (3, 5, 7, 9, 3), (4, 4, 4, 4, 8), (7, 3, 5, 2, 5)]:
@@ -390,3 +424,73 @@ def test_sparse_rows_whose_first_tiles_differ(api):
         ref = oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], wl.h, wl.w,
                                s, s + 1, kept=kept, rows=rows)
         _check(_np(o[b:b + 1, h:h + 1])[:, :, rows], ref, what=f"first tiles differ b{b} h{h}")
+
+
+def test_pruned_rows_written_in_place_and_base_only_scatter(api):
+    """The reconstruction fused into the pruned attention ("ARVAR ...", Key Design 3,
+    Eq. (8)-(9)): the attention writes each retained row straight to its place in the
+    64x64 grid (out_at_index) and the scatter fills only the other rows from the
+    nearest-upsampled base (upd NULL).  In either order the result equals, bit for bit,
+    the oracle's reconstruction from the same base and the attention's rows; the
+    attention rows themselves equal those of the gathered call."""
+    wl = WORKLOADS["var1024_sparse"]
+    q, k, v = make_qkv(wl, 3, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    K = wl.num_scales
+    sel = pruned_index(4096, 0.4, 3)
+    idx = torch.from_numpy(sel).cuda()
+    qs = q[:, :, off[K - 1]:]
+    mp = api.mask_params()
+    rp, ci = api.var_build_tile_mask((wl.h, wl.w), K - 1, K, mp, q_index=idx)
+    base = api.var_attn_dense((wl.h, wl.w), q[:, :, off[K - 2]:off[K - 1]], k, v, K - 2, K - 1,
+                              out_dtype=torch.bfloat16)
+    upd = api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, K - 1, K, rp, ci, q_index=idx, out_dtype=torch.bfloat16)
+    ref = oracle.scatter_restore(base.view(torch.int16).cpu().numpy().reshape(32, 2304, 128), 48, 48,
+                                 upd.view(torch.int16).cpu().numpy().reshape(32, 1638, 128), sel, 64, 64)
+    for order in ("attention first", "scatter first"):
+        out = torch.full((2, 16, 4096, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+        calls = [lambda: api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, K - 1, K, rp, ci, q_index=idx, out=out,
+                                                   out_at_index=True),
+                 lambda: api.var_scatter_restore(base, 48, 48, None, idx, 64, 64, out=out)]
+        for c in (calls if order == "attention first" else calls[::-1]):
+            c()
+        got = out.view(torch.int16).cpu().numpy().reshape(32, 4096, 128)
+        assert np.array_equal(got, ref), order
+    # the same through the dense, key-split and e4m3 kernels: rows land where the gather took them
+    out = torch.zeros(2, 16, 4096, 128, dtype=torch.float32, device="cuda")
+    api.var_attn_dense((wl.h, wl.w), qs, k, v, K - 1, K, q_index=idx, out=out, out_at_index=True)
+    dense_g = api.var_attn_dense((wl.h, wl.w), qs, k, v, K - 1, K, q_index=idx)
+    assert torch.equal(out[:, :, idx.long()], dense_g)
+    untouched = torch.ones(4096, dtype=torch.bool, device="cuda")
+    untouched[idx.long()] = False
+    assert int(torch.count_nonzero(out[:, :, untouched])) == 0
+    ws = api.split_workspace(3, 2, 16, sel.size, 128)
+    out.zero_()
+    api.var_attn_dense((wl.h, wl.w), qs, k, v, K - 1, K, q_index=idx, out=out, out_at_index=True, n_splits=3,
+                       workspace=ws)
+    split_g = api.var_attn_dense((wl.h, wl.w), qs, k, v, K - 1, K, q_index=idx, n_splits=3, workspace=ws)
+    assert torch.equal(out[:, :, idx.long()], split_g)
+    assert int(torch.count_nonzero(out[:, :, untouched])) == 0
+    k8, sk = api.var_quantize_e4m3(k)
+    out8 = torch.zeros(2, 16, 4096, 128, dtype=torch.bfloat16, device="cuda")
+    api.var_attn_block_sparse_e4m3((wl.h, wl.w), qs, k8, sk, v, K - 1, K, rp, ci, q_index=idx, out=out8,
+                                   out_at_index=True)
+    g8 = api.var_attn_block_sparse_e4m3((wl.h, wl.w), qs, k8, sk, v, K - 1, K, rp, ci, q_index=idx,
+                                        out_dtype=torch.bfloat16)
+    assert torch.equal(out8[:, :, idx.long()], g8)
+
+
+def test_out_at_index_fp32_kernel_and_errors(api):
+    wl = WORKLOADS["tiny_fp32"]
+    q, k, v = make_qkv(wl, 4, device="cuda")
+    sel = np.array([1, 4, 8], np.int32)
+    idx = torch.from_numpy(sel).cuda()
+    qs = q[:, :, 5:14]
+    out = torch.full((1, 2, 9, 32), -7.0, device="cuda")
+    api.var_attn_dense((wl.h, wl.w), qs, k, v, 2, 3, q_index=idx, out=out, out_at_index=True)
+    g = api.var_attn_dense((wl.h, wl.w), qs, k, v, 2, 3, q_index=idx)
+    assert torch.equal(out[:, :, idx.long()], g)
+    rest = [i for i in range(9) if i not in sel]
+    assert bool((out[:, :, rest] == -7.0).all())
+    with pytest.raises(ValueError):
+        api.var_attn_dense((wl.h, wl.w), qs, k, v, 2, 3, out_at_index=True)

@@ -164,7 +164,8 @@ def test_sparse_split_matches_oracle(api, step, splits, pruned):
 def test_split_plan_and_errors(api):
     wl = WORKLOADS["var1024"]
     n, nbytes = api.var_attn_split_plan((wl.h, wl.w), 11, 12, 2, 16, 128)
-    assert 1 <= n <= 8 and nbytes == (n * 32 * 2304 * 129 * 4 if n > 1 else 0)
+    # (256 compute units: items 256..287 split, 8192 rows from (b, h) 28, row 1024 on)
+    assert 1 <= n <= 8 and nbytes == (n * 8192 * 129 * 4 if n > 1 else 0)
     q, k, v = make_qkv(wl, 0, device="cuda")
     off = oracle.offsets(wl.h, wl.w)
     qs = q[:, :, off[9]:off[10]]
@@ -175,3 +176,11 @@ def test_split_plan_and_errors(api):
     with pytest.raises(api.VarAttnError) as e:
         api.var_attn_dense((wl.h, wl.w), qs, k, v, 9, 10, n_splits=9, workspace=short)
     assert e.value.status_name == "VAR_ERR_RANGE"
+
+
+def test_device_info_matches_torch(api):
+    """The compute units the split plan assumes are the device's (torch reads them
+    through its own HIP runtime), and the peak clock is a plausible engine clock."""
+    cus, khz = api.var_device_info()
+    assert cus == torch.cuda.get_device_properties(0).multi_processor_count
+    assert 500_000 <= khz <= 5_000_000
