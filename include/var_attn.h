@@ -180,6 +180,26 @@ var_status var_attn_block_sparse_split(const var_schedule* sched, const var_attn
                                        void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * var_attn_dense_split without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the fp32 partials go to a static device array of
+ * the library, VAR_NOALLOC_SCRATCH_BYTES per device (held from library load to
+ * process end; its address is looked up once per device).  The call itself
+ * allocates nothing.  A call whose split partials (the bytes
+ * var_attn_split_plan reports for it) exceed the array returns
+ * VAR_ERR_CAPACITY before any HIP call; n_splits = 1 uses no scratch.  Every
+ * call on a device shares that device's array: calls that overlap on one
+ * device (other streams, other threads) race and must be ordered by the
+ * caller.  Other arguments and errors as in var_attn_dense_split.
+ */
+#define VAR_NOALLOC_SCRATCH_BYTES (64ll << 20)
+var_status var_attn_dense_split_noalloc(const var_schedule* sched, const var_attn_desc* desc,
+                                        const void* q, var_layout q_l, const void* k, var_layout k_l,
+                                        const void* v, var_layout v_l, void* o, var_layout o_l,
+                                        float* lse, const int32_t* q_index, int32_t n_sel,
+                                        int32_t n_splits, void* stream);
+
+/*
  * Split count for a call (host only; reads the current device's compute-unit
  * count, 256 if it cannot): the count with the smallest modelled time
  * (the unsplit rounds, then rounds of parts over the resident workgroups

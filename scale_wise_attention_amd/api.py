@@ -33,6 +33,7 @@ EXPORTED = ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_
             "var_attn_dense_split", "var_attn_block_sparse_split", "var_attn_split_plan",
             "var_attn_block_mass", "var_decision_tiles", "var_mapped_tile_mask", "var_attn_block_sparse_heads",
             "var_quantize_e4m3", "var_attn_dense_e4m3", "var_attn_block_sparse_e4m3", "var_device_info",
+            "var_attn_dense_split_noalloc",
             "var_status_string", "var_last_error")
 
 
@@ -100,6 +101,8 @@ def _load():
     lib.var_attn_block_sparse_e4m3.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, i64,
                                                P, Layout, P, Layout, P, P, i32, P, P, i64, P]
     lib.var_device_info.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.var_attn_dense_split_noalloc.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, Layout, P,
+                                                 Layout, P, P, i32, i32, P]
     for name in EXPORTED[:-2]:
         getattr(lib, name).restype = ctypes.c_int
     lib.var_status_string.argtypes = [ctypes.c_int]
@@ -272,6 +275,22 @@ def var_attn_dense(schedule, q, k, v, q_scale_begin, q_scale_end, out=None, out_
     else:
         wp, wb = _ws_args(n_splits, workspace)
         _check(LIB.var_attn_dense_split(*args, int(n_splits), wp, wb, _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+def var_attn_dense_split_noalloc(schedule, q, k, v, q_scale_begin, q_scale_end, n_splits, out=None,
+                                 out_dtype=None, softmax_scale=0.0, q_index=None, return_lse=False,
+                                 out_at_index=False):
+    """var_attn_dense with n_splits key splits whose partials go to the library's static
+    device scratch instead of a workspace (no allocation in the call)."""
+    s, desc, out, lse, rows = _attn_common(schedule, q, k, v, q_scale_begin, q_scale_end, out, out_dtype,
+                                           softmax_scale, q_index, return_lse, out_at_index=out_at_index)
+    n_sel = rows if q_index is not None else 0
+    if q_index is not None and n_sel == 0:
+        return (out, lse) if return_lse else out
+    _check(LIB.var_attn_dense_split_noalloc(ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k),
+                                            _layout(k), _ptr(v), _layout(v), _ptr(out), _layout(out), _ptr(lse),
+                                            _ptr(q_index), n_sel, int(n_splits), _stream(q.device)))
     return (out, lse) if return_lse else out
 
 

@@ -683,6 +683,67 @@ VAR_EXPORT var_status var_attn_dense_split(const var_schedule* sched, const var_
                       workspace_bytes, stream);
 }
 
+namespace {
+
+// The split partials of var_attn_dense_split_noalloc: a file-scope device
+// array, one copy per device (loaded with the code object), reached from the
+// host through its device address, looked up once per device.
+constexpr int64_t kScratchBytes = VAR_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+void* scratch_address() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void*> addr[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* ptr = addr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        addr[dev].store(ptr, std::memory_order_release);
+    }
+    return ptr;
+}
+
+}  // namespace
+
+VAR_EXPORT var_status var_attn_dense_split_noalloc(const var_schedule* sched, const var_attn_desc* desc,
+                                                   const void* q, var_layout q_l, const void* k, var_layout k_l,
+                                                   const void* v, var_layout v_l, void* o, var_layout o_l,
+                                                   float* lse, const int32_t* q_index, int32_t n_sel,
+                                                   int32_t n_splits, void* stream) {
+    if (n_splits == 1)
+        return dense_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, 1, nullptr, 0, stream);
+    // the partials this call needs, checked against the scratch before any HIP call
+    Offsets off;
+    var_status st = check_schedule(sched, &off);
+    if (st != VAR_OK) return st;
+    if (!desc) return fail(VAR_ERR_NULL, "desc is NULL");
+    if ((st = check_range(off, desc->q_scale_begin, desc->q_scale_end)) != VAR_OK) return st;
+    if (n_splits < 1 || n_splits > varattn::kMaxSplits)
+        return fail(VAR_ERR_RANGE, "n_splits=%d outside [1, %d]", n_splits, varattn::kMaxSplits);
+    if (desc->in_dtype != VAR_BF16 || (desc->head_dim != 64 && desc->head_dim != 128))
+        return fail(VAR_ERR_UNSUPPORTED, "key splits need bf16 input with head_dim 64 or 128");
+    if (desc->batch < 1 || desc->heads < 1 || (int64_t)desc->batch * desc->heads > (1 << 20))
+        return fail(VAR_ERR_RANGE, "batch=%d heads=%d invalid", desc->batch, desc->heads);
+    const int64_t n_q = off.off[desc->q_scale_end] - off.off[desc->q_scale_begin];
+    const int64_t rows = q_index ? n_sel : n_q;
+    if (rows > 0) {
+        const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false);
+        const int64_t cap = (int64_t)device_cu_count() *
+                            varattn::attn_bf16_resident_wgs(desc->head_dim, desc->out_dtype == VAR_BF16, false);
+        const int64_t need = split_need_bytes(n_splits, split_rows((int64_t)desc->batch * desc->heads, rows, rpt,
+                                                                   cap).part_rows, desc->head_dim);
+        if (need > kScratchBytes)
+            return fail(VAR_ERR_CAPACITY, "the call needs %lld bytes of split partials, above the library's "
+                        "static scratch of %lld bytes (use var_attn_dense_split with a workspace)",
+                        (long long)need, (long long)kScratchBytes);
+    }
+    void* ws = scratch_address();
+    if (!ws) return fail(VAR_ERR_HIP, "the address of the static scratch is unavailable on this device");
+    return dense_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, n_splits, ws,
+                      kScratchBytes, stream);
+}
+
 VAR_EXPORT var_status var_attn_block_sparse_split(const var_schedule* sched, const var_attn_desc* desc,
                                                   const void* q, var_layout q_l, const void* k, var_layout k_l,
                                                   const void* v, var_layout v_l, void* o, var_layout o_l,

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header(api):
     declared = _declared()
-    assert len(declared) == 21
+    assert len(declared) == 22
     for name in declared:
         assert hasattr(api.LIB, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True).stdout
@@ -323,3 +323,18 @@ def test_device_info_without_a_device(api):
     with pytest.raises(api.VarAttnError) as e:
         api.var_device_info()
     assert e.value.status_name == "VAR_ERR_HIP"
+
+
+def test_noalloc_split_rejects_oversized_calls_before_any_hip_call(api):
+    """The allocation-free split call checks its partials against the static scratch
+    first: 8 parts of the 32x32 step (135 MB) exceed the 64 MiB."""
+    s = api.make_schedule(W1024, W1024)
+    L = api.Layout(2 * 16 * 4096 * 128, 4096 * 128, 128)
+    P = ctypes.c_void_p
+    d = _desc(api, q_scale_begin=9, q_scale_end=10)
+    r = api.LIB.var_attn_dense_split_noalloc(ctypes.byref(s), ctypes.byref(d), P(FAKE), L, P(FAKE), L, P(FAKE), L,
+                                             P(FAKE), L, P(0), P(0), 0, 8, P(0))
+    assert r == _code(api, "VAR_ERR_CAPACITY")
+    assert b"static scratch" in api.LIB.var_last_error()
+    assert api.LIB.var_attn_dense_split_noalloc(ctypes.byref(s), ctypes.byref(d), P(FAKE), L, P(FAKE), L, P(FAKE),
+                                                L, P(FAKE), L, P(0), P(0), 0, 9, P(0)) == _code(api, "VAR_ERR_RANGE")
