@@ -168,6 +168,10 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32, help="(b, h) pairs in the oracle's CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph replay")
+    ap.add_argument("--profile-launches", type=int, default=0, metavar="N",
+                    help="instead of timing: run each launch group N times, eagerly, one group after another, "
+                         "with a one-element int16 fill before each group (a marker for a profiler's dispatch "
+                         "list), print the group names as JSON and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -358,6 +362,45 @@ def main():
         rows = n_sel if idx is not None else off[s + 1] - off[s]
         sparse_flops.append(acc.sparse_step_flops(wl, rp_h, ci_h, rows, off[s + 1]))
     pass_flops = sum(dense_flops) + sum(sparse_flops)
+
+    if args.profile_launches > 0:
+        # e4m3 keys of the whole sequence for the e4m3 groups
+        k8 = torch.empty(B, H, off[K], D, dtype=torch.uint8, device=dev)
+        sk8 = torch.empty(B, H, -(-off[K] // 64), dtype=torch.float32, device=dev)
+        f8_out = torch.empty(B, H, 4096, D, dtype=bf, device=dev)
+        api.var_quantize_e4m3(k, codes=k8, scale=sk8, first_token=0)
+        # a plain device copy of 256 MiB: the scale of the byte counters
+        copy_src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        copy_dst = torch.empty_like(copy_src)
+        groups = [(f"dense s{s}", lambda s=s: dense_step(s)) for s in range(K)]
+        groups += [(f"mask s{s}", lambda s=s: mask_step(s)) for s in range(K) if not full_mask[s]]
+        groups += [(f"sparse s{s}", lambda s=s: sparse_step(s)) for s in range(K - 1) if not full_mask[s]]
+        groups += [("pruned gathered", lambda: sparse_step(K - 1)),
+                   ("pruned in place", lambda: sparse_step(K - 1, in_place=True)),
+                   ("base scatter", base_scatter),
+                   ("scatter", scatter_step),
+                   ("mask unpruned last", lambda: api.var_build_tile_mask(sched, K - 1, K, mp, row_ptr=full_rp,
+                                                                          col_idx=full_ci)),
+                   ("sparse unpruned last", lambda: api.var_attn_block_sparse(sched, qsteps[K - 1], k, v, K - 1, K,
+                                                                             full_rp, full_ci, out=full_out)),
+                   ("e4m3 quantize last", lambda: api.var_quantize_e4m3(k, codes=k8, scale=sk8,
+                                                                        first_token=off[K - 1])),
+                   ("e4m3 dense last", lambda: api.var_attn_dense_e4m3(sched, qsteps[K - 1], k8, sk8, v, K - 1, K,
+                                                                       out=f8_out)),
+                   ("copy 256MiB", lambda: copy_dst.copy_(copy_src))]
+        marker = torch.empty(1, dtype=torch.int16, device=dev)
+        api.var_build_tile_mask(sched, K - 1, K, mp, row_ptr=full_rp, col_idx=full_ci)
+        torch.cuda.synchronize()
+        for i, (_, fn) in enumerate(groups):
+            marker.fill_(i)
+            for _ in range(args.profile_launches):
+                fn()
+            torch.cuda.synchronize()
+        marker.fill_(len(groups))
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_groups": [g[0] for g in groups], "reps": args.profile_launches,
+                          "dense_key_splits": dense_splits, "sparse_key_splits": sparse_splits}), flush=True)
+        return
 
     # ---- whole-pass throughput (graph replay unless --eager) ---------------
     stream = torch.cuda.current_stream()
