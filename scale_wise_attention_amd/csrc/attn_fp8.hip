@@ -9,14 +9,14 @@
 namespace varattn {
 
 int attn_fp8_resident_wgs(bool out_bf16, bool sparse) {
-    if (sparse) return out_bf16 ? resident_wgs<128, true, true, true>() : resident_wgs<128, false, true, true>();
-    return out_bf16 ? resident_wgs<128, true, false, true>() : resident_wgs<128, false, false, true>();
+    if (sparse) return out_bf16 ? resident_wgs<128, true, true, true, 2>() : resident_wgs<128, false, true, true, 2>();
+    return out_bf16 ? resident_wgs<128, true, false, true, 2>() : resident_wgs<128, false, false, true, 2>();
 }
 
 hipError_t launch_attn_fp8(const AttnParams& p, int D, bool out_bf16, bool sparse, hipStream_t s) {
     if (D != 128) return hipErrorInvalidValue;   // the host layer admits head_dim 128 only
-    if (sparse) return out_bf16 ? launch_one<128, true, true, true>(p, s) : launch_one<128, false, true, true>(p, s);
-    return out_bf16 ? launch_one<128, true, false, true>(p, s) : launch_one<128, false, false, true>(p, s);
+    if (sparse) return out_bf16 ? launch_one<128, true, true, true, 2>(p, s) : launch_one<128, false, true, true, 2>(p, s);
+    return out_bf16 ? launch_one<128, true, false, true, 2>(p, s) : launch_one<128, false, false, true, 2>(p, s);
 }
 
 }  // namespace varattn

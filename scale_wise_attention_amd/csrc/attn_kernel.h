@@ -13,14 +13,17 @@
 // attention); q_index fuses the gather of pruned queries ("ARVAR ...", Key
 // Design 2).
 //
-// Design (dense: one workgroup = 4 waves = 256 query rows of one (batch,
-// head); block-sparse: 2 waves = 128 rows, two workgroups per compute unit;
-// always one wave per SIMD):
-//  * Each wave owns 64 queries in two 32-query column blocks.  S^T = K Q^T is
-//    computed with v_mfma_f32_32x32x16_bf16 (keys on M, queries on N), so a
-//    lane holds 16 logits of each of its two queries and lane l^32 holds the
-//    other 16 of every 32-key block.  Every K operand read from LDS feeds two
-//    MFMAs (one per query block), halving LDS traffic per FLOP.
+// Design (dense: one workgroup = 256 query rows of one (batch, head), 4 waves
+// of 64 rows, one wave per SIMD; block-sparse: 128 rows, two workgroups per
+// compute unit, as 4 waves of 32 rows (two waves per SIMD) at head_dim 128 and
+// 2 waves of 64 rows at 64):
+//  * Each wave owns QB 32-query column blocks (QB = 2: 64 queries; QB = 1:
+//    32).  S^T = K Q^T is computed with v_mfma_f32_32x32x16_bf16 (keys on M,
+//    queries on N), so a lane holds 16 logits of each of its queries and lane
+//    l^32 holds the other 16 of every 32-key block.  With two blocks every K
+//    operand read from LDS feeds two MFMAs, halving LDS traffic per FLOP; one
+//    block leaves each wave at most 256 registers, so two waves share a SIMD
+//    and one's LDS reads and softmax run under the other's MFMAs.
 //  * The same registers, rounded to bf16, are the B operand of
 //    O^T += V^T P^T (d on M, queries on N, keys on K).  The MFMA's k order is
 //    matched by permuting keys inside the V^T tile in LDS, so P never moves
@@ -86,13 +89,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int QW = 64;                 // query rows per wave
-// waves per workgroup: 4 for dense attention; 2 for block-sparse attention,
-// whose workgroup walks the union of its waves' kept tiles (two workgroups
-// then share a compute unit)
-template <bool SPARSE>
-constexpr int waves_per_wg() { return SPARSE ? 2 : 4; }
 constexpr int KT = 64;                 // keys per tile (= sparse tile width)
+// query rows per workgroup: 256 for dense attention; 128 (two 64-row mask rows)
+// for block-sparse attention, whose workgroup walks the union of the two rows'
+// kept tiles (two workgroups then share a compute unit)
+template <bool SPARSE>
+constexpr int rows_per_wg() { return SPARSE ? 2 * KT : 4 * KT; }
+// waves per workgroup when a wave owns QB 32-row query blocks: QB = 2 runs one
+// wave per SIMD, QB = 1 two
+template <bool SPARSE, int QB>
+constexpr int waves_per_wg() { return rows_per_wg<SPARSE>() / (32 * QB); }
 constexpr float kSumLimit = 0x1p100f;  // a row sum above this triggers the exact recompute
 
 // Work of workgroup wg (of nwg): work item `item`, key split `split`, and
@@ -194,28 +200,32 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Slots of the branch-free tile body (one MFMA each): the QK MFMAs of the four
+// Slots of the branch-free tile body (one MFMA each): the QK MFMAs of the 2*QB
 // 32x32 S^T blocks (half h, query block qb) run chain by chain (SK k-steps:
-// slots (2h+qb)*SK .. +SK-1), then the PV MFMAs (chunk C, d block mb, query
-// block qb; NP per chunk) at slot 4*SK + C*NP + 2*mb + qb.  Weight pair i (half i >> 4, block
-// (i >> 3) & 1, chunk (i >> 2) & 1, pair i & 3) takes three stages in slots
-// at[i], at[i]+1, at[i]+2: from two slots after its S^T block is complete, and
-// done before the first PV MFMA that reads it.  Pairs are spread evenly over
+// slots (QB*h+qb)*SK .. +SK-1), then the PV MFMAs (chunk C, d block mb, query
+// block qb; NP = QB * (d blocks) per chunk) at slot 2*QB*SK + C*NP + QB*mb + qb.
+// Weight pair i (half i / (8 QB), block (i / 8) % QB, chunk (i >> 2) & 1, pair
+// i & 3) takes three stages in slots at[i], at[i]+1, at[i]+2: from two slots
+// after its S^T block is complete, and done before the first PV MFMA that
+// reads it.  Pairs are spread evenly over
 // the slots in between (earliest deadline first), at most CAP first stages
 // per slot.
-template <int SK, int NP, int CAP>
+template <int SK, int NP, int CAP, int QB>
 struct WeightSlots {
-    static constexpr int NS = 4 * SK + 4 * NP;
-    int at[32];
-    static constexpr int release(int i) { return (2 * (i >> 4) + ((i >> 3) & 1) + 1) * SK + 1; }
+    static constexpr int NPAIR = 16 * QB;      // weight pairs of a lane per tile
+    static constexpr int NS = 2 * QB * SK + 4 * NP;
+    int at[NPAIR];
+    static constexpr int half_of(int i) { return i / (8 * QB); }
+    static constexpr int qb_of(int i) { return (i / 8) % QB; }
+    static constexpr int release(int i) { return (QB * half_of(i) + qb_of(i) + 1) * SK + 1; }
     static constexpr int deadline(int i) {   // the stage-3 slot must come before this one
-        return 4 * SK + (2 * (i >> 4) + ((i >> 2) & 1)) * NP + ((i >> 3) & 1);
+        return 2 * QB * SK + (2 * half_of(i) + ((i >> 2) & 1)) * NP + qb_of(i);
     }
     constexpr WeightSlots() : at{} {
         const int cap = CAP;
         int first = NS, last = 0;
-        bool done[32] = {};
-        for (int i = 0; i < 32; ++i) {
+        bool done[NPAIR] = {};
+        for (int i = 0; i < NPAIR; ++i) {
             first = release(i) < first ? release(i) : first;
             last = deadline(i) - 3 > last ? deadline(i) - 3 : last;
         }
@@ -223,15 +233,15 @@ struct WeightSlots {
         int placed = 0;
         for (int m = 0; m < NS; ++m) {
             int k = 0;
-            bool tried[32] = {};
+            bool tried[NPAIR] = {};
             while (k < cap) {
                 int best = -1;
-                for (int i = 0; i < 32; ++i)
+                for (int i = 0; i < NPAIR; ++i)
                     if (!done[i] && !tried[i] && release(i) <= m && (best < 0 || deadline(i) < deadline(best))) best = i;
                 if (best < 0) break;
                 tried[best] = true;
                 const bool urgent = deadline(best) - 3 - m <= 0;
-                const int quota = ((m - first + 1) * 32 + span - 1) / span;
+                const int quota = ((m - first + 1) * NPAIR + span - 1) / span;
                 if (urgent || placed < quota) {
                     at[best] = m;
                     done[best] = true;
@@ -242,7 +252,7 @@ struct WeightSlots {
         }
     }
     constexpr bool valid() const {
-        for (int i = 0; i < 32; ++i)
+        for (int i = 0; i < NPAIR; ++i)
             if (at[i] < release(i) || at[i] + 2 >= deadline(i)) return false;
         return true;
     }
@@ -260,11 +270,15 @@ struct TileEnt {
 // QK8: k is e4m3 codes with one scale per 64-key tile, each wave quantises
 // its 64 bf16 query rows to e4m3 (one scale), and S^T comes from
 // v_mfma_f32_32x32x64_f8f6f4 (64 deep per k-step); V stays bf16.
-template <int D, bool OUT_BF16, bool SPARSE, bool QK8>
-__global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(const AttnParams p) {
-    constexpr int NW = waves_per_wg<SPARSE>();   // waves per workgroup
-    constexpr int NT = NW * 64;                  // threads per workgroup
-    constexpr int QT = NW * QW;                  // query rows per workgroup
+template <int D, bool OUT_BF16, bool SPARSE, bool QK8, int QB>
+__global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), (QB == 1 ? 2 : 1)) void attn_kernel(const AttnParams p) {
+    static_assert(QB == 1 || QB == 2, "one or two 32-row query blocks per wave");
+    static_assert(!QK8 || QB == 2, "e4m3 queries are quantised per 64 rows: one wave's rows");
+    constexpr int NW = waves_per_wg<SPARSE, QB>();   // waves per workgroup
+    constexpr int NT = NW * 64;                      // threads per workgroup
+    constexpr int QW = 32 * QB;                      // query rows per wave
+    constexpr int QT = rows_per_wg<SPARSE>();        // query rows per workgroup
+    constexpr int NL = QT / KT;                      // block-sparse: kept-tile lists (64-row mask rows) per workgroup
     constexpr int EK = QK8 ? 1 : 2;            // bytes per k element (q is always bf16)
     constexpr int ROWB = D * EK;               // bytes per K row
     constexpr int KCH = ROWB / 16;             // 16-byte chunks per K row
@@ -307,14 +321,14 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     const int b = bh / p.H;
     const int h = bh - b * p.H;
 
-    // ---- this lane's two query rows ------------------------------------
-    int my_row[2], klim[2];
-    bool row_valid[2];
-    float c2q[2];   // log2-domain logit scale of each of the lane's two queries
-    qop qreg[2][SK];
-    uint32_t qraw[2][QK8 ? SK : 1][4][4];   // e4m3 path: the lane's bf16 query values
+    // ---- this lane's query rows (one per 32-row block) -----------------
+    int my_row[QB], klim[QB];
+    bool row_valid[QB];
+    float c2q[QB];   // log2-domain logit scale of each of the lane's queries
+    qop qreg[QB][SK];
+    uint32_t qraw[QB][QK8 ? SK : 1][4][4];   // e4m3 path: the lane's bf16 query values
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         my_row[qb] = qtile * QT + wave * QW + 32 * qb + n;
         row_valid[qb] = my_row[qb] < p.n_rows;
         const int row_c = row_valid[qb] ? my_row[qb] : (p.n_rows - 1);
@@ -484,7 +498,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         // row and leave the maximum unchanged), in the operand layout.
         uint32_t mx = 0u;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int ks = 0; ks < SK; ++ks)
 #pragma unroll
@@ -495,7 +509,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         const float inv = __fdiv_rn(448.0f, amax);
         const float sq = __fdiv_rn(amax, 448.0f);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             c2q[qb] = p.scale_log2 * sq;
 #pragma unroll
             for (int ks = 0; ks < SK; ++ks) {
@@ -511,18 +525,25 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         // Q is only ever an MFMA operand: keep it in AGPRs (MFMAs read them
         // directly), which leaves the VGPRs to the softmax and the loads
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int ks = 0; ks < SK; ++ks) asm volatile("" : "+a"(qreg[qb][ks]));
     }
-    const int w_kmin = __builtin_amdgcn_readfirstlane(wave_min_i(min(klim[0], klim[1])));
-    const int w_kmax = __builtin_amdgcn_readfirstlane(wave_max_i(max(klim[0], klim[1])));
+    int kl_min = klim[0], kl_max = klim[0];
+#pragma unroll
+    for (int qb = 1; qb < QB; ++qb) {
+        kl_min = min(kl_min, klim[qb]);
+        kl_max = max(kl_max, klim[qb]);
+    }
+    const int w_kmin = __builtin_amdgcn_readfirstlane(wave_min_i(kl_min));
+    const int w_kmax = __builtin_amdgcn_readfirstlane(wave_max_i(kl_max));
 
     // ---- key-tile walk (workgroup-uniform) ------------------------------
     const int n_kt_all = (p.kv_len + KT - 1) / KT;
     int dense_begin = 0, dense_end = 0;   // dense: tiles [dense_begin, dense_end)
     int dense_next = 0;
-    int lbeg[NW], lptr[NW], lend[NW], lhead[NW];   // sparse: one list per wave's query tile
+    int lbeg[NL], lptr[NL], lend[NL], lhead[NL];   // sparse: one list per 64-row mask row
+    const int my_list = wave * QW / KT;             // the list of this wave's rows
     // this (batch, head)'s CSR, read through the constant address space: the
     // launch never writes it and every read is workgroup-uniform, so the
     // reads go through the scalar path into scalar registers
@@ -532,8 +553,8 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     if constexpr (SPARSE) {
         const int n_qt = (p.n_rows + KT - 1) / KT;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            const int r = qtile * NW + w;
+        for (int w = 0; w < NL; ++w) {
+            const int r = qtile * NL + w;
             const int b0 = r < n_qt ? rowp[r] : 0;
             const int cnt = r < n_qt ? rowp[r + 1] - b0 : 0;
             // key split: an equal share of this row's kept tiles (in order; the
@@ -577,12 +598,12 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         if constexpr (SPARSE) {
             int c = INT_MAX;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) c = min(c, lhead[w]);
+            for (int w = 0; w < NL; ++w) c = min(c, lhead[w]);
             e.tile = -1;
             e.mask = 0;
             if (c != INT_MAX) {
 #pragma unroll
-                for (int w = 0; w < NW; ++w) {
+                for (int w = 0; w < NL; ++w) {
                     if (lhead[w] == c) {
                         e.mask |= 1 << w;
                         // (a column repeated right after itself is taken once)
@@ -597,7 +618,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
             }
         } else {
             e.tile = dense_next < dense_end ? dense_next : -1;
-            e.mask = (1 << NW) - 1;
+            e.mask = (1 << NL) - 1;
             ++dense_next;
         }
         e.ks = 1.f;
@@ -611,7 +632,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     auto reset_walk = [&]() __attribute__((always_inline)) {
         if constexpr (SPARSE) {
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
+            for (int w = 0; w < NL; ++w) {
                 lptr[w] = lbeg[w];
                 lhead[w] = lptr[w] < lend[w] ? coli[lptr[w]] : INT_MAX;
             }
@@ -620,7 +641,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         }
     };
     auto mine = [&](const TileEnt& e) __attribute__((always_inline)) -> bool {
-        if constexpr (SPARSE) return e.tile >= 0 && ((e.mask >> wave) & 1);
+        if constexpr (SPARSE) return e.tile >= 0 && ((e.mask >> my_list) & 1);
         else return e.tile >= 0 && e.tile * KT < w_kmax;
     };
 
@@ -647,51 +668,57 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
 #pragma unroll
         for (int ks = 0; ks < SK; ++ks) a[ks] = k_operand(Ks, 32 * half + n, ks);
     };
-    auto qk_mfma = [&](const qop (&a)[SK], f32x16 (&s)[2]) __attribute__((always_inline)) {
-        s[0] = s[1] = f32x16{};
+    auto qk_mfma = [&](const qop (&a)[SK], f32x16 (&s)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int ks = 0; ks < SK; ++ks) {
-            s[0] = qk_step(a[ks], qreg[0][ks], s[0]);
-            s[1] = qk_step(a[ks], qreg[1][ks], s[1]);
-        }
+        for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < SK; ++ks)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[qb] = qk_step(a[ks], qreg[qb][ks], s[qb]);
     };
-    auto qk_half = [&](int slot, int half, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    auto qk_half = [&](int slot, int half, f32x16 (&s)[QB]) __attribute__((always_inline)) {
         qop a[SK];
         k_operands(slot, half, a);
         qk_mfma(a, s);
     };
 
-    f32x16 oacc[MO][2];
-#pragma unroll
-    for (int i = 0; i < MO; ++i) oacc[i][0] = oacc[i][1] = f32x16{};
+    f32x16 oacc[MO][QB];
     // reference max per query, in the log2 domain (logit * log2(e)): the
     // logits of key tiles with different scales compare only after scaling
-    float mref[2] = {-INFINITY, -INFINITY};
-    float nb[2] = {0.f, 0.f};                 // -mref
-    float lsum[2] = {0.f, 0.f};               // this lane's partial row sums
+    float mref[QB];
+    float nb[QB];                             // -mref
+    float lsum[QB];                           // this lane's partial row sums
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+        for (int i = 0; i < MO; ++i) oacc[i][qb] = f32x16{};
+        mref[qb] = -INFINITY;
+        nb[qb] = 0.f;
+        lsum[qb] = 0.f;
+    }
     bool need_ref = true;                     // some row of the wave has no reference yet
     // log2-domain scale of the raw dot products of key tile e: scale *
     // log2(e), times the query's and the key tile's scales for e4m3 codes
-    auto tile_c2 = [&](const TileEnt& e, float (&c2t)[2]) __attribute__((always_inline)) {
-        c2t[0] = QK8 ? c2q[0] * e.ks : c2q[0];
-        c2t[1] = QK8 ? c2q[1] * e.ks : c2q[1];
+    auto tile_c2 = [&](const TileEnt& e, float (&c2t)[QB]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) c2t[qb] = QK8 ? c2q[qb] * e.ks : c2q[qb];
     };
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     // keys at or past `lim` are hidden (-inf) in one 32-key half starting at kb0
-    auto apply_mask = [&](f32x16 (&s)[2], int kb0, const int (&lim)[2]) __attribute__((always_inline)) {
+    auto apply_mask = [&](f32x16 (&s)[QB], int kb0, const int (&lim)[QB]) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb)
+            for (int qb = 0; qb < QB; ++qb)
                 if (key >= lim[qb]) s[qb][r] = -INFINITY;
         }
     };
     // row max of one 32-key half (both query blocks), across the lane pair
-    auto half_max = [&](const f32x16 (&s)[2], float (&mt)[2]) __attribute__((always_inline)) {
+    auto half_max = [&](const f32x16 (&s)[QB], float (&mt)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             float ma = max3(s[qb][0], s[qb][1], s[qb][2]);
             float mb = max3(s[qb][3], s[qb][4], s[qb][5]);
             ma = max3(ma, s[qb][6], s[qb][7]);
@@ -704,19 +731,21 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         }
     };
     // rows without a reference yet take this half's max as their reference
-    auto set_reference = [&](const f32x16 (&s)[2], const float (&c2t)[2]) __attribute__((always_inline)) {
-        float mt[2];
+    auto set_reference = [&](const f32x16 (&s)[QB], const float (&c2t)[QB]) __attribute__((always_inline)) {
+        float mt[QB];
         half_max(s, mt);
+        bool unset = false;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             mref[qb] = (mref[qb] == -INFINITY) ? mt[qb] * c2t[qb] : mref[qb];
             nb[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb];
+            unset |= mref[qb] == -INFINITY;
         }
-        need_ref = __builtin_amdgcn_ballot_w64(mref[0] == -INFINITY || mref[1] == -INFINITY) != 0;
+        need_ref = __builtin_amdgcn_ballot_w64(unset) != 0;
     };
     // weights of one key pair (pair i of 16-key chunk c of a half, MFMA k
     // order) of query block qb, packed to bf16; the pair adds to the row sum
-    auto exp_pair = [&](const f32x16 (&s)[2], int c, int qb, int i, u32x4 (&w)[2], const float (&c2t)[2])
+    auto exp_pair = [&](const f32x16 (&s)[QB], int c, int qb, int i, u32x4 (&w)[QB], const float (&c2t)[QB])
                         __attribute__((always_inline)) {
         const int r = 8 * c + 2 * i;
         const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], c2t[qb], nb[qb]));
@@ -726,9 +755,9 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr), ones, lsum[qb], false);
     };
     // weights of 16-key chunk c (0 or 1) of a half: 4 bf16 pairs per query block
-    auto exp_chunk = [&](const f32x16 (&s)[2], int c, u32x4 (&w)[2], const float (&c2t)[2]) __attribute__((always_inline)) {
+    auto exp_chunk = [&](const f32x16 (&s)[QB], int c, u32x4 (&w)[QB], const float (&c2t)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) exp_pair(s, c, qb, i, w, c2t);
     };
@@ -743,16 +772,15 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
             a[mb] = *reinterpret_cast<const bf16x8*>(Vs + v_addr(d, chunk));
         }
     };
-    auto pv_mfma = [&](const bf16x8 (&a)[MO], const u32x4 (&w)[2]) __attribute__((always_inline)) {
-        const bf16x8 b0 = __builtin_bit_cast(bf16x8, w[0]);
-        const bf16x8 b1 = __builtin_bit_cast(bf16x8, w[1]);
+    auto pv_mfma = [&](const bf16x8 (&a)[MO], const u32x4 (&w)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mb = 0; mb < MO; ++mb) {
-            oacc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b0, oacc[mb][0], 0, 0, 0);
-            oacc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b1, oacc[mb][1], 0, 0, 0);
-        }
+        for (int mb = 0; mb < MO; ++mb)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+                oacc[mb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], __builtin_bit_cast(bf16x8, w[qb]),
+                                                                      oacc[mb][qb], 0, 0, 0);
     };
-    auto pv_chunk = [&](int slot, int ks, const u32x4 (&w)[2]) __attribute__((always_inline)) {
+    auto pv_chunk = [&](int slot, int ks, const u32x4 (&w)[QB]) __attribute__((always_inline)) {
         bf16x8 a[MO];
         v_operands(slot, ks, a);
         pv_mfma(a, w);
@@ -810,6 +838,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
             }
             return idx > 0 && e.tile * KT + KT <= wg_kmin;
         };
+
         // One tile: e's K and V^T sit in LDS slot `slot`; the V of tile nv (if
         // any) is loaded now and staged into slot `vslot`.
         auto body = [&](auto fast_tag, const TileEnt& e, int slot, const TileEnt& nv, int vslot)
@@ -821,8 +850,8 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                 if (FAST || nv.tile >= 0) load_v((nv.tile >= 0 ? nv.tile : e.tile) * KT);
             }
             const int kb = e.tile * KT;
-            f32x16 s0[2], s1[2];
-            float c2t[2];
+            f32x16 s0[QB], s1[QB];
+            float c2t[QB];
             tile_c2(e, c2t);
             if constexpr (MODE == 0 && FAST) {
                 // Software-ordered body: slot m issues MFMA m and a fixed share of
@@ -849,46 +878,61 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                     asm("" : "+a"(x));
                     return x;
                 };
-                constexpr int L = 2 * SK;                  // QK slots per half
-                constexpr int NP = 2 * MO;                 // PV slots per 16-key chunk
+                constexpr int L = QB * SK;                 // QK slots per half
+                constexpr int NP = QB * MO;                // PV slots per 16-key chunk
                 // (e4m3 QK chains are one quarter as long, so the first weights
                 // have fewer slots before their PV MFMA: up to 4 starts a slot)
-                constexpr WeightSlots<SK, NP, QK8 ? 4 : (D == 128 ? 1 : 2)> WS{};
+                constexpr WeightSlots<SK, NP, QK8 ? 4 : (D == 128 ? 1 : 2), QB> WS{};
                 static_assert(WS.valid(), "weight pairs scheduled in time");
                 const bool own = mine(e);
-                const float nbt[2] = {own ? nb[0] : -INFINITY, own ? nb[1] : -INFINITY};
-                u32x4 w[4][2];                             // [chunk][qb]
-                float xs[32][2];                           // weight-pair stage values
+                float nbt[QB];
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) nbt[qb] = own ? nb[qb] : -INFINITY;
+                u32x4 w[4][QB];                            // [chunk][qb]
+                float xs[WS.NPAIR][2];                     // weight-pair stage values
                 qop ka[SK], kb1[SK];
                 bf16x8 va[4][MO];
 #pragma unroll
                 for (int ks = 0; ks < SK; ++ks) ka[ks] = kread(0, ks);
-                s0[0] = s0[1] = s1[0] = s1[1] = f32x16{};
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) s0[qb] = s1[qb] = f32x16{};
                 static_for<2 * L + 4 * NP>([&](auto mc) __attribute__((always_inline)) {
                     constexpr int m = decltype(mc)::value;
                     if constexpr (m < 2 * L) {
-                        // QK chains: S^T block (h, qb) in slots (2h+qb)*SK .. +SK-1
-                        constexpr int chain = m / SK, ks = m % SK, h = chain >> 1, qb = chain & 1;
+                        // QK chains: S^T block (h, qb) in slots (QB*h+qb)*SK .. +SK-1
+                        constexpr int chain = m / SK, ks = m % SK, h = chain / QB, qb = chain % QB;
                         if constexpr (h == 0) s0[qb] = qk_step(in_agpr(ka[ks]), qreg[qb][ks], s0[qb]);
                         else s1[qb] = qk_step(in_agpr(kb1[ks]), qreg[qb][ks], s1[qb]);
-                        // K operands of h1 during QK(h0), V operands of chunks 0, 1 during QK(h1)
-                        if constexpr (m < L && (m & 1) == 1) kb1[m >> 1] = kread(1, m >> 1);
+                        // K operands of h1 during QK(h0), V operands of chunk 0 (two
+                        // query blocks: chunks 0, 1) during QK(h1)
+                        if constexpr (QB == 2) {
+                            if constexpr (m < L && (m & 1) == 1) kb1[m >> 1] = kread(1, m >> 1);
+                        } else {
+                            if constexpr (m < L) kb1[m] = kread(1, m);
+                        }
                         if constexpr (m >= L) {
-                            static_for<2 * MO>([&](auto ec) __attribute__((always_inline)) {
+                            constexpr int NE = QB * MO;
+                            static_for<NE>([&](auto ec) __attribute__((always_inline)) {
                                 constexpr int e = decltype(ec)::value;
-                                if constexpr ((e * L) / (2 * MO) == m - L) va[e / MO][e % MO] = vread(e / MO, e % MO);
+                                if constexpr ((e * L) / NE == m - L) va[e / MO][e % MO] = vread(e / MO, e % MO);
                             });
                         }
                     } else {
-                        // PV chunks 0..3 | V operands of chunks 2, 3 | staging of the next V tile
-                        constexpr int t = m - 2 * L, c = t / NP, mb = (t % NP) >> 1, qb = t & 1;
+                        // PV chunks 0..3 | V operands of the later chunks | staging of the next V tile
+                        constexpr int t = m - 2 * L, c = t / NP, mb = (t % NP) / QB, qb = t % QB;
                         oacc[mb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             in_agpr(va[c][mb]), __builtin_bit_cast(bf16x8, w[c][qb]), oacc[mb][qb], 0, 0, 0);
-                        if constexpr (t < NP) {
-                            static_for<2 * MO>([&](auto ec) __attribute__((always_inline)) {
-                                constexpr int e = decltype(ec)::value;
-                                if constexpr ((e * NP) / (2 * MO) == t) va[2 + e / MO][e % MO] = vread(2 + e / MO, e % MO);
-                            });
+                        if constexpr (QB == 2) {
+                            // (chunks 2, 3 during chunk 0)
+                            if constexpr (t < NP) {
+                                static_for<2 * MO>([&](auto ec) __attribute__((always_inline)) {
+                                    constexpr int e = decltype(ec)::value;
+                                    if constexpr ((e * NP) / (2 * MO) == t) va[2 + e / MO][e % MO] = vread(2 + e / MO, e % MO);
+                                });
+                            }
+                        } else {
+                            // (chunk c + 1 during chunk c, one operand a slot)
+                            if constexpr (c < 3) va[c + 1][t % NP] = vread(c + 1, t % NP);
                         }
                         if constexpr (c == 3) {
                             static_for<4 * V_PER_T>([&](auto ec) __attribute__((always_inline)) {
@@ -898,9 +942,9 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                         }
                     }
                     // weight pipeline: stage 3, stage 2, stage 1 (oldest first)
-                    static_for<32>([&](auto ic) __attribute__((always_inline)) {
+                    static_for<WS.NPAIR>([&](auto ic) __attribute__((always_inline)) {
                         constexpr int i = decltype(ic)::value;
-                        constexpr int h = i >> 4, qb = (i >> 3) & 1, c = (i >> 2) & 1, ii = i & 3;
+                        constexpr int h = WS.half_of(i), qb = WS.qb_of(i), c = (i >> 2) & 1, ii = i & 3;
                         constexpr int r = 8 * c + 2 * ii;
                         constexpr int at = WS.at[i];
                         if constexpr (at + 2 == m) {
@@ -927,10 +971,12 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
             } else {
                 // a tile outside this wave's own list is computed fully masked
                 const bool own = mine(e);
-                const int lim[2] = {own ? klim[0] : -1, own ? klim[1] : -1};
+                int lim[QB];
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) lim[qb] = own ? klim[qb] : -1;
                 const bool need_mask = kb + KT > (own ? w_kmin : -1);
                 if constexpr (MODE == 0) {
-                    u32x4 w00[2], w01[2], w10[2], w11[2];
+                    u32x4 w00[QB], w01[QB], w10[QB], w11[QB];
                     qk_half(slot, 0, s0);
                     if (need_mask) apply_mask(s0, kb, lim);
                     if (need_ref) set_reference(s0, c2t);
@@ -946,17 +992,17 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
                     pv_chunk(slot, 2, w10);
                     pv_chunk(slot, 3, w11);
                 } else {
-                    float mt[2];
+                    float mt[QB];
                     qk_half(slot, 0, s0);
                     if (need_mask) apply_mask(s0, kb, lim);
                     half_max(s0, mt);
-                    mref[0] = __builtin_fmaxf(mref[0], mt[0] * c2t[0]);
-                    mref[1] = __builtin_fmaxf(mref[1], mt[1] * c2t[1]);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) mref[qb] = __builtin_fmaxf(mref[qb], mt[qb] * c2t[qb]);
                     qk_half(slot, 1, s1);
                     if (need_mask) apply_mask(s1, kb + 32, lim);
                     half_max(s1, mt);
-                    mref[0] = __builtin_fmaxf(mref[0], mt[0] * c2t[0]);
-                    mref[1] = __builtin_fmaxf(mref[1], mt[1] * c2t[1]);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) mref[qb] = __builtin_fmaxf(mref[qb], mt[qb] * c2t[qb]);
                 }
             }
             if constexpr (MODE == 0 && !FAST) {
@@ -1022,14 +1068,14 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         bool bad = false;
         uint32_t obits = 0u;   // largest |O| bit pattern of the lane
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int mb = 0; mb < MO; ++mb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) obits = max(obits, __float_as_uint(oacc[mb][qb][r]) & 0x7fffffffu);
         bad |= obits >= 0x7f800000u;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
             const float ltot = lsum[qb] + swap_halves(lsum[qb]);
             // a sum out of range, or a row that saw keys only in branch-free
             // tiles before it had a reference, needs the exact recompute
@@ -1046,10 +1092,11 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
         for (int w = 0; w < NW; ++w) again |= flags[w];
         again = __builtin_amdgcn_readfirstlane(again);
         if (again) {
-            mref[0] = mref[1] = -INFINITY;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) mref[qb] = -INFINITY;
             walk(IntC<1>{});
 #pragma unroll
-            for (int qb = 0; qb < 2; ++qb) {
+            for (int qb = 0; qb < QB; ++qb) {
                 nb[qb] = (mref[qb] == -INFINITY) ? 0.f : -mref[qb];
                 lsum[qb] = 0.f;
 #pragma unroll
@@ -1067,7 +1114,7 @@ __global__ __launch_bounds__(waves_per_wg<SPARSE>() * 64, 1) void attn_kernel(co
     // from the first row of item split_from (part_first), part_rows per split
     const int64_t part_row0 = (int64_t)split * p.part_rows + (int64_t)(b * p.H + h) * p.n_rows - p.part_first;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
         const float ltot = lsum[qb] + swap_halves(lsum[qb]);
         const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
         if (!row_valid[qb]) continue;
@@ -1157,12 +1204,12 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, in
 
 // Workgroups of one instantiation that a compute unit holds at once (1 when
 // the runtime cannot say).
-template <int D, bool OB, bool SP, bool QK8>
+template <int D, bool OB, bool SP, bool QK8, int QB>
 int resident_wgs() {
     static const int n = [] {
         int k = 0;
         const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &k, attn_kernel<D, OB, SP, QK8>, waves_per_wg<SP>() * 64, 0);
+            &k, attn_kernel<D, OB, SP, QK8, QB>, waves_per_wg<SP, QB>() * 64, 0);
         if (e != hipSuccess) (void)hipGetLastError();
         return e == hipSuccess && k > 0 ? k : 1;
     }();
@@ -1171,14 +1218,14 @@ int resident_wgs() {
 
 // The host bounds split_from + (items - split_from) * n_splits below 2^31 and
 // sets split_from = items when n_splits == 1.
-template <int D, bool OB, bool SP, bool QK8>
+template <int D, bool OB, bool SP, bool QK8, int QB>
 hipError_t launch_one(const AttnParams& p, hipStream_t s) {
     const int items = p.n_qtiles * p.B * p.H;
     const int grid = p.split_from + (items - p.split_from) * p.n_splits;
-    hipLaunchKernelGGL((attn_kernel<D, OB, SP, QK8>), dim3(grid), dim3(waves_per_wg<SP>() * 64), 0, s, p);
+    hipLaunchKernelGGL((attn_kernel<D, OB, SP, QK8, QB>), dim3(grid), dim3(waves_per_wg<SP, QB>() * 64), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split_from == items) return e;
-    constexpr int QT = waves_per_wg<SP>() * QW;
+    constexpr int QT = rows_per_wg<SP>();
     const int64_t threads = (int64_t)(items - p.split_from) * QT * (D / 4);
     hipLaunchKernelGGL((split_merge_kernel<OB>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p, D,
                        QT);
