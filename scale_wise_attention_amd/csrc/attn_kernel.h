@@ -14,9 +14,10 @@
 // Design 2).
 //
 // Design (dense: one workgroup = 256 query rows of one (batch, head), 4 waves
-// of 64 rows, one wave per SIMD; block-sparse: 128 rows, two workgroups per
-// compute unit, as 4 waves of 32 rows (two waves per SIMD) at head_dim 128 and
-// 2 waves of 64 rows at 64):
+// of 64 rows, one wave per SIMD, or for short launches at head_dim 128 8 waves
+// of 32 rows; block-sparse: 128 rows, two workgroups per compute unit, as 4
+// waves of 32 rows (two waves per SIMD) at head_dim 128 and 2 waves of 64 rows
+// at 64):
 //  * Each wave owns QB 32-query column blocks (QB = 2: 64 queries; QB = 1:
 //    32).  S^T = K Q^T is computed with v_mfma_f32_32x32x16_bf16 (keys on M,
 //    queries on N), so a lane holds 16 logits of each of its queries and lane
