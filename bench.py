@@ -156,7 +156,19 @@ def cpu_baseline(wl, q, k, v, heads):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"dense generation (13 steps, 10521 tokens, D=128) for {len(pairs)} of 32 (batch, head) "
                       f"pairs, NumPy float64: {flops / 1e9:.1f} GFLOP in {dt:.2f} s",
-            "seconds": dt}
+            "cpu_model": _cpu_model(), "seconds": dt}
+
+
+def _cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():

@@ -133,6 +133,38 @@ def test_gather_splits_full_sequence_recompute(api):
     _check(o, lse, res, vn, "full sequence")
 
 
+def test_dense_recompute_both_wave_shapes(api):
+    """A 32x32 step (1024 queries x 2521 keys = 40 key tiles, head_dim 128): unsplit,
+    each workgroup walks 40 tiles and the kernel runs 64-row waves; with two key
+    splits it walks 20 and runs 32-row waves (two per SIMD).  Both against the
+    oracle with the recompute forced, plus a gathered subset of the rows."""
+    grids = GRIDS + (32,)
+    wl = custom_workload(grids, 1, 2, 128)
+    q, k, v = make_qkv(wl, 14, device="cuda")
+    off = oracle.offsets(wl.h, wl.w)
+    s = len(grids) - 1
+    assert -(-off[s + 1] // 64) == 40
+    qs = q[:, :, off[s]:off[s + 1]]
+    n = off[s + 1] - off[s]
+    qn, kn, vn = _np(qs), _np(k), _np(v)
+    assert _spread(qn, kn, wl.h, wl.w, s) > 100    # the recompute is needed
+    res = oracle.attention(qn, kn, vn, wl.h, wl.w, s, s + 1, softmax_scale=SCALE, return_lse=True,
+                           return_probs=True)
+    sel = np.random.default_rng(15).choice(n, 300, replace=False).astype(np.int32)
+    sel.sort()
+    idx = torch.from_numpy(sel).cuda()
+    res_g = oracle.attention(qn, kn, vn, wl.h, wl.w, s, s + 1, q_index=sel, softmax_scale=SCALE, return_lse=True,
+                             return_probs=True)
+    for splits in (1, 2):
+        ws = api.split_workspace(splits, 1, 2, n, 128) if splits > 1 else None
+        o, lse = api.var_attn_dense((wl.h, wl.w), qs, k, v, s, s + 1, softmax_scale=SCALE, return_lse=True,
+                                    n_splits=splits, workspace=ws)
+        _check(o, lse, res, vn, f"32x32 step, splits={splits}")
+        o, lse = api.var_attn_dense((wl.h, wl.w), qs, k, v, s, s + 1, q_index=idx, softmax_scale=SCALE,
+                                    return_lse=True, n_splits=splits, workspace=ws)
+        _check(o, lse, res_g, vn, f"32x32 step gather, splits={splits}")
+
+
 def test_sparse_recompute(api):
     wl = custom_workload(GRIDS, 2, 2, 128)
     q, k, v = make_qkv(wl, 14, device="cuda")
