@@ -42,11 +42,16 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "dense_attn_1024_counters.txt")
 KERNEL_SRCS = [os.path.join(ROOT, "scale_wise_attention_amd", "csrc", f) for f in ("attn_kernel.h", "attn_bf16.hip")]
 
 
-def _kernel_hash():
+def _kernel_hash(paths=None):
+    """sha256[:16] of the kernel sources' code: comments (from // to the line's
+    end) and blank lines are left out, so a comment edit keeps the hash."""
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+    for path in paths or KERNEL_SRCS:
+        with open(path) as f:
+            for ln in f:
+                code = ln.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -481,7 +486,8 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    def time_launch(fn, reps=R, replays=3):
+    def time_launch_samples(fn, reps=R, replays=3):
+        """per-launch times (ms): one sample per graph replay (or per eager launch)"""
         if graph is None:       # eager fallback: events around each launch
             es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
             for a, b in es:
@@ -489,7 +495,7 @@ def main():
                 fn()
                 b.record()
             torch.cuda.synchronize()
-            return statistics.median([a.elapsed_time(b) for a, b in es])
+            return [a.elapsed_time(b) for a, b in es]
         g = graph_of(fn, reps)
         g.replay()
         torch.cuda.synchronize()
@@ -501,11 +507,25 @@ def main():
             b.record()
             torch.cuda.synchronize()
             vals.append(a.elapsed_time(b) / reps)
-        return statistics.median(vals)
+        return vals
 
-    dense_ms = [time_launch(lambda s=s: dense_step(s)) for s in range(K)]
+    def time_launch(fn, reps=R, replays=3):
+        return statistics.median(time_launch_samples(fn, reps, replays))
+
+    def pct(vals, q):
+        v = sorted(vals)
+        return v[min(len(v) - 1, int(q * len(v)))]
+
+    # per-step spread: 10 replays of each step's graph (p10, median, p90)
+    def step_stats(fn):
+        v = time_launch_samples(fn, replays=10)
+        return statistics.median(v), pct(v, 0.1), pct(v, 0.9)
+
+    dense_st = [step_stats(lambda s=s: dense_step(s)) for s in range(K)]
     mask_ms = [time_launch(lambda s=s: mask_step(s)) for s in range(K)]
-    sparse_ms = [time_launch(lambda s=s: sparse_step(s)) for s in range(K)]
+    sparse_st = [step_stats(lambda s=s: sparse_step(s)) for s in range(K)]
+    dense_ms = [x[0] for x in dense_st]
+    sparse_ms = [x[0] for x in sparse_st]
     scatter_ms = time_launch(scatter_step)
     base_scatter_ms = time_launch(base_scatter)
     pruned_in_place_ms = time_launch(lambda: sparse_step(K - 1, in_place=True))
@@ -731,6 +751,7 @@ def main():
             "generation_ms": round(dense_gen_ms, 4),
             "generation_tflops": round(sum(dense_flops) / (dense_gen_ms * 1e-3) / 1e12, 2),
             "per_step_ms": [round(x, 4) for x in dense_ms],
+            "per_step_ms_p10_p90": [[round(x[1], 4), round(x[2], 4)] for x in dense_st],
             # the small steps are bound by latency (launch, two memory round
             # trips, one tile), far below both the HBM and the MFMA roofs
             "per_step_algorithmic_mb": [round(acc.dense_step_bytes(wl, s_) / 1e6, 3) for s_ in range(K)],
@@ -748,6 +769,7 @@ def main():
             "generation_ms": round(sparse_gen_ms, 4),
             "generation_tflops": round(sum(sparse_flops) / (sparse_gen_ms * 1e-3) / 1e12, 2),
             "per_step_attn_ms": [round(x, 4) for x in sparse_ms],
+            "per_step_attn_ms_p10_p90": [[round(x[1], 4), round(x[2], 4)] for x in sparse_st],
             "per_step_bound": [r[0] for r in sparse_roofs],
             "per_step_frac": [round(r[1], 4) for r in sparse_roofs],
             "per_step_mask_ms": [round(x, 4) for x in mask_ms],

@@ -52,9 +52,9 @@
 //    (QK only), then the weights against them (all <= 1).  Row sums
 //    accumulate the bf16-rounded weights with v_dot2 (the same weights that
 //    multiply V).
-//  * Block-sparse: a workgroup's 2 waves cover 2 consecutive 64-row query
-//    tiles; the workgroup walks the merged (union) list of their kept key
-//    tiles and each wave takes only the tiles of its own list.
+//  * Block-sparse: a workgroup covers 2 consecutive 64-row query tiles; it
+//    walks the merged (union) list of their kept key tiles and the waves of
+//    each query tile weight only the tiles of that tile's own list.
 //  * Key splits (n_splits > 1): the work items that fill whole rounds of the
 //    device's resident workgroups run unsplit; each remaining item runs as
 //    n_splits workgroups, each with an equal share of its key tiles, which
