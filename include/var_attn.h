@@ -23,9 +23,12 @@
  *
  * Conventions for every call:
  *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
- *    allocates nothing, keeps no state between calls and never frees.
- *  - Host-side argument checks run before any HIP call; a failed check returns
- *    its status and launches nothing.  Calls are asynchronous: they enqueue on
+ *    allocates nothing and never frees (var_attn_dense_split_noalloc's scratch
+ *    is a static array of the library's code object); between calls it keeps
+ *    only cached device properties and that array's per-device address.
+ *  - Host-side argument checks run before anything is launched (some query
+ *    the device's compute-unit count or a kernel's occupancy); a failed check
+ *    returns its status and launches nothing.  Calls are asynchronous: they enqueue on
  *    `stream` (a hipStream_t; NULL = the legacy default stream) and return.
  *  - Errors are return codes; var_last_error() gives a thread-local detail
  *    string for the last failing call on the calling thread.
@@ -187,7 +190,8 @@ var_status var_attn_block_sparse_split(const var_schedule* sched, const var_attn
  * process end; its address is looked up once per device).  The call itself
  * allocates nothing.  A call whose split partials (the bytes
  * var_attn_split_plan reports for it) exceed the array returns
- * VAR_ERR_CAPACITY before any HIP call; n_splits = 1 uses no scratch.  Every
+ * VAR_ERR_CAPACITY before anything is launched (it only queries the
+ * device's compute-unit count and occupancy); n_splits = 1 uses no scratch.  Every
  * call on a device shares that device's array: calls that overlap on one
  * device (other streams, other threads) race and must be ordered by the
  * caller.  Other arguments and errors as in var_attn_dense_split.

@@ -713,7 +713,8 @@ VAR_EXPORT var_status var_attn_dense_split_noalloc(const var_schedule* sched, co
                                                    int32_t n_splits, void* stream) {
     if (n_splits == 1)
         return dense_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, 1, nullptr, 0, stream);
-    // the partials this call needs, checked against the scratch before any HIP call
+    // the partials this call needs, checked against the scratch before anything
+    // is launched (only the device's compute-unit count and occupancy are queried)
     Offsets off;
     var_status st = check_schedule(sched, &off);
     if (st != VAR_OK) return st;
