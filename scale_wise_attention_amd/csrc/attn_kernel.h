@@ -53,8 +53,9 @@
 //    accumulate the bf16-rounded weights with v_dot2 (the same weights that
 //    multiply V).
 //  * Block-sparse: a workgroup covers 2 consecutive 64-row query tiles; it
-//    walks the merged (union) list of their kept key tiles and the waves of
-//    each query tile weight only the tiles of that tile's own list.
+//    walks the merged (union) list of their kept key tiles, and the waves of
+//    each query tile compute only the tiles of that tile's own list (on the
+//    others they just stage their share of the next V tile).
 //  * Key splits (n_splits > 1): the work items that fill whole rounds of the
 //    device's resident workgroups run unsplit; each remaining item runs as
 //    n_splits workgroups, each with an equal share of its key tiles, which
@@ -791,9 +792,10 @@ __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), (QB == 1 ? 2 : 1
     // mode 0: weights against the per-row reference (the fast path)
     // mode 1: exact row maxima only (QK, no weights); they become the references
     //
-    // Tiles that need no mask run a branch-free, software-ordered body (waves
-    // that do not own such a tile in a block-sparse walk take it with zero
-    // weights); tiles that set a wave's references and masked tiles run a
+    // Tiles that need no mask run a branch-free, software-ordered body (in a
+    // dense walk a wave whose rows all end before such a tile takes it with
+    // zero weights; in a block-sparse walk a wave skips the tiles it does not
+    // own); tiles that set a wave's references and masked tiles run a
     // general body.  The two bodies sit in separate loops, so the
     // accumulators only flow from one loop into the next.
     auto walk = [&](auto mode_tag) __attribute__((always_inline)) {
@@ -827,9 +829,9 @@ __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), (QB == 1 ? 2 : 1
 
         int j = 0;
         auto fast = [&](const TileEnt& e, int idx) __attribute__((always_inline)) -> bool {
-            // (a tile that only some waves own also runs the branch-free body: the
-            // other waves shift their logits to -inf, so their weights are zero.
-            // In a block-sparse walk a wave's first owned tile need not be the
+            // (in a dense walk a tile past some waves' key limits also runs the
+            // branch-free body there: those waves shift their logits to -inf, so
+            // their weights are zero.  In a block-sparse walk a wave's first owned tile need not be the
             // walk's first, so a tile that a wave owns while its rows have no
             // reference max yet takes the general body, which sets it.  In a
             // dense walk a row that sees any tile of its key range sees the
@@ -1020,7 +1022,21 @@ __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), (QB == 1 ? 2 : 1
         auto single = [&](auto fast_tag) __attribute__((always_inline)) {
             const TileEnt nx = AHEAD == 2 ? e2 : e1;
             if (nx.tile >= 0) load_k(nx.tile * KT, (j + AHEAD) % RING);
-            body(fast_tag, e0, j % RING, nx, (j + AHEAD) % RING);
+            if constexpr (decltype(fast_tag)::value == 2) {
+                // Block-sparse, a tile outside this wave's own list: it adds
+                // nothing to the wave's rows (their weights there are zero), so
+                // the wave only stages its share of the next V tile, and the
+                // SIMD's matrix unit goes to the other wave on it (of the other
+                // workgroup)
+                if constexpr (MODE == 0) {
+                    if (nx.tile >= 0) {
+                        load_v(nx.tile * KT);
+                        store_v((j + AHEAD) % RING);
+                    }
+                }
+            } else {
+                body(BoolC<decltype(fast_tag)::value == 1>{}, e0, j % RING, nx, (j + AHEAD) % RING);
+            }
             tile_barrier();
             e0 = e1;
             if constexpr (AHEAD == 2) {
@@ -1049,12 +1065,17 @@ __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), (QB == 1 ? 2 : 1
             if constexpr (MODE == 0 && !SPARSE) {
                 // (the pair decision is workgroup-uniform in a dense walk)
                 while (e1.tile >= 0 && fast(e0, j) && fast(e1, j + 1)) pair();
-                if (e0.tile >= 0) single(BoolC<false>{});
+                if (e0.tile >= 0) single(IntC<0>{});
             } else {
-                if constexpr (MODE == 0) {
-                    while (e0.tile >= 0 && fast(e0, j)) single(BoolC<true>{});
+                // (block-sparse: three loops, one per body, one barrier per tile
+                // in each, so the waves of a workgroup may sit in different loops)
+                if constexpr (SPARSE) {
+                    while (e0.tile >= 0 && !mine(e0)) single(IntC<2>{});
                 }
-                while (e0.tile >= 0 && (MODE != 0 || !fast(e0, j))) single(BoolC<false>{});
+                if constexpr (MODE == 0) {
+                    while (e0.tile >= 0 && (!SPARSE || mine(e0)) && fast(e0, j)) single(IntC<1>{});
+                }
+                while (e0.tile >= 0 && (!SPARSE || mine(e0)) && (MODE != 0 || !fast(e0, j))) single(IntC<0>{});
             }
         }
     };
