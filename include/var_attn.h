@@ -205,8 +205,8 @@ var_status var_attn_dense_split_noalloc(const var_schedule* sched, const var_att
 
 /*
  * Split count for a call (host only; reads the current device's compute-unit
- * count, 256 if it cannot): the count with the smallest modelled time
- * (the unsplit rounds, then rounds of parts over the resident workgroups
+ * count, 256 if it cannot): the fewest splits whose modelled time is within
+ * 3% of the lowest (the unsplit rounds, then rounds of parts over the resident workgroups
  * times key tiles per part, plus the combining launch and its workspace
  * traffic).  kv_tiles_hint: 64-key
  * tiles a work item visits (0 = ceil(kv_len / 64), the dense count; pass the

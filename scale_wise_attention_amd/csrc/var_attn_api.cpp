@@ -258,7 +258,8 @@ var_status set_split_items(varattn::AttnParams* p, int resident_per_cu, int rpt,
     return VAR_OK;
 }
 
-// Split count with the smallest modelled time, in units of one 64-key
+// Split count: the fewest splits whose modelled time is within 3% of the
+// lowest (the model's noise).  Time is counted in units of one 64-key
 // iteration of a workgroup (about 1.8 us on MI355X at the 1024px shapes).
 // The items that fill whole rounds of the `cap` resident workgroups run
 // unsplit, a round taking `tiles` iterations; the rest, split s ways, take
@@ -269,19 +270,22 @@ var_status set_split_items(varattn::AttnParams* p, int resident_per_cu, int rpt,
 int32_t choose_splits(int64_t tasks, int64_t tiles, int64_t bh_rows, int32_t D, int64_t cap) {
     auto rounds = [&](int64_t n) { return (n + cap - 1) / cap; };
     const int64_t whole = tasks / cap * cap, rest = tasks - whole;
-    double best = (double)rounds(tasks) * tiles;
-    int32_t best_s = 1;
     if (rest == 0) return 1;
     const double rest_rows = (double)bh_rows * rest / tasks;
+    double cost[varattn::kMaxSplits + 1];
+    cost[1] = (double)rounds(tasks) * tiles;
+    double lowest = cost[1];
+    int32_t s_max = 1;
     for (int32_t s = 2; s <= varattn::kMaxSplits && tiles >= 2 * s; ++s) {
-        const double cost = (double)(whole / cap) * tiles + (double)rounds(rest * s) * ((tiles + s - 1) / s) + 3.0 +
-                            (double)s * rest_rows * D * 8.0 / 7.2e6;
-        if (cost < 0.97 * best) {   // a split must win by 3% (the model's noise)
-            best = cost;
-            best_s = s;
-        }
+        cost[s] = (double)(whole / cap) * tiles + (double)rounds(rest * s) * ((tiles + s - 1) / s) + 3.0 +
+                  (double)s * rest_rows * D * 8.0 / 7.2e6;
+        lowest = cost[s] < lowest ? cost[s] : lowest;
+        s_max = s;
     }
-    return best_s;
+    // the fewest splits within 3% of the lowest modelled cost (the model's noise)
+    for (int32_t s = 1; s <= s_max; ++s)
+        if (cost[s] <= 1.03 * lowest) return s;
+    return 1;
 }
 
 }  // namespace

@@ -225,6 +225,15 @@ def test_split_validation_and_plan(api):
     # 288 work items: one whole round of 256 plus 32 items of 101 key tiles that the split spreads
     n, nbytes = api.var_attn_split_plan((W1024, W1024), 11, 12, 2, 16, 128)
     assert n >= 4 and nbytes == n * 8192 * 129 * 4         # only the 32 split items' rows
+    # the plan on every 1024px step (256 compute units): dense, then sparse with the
+    # mean kept tiles per mask row as the hint; the fewest splits within 3% of the
+    # lowest modelled cost (48x48 sparse: 5 splits cost 38.8 units, 4 cost 39.7)
+    dense = [api.var_attn_split_plan((W1024, W1024), st, st + 1, 2, 16, 128)[0] for st in range(13)]
+    assert dense == [1, 1, 1, 1, 1, 1, 1, 3, 2, 2, 1, 6, 1]
+    hints = {7: 11, 8: 15, 9: 18, 10: 21, 11: 25}
+    sparse = [api.var_attn_split_plan((W1024, W1024), st, st + 1, 2, 16, 128, kv_tiles_hint=h)[0]
+              for st, h in hints.items()]
+    assert sparse == [1, 1, 1, 1, 4]
     sp = api.LIB.var_attn_block_sparse_split
     r = sp(ctypes.byref(s), ctypes.byref(d), P(FAKE), L, P(FAKE), L, P(FAKE), L, P(FAKE), L, P(0), P(0), 0,
            P(FAKE), P(FAKE), 64, 64, 9, P(FAKE), 1 << 40, P(0))
