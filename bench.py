@@ -303,10 +303,10 @@ def main():
 
     # The masks depend on positions (and, for the last step, the retained
     # index list) only, so the sparse generation builds them on a second
-    # stream (default priority) from its start, in step order, while the
-    # steps run; each sparse step waits for its own mask.  The fork from the
-    # launch stream also orders them after every earlier use of the CSR
-    # buffers.
+    # stream (default priority) from its start, in step order, while its
+    # first (dense-kernel) steps run; the first masked step waits once, for
+    # the last mask.  The fork from the launch stream also orders them after
+    # every earlier use of the CSR buffers.
     # The reconstruction of the pruned last step is split in two disjoint halves:
     # the attention writes the retained rows in place, and the base-only
     # scatter fills the other rows from the upsampled 48x48 output, right
@@ -334,7 +334,11 @@ def main():
                 api.var_attn_dense(sched, qsteps[s], k, v, s, s + 1, out=sparse_out[s], n_splits=dense_splits[s],
                                    workspace=workspace)
             else:
-                main.wait_event(ready[s])
+                # one wait, for the last mask, before the first masked step: the
+                # masks finish while the dense-kernel steps run, and each
+                # cross-stream wait in the graph costs a few microseconds
+                if s == min(ready):
+                    main.wait_event(ready[max(ready)])
                 sparse_step(s, in_place=True)
             if s == K - 2:
                 base_scatter()
