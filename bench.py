@@ -11,8 +11,8 @@ B=2 (CFG cond + uncond), H=16, D=128, bf16 in, fp32 accumulate, bf16 out):
      kernel walks it; the last step keeps a seeded 40 % subset of its 4096
      queries (fused gather), and its outputs are scattered over the
      nearest-upsampled 48x48 output of the previous step.  The masks depend
-     on positions only, so they are built on a second stream from the start
-     of the sparse generation, overlapping its steps.
+     on positions only, so the sparse generation builds them all at its start
+     in one batched build.
 
 The pass is captured once into a HIP graph and replayed (launch overhead of
 the 13+28 launches off the host); every kernel of the pass runs in every
@@ -302,43 +302,37 @@ def main():
             sparse_step(s)
 
     # The masks depend on positions (and, for the last step, the retained
-    # index list) only, so the sparse generation builds them on a second
-    # stream (default priority) from its start, in step order, while its
-    # first (dense-kernel) steps run; the first masked step waits once, for
-    # the last mask.  The fork from the launch stream also orders them after
-    # every earlier use of the CSR buffers.
+    # index list) only, so the sparse generation builds them all at its start,
+    # in one batched build on the launch stream (about 16 us).  Measured: the
+    # same build on a second stream, overlapping the first steps, was slower,
+    # the fork and join in the graph costing more than the build; and one
+    # build per step (two launches each) on that stream slower still.
     # The reconstruction of the pruned last step is split in two disjoint halves:
     # the attention writes the retained rows in place, and the base-only
     # scatter fills the other rows from the upsampled 48x48 output, right
     # after the 48x48 step (the two touch disjoint rows, so no order is needed
     # between them; measured, running them on two streams side by side was
     # slower than one after the other).
-    mask_stream = torch.cuda.Stream()
 
     def base_scatter():
         api.var_scatter_restore(sparse_out[K - 2], wl.grids[K - 2], wl.grids[K - 2], None, sel_t,
                                 wl.grids[K - 1], wl.grids[K - 1], out=restored)
 
-    def sparse_gen_steps_overlapped():
-        main = torch.cuda.current_stream()
-        mask_stream.wait_stream(main)
-        ready = {}
-        with torch.cuda.stream(mask_stream):
-            for s in range(K):
-                if not full_mask[s]:
-                    mask_step(s)
-                    ready[s] = torch.cuda.Event()
-                    ready[s].record(mask_stream)
+    # every mask of the sparse generation in one batched build (one launch for
+    # the rows of all steps, one for the compaction)
+    masked = [s for s in range(K) if not full_mask[s]]
+    batch_calls = [(s, s + 1, csr[s][2], csr[s][0], csr[s][1]) for s in masked]
+
+    def build_masks():
+        api.var_build_tile_masks(sched, mp, batch_calls)
+
+    def sparse_gen_steps():
+        build_masks()
         for s in range(K):
             if full_mask[s]:
                 api.var_attn_dense(sched, qsteps[s], k, v, s, s + 1, out=sparse_out[s], n_splits=dense_splits[s],
                                    workspace=workspace)
             else:
-                # one wait, for the last mask, before the first masked step: the
-                # masks finish while the dense-kernel steps run, and each
-                # cross-stream wait in the graph costs a few microseconds
-                if s == min(ready):
-                    main.wait_event(ready[max(ready)])
                 sparse_step(s, in_place=True)
             if s == K - 2:
                 base_scatter()
@@ -351,11 +345,12 @@ def main():
     def run_pass():
         for s in range(K):
             dense_step(s)
-        sparse_gen_steps_overlapped()
+        sparse_gen_steps()
 
     # ---- algorithmic work ---------------------------------------------------
-    # (the sparse outputs of the pass, with its masks on the second stream,
-    # must equal those of the same steps with each mask built inline)
+    # (the sparse outputs of the pass, with its masks from the batched build,
+    # must equal those of the same steps with each mask built on its own
+    # right before its step)
     for s in range(K):
         sparse_gen_step(s)
     scatter_step()
@@ -527,6 +522,7 @@ def main():
 
     dense_st = [step_stats(lambda s=s: dense_step(s)) for s in range(K)]
     mask_ms = [time_launch(lambda s=s: mask_step(s)) for s in range(K)]
+    masks_batched_ms = time_launch(build_masks)
     sparse_st = [step_stats(lambda s=s: sparse_step(s)) for s in range(K)]
     dense_ms = [x[0] for x in dense_st]
     sparse_ms = [x[0] for x in sparse_st]
@@ -545,7 +541,7 @@ def main():
     sparse_full_flops = acc.sparse_step_flops(wl, full_rp.cpu().numpy(), full_ci.cpu().numpy(), 4096, off[K])
     dense_gen_ms = time_launch(lambda: [dense_step(s) for s in range(K)], reps=max(2, R // 4))
 
-    sparse_gen_ms = time_launch(sparse_gen_steps_overlapped, reps=max(2, R // 4))
+    sparse_gen_ms = time_launch(sparse_gen_steps, reps=max(2, R // 4))
 
     # the same with each mask built on the launch stream right before its step
     def sparse_gen_inline_masks():
@@ -719,8 +715,9 @@ def main():
         "config": {
             "workload": "1024px VAR generation: grids 1,2,4,6,8,12,16,20,24,32,40,48,64 (10521 tokens), "
                         "B=2 (CFG), H=16, D=128, bf16 in / fp32 accumulate / bf16 out; dense block-causal "
-                        "(13 launches) + block-sparse (64x64 tiles, 7 sink scales, radius 2; masks built per "
-                        "step on a second stream, overlapping the steps) with the last step pruned to 1638 of "
+                        "(13 launches) + block-sparse (64x64 tiles, 7 sink scales, radius 2; the steps' masks "
+                        "built in one batch at the start of the sparse generation) with the last step "
+                        "pruned to 1638 of "
                         "4096 queries and scattered over 48x48",
             "launch": "hipGraph replay of the whole pass" if graph is not None else "eager",
             "pass_gflop": round(pass_flops / 1e9, 3),
@@ -777,6 +774,8 @@ def main():
             "per_step_bound": [r[0] for r in sparse_roofs],
             "per_step_frac": [round(r[1], 4) for r in sparse_roofs],
             "per_step_mask_ms": [round(x, 4) for x in mask_ms],
+            "masks_batched_ms": round(masks_batched_ms, 4),
+            "masks_batched_steps": masked,
             "full_mask_steps_run_dense": [s for s in range(K) if full_mask[s]],
             "generation_masks_inline_ms": round(sparse_gen_inline_ms, 4),
             "generation_masks_prebuilt_ms": round(sparse_gen_pre_ms, 4),

@@ -247,6 +247,31 @@ var_status var_build_tile_mask(const var_schedule* sched, int32_t q_scale_begin,
                                void* stream);
 
 /*
+ * Several tile masks of one schedule and one rule at once: a generation's
+ * masks depend on positions (and the retained index lists) only, so they are
+ * all known up front.  calls[i] asks for what var_build_tile_mask builds for
+ * its own query range, gather and CSR arrays, under the same contract per
+ * call; the result equals n_calls calls of var_build_tile_mask.  The rows of
+ * every call are built by one launch and the lists compacted by a second (a
+ * workgroup per call), so the calls run side by side instead of one after
+ * another.  1 <= n_calls <= VAR_MAX_MASK_CALLS; every call is checked on the
+ * host before anything is launched (a failed check names the call).  The
+ * CSR arrays of different calls must not overlap.
+ */
+#define VAR_MAX_MASK_CALLS 16
+typedef struct var_tile_mask_call {
+    int32_t q_scale_begin;
+    int32_t q_scale_end;
+    const int32_t* q_index;   /* device, positions in [0, n_q), or NULL */
+    int32_t n_sel;            /* entries of q_index (0 without) */
+    int32_t* row_ptr;         /* device int32[n_qt + 1] */
+    int32_t* col_idx;         /* device int32[col_capacity] */
+    int64_t col_capacity;     /* >= n_qt * n_kt */
+} var_tile_mask_call;
+var_status var_build_tile_masks(const var_schedule* sched, const var_mask_params* mp,
+                                const var_tile_mask_call* calls, int32_t n_calls, void* stream);
+
+/*
  * Block-sparse next-scale attention: var_attn_dense restricted to the kept
  * tiles of a CSR tile mask (as produced by var_build_tile_mask).  Inside a
  * kept tile every block-causally visible pair is attended.  tile_q = tile_k

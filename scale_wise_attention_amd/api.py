@@ -33,7 +33,7 @@ EXPORTED = ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_
             "var_attn_dense_split", "var_attn_block_sparse_split", "var_attn_split_plan",
             "var_attn_block_mass", "var_decision_tiles", "var_mapped_tile_mask", "var_attn_block_sparse_heads",
             "var_quantize_e4m3", "var_attn_dense_e4m3", "var_attn_block_sparse_e4m3", "var_device_info",
-            "var_attn_dense_split_noalloc",
+            "var_attn_dense_split_noalloc", "var_build_tile_masks",
             "var_status_string", "var_last_error")
 
 
@@ -65,6 +65,15 @@ class MaskParams(ctypes.Structure):
                 ("local_from_scale", ctypes.c_int32), ("radius_y", ctypes.c_int32), ("radius_x", ctypes.c_int32)]
 
 
+class TileMaskCall(ctypes.Structure):
+    _fields_ = [("q_scale_begin", ctypes.c_int32), ("q_scale_end", ctypes.c_int32), ("q_index", ctypes.c_void_p),
+                ("n_sel", ctypes.c_int32), ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
+                ("col_capacity", ctypes.c_int64)]
+
+
+MAX_MASK_CALLS = 16
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m scale_wise_attention_amd.build`")
@@ -78,6 +87,7 @@ def _load():
     lib.var_tile_mask_dims.argtypes = [SP, i32, i32, ctypes.POINTER(MaskParams), i32,
                                        ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.var_build_tile_mask.argtypes = [SP, i32, i32, ctypes.POINTER(MaskParams), P, i32, P, P, i64, P]
+    lib.var_build_tile_masks.argtypes = [SP, ctypes.POINTER(MaskParams), ctypes.POINTER(TileMaskCall), i32, P]
     lib.var_attn_block_sparse.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, Layout, P, Layout,
                                           P, P, i32, P, P, i32, i32, P]
     lib.var_scatter_restore.argtypes = [i32, i32, ctypes.c_int, P, i64, i64, i32, i32, P, i64, i64, P, i32,
@@ -331,6 +341,40 @@ def var_build_tile_mask(schedule, q_scale_begin, q_scale_end, params, q_index=No
                                    qi, n_sel, _ptr(row_ptr), _ptr(col_idx), col_idx.numel(),
                                    _stream(dev)))
     return row_ptr, col_idx
+
+
+def var_build_tile_masks(schedule, params, calls, device="cuda"):
+    """Several tile masks of one schedule and rule in one pair of launches.  calls: a
+    list of (q_scale_begin, q_scale_end, q_index or None[, row_ptr, col_idx]); returns the
+    list of (row_ptr, col_idx), each as var_build_tile_mask would return it."""
+    s = _as_schedule(schedule)
+    if not 1 <= len(calls) <= MAX_MASK_CALLS:
+        raise ValueError(f"1 to {MAX_MASK_CALLS} calls")
+    arr = (TileMaskCall * len(calls))()
+    out = []
+    dev = torch.device(device)
+    for i, c in enumerate(calls):
+        b, e, q_index = c[0], c[1], c[2]
+        row_ptr, col_idx = (c[3], c[4]) if len(c) > 3 else (None, None)
+        n_sel = 0 if q_index is None else int(q_index.numel())
+        d = q_index.device if q_index is not None else dev
+        _check_index(q_index, d)
+        n_qt, n_kt = var_tile_mask_dims(s, b, e, params, n_sel)
+        if q_index is not None and n_sel == 0:
+            n_qt = 0          # empty selection: row_ptr = [0]
+        if row_ptr is None:
+            row_ptr = torch.empty(n_qt + 1, dtype=torch.int32, device=d)
+        if col_idx is None:
+            col_idx = torch.empty(max(1, n_qt * n_kt), dtype=torch.int32, device=d)
+        if row_ptr.numel() < n_qt + 1 or row_ptr.dtype != torch.int32 or col_idx.dtype != torch.int32:
+            raise ValueError("row_ptr must be int32 with n_qt+1 entries; col_idx int32")
+        qi = _ptr(q_index)
+        if q_index is not None and n_sel == 0:
+            qi = _ptr(row_ptr)     # non-NULL q_index with n_sel = 0: the empty selection (never read)
+        arr[i] = TileMaskCall(b, e, qi.value, n_sel, _ptr(row_ptr).value, _ptr(col_idx).value, col_idx.numel())
+        out.append((row_ptr, col_idx))
+    _check(LIB.var_build_tile_masks(ctypes.byref(s), ctypes.byref(params), arr, len(calls), _stream(dev)))
+    return out
 
 
 def var_attn_block_sparse(schedule, q, k, v, q_scale_begin, q_scale_end, row_ptr, col_idx, out=None,

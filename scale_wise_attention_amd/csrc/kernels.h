@@ -184,6 +184,31 @@ hipError_t launch_tile_mask(const MaskParams& p, hipStream_t s);
 hipError_t launch_block_mass(const MassParams& p, int head_dim, hipStream_t s);
 hipError_t launch_decision(const DecisionParams& p, int rows, hipStream_t s);
 hipError_t launch_mapped_mask(const MappedParams& p, int maps, hipStream_t s);
+// Several tile masks of one schedule and one rule (var_build_tile_masks):
+// the schedule and rule once, then per call its query range, gather and
+// CSR; built by one rows launch over every call's query tiles and one
+// compaction launch with a workgroup per call.
+constexpr int kMaxMaskBatch = 16;
+struct MaskCall {
+    const int32_t* q_index;   // nullable
+    int32_t* row_ptr;
+    int32_t* col_idx;
+    int32_t n_rows, n_q, q_first, kv_len;
+    int32_t n_qt, n_kt;
+    int32_t num_scales;       // q_scale_end of the call
+};
+struct MaskBatch {
+    MaskCall c[kMaxMaskBatch];
+    int32_t first_block[kMaxMaskBatch + 1];   // rows-launch workgroups of call i: [first_block[i], first_block[i + 1])
+    int32_t n_calls;
+    int32_t tile_q, tile_k;
+    int32_t sink_scales, local_from_scale, radius_y, radius_x;
+    int32_t off[VAR_MAX_SCALES + 1];
+    int32_t h[VAR_MAX_SCALES];
+    int32_t w[VAR_MAX_SCALES];
+};
+hipError_t launch_tile_mask_batch(const MaskBatch& b, hipStream_t s);
+
 // The compaction of launch_tile_mask alone, one workgroup per map.
 hipError_t launch_mask_compact(const MaskParams& p, int maps, hipStream_t s);
 hipError_t launch_saliency(const SaliencyParams& p, int head_dim, hipStream_t s);

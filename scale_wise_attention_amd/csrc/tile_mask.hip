@@ -41,9 +41,28 @@ constexpr int kChunkWords = kChunkTiles / 32;
 __device__ __forceinline__ int floor_div(int a, int m) { return a >= 0 ? a / m : -((m - 1 - a) / m); }
 __device__ __forceinline__ int ceil_div(int a, int m) { return -floor_div(-a, m); }
 
+static_assert(sizeof(MaskBatch) <= 4096, "a mask batch travels as kernel arguments (at most 4 KB)");
+
+// One call of a batch, seen with the field names of MaskParams (the
+// schedule arrays point into the batch's kernel arguments).
+struct MaskView {
+    const int32_t* q_index;
+    int32_t n_rows, n_q, q_first, n_kt, num_scales;
+    int32_t tile_q, tile_k, sink_scales, local_from_scale, radius_y, radius_x;
+    const int32_t* off;
+    const int32_t* h;
+    const int32_t* w;
+};
+__device__ __forceinline__ MaskView view_of(const MaskBatch& b, int i) {
+    const MaskCall& c = b.c[i];
+    return MaskView{c.q_index, c.n_rows, c.n_q, c.q_first, c.n_kt, c.num_scales, b.tile_q, b.tile_k,
+                    b.sink_scales, b.local_from_scale, b.radius_y, b.radius_x, b.off, b.h, b.w};
+}
+
 // Scale, row and column of query row i of the call (q_index gathered and
 // clamped into [0, n_q) so that a bad index cannot read outside the schedule).
-__device__ __forceinline__ void row_coords(const MaskParams& p, int i, int& s, int& y, int& x) {
+template <class P>
+__device__ __forceinline__ void row_coords(const P& p, int i, int& s, int& y, int& x) {
     int pos = p.q_index ? p.q_index[i] : i;
     pos = pos < 0 ? 0 : (pos >= p.n_q ? p.n_q - 1 : pos);
     const int tok = p.q_first + pos;
@@ -78,7 +97,8 @@ struct RowShared {
 // Kept key tiles of query tile r, written in ascending order at out[0 ..);
 // returns their count (to every thread).  Keys are processed in chunks of
 // kChunkTiles tiles (one pass for every workload up to 8192 key tiles).
-__device__ int build_row(const MaskParams& p, int r, int* out, RowShared& sh) {
+template <class P>
+__device__ int build_row(const P& p, int r, int* out, RowShared& sh) {
     uint32_t* const bits = sh.bits;
     int* const wave_cnt = sh.wave_cnt;
     int& running = sh.running;
@@ -189,6 +209,21 @@ __global__ __launch_bounds__(kRowThreads) void mask_direct_kernel(const MaskPara
     if (threadIdx.x == 0) p.row_ptr[0] = 0;
 }
 
+// The rows of every call of a batch: workgroup i of the launch builds query
+// tile i - first_block[c] of call c (calls without query tiles own no
+// workgroup).
+__global__ __launch_bounds__(kRowThreads) void mask_rows_batch_kernel(const MaskBatch b) {
+    __shared__ RowShared sh;
+    int c = 0;
+    while (c + 1 < b.n_calls && (int)blockIdx.x >= b.first_block[c + 1]) ++c;
+    const MaskView p = view_of(b, c);
+    const int r = blockIdx.x - b.first_block[c];
+    const int cnt = build_row(p, r, b.c[c].col_idx + (int64_t)r * p.n_kt, sh);
+    if (threadIdx.x == 0) {
+        b.c[c].row_ptr[r + 1] = cnt;
+        if (r == 0) b.c[c].row_ptr[0] = 0;
+    }
+}
 
 constexpr int kCompactThreads = 1024;
 constexpr int kPtrCap = 8192;                  // row offsets staged in LDS up to this many rows
@@ -200,15 +235,23 @@ constexpr int kMovePerThread = 4;
 // all reads of a chunk complete before its writes, and every later chunk
 // reads from positions at or beyond its own entries, past what this chunk
 // writes, so the in-place move is safe.
-__global__ __launch_bounds__(kCompactThreads) void mask_compact_kernel(const MaskParams p) {
-    __shared__ int carry;
-    __shared__ int buf[kCompactThreads];
-    __shared__ int ptr_l[kPtrCap + 1];
-    __shared__ int stage[kCompactThreads * kMovePerThread];
+struct CompactShared {
+    int carry;
+    int buf[kCompactThreads];
+    int ptr_l[kPtrCap + 1];
+    int stage[kCompactThreads * kMovePerThread];
+};
+
+// The compaction of one map: n_qt rows of at most n_kt entries at col_idx[r * n_kt].
+__device__ void compact_map(int n_qt, int n_kt, int32_t* const row_ptr, int32_t* const col_idx, CompactShared& sh) {
+    int& carry = sh.carry;
+    int* const buf = sh.buf;
+    int* const ptr_l = sh.ptr_l;
+    int* const stage = sh.stage;
     const int tid = threadIdx.x;
-    // one workgroup per map (per (batch, head) for per-head masks)
-    int32_t* const row_ptr = p.row_ptr + (int64_t)blockIdx.x * p.rp_map_stride;
-    int32_t* const col_idx = p.col_idx + (int64_t)blockIdx.x * p.ci_map_stride;
+    const struct {
+        int n_qt, n_kt;
+    } p{n_qt, n_kt};
     const bool staged = p.n_qt <= kPtrCap;
     if (tid == 0) {
         carry = 0;
@@ -277,6 +320,24 @@ __global__ __launch_bounds__(kCompactThreads) void mask_compact_kernel(const Mas
     }
 }
 
+__global__ __launch_bounds__(kCompactThreads) void mask_compact_kernel(const MaskParams p) {
+    __shared__ CompactShared sh;
+    // one workgroup per map (per (batch, head) for per-head masks)
+    compact_map(p.n_qt, p.n_kt, p.row_ptr + (int64_t)blockIdx.x * p.rp_map_stride,
+                p.col_idx + (int64_t)blockIdx.x * p.ci_map_stride, sh);
+}
+
+// One workgroup per call of a batch; a call without query tiles gets row_ptr = {0}.
+__global__ __launch_bounds__(kCompactThreads) void mask_compact_batch_kernel(const MaskBatch b) {
+    __shared__ CompactShared sh;
+    const MaskCall& c = b.c[blockIdx.x];
+    if (c.n_qt == 0) {
+        if (threadIdx.x == 0) c.row_ptr[0] = 0;
+        return;
+    }
+    compact_map(c.n_qt, c.n_kt, c.row_ptr, c.col_idx, sh);
+}
+
 __global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
 
 }  // namespace
@@ -288,6 +349,17 @@ hipError_t launch_zero_i32(int32_t* p, hipStream_t s) {
 
 hipError_t launch_mask_compact(const MaskParams& p, int maps, hipStream_t s) {
     hipLaunchKernelGGL(mask_compact_kernel, dim3(maps), dim3(1024), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile_mask_batch(const MaskBatch& b, hipStream_t s) {
+    const int blocks = b.first_block[b.n_calls];
+    if (blocks > 0) {
+        hipLaunchKernelGGL(mask_rows_batch_kernel, dim3(blocks), dim3(kRowThreads), 0, s, b);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(mask_compact_batch_kernel, dim3(b.n_calls), dim3(kCompactThreads), 0, s, b);
     return hipGetLastError();
 }
 

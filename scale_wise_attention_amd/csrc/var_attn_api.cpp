@@ -841,6 +841,65 @@ VAR_EXPORT var_status var_build_tile_mask(const var_schedule* sched, int32_t b, 
     return hip_status(varattn::launch_tile_mask(p, s), "var_build_tile_mask launch");
 }
 
+VAR_EXPORT var_status var_build_tile_masks(const var_schedule* sched, const var_mask_params* mp,
+                                           const var_tile_mask_call* calls, int32_t n_calls, void* stream) {
+    static_assert(VAR_MAX_MASK_CALLS == varattn::kMaxMaskBatch, "batch capacity");
+    if (!calls) return fail(VAR_ERR_NULL, "calls is NULL");
+    if (n_calls < 1 || n_calls > VAR_MAX_MASK_CALLS)
+        return fail(VAR_ERR_RANGE, "n_calls=%d outside [1, %d]", n_calls, VAR_MAX_MASK_CALLS);
+    varattn::MaskBatch bt;
+    std::memset(&bt, 0, sizeof(bt));
+    Offsets off{};
+    int64_t blocks = 0;
+    for (int32_t i = 0; i < n_calls; ++i) {
+        const var_tile_mask_call& c = calls[i];
+        int32_t rows, n_qt, n_kt;
+        var_status st = mask_dims(sched, c.q_scale_begin, c.q_scale_end, mp, c.q_index != nullptr, c.n_sel, &off,
+                                  &rows, &n_qt, &n_kt);
+        if (st != VAR_OK) {
+            char msg[256];
+            std::snprintf(msg, sizeof(msg), "%s", var_last_error());   // (fail rewrites the same buffer)
+            return fail(st, "call %d: %s", i, msg);
+        }
+        if (!c.row_ptr || (!c.col_idx && n_qt > 0))
+            return fail(VAR_ERR_NULL, "call %d: row_ptr and col_idx must be non-NULL", i);
+        if (c.col_capacity < (int64_t)n_qt * n_kt)
+            return fail(VAR_ERR_CAPACITY, "call %d: col_capacity=%lld below n_qt*n_kt=%lld", i,
+                        (long long)c.col_capacity, (long long)n_qt * n_kt);
+        if ((int64_t)n_qt * n_kt >= (int64_t)1 << 31) return fail(VAR_ERR_RANGE, "call %d: tile mask too large", i);
+        varattn::MaskCall& m = bt.c[i];
+        m.q_index = c.q_index;
+        m.row_ptr = c.row_ptr;
+        m.col_idx = c.col_idx;
+        m.n_rows = rows;
+        m.q_first = off.off[c.q_scale_begin];
+        m.n_q = off.off[c.q_scale_end] - off.off[c.q_scale_begin];
+        m.kv_len = off.off[c.q_scale_end];
+        m.n_qt = n_qt;
+        m.n_kt = n_kt;
+        m.num_scales = c.q_scale_end;
+        bt.first_block[i] = (int32_t)blocks;
+        blocks += n_qt;
+        if (blocks >= ((int64_t)1 << 31)) return fail(VAR_ERR_RANGE, "too many query tiles in the batch");
+    }
+    bt.first_block[n_calls] = (int32_t)blocks;
+    for (int32_t i = n_calls + 1; i <= varattn::kMaxMaskBatch; ++i) bt.first_block[i] = (int32_t)blocks;
+    bt.n_calls = n_calls;
+    bt.tile_q = mp->tile_q;
+    bt.tile_k = mp->tile_k;
+    bt.sink_scales = mp->sink_scales;
+    bt.local_from_scale = mp->local_from_scale;
+    bt.radius_y = mp->radius_y;
+    bt.radius_x = mp->radius_x;
+    for (int i = 0; i <= VAR_MAX_SCALES; ++i) bt.off[i] = i <= off.num_scales ? off.off[i] : off.off[off.num_scales];
+    for (int i = 0; i < VAR_MAX_SCALES; ++i) {
+        bt.h[i] = i < off.num_scales ? sched->h[i] : 1;
+        bt.w[i] = i < off.num_scales ? sched->w[i] : 1;
+    }
+    return hip_status(varattn::launch_tile_mask_batch(bt, reinterpret_cast<hipStream_t>(stream)),
+                      "var_build_tile_masks launch");
+}
+
 VAR_EXPORT var_status var_attn_saliency(const var_schedule* sched, const var_attn_desc* d, const void* q,
                                         var_layout q_l, const void* k, var_layout k_l, const float* lse,
                                         float* saliency, void* stream) {

@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header(api):
     declared = _declared()
-    assert len(declared) == 22
+    assert len(declared) == 23
     for name in declared:
         assert hasattr(api.LIB, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True).stdout
@@ -347,3 +347,37 @@ def test_noalloc_split_rejects_oversized_calls_before_any_hip_call(api):
     assert b"static scratch" in api.LIB.var_last_error()
     assert api.LIB.var_attn_dense_split_noalloc(ctypes.byref(s), ctypes.byref(d), P(FAKE), L, P(FAKE), L, P(FAKE),
                                                 L, P(FAKE), L, P(0), P(0), 0, 9, P(0)) == _code(api, "VAR_ERR_RANGE")
+
+
+def test_batched_masks_validation_errors(api):
+    """var_build_tile_masks checks every call on the host before it launches anything,
+    and names the call that failed."""
+    s = api.make_schedule(W1024, W1024)
+    mp = api.mask_params()
+    P = ctypes.c_void_p
+    build = api.LIB.var_build_tile_masks
+
+    def calls(*cs):
+        arr = (api.TileMaskCall * len(cs))()
+        for i, c in enumerate(cs):
+            arr[i] = api.TileMaskCall(*c)
+        return arr
+
+    good = (12, 13, None, 0, FAKE, FAKE, 64 * 165)
+    assert build(ctypes.byref(s), ctypes.byref(mp), None, 1, P(0)) == _code(api, "VAR_ERR_NULL")
+    assert build(ctypes.byref(s), ctypes.byref(mp), calls(good), 0, P(0)) == _code(api, "VAR_ERR_RANGE")
+    many = calls(*([good] * (api.MAX_MASK_CALLS + 1)))
+    assert build(ctypes.byref(s), ctypes.byref(mp), many, api.MAX_MASK_CALLS + 1, P(0)) == _code(api, "VAR_ERR_RANGE")
+    # call 1: a scale range past the schedule
+    r = build(ctypes.byref(s), ctypes.byref(mp), calls(good, (12, 14, None, 0, FAKE, FAKE, 64 * 165)), 2, P(0))
+    assert r == _code(api, "VAR_ERR_RANGE") and api.LIB.var_last_error().startswith(b"call 1: ")
+    # call 2: col_idx too small for its 26 x 165 pruned mask
+    short = (12, 13, FAKE, 1638, FAKE, FAKE, 26 * 165 - 1)
+    r = build(ctypes.byref(s), ctypes.byref(mp), calls(good, good, short), 3, P(0))
+    assert r == _code(api, "VAR_ERR_CAPACITY") and b"call 2" in api.LIB.var_last_error()
+    # call 0: NULL row_ptr
+    r = build(ctypes.byref(s), ctypes.byref(mp), calls((11, 12, None, 0, None, FAKE, 36 * 101)), 1, P(0))
+    assert r == _code(api, "VAR_ERR_NULL") and b"call 0" in api.LIB.var_last_error()
+    # the mask rule itself is checked as in var_build_tile_mask
+    bad = api.mask_params(0, 64)
+    assert build(ctypes.byref(s), ctypes.byref(bad), calls(good), 1, P(0)) == _code(api, "VAR_ERR_RANGE")

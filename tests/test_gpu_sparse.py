@@ -73,6 +73,45 @@ def test_mask_1024_pruned_last_step(api):
         _assert_mask_equal(api, wl.h, wl.w, K - 1, K, 64, 64, 7, 7, 2, 2, q_index=sel, what=f"pruned seed {seed}")
 
 
+def test_batched_masks_equal_oracle_and_single_builds(api):
+    """var_build_tile_masks over every step of the 1024px generation, the pruned last
+    step, an empty selection and the whole sequence in one call: each CSR bit-exact
+    against the oracle and against var_build_tile_mask; then a second batch reusing
+    the same buffers (stale contents) with another rule."""
+    wl = WORKLOADS["var1024_sparse"]
+    K = wl.num_scales
+    sel = pruned_index(4096, 0.4, 0)
+    idx = torch.from_numpy(sel).cuda()
+    empty = torch.empty(0, dtype=torch.int32, device="cuda")
+    specs = [(s, s + 1, None) for s in range(K)] + [(K - 1, K, sel), (K - 1, K, np.zeros(0, np.int32)),
+                                                   (0, K, None)]
+    assert len(specs) == api.MAX_MASK_CALLS
+    for sink, local, r in ((7, 7, 2), (3, 9, 1)):
+        mp = api.mask_params(64, 64, sink, local, r, r)
+        calls = []
+        for qb, qe, q in specs:
+            qi = None if q is None else (empty if q.size == 0 else idx)
+            calls.append((qb, qe, qi))
+        if sink == 7:
+            got = api.var_build_tile_masks((wl.h, wl.w), mp, calls)
+            first = got
+        else:   # the same buffers again, holding the first batch's lists
+            got = api.var_build_tile_masks((wl.h, wl.w), mp, [c + b for c, b in zip(calls, first)])
+        torch.cuda.synchronize()
+        for (qb, qe, q), (rp, ci), c in zip(specs, got, calls):
+            what = f"batch sink {sink} steps {qb}..{qe} {'pruned' if q is not None and q.size else 'empty' if q is not None else ''}"
+            rp_h, ci_h = _csr_host(rp, ci)
+            kept = oracle.tile_mask(wl.h, wl.w, qb, qe, 64, 64, sink, local, r, r, q_index=q)
+            erp, eci = oracle.mask_to_csr(kept)
+            print(f"[{what}] nnz {rp_h[-1]}", flush=True)
+            assert np.array_equal(rp_h, erp), what
+            assert np.array_equal(ci_h, eci), what
+            srp, sci = api.var_build_tile_mask((wl.h, wl.w), qb, qe, mp, q_index=c[2])
+            torch.cuda.synchronize()
+            srp_h, sci_h = _csr_host(srp, sci)
+            assert np.array_equal(rp_h, srp_h) and np.array_equal(ci_h, sci_h), what
+
+
 @pytest.mark.parametrize("tk,sink,local", [(1, 7, 7), (1, 13, 13), (3, 2, 9)])
 def test_mask_1024_last_step_many_key_tiles(api, tk, sink, local):
     # more than 8192 key tiles: the builder's bitmap takes several passes
