@@ -206,16 +206,18 @@ var_status var_attn_dense_split_noalloc(const var_schedule* sched, const var_att
 /*
  * Split count for a call (host only; reads the current device's compute-unit
  * count, 256 if it cannot): the fewest splits whose modelled time is within
- * 3% of the lowest (the unsplit rounds, then rounds of parts over the resident workgroups
- * times key tiles per part, plus the combining launch and its workspace
- * traffic).  kv_tiles_hint: 64-key
- * tiles a work item visits (0 = ceil(kv_len / 64), the dense count; pass the
- * mean kept tiles per mask row for a sparse call; the model still counts the
- * dense kernel's work items, 256 query rows each, one workgroup per compute
- * unit, so for sparse calls it is a rougher guide).  Writes *n_splits and the
- * workspace bytes a dense or block-sparse call with that count needs on this
- * device (either pointer may be NULL).  n_sel as in
- * var_attn_dense (0 = no gather).  f32 input always gives 1 and 0 bytes.
+ * 3% of the lowest (the unsplit rounds, then rounds of parts over the
+ * resident workgroups times key tiles per part, plus the combining launch and
+ * its workspace traffic).  A dense work item is 128 query rows at head_dim
+ * 128 when all of the call's 128-row items fit one round of the compute
+ * units, else 256 rows.  kv_tiles_hint: 64-key tiles a work item visits
+ * (0 = ceil(kv_len / 64), the dense count; pass the mean kept tiles per mask
+ * row for a sparse call; the model still counts the dense kernel's work
+ * items, one workgroup per compute unit, so for sparse calls it is a rougher
+ * guide).  Writes *n_splits and the workspace bytes a dense or block-sparse
+ * call with that count needs on this device (either pointer may be NULL).
+ * n_sel as in var_attn_dense (0 = no gather).  f32 input always gives 1 and
+ * 0 bytes.
  */
 var_status var_attn_split_plan(const var_schedule* sched, const var_attn_desc* desc, int32_t n_sel,
                                int32_t kv_tiles_hint, int32_t* n_splits, int64_t* workspace_bytes);

@@ -8,6 +8,8 @@
 
 namespace varattn {
 
+int attn_fp8_rows_per_tile(bool sparse) { return sparse ? rows_per_wg<true, 2>() : rows_per_wg<false, 2>(); }
+
 int attn_fp8_resident_wgs(bool out_bf16, bool sparse) {
     if (sparse) return out_bf16 ? resident_wgs<128, true, true, true, 2>() : resident_wgs<128, false, true, true, 2>();
     return out_bf16 ? resident_wgs<128, true, false, true, 2>() : resident_wgs<128, false, false, true, 2>();

@@ -14,17 +14,18 @@
 // Design 2).
 //
 // Design (dense: one workgroup = 256 query rows of one (batch, head), 4 waves
-// of 64 rows, one wave per SIMD, or for short launches at head_dim 128 8 waves
-// of 32 rows; block-sparse: 128 rows, two workgroups per compute unit, as 4
-// waves of 32 rows (two waves per SIMD) at head_dim 128 and 2 waves of 64 rows
-// at 64):
+// of 64 rows, one wave per SIMD, or, at head_dim 128 for launches whose work
+// items fit one round of the device, 128 rows as 4 waves of 32; block-sparse:
+// 128 rows, two workgroups per compute unit, as 4 waves of 32 rows (two waves
+// per SIMD) at head_dim 128 and 2 waves of 64 rows at 64):
 //  * Each wave owns QB 32-query column blocks (QB = 2: 64 queries; QB = 1:
 //    32).  S^T = K Q^T is computed with v_mfma_f32_32x32x16_bf16 (keys on M,
 //    queries on N), so a lane holds 16 logits of each of its queries and lane
 //    l^32 holds the other 16 of every 32-key block.  With two blocks every K
 //    operand read from LDS feeds two MFMAs, halving LDS traffic per FLOP; one
-//    block leaves each wave at most 256 registers, so two waves share a SIMD
-//    and one's LDS reads and softmax run under the other's MFMAs.
+//    block shortens a wave's tile (half the MFMAs) and leaves it at most 256
+//    registers, so in a block-sparse workgroup two waves share a SIMD and
+//    one's LDS reads and softmax run under the other's MFMAs.
 //  * The same registers, rounded to bf16, are the B operand of
 //    O^T += V^T P^T (d on M, queries on N, keys on K).  The MFMA's k order is
 //    matched by permuting keys inside the V^T tile in LDS, so P never moves
@@ -92,15 +93,17 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int KT = 64;                 // keys per tile (= sparse tile width)
-// query rows per workgroup: 256 for dense attention; 128 (two 64-row mask rows)
-// for block-sparse attention, whose workgroup walks the union of the two rows'
-// kept tiles (two workgroups then share a compute unit)
-template <bool SPARSE>
-constexpr int rows_per_wg() { return SPARSE ? 2 * KT : 4 * KT; }
-// waves per workgroup when a wave owns QB 32-row query blocks: QB = 2 runs one
-// wave per SIMD, QB = 1 two
+// query rows per workgroup when a wave owns QB 32-row query blocks:
+// block-sparse 128 (two 64-row mask rows; the workgroup walks the union of
+// the two rows' kept tiles, and two workgroups share a compute unit); dense
+// 256 with QB = 2 (4 waves of 64 rows, the throughput shape) and 128 with
+// QB = 1 (4 waves of 32 rows, one per SIMD: for launches whose work items fit
+// one round of the device, where the latency of a tile counts, not the rate)
 template <bool SPARSE, int QB>
-constexpr int waves_per_wg() { return rows_per_wg<SPARSE>() / (32 * QB); }
+constexpr int rows_per_wg() { return SPARSE ? 2 * KT : (QB == 1 ? 2 * KT : 4 * KT); }
+// waves per workgroup
+template <bool SPARSE, int QB>
+constexpr int waves_per_wg() { return rows_per_wg<SPARSE, QB>() / (32 * QB); }
 constexpr float kSumLimit = 0x1p100f;  // a row sum above this triggers the exact recompute
 
 // Work of workgroup wg (of nwg): work item `item`, key split `split`, and
@@ -273,13 +276,13 @@ struct TileEnt {
 // its 64 bf16 query rows to e4m3 (one scale), and S^T comes from
 // v_mfma_f32_32x32x64_f8f6f4 (64 deep per k-step); V stays bf16.
 template <int D, bool OUT_BF16, bool SPARSE, bool QK8, int QB>
-__global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), (QB == 1 ? 2 : 1)) void attn_kernel(const AttnParams p) {
+__global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), ((SPARSE && QB == 1) ? 2 : 1)) void attn_kernel(const AttnParams p) {
     static_assert(QB == 1 || QB == 2, "one or two 32-row query blocks per wave");
     static_assert(!QK8 || QB == 2, "e4m3 queries are quantised per 64 rows: one wave's rows");
     constexpr int NW = waves_per_wg<SPARSE, QB>();   // waves per workgroup
     constexpr int NT = NW * 64;                      // threads per workgroup
     constexpr int QW = 32 * QB;                      // query rows per wave
-    constexpr int QT = rows_per_wg<SPARSE>();        // query rows per workgroup
+    constexpr int QT = rows_per_wg<SPARSE, QB>();    // query rows per workgroup
     constexpr int NL = QT / KT;                      // block-sparse: kept-tile lists (64-row mask rows) per workgroup
     constexpr int EK = QK8 ? 1 : 2;            // bytes per k element (q is always bf16)
     constexpr int ROWB = D * EK;               // bytes per K row
@@ -1247,7 +1250,7 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
     hipLaunchKernelGGL((attn_kernel<D, OB, SP, QK8, QB>), dim3(grid), dim3(waves_per_wg<SP, QB>() * 64), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split_from == items) return e;
-    constexpr int QT = rows_per_wg<SP>();
+    constexpr int QT = rows_per_wg<SP, QB>();
     const int64_t threads = (int64_t)(items - p.split_from) * QT * (D / 4);
     hipLaunchKernelGGL((split_merge_kernel<OB>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p, D,
                        QT);

@@ -99,7 +99,9 @@ struct ScatterParams {
 };
 
 // Launchers: return the hipError_t of the launch.
-hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, bool out_bf16, bool sparse, hipStream_t s);
+// rows_per_tile: attn_bf16_rows_per_tile of the call (it selects the kernel).
+hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, bool out_bf16, bool sparse, int rows_per_tile,
+                            hipStream_t s);
 // The same attention with k as e4m3 codes (k_scale set) and q quantised to
 // e4m3 in the kernel, one scale per 64-row tile of the call; v bf16.
 hipError_t launch_attn_fp8(const AttnParams& p, int head_dim, bool out_bf16, bool sparse, hipStream_t s);
@@ -216,11 +218,16 @@ hipError_t launch_select_topk(const SelectParams& p, hipStream_t s);
 hipError_t launch_scatter(const ScatterParams& p, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, hipStream_t s);
 
-// Query-tile height of the bf16 kernels (rows per workgroup).
-int attn_bf16_rows_per_tile(int head_dim, bool sparse);
+// Query-tile height (rows per workgroup) of a bf16 launch over bh maps of
+// `rows` rows each on a device of `cus` compute units: 128 for block-sparse
+// attention; for dense attention 128 at head_dim 128 when those work items fit
+// one round of the device's resident workgroups, else 256.
+int attn_bf16_rows_per_tile(int head_dim, bool sparse, int64_t bh, int64_t rows, int cus);
+// The same for the e4m3 kernels: 128 block-sparse, 256 dense.
+int attn_fp8_rows_per_tile(bool sparse);
 // Workgroups of the bf16 / e4m3 attention kernel that one compute unit holds
 // at once (from the runtime's occupancy query; 1 when it cannot say).
-int attn_bf16_resident_wgs(int head_dim, bool out_bf16, bool sparse);
+int attn_bf16_resident_wgs(int head_dim, bool out_bf16, bool sparse, int rows_per_tile);
 int attn_fp8_resident_wgs(bool out_bf16, bool sparse);
 constexpr int kF32RowsPerTile = 64;
 

@@ -370,7 +370,7 @@ var_status dense_impl(const var_schedule* sched, const var_attn_desc* desc, cons
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (e4m3) {
         attach_e4m3(&p, *e4m3);
-        const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false);
+        const int rpt = varattn::attn_fp8_rows_per_tile(false);
         p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
         if ((st = set_split_items(&p, varattn::attn_fp8_resident_wgs(desc->out_dtype == VAR_BF16, false), rpt,
                                   desc->head_dim, ws_bytes)) != VAR_OK)
@@ -379,14 +379,14 @@ var_status dense_impl(const var_schedule* sched, const var_attn_desc* desc, cons
                           "var_attn_dense_e4m3 launch");
     }
     if (desc->in_dtype == VAR_BF16) {
-        const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false);
+        const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false, (int64_t)p.B * p.H, p.n_rows,
+                                                         device_cu_count());
         p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
         const bool ob = desc->out_dtype == VAR_BF16;
-        if ((st = set_split_items(&p, varattn::attn_bf16_resident_wgs(desc->head_dim, ob, false), rpt,
+        if ((st = set_split_items(&p, varattn::attn_bf16_resident_wgs(desc->head_dim, ob, false, rpt), rpt,
                                   desc->head_dim, ws_bytes)) != VAR_OK)
             return st;
-        return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, desc->out_dtype == VAR_BF16, false, s),
-                          "var_attn_dense launch");
+        return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, ob, false, rpt, s), "var_attn_dense launch");
     }
     p.n_qtiles = (p.n_rows + varattn::kF32RowsPerTile - 1) / varattn::kF32RowsPerTile;
     return hip_status(varattn::launch_attn_f32(p, desc->head_dim, false, s), "var_attn_dense launch");
@@ -423,18 +423,20 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (desc->in_dtype == VAR_BF16) {
         // each workgroup covers a whole number of 64-row tiles of the mask
-        const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, true);
+        const int rpt = e4m3 ? varattn::attn_fp8_rows_per_tile(true)
+                             : varattn::attn_bf16_rows_per_tile(desc->head_dim, true, (int64_t)p.B * p.H, p.n_rows,
+                                                                device_cu_count());
         p.n_qtiles = (p.n_rows + rpt - 1) / rpt;
         const bool ob = desc->out_dtype == VAR_BF16;
         const int resident = e4m3 ? varattn::attn_fp8_resident_wgs(ob, true)
-                                  : varattn::attn_bf16_resident_wgs(desc->head_dim, ob, true);
+                                  : varattn::attn_bf16_resident_wgs(desc->head_dim, ob, true, rpt);
         if ((st = set_split_items(&p, resident, rpt, desc->head_dim, ws_bytes)) != VAR_OK) return st;
         if (e4m3) {
             attach_e4m3(&p, *e4m3);
             return hip_status(varattn::launch_attn_fp8(p, desc->head_dim, desc->out_dtype == VAR_BF16, true, s),
                               "var_attn_block_sparse_e4m3 launch");
         }
-        return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, desc->out_dtype == VAR_BF16, true, s),
+        return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, ob, true, rpt, s),
                           "var_attn_block_sparse launch");
     }
     p.n_qtiles = (p.n_rows + varattn::kF32RowsPerTile - 1) / varattn::kF32RowsPerTile;
@@ -655,11 +657,12 @@ VAR_EXPORT var_status var_attn_split_plan(const var_schedule* sched, const var_a
     const int64_t bh = (int64_t)d->batch * d->heads;
     int32_t s = 1;
     if (d->in_dtype == VAR_BF16) {
-        const int rpt = varattn::attn_bf16_rows_per_tile(d->head_dim, false);
+        const int cus = device_cu_count();
+        const int rpt = varattn::attn_bf16_rows_per_tile(d->head_dim, false, bh, rows, cus);
         const int64_t tasks = bh * ((rows + rpt - 1) / rpt);
         const int64_t tiles = kv_tiles_hint > 0 ? kv_tiles_hint : (off.off[d->q_scale_end] + 63) / 64;
         const int64_t cap =
-            (int64_t)device_cu_count() * varattn::attn_bf16_resident_wgs(d->head_dim, d->out_dtype == VAR_BF16, false);
+            (int64_t)cus * varattn::attn_bf16_resident_wgs(d->head_dim, d->out_dtype == VAR_BF16, false, rpt);
         s = choose_splits(tasks, tiles, bh * rows, d->head_dim, cap);
     }
     if (n_splits) *n_splits = s;
@@ -667,9 +670,9 @@ VAR_EXPORT var_status var_attn_split_plan(const var_schedule* sched, const var_a
         *workspace_bytes = 0;
         if (s > 1) {   // enough for a dense or a block-sparse call (their work items differ)
             for (const bool sp : {false, true}) {
-                const int rpt = varattn::attn_bf16_rows_per_tile(d->head_dim, sp);
+                const int rpt = varattn::attn_bf16_rows_per_tile(d->head_dim, sp, bh, rows, device_cu_count());
                 const int64_t cap = (int64_t)device_cu_count() *
-                                    varattn::attn_bf16_resident_wgs(d->head_dim, d->out_dtype == VAR_BF16, sp);
+                                    varattn::attn_bf16_resident_wgs(d->head_dim, d->out_dtype == VAR_BF16, sp, rpt);
                 const int64_t need = split_need_bytes(s, split_rows(bh, rows, rpt, cap).part_rows, d->head_dim);
                 *workspace_bytes = need > *workspace_bytes ? need : *workspace_bytes;
             }
@@ -733,11 +736,11 @@ VAR_EXPORT var_status var_attn_dense_split_noalloc(const var_schedule* sched, co
     const int64_t n_q = off.off[desc->q_scale_end] - off.off[desc->q_scale_begin];
     const int64_t rows = q_index ? n_sel : n_q;
     if (rows > 0) {
-        const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false);
+        const int64_t bh = (int64_t)desc->batch * desc->heads;
+        const int rpt = varattn::attn_bf16_rows_per_tile(desc->head_dim, false, bh, rows, device_cu_count());
         const int64_t cap = (int64_t)device_cu_count() *
-                            varattn::attn_bf16_resident_wgs(desc->head_dim, desc->out_dtype == VAR_BF16, false);
-        const int64_t need = split_need_bytes(n_splits, split_rows((int64_t)desc->batch * desc->heads, rows, rpt,
-                                                                   cap).part_rows, desc->head_dim);
+                            varattn::attn_bf16_resident_wgs(desc->head_dim, desc->out_dtype == VAR_BF16, false, rpt);
+        const int64_t need = split_need_bytes(n_splits, split_rows(bh, rows, rpt, cap).part_rows, desc->head_dim);
         if (need > kScratchBytes)
             return fail(VAR_ERR_CAPACITY, "the call needs %lld bytes of split partials, above the library's "
                         "static scratch of %lld bytes (use var_attn_dense_split with a workspace)",

@@ -219,17 +219,22 @@ def test_split_validation_and_plan(api):
     assert call(f32, 2) == E("VAR_ERR_UNSUPPORTED")
     n, nbytes = api.var_attn_split_plan((W1024, W1024), 12, 13, 2, 16, 128)
     assert n == 1 and nbytes == 0                      # 512 work items already fill 256 compute units
-    n, nbytes = api.var_attn_split_plan((W1024, W1024), 9, 10, 2, 16, 128)
-    assert n > 1 and nbytes == n * 32 * 1024 * 129 * 4  # 128 work items of 40 key tiles
+    # the 32x32 step: 256 work items of 128 rows fill the 256 compute units; with
+    # one batch, 128 items of 40 key tiles leave half of them idle, and their
+    # split rows are all of the call's
+    assert api.var_attn_split_plan((W1024, W1024), 9, 10, 2, 16, 128) == (1, 0)
+    n, nbytes = api.var_attn_split_plan((W1024, W1024), 9, 10, 1, 16, 128)
+    assert n > 1 and nbytes == n * 16 * 1024 * 129 * 4
     assert api.var_attn_split_plan((W1024, W1024), 9, 10, 2, 16, 64, dtype=torch.float32) == (1, 0)
     # 288 work items: one whole round of 256 plus 32 items of 101 key tiles that the split spreads
     n, nbytes = api.var_attn_split_plan((W1024, W1024), 11, 12, 2, 16, 128)
     assert n >= 4 and nbytes == n * 8192 * 129 * 4         # only the 32 split items' rows
     # the plan on every 1024px step (256 compute units): dense, then sparse with the
     # mean kept tiles per mask row as the hint; the fewest splits within 3% of the
-    # lowest modelled cost (48x48 sparse: 5 splits cost 38.8 units, 4 cost 39.7)
+    # lowest modelled cost (48x48 sparse: 5 splits cost 38.8 units, 4 cost 39.7).
+    # Dense steps up to 32x32 run 128-row work items, all in one round: unsplit.
     dense = [api.var_attn_split_plan((W1024, W1024), st, st + 1, 2, 16, 128)[0] for st in range(13)]
-    assert dense == [1, 1, 1, 1, 1, 1, 1, 3, 2, 2, 1, 6, 1]
+    assert dense == [1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 6, 1]
     hints = {7: 11, 8: 15, 9: 18, 10: 21, 11: 25}
     sparse = [api.var_attn_split_plan((W1024, W1024), st, st + 1, 2, 16, 128, kv_tiles_hint=h)[0]
               for st, h in hints.items()]
@@ -336,11 +341,12 @@ def test_device_info_without_a_device(api):
 
 def test_noalloc_split_rejects_oversized_calls_before_any_hip_call(api):
     """The allocation-free split call checks its partials against the static scratch
-    first: 8 parts of the 32x32 step (135 MB) exceed the 64 MiB."""
+    first: 8 parts of the 24x24 step (160 work items of 128 rows, all split: 76 MB)
+    exceed the 64 MiB."""
     s = api.make_schedule(W1024, W1024)
     L = api.Layout(2 * 16 * 4096 * 128, 4096 * 128, 128)
     P = ctypes.c_void_p
-    d = _desc(api, q_scale_begin=9, q_scale_end=10)
+    d = _desc(api, q_scale_begin=8, q_scale_end=9)
     r = api.LIB.var_attn_dense_split_noalloc(ctypes.byref(s), ctypes.byref(d), P(FAKE), L, P(FAKE), L, P(FAKE), L,
                                              P(FAKE), L, P(0), P(0), 0, 8, P(0))
     assert r == _code(api, "VAR_ERR_CAPACITY")

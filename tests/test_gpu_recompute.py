@@ -133,36 +133,48 @@ def test_gather_splits_full_sequence_recompute(api):
     _check(o, lse, res, vn, "full sequence")
 
 
-def test_dense_recompute_both_wave_shapes(api):
-    """A 32x32 step (1024 queries x 2521 keys = 40 key tiles, head_dim 128): unsplit,
-    each workgroup walks 40 tiles and the kernel runs 64-row waves; with two key
-    splits it walks 20 and runs 32-row waves (two per SIMD).  Both against the
-    oracle with the recompute forced, plus a gathered subset of the rows."""
+@pytest.mark.parametrize("bh", [(1, 2), (2, 20)])
+def test_dense_recompute_both_wave_shapes(api, bh):
+    """A 32x32 step (1024 queries x 2521 keys = 40 key tiles, head_dim 128) with the
+    recompute forced.  With 2 (batch, head) maps the call's 16 work items of 128
+    rows fit one round of the device, so it runs 128-row workgroups of 32-row
+    waves; with 40 maps (320 such items, more than the 256 compute units) it runs
+    256-row workgroups of 64-row waves.  Unsplit and with two key splits, on the
+    first and last map against the oracle, plus a gathered subset of the rows."""
+    B, H = bh
+    assert (B * H * 8 <= torch.cuda.get_device_properties(0).multi_processor_count) == (bh == (1, 2))
     grids = GRIDS + (32,)
-    wl = custom_workload(grids, 1, 2, 128)
+    wl = custom_workload(grids, B, H, 128)
     q, k, v = make_qkv(wl, 14, device="cuda")
     off = oracle.offsets(wl.h, wl.w)
     s = len(grids) - 1
     assert -(-off[s + 1] // 64) == 40
     qs = q[:, :, off[s]:off[s + 1]]
     n = off[s + 1] - off[s]
-    qn, kn, vn = _np(qs), _np(k), _np(v)
-    assert _spread(qn, kn, wl.h, wl.w, s) > 100    # the recompute is needed
-    res = oracle.attention(qn, kn, vn, wl.h, wl.w, s, s + 1, softmax_scale=SCALE, return_lse=True,
-                           return_probs=True)
     sel = np.random.default_rng(15).choice(n, 300, replace=False).astype(np.int32)
     sel.sort()
     idx = torch.from_numpy(sel).cuda()
-    res_g = oracle.attention(qn, kn, vn, wl.h, wl.w, s, s + 1, q_index=sel, softmax_scale=SCALE, return_lse=True,
-                             return_probs=True)
+    maps = [(0, 0), (B - 1, H - 1)]
+    refs = {}
+    for (b, h) in maps:
+        qn, kn, vn = _np(qs[b:b + 1, h:h + 1]), _np(k[b:b + 1, h:h + 1]), _np(v[b:b + 1, h:h + 1])
+        assert _spread(qn, kn, wl.h, wl.w, s) > 100    # the recompute is needed
+        refs[(b, h)] = (vn,
+                        oracle.attention(qn, kn, vn, wl.h, wl.w, s, s + 1, softmax_scale=SCALE, return_lse=True,
+                                         return_probs=True),
+                        oracle.attention(qn, kn, vn, wl.h, wl.w, s, s + 1, q_index=sel, softmax_scale=SCALE,
+                                         return_lse=True, return_probs=True))
     for splits in (1, 2):
-        ws = api.split_workspace(splits, 1, 2, n, 128) if splits > 1 else None
+        ws = api.split_workspace(splits, B, H, n, 128) if splits > 1 else None
         o, lse = api.var_attn_dense((wl.h, wl.w), qs, k, v, s, s + 1, softmax_scale=SCALE, return_lse=True,
                                     n_splits=splits, workspace=ws)
-        _check(o, lse, res, vn, f"32x32 step, splits={splits}")
-        o, lse = api.var_attn_dense((wl.h, wl.w), qs, k, v, s, s + 1, q_index=idx, softmax_scale=SCALE,
-                                    return_lse=True, n_splits=splits, workspace=ws)
-        _check(o, lse, res_g, vn, f"32x32 step gather, splits={splits}")
+        og, lseg = api.var_attn_dense((wl.h, wl.w), qs, k, v, s, s + 1, q_index=idx, softmax_scale=SCALE,
+                                      return_lse=True, n_splits=splits, workspace=ws)
+        for (b, h) in maps:
+            vn, res, res_g = refs[(b, h)]
+            m = (slice(b, b + 1), slice(h, h + 1))
+            _check(o[m], lse[m], res, vn, f"32x32 step {B}x{H}, splits={splits}, map ({b}, {h})")
+            _check(og[m], lseg[m], res_g, vn, f"32x32 step {B}x{H} gather, splits={splits}, map ({b}, {h})")
 
 
 def test_sparse_recompute(api):

@@ -168,13 +168,16 @@ def test_split_plan_and_errors(api):
     assert 1 <= n <= 8 and nbytes == (n * 8192 * 129 * 4 if n > 1 else 0)
     q, k, v = make_qkv(wl, 0, device="cuda")
     off = oracle.offsets(wl.h, wl.w)
-    qs = q[:, :, off[9]:off[10]]
-    short = api.split_workspace(2, 2, 16, 1000, 128)
+    # (the 24x24 step: 160 work items of 128 rows, fewer than the compute units,
+    # so every item runs split and all 32 x 576 rows are partial rows; the
+    # workspace holds 500 per map)
+    qs = q[:, :, off[8]:off[9]]
+    short = api.split_workspace(2, 2, 16, 500, 128)
     with pytest.raises(api.VarAttnError) as e:
-        api.var_attn_dense((wl.h, wl.w), qs, k, v, 9, 10, n_splits=2, workspace=short)
+        api.var_attn_dense((wl.h, wl.w), qs, k, v, 8, 9, n_splits=2, workspace=short)
     assert e.value.status_name == "VAR_ERR_CAPACITY"
     with pytest.raises(api.VarAttnError) as e:
-        api.var_attn_dense((wl.h, wl.w), qs, k, v, 9, 10, n_splits=9, workspace=short)
+        api.var_attn_dense((wl.h, wl.w), qs, k, v, 8, 9, n_splits=9, workspace=short)
     assert e.value.status_name == "VAR_ERR_RANGE"
 
 

@@ -41,9 +41,10 @@ def wl_sched(wl):
 def test_noalloc_matches_workspace_call_twice_second_smaller(api):
     wl = WORKLOADS["var1024"]
     q, k, v = make_qkv(wl, 21, device="cuda")
-    # first: the 32x32 step, every work item split in 2 (33.8 MB of partials);
-    # second: the 20x20 step split in 3 (fewer rows, reusing what the first left)
-    for s, n_splits in ((9, 2), (7, 3)):
+    # first: the 24x24 step, every work item (160 of 128 rows) split in 3 (28.5 MB
+    # of partials); second: the 20x20 step split in 2 (fewer rows, 13.2 MB,
+    # reusing what the first left)
+    for s, n_splits in ((8, 3), (7, 2)):
         (oa, la), (ob, lb), qs = _call_pair(api, wl, q, k, v, s, n_splits)
         torch.cuda.synchronize()
         print(f"[noalloc step {s} x{n_splits}] equal: {torch.equal(oa, ob)} {torch.equal(la, lb)}", flush=True)
@@ -63,7 +64,7 @@ def test_noalloc_rejects_calls_beyond_the_scratch(api):
     wl = WORKLOADS["var1024"]
     q, k, v = make_qkv(wl, 23, device="cuda")
     off = oracle.offsets(wl.h, wl.w)
-    # the 32x32 step split 8 ways needs 8 x 32768 x 129 x 4 bytes = 135 MB > 64 MiB
+    # the 24x24 step split 8 ways needs 8 x 18432 x 129 x 4 bytes = 76 MB > 64 MiB
     with pytest.raises(api.VarAttnError) as e:
-        api.var_attn_dense_split_noalloc(wl_sched(wl), q[:, :, off[9]:off[10]], k, v, 9, 10, 8)
+        api.var_attn_dense_split_noalloc(wl_sched(wl), q[:, :, off[8]:off[9]], k, v, 8, 9, 8)
     assert e.value.status_name == "VAR_ERR_CAPACITY"
