@@ -390,6 +390,7 @@ def main():
         copy_dst = torch.empty_like(copy_src)
         groups = [(f"dense s{s}", lambda s=s: dense_step(s)) for s in range(K)]
         groups += [(f"mask s{s}", lambda s=s: mask_step(s)) for s in range(K) if not full_mask[s]]
+        groups += [("masks batched", build_masks)]
         groups += [(f"sparse s{s}", lambda s=s: sparse_step(s)) for s in range(K - 1) if not full_mask[s]]
         groups += [("pruned gathered", lambda: sparse_step(K - 1)),
                    ("pruned in place", lambda: sparse_step(K - 1, in_place=True)),
