@@ -275,9 +275,14 @@ struct TileEnt {
 // QK8: k is e4m3 codes with one scale per 64-key tile, each wave quantises
 // its 64 bf16 query rows to e4m3 (one scale), and S^T comes from
 // v_mfma_f32_32x32x64_f8f6f4 (64 deep per k-step); V stays bf16.
-template <int D, bool OUT_BF16, bool SPARSE, bool QK8, int QB>
-__global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), ((SPARSE && QB == 1) ? 2 : 1)) void attn_kernel(const AttnParams p) {
+// WIDE: the 4-slot ring (two tiles ahead) and tile pairs, one workgroup per
+// compute unit: every dense walk, and block-sparse launches whose workgroups
+// all fit one round of the device (the others keep two workgroups per unit
+// with a 2-slot ring)
+template <int D, bool OUT_BF16, bool SPARSE, bool QK8, int QB, bool WIDE = !SPARSE>
+__global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), ((SPARSE && QB == 1 && !WIDE) ? 2 : 1)) void attn_kernel(const AttnParams p) {
     static_assert(QB == 1 || QB == 2, "one or two 32-row query blocks per wave");
+    static_assert(WIDE || SPARSE, "dense walks use the 4-slot ring");
     static_assert(!QK8 || QB == 2, "e4m3 queries are quantised per 64 rows: one wave's rows");
     constexpr int NW = waves_per_wg<SPARSE, QB>();   // waves per workgroup
     constexpr int NT = NW * 64;                      // threads per workgroup
@@ -300,8 +305,9 @@ __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), ((SPARSE && QB =
     constexpr int MO = D / 32;                 // 32-row blocks of O^T
 
     // LDS ring of K and V^T tiles: 4 slots (two tiles ahead, pairs of tiles
-    // per barrier) in a dense walk, 2 (one tile ahead) in a block-sparse walk
-    constexpr int RING = SPARSE ? 2 : 4;
+    // per barrier) in a wide walk, 2 (one tile ahead) in a block-sparse walk
+    // that shares its compute unit
+    constexpr int RING = WIDE ? 4 : 2;
     constexpr int AHEAD = RING / 2;
     __shared__ __attribute__((aligned(16))) unsigned char smem[RING * K_BYTES + RING * V_BYTES];
     unsigned char* const Kbuf = smem;
@@ -575,6 +581,9 @@ __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), ((SPARSE && QB =
     }
     // workgroup reductions in LDS words of their own (a K DMA may be in flight)
     __shared__ int wg_words[3 * NW];
+    // wide block-sparse walks: each wave's "rows without a reference" flag,
+    // posted per tile (two sets, by tile parity) until no wave has one
+    __shared__ int ref_words[2][NW];
     int wg_kmin;   // smallest key limit in the workgroup: tiles below it need no mask
     {
         int* red = wg_words;
@@ -1021,6 +1030,17 @@ __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), ((SPARSE && QB =
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
             __syncthreads();
         };
+        // Wide block-sparse walk: tile pairs once no wave of the workgroup
+        // lacks a reference (a workgroup-uniform flag, from the words the
+        // waves post at each single tile's barrier) and neither tile needs a
+        // mask; a wave that does not own a tile of the pair takes it with
+        // zero weights
+        constexpr bool SPAIRS = SPARSE && WIDE && MODE == 0;
+        bool all_ref = false;
+        auto pair_ok = [&]() __attribute__((always_inline)) -> bool {
+            return SPAIRS && all_ref && e1.tile >= 0 && j > 0 && e0.tile * KT + KT <= wg_kmin &&
+                   e1.tile * KT + KT <= wg_kmin;
+        };
         // one tile per barrier; the tile AHEAD places on is loaded meanwhile
         auto single = [&](auto fast_tag) __attribute__((always_inline)) {
             const TileEnt nx = AHEAD == 2 ? e2 : e1;
@@ -1040,7 +1060,18 @@ __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), ((SPARSE && QB =
             } else {
                 body(BoolC<decltype(fast_tag)::value == 1>{}, e0, j % RING, nx, (j + AHEAD) % RING);
             }
+            if constexpr (SPAIRS) {
+                if (!all_ref && lane == 0) ref_words[j & 1][wave] = need_ref ? 1 : 0;
+            }
             tile_barrier();
+            if constexpr (SPAIRS) {
+                if (!all_ref) {
+                    int any = 0;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) any |= ref_words[j & 1][w];
+                    all_ref = __builtin_amdgcn_readfirstlane(any) == 0;
+                }
+            }
             e0 = e1;
             if constexpr (AHEAD == 2) {
                 e1 = e2;
@@ -1050,7 +1081,7 @@ __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), ((SPARSE && QB =
             }
             ++j;
         };
-        // two branch-free tiles per barrier (dense walks): the two after them are
+        // two branch-free tiles per barrier (wide walks): the two after them are
         // loaded meanwhile
         auto pair = [&]() __attribute__((always_inline)) {
             const TileEnt e3 = next_tile();
@@ -1071,14 +1102,19 @@ __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), ((SPARSE && QB =
                 if (e0.tile >= 0) single(IntC<0>{});
             } else {
                 // (block-sparse: three loops, one per body, one barrier per tile
-                // in each, so the waves of a workgroup may sit in different loops)
+                // in each, so the waves of a workgroup may sit in different loops;
+                // a wide walk leaves them all, at the same tile, for tile pairs)
+                if constexpr (SPAIRS) {
+                    while (pair_ok()) pair();
+                }
                 if constexpr (SPARSE) {
-                    while (e0.tile >= 0 && !mine(e0)) single(IntC<2>{});
+                    while (e0.tile >= 0 && !mine(e0) && !pair_ok()) single(IntC<2>{});
                 }
                 if constexpr (MODE == 0) {
-                    while (e0.tile >= 0 && (!SPARSE || mine(e0)) && fast(e0, j)) single(IntC<1>{});
+                    while (e0.tile >= 0 && (!SPARSE || mine(e0)) && fast(e0, j) && !pair_ok()) single(IntC<1>{});
                 }
-                while (e0.tile >= 0 && (!SPARSE || mine(e0)) && (MODE != 0 || !fast(e0, j))) single(IntC<0>{});
+                while (e0.tile >= 0 && (!SPARSE || mine(e0)) && (MODE != 0 || !fast(e0, j)) && !pair_ok())
+                    single(IntC<0>{});
             }
         }
     };
@@ -1229,12 +1265,12 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, in
 
 // Workgroups of one instantiation that a compute unit holds at once (1 when
 // the runtime cannot say).
-template <int D, bool OB, bool SP, bool QK8, int QB>
+template <int D, bool OB, bool SP, bool QK8, int QB, bool WIDE = !SP>
 int resident_wgs() {
     static const int n = [] {
         int k = 0;
         const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &k, attn_kernel<D, OB, SP, QK8, QB>, waves_per_wg<SP, QB>() * 64, 0);
+            &k, attn_kernel<D, OB, SP, QK8, QB, WIDE>, waves_per_wg<SP, QB>() * 64, 0);
         if (e != hipSuccess) (void)hipGetLastError();
         return e == hipSuccess && k > 0 ? k : 1;
     }();
@@ -1243,11 +1279,11 @@ int resident_wgs() {
 
 // The host bounds split_from + (items - split_from) * n_splits below 2^31 and
 // sets split_from = items when n_splits == 1.
-template <int D, bool OB, bool SP, bool QK8, int QB>
+template <int D, bool OB, bool SP, bool QK8, int QB, bool WIDE = !SP>
 hipError_t launch_one(const AttnParams& p, hipStream_t s) {
     const int items = p.n_qtiles * p.B * p.H;
     const int grid = p.split_from + (items - p.split_from) * p.n_splits;
-    hipLaunchKernelGGL((attn_kernel<D, OB, SP, QK8, QB>), dim3(grid), dim3(waves_per_wg<SP, QB>() * 64), 0, s, p);
+    hipLaunchKernelGGL((attn_kernel<D, OB, SP, QK8, QB, WIDE>), dim3(grid), dim3(waves_per_wg<SP, QB>() * 64), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split_from == items) return e;
     constexpr int QT = rows_per_wg<SP, QB>();

@@ -99,9 +99,11 @@ struct ScatterParams {
 };
 
 // Launchers: return the hipError_t of the launch.
-// rows_per_tile: attn_bf16_rows_per_tile of the call (it selects the kernel).
+// rows_per_tile: attn_bf16_rows_per_tile of the call (it selects the kernel);
+// cus: the device's compute units (a block-sparse launch that fits one round
+// of them runs one workgroup per unit with a deeper ring).
 hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, bool out_bf16, bool sparse, int rows_per_tile,
-                            hipStream_t s);
+                            int cus, hipStream_t s);
 // The same attention with k as e4m3 codes (k_scale set) and q quantised to
 // e4m3 in the kernel, one scale per 64-row tile of the call; v bf16.
 hipError_t launch_attn_fp8(const AttnParams& p, int head_dim, bool out_bf16, bool sparse, hipStream_t s);

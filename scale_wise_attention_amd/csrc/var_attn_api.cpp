@@ -386,7 +386,8 @@ var_status dense_impl(const var_schedule* sched, const var_attn_desc* desc, cons
         if ((st = set_split_items(&p, varattn::attn_bf16_resident_wgs(desc->head_dim, ob, false, rpt), rpt,
                                   desc->head_dim, ws_bytes)) != VAR_OK)
             return st;
-        return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, ob, false, rpt, s), "var_attn_dense launch");
+        return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, ob, false, rpt, device_cu_count(), s),
+                          "var_attn_dense launch");
     }
     p.n_qtiles = (p.n_rows + varattn::kF32RowsPerTile - 1) / varattn::kF32RowsPerTile;
     return hip_status(varattn::launch_attn_f32(p, desc->head_dim, false, s), "var_attn_dense launch");
@@ -436,7 +437,7 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
             return hip_status(varattn::launch_attn_fp8(p, desc->head_dim, desc->out_dtype == VAR_BF16, true, s),
                               "var_attn_block_sparse_e4m3 launch");
         }
-        return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, ob, true, rpt, s),
+        return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, ob, true, rpt, device_cu_count(), s),
                           "var_attn_block_sparse launch");
     }
     p.n_qtiles = (p.n_rows + varattn::kF32RowsPerTile - 1) / varattn::kF32RowsPerTile;

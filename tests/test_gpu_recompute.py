@@ -177,20 +177,29 @@ def test_dense_recompute_both_wave_shapes(api, bh):
             _check(og[m], lseg[m], res_g, vn, f"32x32 step {B}x{H} gather, splits={splits}, map ({b}, {h})")
 
 
-def test_sparse_recompute(api):
-    wl = custom_workload(GRIDS, 2, 2, 128)
+@pytest.mark.parametrize("bh", [(2, 2), (2, 27)])
+def test_sparse_recompute(api, bh):
+    """The 24x24 step block-sparse with the recompute forced: with 4 maps its 20
+    workgroups run one per compute unit with tile pairs; with 54 maps (270
+    workgroups, more than the compute units) two share a unit, one tile per
+    barrier.  The first and last map against the oracle."""
+    B, H = bh
+    wl = custom_workload(GRIDS, B, H, 128)
     q, k, v = make_qkv(wl, 14, device="cuda")
     off = oracle.offsets(wl.h, wl.w)
     s = len(GRIDS) - 1
+    assert (B * H * 5 <= torch.cuda.get_device_properties(0).multi_processor_count) == (bh == (2, 2))
     qs = q[:, :, off[s]:off[s + 1]]
     rp, ci = api.var_build_tile_mask((wl.h, wl.w), s, s + 1, api.mask_params(64, 64, 2, 3, 1, 1))
     kept = oracle.tile_mask(wl.h, wl.w, s, s + 1, 64, 64, 2, 3, 1, 1)
     o, lse = api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, s, s + 1, rp, ci, softmax_scale=SCALE,
                                        return_lse=True)
-    vn = _np(v)
-    res = oracle.attention(_np(qs), _np(k), vn, wl.h, wl.w, s, s + 1, kept=kept, softmax_scale=SCALE,
-                           return_lse=True, return_probs=True)
-    _check(o, lse, res, vn, "sparse")
+    for (b, h) in [(0, 0), (B - 1, H - 1)]:
+        m = (slice(b, b + 1), slice(h, h + 1))
+        vn = _np(v[m])
+        res = oracle.attention(_np(qs[m]), _np(k[m]), vn, wl.h, wl.w, s, s + 1, kept=kept, softmax_scale=SCALE,
+                               return_lse=True, return_probs=True)
+        _check(o[m], lse[m], res, vn, f"sparse {B}x{H} map ({b}, {h})")
 
 
 def test_e4m3_recompute(api):
