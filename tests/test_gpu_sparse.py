@@ -341,8 +341,8 @@ def test_scatter_restore_bit_exact(api, dtype):
 
 
 def test_scatter_more_row_groups_than_workgroups(api):
-    """260 maps x 256 row groups of 16 rows: more groups than the launch's 65536
-    workgroups, so workgroups take a second group (and reset its marks)."""
+    """260 maps x 32 row groups of 128 rows (8320): more groups than the launch's
+    8192 workgroups, so workgroups take a second group (and reset its marks)."""
     maps, E = 260, 128
     base = torch.from_numpy(normal_tensor((maps, 48 * 48, E), 3)).to(torch.bfloat16).cuda()
     sel = pruned_index(4096, 0.4, 1)
@@ -356,7 +356,7 @@ def test_scatter_more_row_groups_than_workgroups(api):
 @pytest.mark.parametrize("path", ["short list", "long list"])
 def test_scatter_paths_full_and_base_only(api, path):
     """A short index list (1638 of 64x64) and a long one (20000 of 160x160, 42 maps x
-    1600 row groups, more than the launch's 65536 workgroups).  Full scatter bit-exact
+    200 row groups of 128 rows, more than the launch's 8192 workgroups).  Full scatter bit-exact
     against the oracle; base-only (upd NULL) leaves the retained rows untouched and
     writes every other row as the oracle."""
     if path == "short list":
