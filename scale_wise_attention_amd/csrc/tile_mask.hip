@@ -87,11 +87,15 @@ __device__ __forceinline__ void mark_tiles(uint32_t* bits, int t0, int t1, int c
     }
 }
 
+// Scale and grid position of the first kRowThreads rows of a query tile,
+// computed once per row (a gathered row costs a load of its index) and read
+// by every (row, window scale) item.
 struct RowShared {
     uint32_t bits[kChunkWords];
     int wave_cnt[kRowThreads / 64];
     int running;
     int sink_end;
+    int rs[kRowThreads], ry[kRowThreads], rx[kRowThreads];
 };
 
 // Kept key tiles of query tile r, written in ascending order at out[0 ..);
@@ -113,12 +117,23 @@ __device__ int build_row(const P& p, int r, int* out, RowShared& sh) {
         running = 0;
         sink_end = 0;
     }
+    // this thread's row (rows past kRowThreads are recomputed where used)
+    auto coords = [&](int t, int& s, int& y, int& x) __attribute__((always_inline)) {
+        if (t < kRowThreads) {
+            s = sh.rs[t];
+            y = sh.ry[t];
+            x = sh.rx[t];
+        } else {
+            row_coords(p, i0 + t, s, y, x);
+        }
+    };
+    if (tid < n_rows) row_coords(p, i0 + tid, sh.rs[tid], sh.ry[tid], sh.rx[tid]);
     __syncthreads();
     if (p.sink_scales > 0) {
         int se = 0;
         for (int t = tid; t < n_rows; t += kRowThreads) {
             int s, y, x;
-            row_coords(p, i0 + t, s, y, x);
+            coords(t, s, y, x);
             se = max(se, p.off[min(p.sink_scales, s + 1)]);
         }
         if (se > 0) atomicMax(&sink_end, se);
@@ -132,7 +147,7 @@ __device__ int build_row(const P& p, int r, int* out, RowShared& sh) {
             const int t = it / nj;
             const int j = jw + (it - t * nj);
             int s, yq, xq;
-            row_coords(p, i0 + t, s, yq, xq);
+            coords(t, s, yq, xq);
             if (j > s) continue;                   // key scale not visible to this row
             const int hq = p.h[s], wq = p.w[s], hj = p.h[j], wj = p.w[j];
             const int ylo = max(ceil_div(yq * hj - p.radius_y * hq, hq), 0);
