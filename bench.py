@@ -307,12 +307,19 @@ def main():
     # same build on a second stream, overlapping the first steps, was slower,
     # the fork and join in the graph costing more than the build; and one
     # build per step (two launches each) on that stream slower still.
-    # The reconstruction of the pruned last step is split in two disjoint halves:
-    # the attention writes the retained rows in place, and the base-only
-    # scatter fills the other rows from the upsampled 48x48 output, right
-    # after the 48x48 step (the two touch disjoint rows, so no order is needed
-    # between them; measured, running them on two streams side by side was
-    # slower than one after the other).
+    # The reconstruction of the pruned last step runs in the attention's own
+    # launch (var_attn_block_sparse_restore): the attention writes the retained
+    # rows in place, and workgroups after the attention's, in the compute-unit
+    # slots its last round leaves free, fill the other rows from the upsampled
+    # 48x48 output.  (Before: the base-only scatter as a launch of its own after
+    # the 48x48 step, about 12-15 us on the critical path; on a second stream
+    # beside the attention it was slower still.)
+    assert sparse_splits[K - 1] == 1, "the one-launch reconstruction runs unsplit"
+
+    def restore_step():
+        rp, ci, idx = csr[K - 1]
+        api.var_attn_block_sparse_restore(sched, qsteps[K - 1], k, v, K - 1, rp, ci, idx, sparse_out[K - 2],
+                                          wl.grids[K - 2], wl.grids[K - 2], out=restored)
 
     def base_scatter():
         api.var_scatter_restore(sparse_out[K - 2], wl.grids[K - 2], wl.grids[K - 2], None, sel_t,
@@ -332,10 +339,10 @@ def main():
             if full_mask[s]:
                 api.var_attn_dense(sched, qsteps[s], k, v, s, s + 1, out=sparse_out[s], n_splits=dense_splits[s],
                                    workspace=workspace)
+            elif s == K - 1:
+                restore_step()
             else:
-                sparse_step(s, in_place=True)
-            if s == K - 2:
-                base_scatter()
+                sparse_step(s)
 
     def scatter_step():
         # the separate reconstruction from the gathered rows (the reference path)
@@ -361,8 +368,8 @@ def main():
     torch.cuda.synchronize()
 
     def check_sparse_outputs(what):
-        # (the restored grid, bit for bit: rows written in place + base-only scatter
-        # against gathered rows + the separate scatter)
+        # (the restored grid, bit for bit: the one-launch reconstruction against
+        # gathered rows + the separate scatter)
         same = all(torch.equal(a.view(torch.int16), b.view(torch.int16))
                    for a, b in zip(inline_outs, list(sparse_out) + [restored]))
         if not same:
@@ -394,6 +401,7 @@ def main():
         groups += [(f"sparse s{s}", lambda s=s: sparse_step(s)) for s in range(K - 1) if not full_mask[s]]
         groups += [("pruned gathered", lambda: sparse_step(K - 1)),
                    ("pruned in place", lambda: sparse_step(K - 1, in_place=True)),
+                   ("pruned restore", restore_step),
                    ("base scatter", base_scatter),
                    ("scatter", scatter_step),
                    ("mask unpruned last", lambda: api.var_build_tile_mask(sched, K - 1, K, mp, row_ptr=full_rp,
@@ -538,6 +546,7 @@ def main():
         sparse_step(K - 1, in_place=True)
 
     pruned_recon_ms = time_launch(pruned_with_reconstruction)
+    restore_ms = time_launch(restore_step)
     sparse_full_ms = time_launch(sparse_full_last_step)
     sparse_full_flops = acc.sparse_step_flops(wl, full_rp.cpu().numpy(), full_ci.cpu().numpy(), 4096, off[K])
     dense_gen_ms = time_launch(lambda: [dense_step(s) for s in range(K)], reps=max(2, R // 4))
@@ -559,9 +568,10 @@ def main():
             if full_mask[s]:
                 api.var_attn_dense(sched, qsteps[s], k, v, s, s + 1, out=sparse_out[s], n_splits=dense_splits[s],
                                    workspace=workspace)
+            elif s == K - 1:
+                restore_step()
             else:
-                sparse_step(s, in_place=True)
-        base_scatter()
+                sparse_step(s)
 
     sparse_gen_pre_ms = time_launch(sparse_gen_prebuilt_masks, reps=max(2, R // 4))
 
@@ -789,14 +799,16 @@ def main():
                 "base_only_scatter_ms": round(base_scatter_ms, 4),
                 "base_only_scatter_gbps": round(acc.scatter_bytes(B * H, D * 2, 0, 4096 - n_sel) /
                                                 (base_scatter_ms * 1e-3) / 1e9, 1),
-                "pruned_attn_plus_reconstruction_ms": round(pruned_recon_ms, 4),
-                "reconstruction_cost_on_critical_path_ms": round(pruned_recon_ms - sparse_ms[last], 4),
+                "pruned_attn_then_base_only_scatter_ms": round(pruned_recon_ms, 4),
+                "one_launch_ms": round(restore_ms, 4),
+                "pruned_attn_plus_reconstruction_ms": round(restore_ms, 4),
+                "reconstruction_cost_on_critical_path_ms": round(restore_ms - sparse_ms[last], 4),
             },
             "last_step_unpruned_ms": round(sparse_full_ms, 4),
             "last_step_unpruned_gflop": round(sparse_full_flops / 1e9, 3),
             "last_step_unpruned_tflops": round(sparse_full_flops / (sparse_full_ms * 1e-3) / 1e12, 2),
             "speedup_last_step_unpruned_vs_dense": round(dense_ms[last] / sparse_full_ms, 3),
-            "speedup_last_step_pruned_vs_dense": round(dense_ms[last] / (mask_ms[last] + pruned_recon_ms), 3),
+            "speedup_last_step_pruned_vs_dense": round(dense_ms[last] / (mask_ms[last] + restore_ms), 3),
             "speedup_generation_vs_dense": round(dense_gen_ms / sparse_gen_ms, 3),
         },
         "smaller_configs": small,

@@ -297,6 +297,38 @@ var_status var_attn_block_sparse(const var_schedule* sched, const var_attn_desc*
                                  int32_t tile_q, int32_t tile_k, void* stream);
 
 /*
+ * A pruned block-sparse step and its structural reconstruction in one
+ * launch ("ARVAR ...", Key Design 3, Equations (8)-(9)): the attention of
+ * var_attn_block_sparse with desc->out_at_index = 1 writes output row i to
+ * row q_index[i] of the step's full grid o, and workgroups of the same
+ * launch fill every other row of o from the nearest-upsampled base (source
+ * (floor(y*h_in/h), floor(x*w_in/w)), the rule of var_scatter_restore), in
+ * the compute-unit slots the attention leaves free.  The result equals
+ * var_attn_block_sparse (out_at_index = 1) followed by var_scatter_restore
+ * with upd = NULL, bit for bit.
+ *  desc    bf16 input, out_at_index = 1, one step: q_scale_end =
+ *          q_scale_begin + 1, whose grid h x w (from sched) is the output grid.
+ *  o       [B][H][h*w][D] (o_l) of out_dtype, every row written.
+ *  base    [B][H][>= h_in*w_in][D] (base_l) of out_dtype, read only.
+ *  q_index device int32[n_sel], strictly ascending, in [0, h*w) (NULL allowed
+ *          when n_sel = 0: then every row comes from the base).
+ *  err_flag NULL or a device int32 the caller has zeroed: 1 is ORed in for an
+ *          index out of range, 2 for a pair not strictly ascending; rows are
+ *          then unspecified but every access stays in bounds.
+ * Other arguments as in var_attn_block_sparse (its CSR contract included;
+ * no key splits).  o and base 16-byte aligned, all their strides multiples
+ * of 16 bytes, token strides >= D, and (for batch > 1) batch stride = heads
+ * x head stride, else VAR_ERR_STRIDE.  Nothing is launched on an error.
+ */
+var_status var_attn_block_sparse_restore(const var_schedule* sched, const var_attn_desc* desc,
+                                         const void* q, var_layout q_l, const void* k, var_layout k_l,
+                                         const void* v, var_layout v_l, void* o, var_layout o_l,
+                                         float* lse, const int32_t* q_index, int32_t n_sel,
+                                         const int32_t* row_ptr, const int32_t* col_idx,
+                                         int32_t tile_q, int32_t tile_k, const void* base, var_layout base_l,
+                                         int32_t h_in, int32_t w_in, int32_t* err_flag, void* stream);
+
+/*
  * Saliency of the positions of one (small) step, the signal of attention-guided
  * pruning ("ARVAR ...", Key Design 2: the attention of an earlier step of the
  * same layer is reduced to one score per position of its grid; A Worked

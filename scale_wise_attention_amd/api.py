@@ -33,7 +33,7 @@ EXPORTED = ("var_schedule_extent", "var_attn_dense", "var_tile_mask_dims", "var_
             "var_attn_dense_split", "var_attn_block_sparse_split", "var_attn_split_plan",
             "var_attn_block_mass", "var_decision_tiles", "var_mapped_tile_mask", "var_attn_block_sparse_heads",
             "var_quantize_e4m3", "var_attn_dense_e4m3", "var_attn_block_sparse_e4m3", "var_device_info",
-            "var_attn_dense_split_noalloc", "var_build_tile_masks",
+            "var_attn_dense_split_noalloc", "var_build_tile_masks", "var_attn_block_sparse_restore",
             "var_status_string", "var_last_error")
 
 
@@ -90,6 +90,8 @@ def _load():
     lib.var_build_tile_masks.argtypes = [SP, ctypes.POINTER(MaskParams), ctypes.POINTER(TileMaskCall), i32, P]
     lib.var_attn_block_sparse.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, Layout, P, Layout,
                                           P, P, i32, P, P, i32, i32, P]
+    lib.var_attn_block_sparse_restore.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, Layout, P,
+                                                  Layout, P, P, i32, P, P, i32, i32, P, Layout, i32, i32, P, P]
     lib.var_scatter_restore.argtypes = [i32, i32, ctypes.c_int, P, i64, i64, i32, i32, P, i64, i64, P, i32,
                                         P, i64, i64, i32, i32, P, P]
     lib.var_attn_saliency.argtypes = [SP, ctypes.POINTER(AttnDesc), P, Layout, P, Layout, P, P, P]
@@ -398,6 +400,35 @@ def var_attn_block_sparse(schedule, q, k, v, q_scale_begin, q_scale_end, row_ptr
     else:
         wp, wb = _ws_args(n_splits, workspace)
         _check(LIB.var_attn_block_sparse_split(*args, int(n_splits), wp, wb, _stream(q.device)))
+    return (out, lse) if return_lse else out
+
+
+def var_attn_block_sparse_restore(schedule, q, k, v, step, row_ptr, col_idx, q_index, base, h_in, w_in, out=None,
+                                  out_dtype=None, softmax_scale=0.0, return_lse=False, err_flag=None, tile_q=64,
+                                  tile_k=64):
+    """Pruned block-sparse attention of one step plus its reconstruction, one launch.
+
+    Output row i of the attention over the queries q_index (ascending positions of
+    the step's grid) goes to row q_index[i] of out [B, H, h*w, D]; every other row
+    of out is the nearest-upsampled row of base [B, H, >= h_in*w_in, D].
+    """
+    s, desc, out, lse, rows = _attn_common(schedule, q, k, v, step, step + 1, out, out_dtype, softmax_scale,
+                                           q_index, return_lse, out_at_index=True)
+    n_sel = rows
+    if base.dim() != 4 or base.dtype != out.dtype or base.device != q.device or base.stride(3) != 1:
+        raise ValueError("base must be a [B, H, tokens, D] device tensor of out's dtype with contiguous rows")
+    if tuple(base.shape[:2]) != tuple(out.shape[:2]) or base.shape[3] != out.shape[3] or base.shape[2] < h_in * w_in:
+        raise ValueError("base must be [B, H, >= h_in*w_in, D] with out's B, H and D")
+    n_qt = -(-rows // tile_q)
+    for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous 1-D int32 tensor on q's device")
+    if row_ptr.numel() < n_qt + 1:
+        raise ValueError(f"row_ptr needs {n_qt + 1} entries")
+    _check(LIB.var_attn_block_sparse_restore(
+        ctypes.byref(s), ctypes.byref(desc), _ptr(q), _layout(q), _ptr(k), _layout(k), _ptr(v), _layout(v),
+        _ptr(out), _layout(out), _ptr(lse), _ptr(q_index), n_sel, _ptr(row_ptr), _ptr(col_idx), tile_q, tile_k,
+        _ptr(base), _layout(base), h_in, w_in, _ptr(err_flag), _stream(q.device)))
     return (out, lse) if return_lse else out
 
 

@@ -40,8 +40,42 @@ int attn_bf16_resident_wgs(int D, bool out_bf16, bool sparse, int rows_per_tile)
     return out_bf16 ? resident_wgs<64, true, false, false, 2>() : resident_wgs<64, false, false, false, 2>();
 }
 
+namespace {
+// Reconstruction workgroups that follow a block-sparse launch of n_attn
+// attention workgroups (cap resident at once): the slots its last round leaves
+// free, so that they run beside the attention, but at least 64 (they then
+// start as attention workgroups finish) and at most one per row group.
+template <int D, bool OB, int QB, bool WIDE>
+hipError_t launch_restore(AttnParams p, int64_t n_attn, int cus, hipStream_t s) {
+    constexpr int NT = waves_per_wg<true, QB>() * 64;
+    p.rs_rows_per_group = scatter_rows_per_group(p.rs.row_bytes, 16, NT);
+    const int64_t n_out = (int64_t)p.rs.h_out * p.rs.w_out;
+    const int64_t groups = (int64_t)p.rs.maps * ((n_out + p.rs_rows_per_group - 1) / p.rs_rows_per_group);
+    const int64_t cap = (int64_t)cus * resident_wgs<D, OB, true, false, QB, WIDE, true>();
+    const int64_t free = n_attn % cap ? cap - n_attn % cap : 0;
+    int64_t w = free > 64 ? free : 64;
+    w = w < groups ? w : groups;
+    p.rs_wgs = (int)(w > 1 ? w : 1);
+    return launch_one<D, OB, true, false, QB, WIDE, true>(p, s);
+}
+}  // namespace
+
 hipError_t launch_attn_bf16(const AttnParams& p, int D, bool out_bf16, bool sparse, int rows_per_tile, int cus,
-                            hipStream_t s) {
+                            hipStream_t s, bool restore) {
+    if (restore) {
+        // (block-sparse, unsplit: the reconstruction workgroups follow the attention's)
+        if (!sparse || p.n_splits != 1 || rows_per_tile != rows_per_wg<true, 1>()) return hipErrorInvalidValue;
+        const int64_t n_attn = (int64_t)p.n_qtiles * p.B * p.H;
+        if (D == 128) {
+            if (n_attn <= (int64_t)cus * resident_wgs<128, true, true, false, kQBSparse128, true>())
+                return out_bf16 ? launch_restore<128, true, kQBSparse128, true>(p, n_attn, cus, s)
+                                : launch_restore<128, false, kQBSparse128, true>(p, n_attn, cus, s);
+            return out_bf16 ? launch_restore<128, true, kQBSparse128, false>(p, n_attn, cus, s)
+                            : launch_restore<128, false, kQBSparse128, false>(p, n_attn, cus, s);
+        }
+        return out_bf16 ? launch_restore<64, true, 2, false>(p, n_attn, cus, s)
+                        : launch_restore<64, false, 2, false>(p, n_attn, cus, s);
+    }
     if (sparse) {
         if (rows_per_tile != rows_per_wg<true, 1>()) return hipErrorInvalidValue;
         if (D == 128) {

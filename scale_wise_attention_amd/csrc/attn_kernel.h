@@ -81,6 +81,7 @@
 
 #include "e4m3.h"
 #include "kernels.h"
+#include "scatter_rows.h"
 
 namespace varattn {
 namespace {
@@ -279,9 +280,14 @@ struct TileEnt {
 // compute unit: every dense walk, and block-sparse launches whose workgroups
 // all fit one round of the device (the others keep two workgroups per unit
 // with a 2-slot ring)
-template <int D, bool OUT_BF16, bool SPARSE, bool QK8, int QB, bool WIDE = !SPARSE>
+// RESTORE: the last p.rs_wgs workgroups of the grid do not attend; they fill
+// the rows of the full output grid that the (out_at_index) pruned call does
+// not write, from the nearest-upsampled base, in the slots the attention's
+// workgroups leave free
+template <int D, bool OUT_BF16, bool SPARSE, bool QK8, int QB, bool WIDE = !SPARSE, bool RESTORE = false>
 __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), ((SPARSE && QB == 1 && !WIDE) ? 2 : 1)) void attn_kernel(const AttnParams p) {
     static_assert(QB == 1 || QB == 2, "one or two 32-row query blocks per wave");
+    static_assert(!RESTORE || (SPARSE && !QK8), "reconstruction rides on bf16 block-sparse launches");
     static_assert(WIDE || SPARSE, "dense walks use the 4-slot ring");
     static_assert(!QK8 || QB == 2, "e4m3 queries are quantised per 64 rows: one wave's rows");
     constexpr int NW = waves_per_wg<SPARSE, QB>();   // waves per workgroup
@@ -319,10 +325,22 @@ __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), ((SPARSE && QB =
     const int g = lane >> 5;      // lane half
     const int n = lane & 31;      // column inside a 32-query block
 
+    // workgroups of the attention itself (those after them reconstruct)
+    const int n_attn = RESTORE ? (int)gridDim.x - p.rs_wgs : (int)gridDim.x;
+    if constexpr (RESTORE) {
+        static_assert(kScatterPasses * NT * (int)sizeof(int) <= (int)sizeof(smem), "row-group marks fit the ring");
+        if ((int)blockIdx.x >= n_attn) {
+            const int wg = (int)blockIdx.x - n_attn;
+            scatter_check_index<NT>(p.rs, wg, p.rs_wgs);
+            scatter_groups<16, NT>(p.rs, p.rs_rows_per_group, wg, p.rs_wgs, reinterpret_cast<int*>(smem));
+            return;
+        }
+    }
+
     // work item = (batch, head, query tile), whole or one of its key splits
     int item, split;
     bool whole;
-    decode_work(blockIdx.x, gridDim.x, p.split_from, p.n_splits, item, split, whole);
+    decode_work(blockIdx.x, n_attn, p.split_from, p.n_splits, item, split, whole);
     // this workgroup's share count (1: the whole item).  The later tests use
     // this integer, not the flag: a flag kept for them cost the key loop
     // about a dozen registers (moved through AGPRs every tile).
@@ -1265,12 +1283,12 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, in
 
 // Workgroups of one instantiation that a compute unit holds at once (1 when
 // the runtime cannot say).
-template <int D, bool OB, bool SP, bool QK8, int QB, bool WIDE = !SP>
+template <int D, bool OB, bool SP, bool QK8, int QB, bool WIDE = !SP, bool RESTORE = false>
 int resident_wgs() {
     static const int n = [] {
         int k = 0;
         const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &k, attn_kernel<D, OB, SP, QK8, QB, WIDE>, waves_per_wg<SP, QB>() * 64, 0);
+            &k, attn_kernel<D, OB, SP, QK8, QB, WIDE, RESTORE>, waves_per_wg<SP, QB>() * 64, 0);
         if (e != hipSuccess) (void)hipGetLastError();
         return e == hipSuccess && k > 0 ? k : 1;
     }();
@@ -1278,12 +1296,14 @@ int resident_wgs() {
 }
 
 // The host bounds split_from + (items - split_from) * n_splits below 2^31 and
-// sets split_from = items when n_splits == 1.
-template <int D, bool OB, bool SP, bool QK8, int QB, bool WIDE = !SP>
+// sets split_from = items when n_splits == 1.  RESTORE: p.rs_wgs
+// reconstruction workgroups follow the attention's (no key splits).
+template <int D, bool OB, bool SP, bool QK8, int QB, bool WIDE = !SP, bool RESTORE = false>
 hipError_t launch_one(const AttnParams& p, hipStream_t s) {
     const int items = p.n_qtiles * p.B * p.H;
-    const int grid = p.split_from + (items - p.split_from) * p.n_splits;
-    hipLaunchKernelGGL((attn_kernel<D, OB, SP, QK8, QB, WIDE>), dim3(grid), dim3(waves_per_wg<SP, QB>() * 64), 0, s, p);
+    const int grid = p.split_from + (items - p.split_from) * p.n_splits + (RESTORE ? p.rs_wgs : 0);
+    hipLaunchKernelGGL((attn_kernel<D, OB, SP, QK8, QB, WIDE, RESTORE>), dim3(grid), dim3(waves_per_wg<SP, QB>() * 64), 0,
+                       s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.split_from == items) return e;
     constexpr int QT = rows_per_wg<SP, QB>();

@@ -9,6 +9,20 @@
 
 namespace varattn {
 
+struct ScatterParams {
+    const unsigned char* base;
+    const unsigned char* upd;
+    unsigned char* out;
+    const int32_t* q_index;
+    int32_t* err_flag;
+    int64_t base_map_stride, base_row_stride;   // bytes
+    int64_t upd_map_stride, upd_row_stride;     // bytes
+    int64_t out_map_stride, out_row_stride;     // bytes
+    int32_t maps, row_bytes, n_sel;
+    int32_t h_in, w_in, h_out, w_out;
+    int32_t unit;     // copy width in bytes (16, 4 or 2) dividing rows, strides and pointers
+};
+
 // Everything one attention launch needs.  Passed by value as kernel argument.
 struct AttnParams {
     const void* q;
@@ -56,6 +70,13 @@ struct AttnParams {
     // key / 64 at k_scale[bh * k_scale_stride + key / 64]
     const float* k_scale;
     int64_t k_scale_stride;
+    // reconstruction in the same launch (block-sparse bf16, out_at_index): the
+    // last rs_wgs workgroups of the grid fill the rows of o that q_index does
+    // not name from the nearest-upsampled base (rs.upd NULL), in groups of
+    // rs_rows_per_group rows; 0 for every other launch
+    ScatterParams rs;
+    int32_t rs_wgs;
+    int32_t rs_rows_per_group;
 };
 
 // Row of o that output row `row` of an attention call is written to: itself,
@@ -84,26 +105,15 @@ struct MaskParams {
     int64_t rp_map_stride, ci_map_stride;   // per-map CSR strides of the compaction (0: one map)
 };
 
-struct ScatterParams {
-    const unsigned char* base;
-    const unsigned char* upd;
-    unsigned char* out;
-    const int32_t* q_index;
-    int32_t* err_flag;
-    int64_t base_map_stride, base_row_stride;   // bytes
-    int64_t upd_map_stride, upd_row_stride;     // bytes
-    int64_t out_map_stride, out_row_stride;     // bytes
-    int32_t maps, row_bytes, n_sel;
-    int32_t h_in, w_in, h_out, w_out;
-    int32_t unit;     // copy width in bytes (16, 4 or 2) dividing rows, strides and pointers
-};
 
 // Launchers: return the hipError_t of the launch.
 // rows_per_tile: attn_bf16_rows_per_tile of the call (it selects the kernel);
 // cus: the device's compute units (a block-sparse launch that fits one round
 // of them runs one workgroup per unit with a deeper ring).
+// restore: a block-sparse unsplit launch with p.rs set, followed by
+// reconstruction workgroups (the launcher sets rs_wgs and rs_rows_per_group).
 hipError_t launch_attn_bf16(const AttnParams& p, int head_dim, bool out_bf16, bool sparse, int rows_per_tile,
-                            int cus, hipStream_t s);
+                            int cus, hipStream_t s, bool restore = false);
 // The same attention with k as e4m3 codes (k_scale set) and q quantised to
 // e4m3 in the kernel, one scale per 64-row tile of the call; v bf16.
 hipError_t launch_attn_fp8(const AttnParams& p, int head_dim, bool out_bf16, bool sparse, hipStream_t s);

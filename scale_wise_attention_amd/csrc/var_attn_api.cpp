@@ -398,7 +398,7 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
                        float* lse, const int32_t* q_index, int32_t n_sel, const int32_t* row_ptr,
                        const int32_t* col_idx, int32_t tile_q, int32_t tile_k, int32_t splits, void* ws,
                        int64_t ws_bytes, void* stream, int64_t col_bh_stride = -1,
-                       const E4m3Keys* e4m3 = nullptr) {
+                       const E4m3Keys* e4m3 = nullptr, const varattn::ScatterParams* restore = nullptr) {
     if (tile_q != 64 || tile_k != 64)
         return fail(VAR_ERR_UNSUPPORTED, "block-sparse attention supports 64x64 tiles, got %dx%d", tile_q, tile_k);
     if (!row_ptr || !col_idx) return fail(VAR_ERR_NULL, "row_ptr and col_idx must be non-NULL");
@@ -437,6 +437,11 @@ var_status sparse_impl(const var_schedule* sched, const var_attn_desc* desc, con
             return hip_status(varattn::launch_attn_fp8(p, desc->head_dim, desc->out_dtype == VAR_BF16, true, s),
                               "var_attn_block_sparse_e4m3 launch");
         }
+        if (restore) {
+            p.rs = *restore;
+            return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, ob, true, rpt, device_cu_count(), s, true),
+                              "var_attn_block_sparse_restore launch");
+        }
         return hip_status(varattn::launch_attn_bf16(p, desc->head_dim, ob, true, rpt, device_cu_count(), s),
                           "var_attn_block_sparse launch");
     }
@@ -461,6 +466,69 @@ VAR_EXPORT var_status var_attn_block_sparse(const var_schedule* sched, const var
                                             void* stream) {
     return sparse_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, row_ptr, col_idx, tile_q,
                        tile_k, 1, nullptr, 0, stream);
+}
+
+VAR_EXPORT var_status var_attn_block_sparse_restore(const var_schedule* sched, const var_attn_desc* desc,
+                                                    const void* q, var_layout q_l, const void* k, var_layout k_l,
+                                                    const void* v, var_layout v_l, void* o, var_layout o_l,
+                                                    float* lse, const int32_t* q_index, int32_t n_sel,
+                                                    const int32_t* row_ptr, const int32_t* col_idx, int32_t tile_q,
+                                                    int32_t tile_k, const void* base, var_layout base_l,
+                                                    int32_t h_in, int32_t w_in, int32_t* err_flag, void* stream) {
+    Offsets off;
+    var_status st = check_schedule(sched, &off);
+    if (st != VAR_OK) return st;
+    if (!desc) return fail(VAR_ERR_NULL, "desc is NULL");
+    if ((st = check_range(off, desc->q_scale_begin, desc->q_scale_end)) != VAR_OK) return st;
+    if (desc->q_scale_end != desc->q_scale_begin + 1)
+        return fail(VAR_ERR_RANGE, "the reconstruction covers one step: q_scale_end must be q_scale_begin + 1");
+    if (desc->in_dtype != VAR_BF16) return fail(VAR_ERR_UNSUPPORTED, "the reconstruction call takes bf16 input");
+    if (desc->out_at_index != 1) return fail(VAR_ERR_RANGE, "the reconstruction call needs out_at_index = 1");
+    if (desc->out_dtype != VAR_F32 && desc->out_dtype != VAR_BF16)
+        return fail(VAR_ERR_UNSUPPORTED, "unknown out_dtype %d", (int)desc->out_dtype);
+    if (desc->batch < 1 || desc->heads < 1 || (int64_t)desc->batch * desc->heads > (1 << 20))
+        return fail(VAR_ERR_RANGE, "batch=%d heads=%d invalid", desc->batch, desc->heads);
+    if (h_in < 1 || w_in < 1 || (int64_t)h_in * w_in >= kMaxTokens) return fail(VAR_ERR_RANGE, "base grid invalid");
+    if (!base || !o) return fail(VAR_ERR_NULL, "base and o must be non-NULL");
+    const int eb = desc->out_dtype == VAR_BF16 ? 2 : 4;
+    const int D = desc->head_dim;
+    // rows are copied 16 bytes a lane: every row start must be 16-byte aligned
+    const int64_t bs[3] = {base_l.batch, base_l.head, base_l.token}, os[3] = {o_l.batch, o_l.head, o_l.token};
+    for (int i = 0; i < 3; ++i)
+        if (bs[i] < 0 || os[i] < 0 || (bs[i] * eb) % 16 || (os[i] * eb) % 16)
+            return fail(VAR_ERR_STRIDE, "o and base strides must be non-negative multiples of 16 bytes");
+    if (!aligned16(base) || !aligned16(o)) return fail(VAR_ERR_STRIDE, "o and base must be 16-byte aligned");
+    if (base_l.token < D || o_l.token < D) return fail(VAR_ERR_STRIDE, "token strides must be >= head_dim");
+    // map m = b * heads + h at m * head stride: batch stride = heads * head stride (any when batch = 1)
+    if (desc->batch > 1 && (o_l.batch != (int64_t)desc->heads * o_l.head || base_l.batch != (int64_t)desc->heads * base_l.head))
+        return fail(VAR_ERR_STRIDE, "o and base need batch stride = heads * head stride");
+    varattn::ScatterParams r;
+    std::memset(&r, 0, sizeof(r));
+    r.base = static_cast<const unsigned char*>(base);
+    r.upd = nullptr;
+    r.out = static_cast<unsigned char*>(o);
+    r.q_index = q_index;
+    r.err_flag = err_flag;
+    r.base_map_stride = base_l.head * eb;
+    r.base_row_stride = base_l.token * eb;
+    r.out_map_stride = o_l.head * eb;
+    r.out_row_stride = o_l.token * eb;
+    r.maps = desc->batch * desc->heads;
+    r.row_bytes = D * eb;
+    r.n_sel = n_sel;
+    r.h_in = h_in;
+    r.w_in = w_in;
+    r.h_out = sched->h[desc->q_scale_begin];
+    r.w_out = sched->w[desc->q_scale_begin];
+    r.unit = 16;
+    if (n_sel < 0 || (int64_t)n_sel > (int64_t)r.h_out * r.w_out)
+        return fail(VAR_ERR_INDEX, "n_sel=%d outside [0, h*w of the step]", n_sel);
+    if (n_sel == 0)   // nothing to attend: every row comes from the base
+        return hip_status(varattn::launch_scatter(r, reinterpret_cast<hipStream_t>(stream)),
+                          "var_attn_block_sparse_restore launch");
+    if (!q_index) return fail(VAR_ERR_NULL, "q_index must be non-NULL when n_sel > 0");
+    return sparse_impl(sched, desc, q, q_l, k, k_l, v, v_l, o, o_l, lse, q_index, n_sel, row_ptr, col_idx, tile_q,
+                       tile_k, 1, nullptr, 0, stream, -1, nullptr, &r);
 }
 
 VAR_EXPORT var_status var_attn_block_sparse_heads(const var_schedule* sched, const var_attn_desc* desc,

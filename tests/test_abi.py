@@ -27,7 +27,7 @@ def _declared():
 
 def test_exports_match_header(api):
     declared = _declared()
-    assert len(declared) == 23
+    assert len(declared) == 24
     for name in declared:
         assert hasattr(api.LIB, name), name
     nm = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True, text=True).stdout
@@ -327,6 +327,37 @@ def test_out_at_index_needs_q_index(api):
     s = api.make_schedule(W1024, W1024)
     assert _dense(api, s, _desc(api, out_at_index=1)) == _code(api, "VAR_ERR_INDEX")
     assert _dense(api, s, _desc(api, out_at_index=2), q_index=FAKE, n_sel=16) == _code(api, "VAR_ERR_RANGE")
+
+
+def test_restore_validation_errors(api):
+    """var_attn_block_sparse_restore refuses, before any HIP call, what its one
+    launch cannot do: more than one step, fp32 input, out_at_index other than 1,
+    misaligned or non-uniform map strides, and bad selections."""
+    s = api.make_schedule(W1024, W1024)
+    E = lambda n: _code(api, n)
+    P = ctypes.c_void_p
+    L = api.Layout(16 * 4096 * 128, 4096 * 128, 128)
+    LB = api.Layout(16 * 2304 * 128, 2304 * 128, 128)
+
+    def call(desc=None, base=FAKE, base_l=None, o_l=None, q_index=FAKE, n_sel=1638, h_in=48, w_in=48):
+        d = desc or _desc(api, out_at_index=1, out_dtype=api.VAR_BF16)
+        return api.LIB.var_attn_block_sparse_restore(
+            ctypes.byref(s), ctypes.byref(d), P(FAKE), L, P(FAKE), L, P(FAKE), L, P(FAKE), o_l or L, P(0),
+            P(q_index), n_sel, P(FAKE), P(FAKE), 64, 64, P(base), base_l or LB, h_in, w_in, P(0), P(0))
+
+    assert call(desc=_desc(api, out_at_index=1, q_scale_begin=11)) == E("VAR_ERR_RANGE")
+    assert call(desc=_desc(api, out_at_index=0)) == E("VAR_ERR_RANGE")
+    assert call(desc=_desc(api, out_at_index=1, head_dim=64, in_dtype=api.VAR_F32)) == E("VAR_ERR_UNSUPPORTED")
+    assert call(base=0) == E("VAR_ERR_NULL")
+    assert call(base=FAKE + 8) == E("VAR_ERR_STRIDE")
+    assert call(base_l=api.Layout(16 * 2304 * 132, 2304 * 132, 132)) == E("VAR_ERR_STRIDE")
+    assert call(base_l=api.Layout(2304 * 128, 2304 * 128, 128)) == E("VAR_ERR_STRIDE")
+    assert call(o_l=api.Layout(0, 4096 * 128, 128)) == E("VAR_ERR_STRIDE")
+    assert call(h_in=0) == E("VAR_ERR_RANGE")
+    assert call(n_sel=4097) == E("VAR_ERR_INDEX")
+    assert call(n_sel=-1) == E("VAR_ERR_INDEX")
+    assert call(q_index=0) == E("VAR_ERR_NULL")
+    assert "q_index" in api.LIB.var_last_error().decode()
 
 
 def test_device_info_without_a_device(api):

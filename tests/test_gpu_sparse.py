@@ -537,3 +537,98 @@ def test_out_at_index_fp32_kernel_and_errors(api):
     assert bool((out[:, :, rest] == -7.0).all())
     with pytest.raises(ValueError):
         api.var_attn_dense((wl.h, wl.w), qs, k, v, 2, 3, out_at_index=True)
+
+
+def _restore_case(api, wl_name, seed, frac, B=None, H=None, out_dtype=torch.bfloat16):
+    wl = WORKLOADS[wl_name]
+    q, k, v = make_qkv(wl, seed, device="cuda")
+    if B is not None:
+        q, k, v = q[:B, :H], k[:B, :H], v[:B, :H]
+    off = oracle.offsets(wl.h, wl.w)
+    K = wl.num_scales
+    n = wl.h[-1] * wl.w[-1]
+    sel = pruned_index(n, frac, seed) if frac < 1 else np.arange(n, dtype=np.int32)
+    idx = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).cuda()
+    qs = q[:, :, off[K - 1]:]
+    sink = 7 if wl_name.startswith("var1024") else 3
+    mp = api.mask_params(64, 64, sink, sink, 2, 2)
+    rp, ci = api.var_build_tile_mask((wl.h, wl.w), K - 1, K, mp, q_index=idx)
+    base = api.var_attn_dense((wl.h, wl.w), q[:, :, off[K - 2]:off[K - 1]], k, v, K - 2, K - 1,
+                              out_dtype=out_dtype)
+    return wl, q, k, v, K, n, sel, idx, qs, rp, ci, base
+
+
+@pytest.mark.parametrize("wl_name,frac,maps,out_dtype", [
+    ("var1024_sparse", 0.4, None, torch.bfloat16),    # 416 attention workgroups, two per compute unit
+    ("var1024_sparse", 0.4, None, torch.float32),
+    ("var1024_sparse", 0.4, (1, 2), torch.bfloat16),  # a few workgroups: the one-per-unit walk
+    ("var1024_sparse", 0.05, None, torch.bfloat16),   # mostly reconstruction
+    ("var256", 0.4, None, torch.bfloat16),            # head_dim 64
+    ("var256", 1.0, None, torch.float32),             # every row retained: nothing from the base
+])
+def test_sparse_restore_one_launch(api, wl_name, frac, maps, out_dtype):
+    """A pruned step and its reconstruction ("ARVAR ...", Key Design 3, Eq. (8)-(9)) in one
+    launch: equal, bit for bit over a NaN-filled output, to the attention writing its rows
+    in place followed by the base-only scatter, and to the oracle's reconstruction from the
+    same base and the gathered call's rows; the retained rows on a few heads against the
+    oracle's attention."""
+    B, H = maps if maps else (None, None)
+    wl, q, k, v, K, n, sel, idx, qs, rp, ci, base = _restore_case(api, wl_name, 5, frac, B, H, out_dtype)
+    Bq, Hq, D = qs.shape[0], qs.shape[1], qs.shape[3]
+    hi, wi, ho, wo = wl.h[-2], wl.w[-2], wl.h[-1], wl.w[-1]
+    out = torch.full((Bq, Hq, n, D), float("nan"), dtype=out_dtype, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.var_attn_block_sparse_restore((wl.h, wl.w), qs, k, v, K - 1, rp, ci, idx, base, hi, wi, out=out,
+                                      err_flag=flag)
+    two = torch.full_like(out, float("nan"))
+    api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, K - 1, K, rp, ci, q_index=idx, out=two, out_at_index=True)
+    api.var_scatter_restore(base, hi, wi, None, idx, ho, wo, out=two)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    ib = torch.int16 if out_dtype == torch.bfloat16 else torch.int32
+    got = out.view(ib).cpu().numpy().reshape(Bq * Hq, n, D)
+    assert np.array_equal(got, two.view(ib).cpu().numpy().reshape(Bq * Hq, n, D)), "one launch vs two calls"
+    upd = api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, K - 1, K, rp, ci, q_index=idx, out_dtype=out_dtype)
+    ref = oracle.scatter_restore(base.view(ib).cpu().numpy().reshape(Bq * Hq, -1, D), hi, wi,
+                                 upd.view(ib).cpu().numpy().reshape(Bq * Hq, sel.size, D), sel, ho, wo)
+    assert np.array_equal(got, ref), "oracle reconstruction"
+    kept = oracle.tile_mask(wl.h, wl.w, K - 1, K, 64, 64, 7 if wl_name.startswith("var1024") else 3,
+                            7 if wl_name.startswith("var1024") else 3, 2, 2, q_index=sel)
+    qn, kn, vn = _np(qs), _np(k), _np(v)
+    rows = np.arange(0, sel.size, 7)
+    for (b, h) in ((0, 0), (Bq - 1, Hq - 1)):
+        att = oracle.attention(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], wl.h, wl.w,
+                               K - 1, K, q_index=sel, kept=kept, rows=rows)
+        _check(_np(out[b:b + 1, h:h + 1])[:, :, sel[rows]], att, what=f"restore {wl_name} {frac} b{b} h{h}")
+
+
+def test_sparse_restore_edge_cases_and_errors(api):
+    """No retained row: the launch is the upsampling alone.  Bad indices set the flag
+    with every access in bounds.  Inputs outside the call's contract are refused
+    before anything runs."""
+    wl, q, k, v, K, n, sel, idx, qs, rp, ci, base = _restore_case(api, "var256", 2, 0.4)
+    hi, wi, ho, wo = wl.h[-2], wl.w[-2], wl.h[-1], wl.w[-1]
+    empty = torch.zeros(0, dtype=torch.int32, device="cuda")
+    out = torch.full((2, 16, n, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    api.var_attn_block_sparse_restore((wl.h, wl.w), qs, k, v, K - 1, rp, ci, empty, base, hi, wi, out=out)
+    ref = oracle.scatter_restore(base.view(torch.int16).cpu().numpy().reshape(32, -1, 64), hi, wi,
+                                 np.zeros((32, 0, 64), np.int16), np.zeros(0, np.int32), ho, wo)
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().reshape(32, n, 64), ref)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bad = torch.tensor([3, 3, 9], dtype=torch.int32, device="cuda")
+    rpb, cib = api.var_build_tile_mask((wl.h, wl.w), K - 1, K, api.mask_params(64, 64, 3, 3, 2, 2), q_index=bad)
+    api.var_attn_block_sparse_restore((wl.h, wl.w), qs, k, v, K - 1, rpb, cib, bad, base, hi, wi, out=out,
+                                      err_flag=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) & 2
+    VarAttnError = api.VarAttnError
+    with pytest.raises(VarAttnError):   # fp32 input
+        api.var_attn_block_sparse_restore((wl.h, wl.w), qs.float(), k.float(), v.float(), K - 1, rp, ci, idx,
+                                          base.float(), hi, wi, out=out.float())
+    with pytest.raises(ValueError):     # base of another dtype
+        api.var_attn_block_sparse_restore((wl.h, wl.w), qs, k, v, K - 1, rp, ci, idx, base.float(), hi, wi,
+                                          out=out)
+    with pytest.raises(VarAttnError):   # rows of base not 16-byte aligned
+        wide = torch.zeros(2, 16, hi * wi, 68, dtype=torch.bfloat16, device="cuda")
+        api.var_attn_block_sparse_restore((wl.h, wl.w), qs, k, v, K - 1, rp, ci, idx, wide[..., :64], hi, wi,
+                                          out=out)
