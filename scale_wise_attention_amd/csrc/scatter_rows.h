@@ -8,6 +8,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace varattn {
@@ -64,10 +66,11 @@ __device__ __forceinline__ void scatter_check_index(const ScatterParams& p, int6
 
 // Workgroup `wg` of `nwg` (NT lanes) copies every nwg-th group of
 // `rows_per_group` consecutive output rows of one map, one UNIT-byte unit per
-// lane per pass.  Per group, wave 0 finds the group's first retained position
-// with one wave-wide search and marks the group's retained rows in src_of
-// (LDS, kScatterPasses * NT ints); every output row then takes its single
-// source: update row i if retained (skipped when upd is NULL: the attention
+// lane per pass.  Per group, wave 0 writes each row's source into src_of (LDS,
+// kScatterPasses * NT ints): -(b + 1) for base row b of the nearest
+// upsampling, then, after one wave-wide search of the index list, k >= 0 for a
+// row retained as update row k.  Every output row then takes its single
+// source: update row k if retained (skipped when upd is NULL: the attention
 // call wrote it in place), else the upsampled base row.
 template <int UNIT, int NT>
 __device__ __forceinline__ void scatter_groups(const ScatterParams& p, int rows_per_group, int64_t wg, int64_t nwg,
@@ -77,12 +80,20 @@ __device__ __forceinline__ void scatter_groups(const ScatterParams& p, int rows_
     const int groups_per_map = (n_out + rows_per_group - 1) / rows_per_group;
     const int64_t groups = (int64_t)p.maps * groups_per_map;
     const int tid = threadIdx.x;
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    typedef typename std::conditional<UNIT == 16, u32x4_t, typename std::conditional<UNIT == 4, uint32_t, uint16_t>::type>::type unit_t;
     for (int64_t gi = wg; gi < groups; gi += nwg) {
         const int m = (int)(gi / groups_per_map);
         const int t0 = (int)(gi - (int64_t)m * groups_per_map) * rows_per_group;
         const int rows = min(rows_per_group, n_out - t0);
         if (tid < 64) {
-            for (int r = tid; r < rows; r += 64) src_of[r] = -1;
+            for (int r = tid; r < rows; r += 64) {
+                const int t = t0 + r;
+                const int y = t / p.w_out, x = t - y * p.w_out;
+                const int ys = (int)(((int64_t)y * p.h_in) / p.h_out);
+                const int xs = (int)(((int64_t)x * p.w_in) / p.w_out);
+                src_of[r] = -(ys * p.w_in + xs) - 1;
+            }
             if (p.n_sel > 0) {
                 // an ascending list holds the group's retained rows in [first, first + rows);
                 // with a list that breaks the contract the rows are unspecified but every
@@ -98,30 +109,35 @@ __device__ __forceinline__ void scatter_groups(const ScatterParams& p, int rows_
             }
         }
         __syncthreads();
-        const int64_t work = (int64_t)rows * per_row;
-        for (int64_t w = tid; w < work; w += NT) {
-            const int r = (int)(w / per_row);
-            const int64_t chunk = w - (int64_t)r * per_row;
-            const int t = t0 + r;
-            const int i = src_of[r];
-            const unsigned char* src;
-            if (i >= 0) {
-                if (!p.upd) continue;   // a retained row written by the attention call itself
-                src = p.upd + m * p.upd_map_stride + (int64_t)i * p.upd_row_stride;
-            } else {
-                const int y = t / p.w_out, x = t - y * p.w_out;
-                const int ys = (int)(((int64_t)y * p.h_in) / p.h_out);
-                const int xs = (int)(((int64_t)x * p.w_in) / p.w_out);
-                src = p.base + m * p.base_map_stride + (int64_t)(ys * p.w_in + xs) * p.base_row_stride;
+        // kScatterPasses units a lane, all loads issued before the first store
+        // (a load-store pair per pass waits one memory round trip each).  The
+        // loads are unconditional, from a valid row for every unit (a unit past
+        // the group, or of a retained row that is not copied, reads base row 0
+        // and stores nothing), so no branch separates them.
+        const int work = rows * per_row;   // at most max(kScatterPasses * NT, per_row)
+        for (int w0 = tid; w0 < work; w0 += kScatterPasses * NT) {
+            unit_t val[kScatterPasses];
+            unsigned char* dst[kScatterPasses];
+#pragma unroll
+            for (int k = 0; k < kScatterPasses; ++k) {
+                const int w = w0 + k * NT;
+                const bool in = w < work;
+                const int r = in ? w / per_row : 0;
+                const int chunk = in ? w - r * per_row : 0;
+                const int code = in ? src_of[r] : -1;
+                const bool from_upd = code >= 0 && p.upd;
+                const unsigned char* src =
+                    from_upd ? p.upd + m * p.upd_map_stride + (int64_t)code * p.upd_row_stride
+                             : p.base + m * p.base_map_stride + (int64_t)(code < 0 ? -code - 1 : 0) * p.base_row_stride;
+                val[k] = *reinterpret_cast<const unit_t*>(src + (int64_t)chunk * UNIT);
+                // (a retained row without update rows was written by the attention call itself)
+                dst[k] = in && (code < 0 || p.upd)
+                             ? p.out + m * p.out_map_stride + (int64_t)(t0 + r) * p.out_row_stride + (int64_t)chunk * UNIT
+                             : nullptr;
             }
-            unsigned char* dst = p.out + m * p.out_map_stride + (int64_t)t * p.out_row_stride;
-            if constexpr (UNIT == 16) {
-                *reinterpret_cast<uint4*>(dst + chunk * 16) = *reinterpret_cast<const uint4*>(src + chunk * 16);
-            } else if constexpr (UNIT == 4) {
-                *reinterpret_cast<uint32_t*>(dst + chunk * 4) = *reinterpret_cast<const uint32_t*>(src + chunk * 4);
-            } else {
-                *reinterpret_cast<uint16_t*>(dst + chunk * 2) = *reinterpret_cast<const uint16_t*>(src + chunk * 2);
-            }
+#pragma unroll
+            for (int k = 0; k < kScatterPasses; ++k)
+                if (dst[k]) *reinterpret_cast<unit_t*>(dst[k]) = val[k];
         }
         __syncthreads();   // the group's marks are read before the next group resets them
     }
