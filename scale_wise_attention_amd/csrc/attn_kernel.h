@@ -1237,7 +1237,8 @@ __global__ __launch_bounds__((waves_per_wg<SPARSE, QB>() * 64), ((SPARSE && QB =
 // exp(LSE_s - M), M the largest LSE_s (a split in which the row sees no key
 // has LSE_s = -inf and weight 0).  One thread per 4 output columns of a row;
 // the threads cover items [split_from, items) only, rows_per_item rows each.
-template <bool OUT_BF16>
+// NS = n_splits, so every load of a thread is issued before the first is used.
+template <bool OUT_BF16, int NS>
 __global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, int D, int rows_per_item) {
     const int cpr = D / 4;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1253,19 +1254,27 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, in
     const int b = bh / p.H, h = bh - b * p.H;
     const int64_t rr = (int64_t)bh * p.n_rows + row;
     const int64_t plane = p.part_rows;
-    float m = -INFINITY;
     const int64_t pr = rr - p.part_first;   // this row among the split items' rows
-    for (int s = 0; s < p.n_splits; ++s) m = __builtin_fmaxf(m, p.part_lse[s * plane + pr]);
+    float l[NS];
+    float4 o[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        l[s] = p.part_lse[s * plane + pr];
+        o[s] = *reinterpret_cast<const float4*>(p.part_o + (s * plane + pr) * D + 4 * c);
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) m = __builtin_fmaxf(m, l[s]);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float wsum = 0.f;
     if (m != -INFINITY) {
-        for (int s = 0; s < p.n_splits; ++s) {
-            const float w = __expf(p.part_lse[s * plane + pr] - m);
-            const float4 o = *reinterpret_cast<const float4*>(p.part_o + (s * plane + pr) * D + 4 * c);
-            acc.x += w * o.x;
-            acc.y += w * o.y;
-            acc.z += w * o.z;
-            acc.w += w * o.w;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const float w = __expf(l[s] - m);
+            acc.x += w * o[s].x;
+            acc.y += w * o[s].y;
+            acc.z += w * o[s].z;
+            acc.w += w * o[s].w;
             wsum += w;
         }
     }
@@ -1279,6 +1288,22 @@ __global__ __launch_bounds__(256) void split_merge_kernel(const AttnParams p, in
             make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
     if (p.lse && c == 0) p.lse[rr] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+}
+
+template <bool OUT_BF16>
+hipError_t launch_merge(const AttnParams& p, int D, int rows_per_item, unsigned blocks, hipStream_t s) {
+    static_assert(kMaxSplits == 8, "one instantiation per split count");
+    switch (p.n_splits) {
+    case 2: hipLaunchKernelGGL((split_merge_kernel<OUT_BF16, 2>), dim3(blocks), dim3(256), 0, s, p, D, rows_per_item); break;
+    case 3: hipLaunchKernelGGL((split_merge_kernel<OUT_BF16, 3>), dim3(blocks), dim3(256), 0, s, p, D, rows_per_item); break;
+    case 4: hipLaunchKernelGGL((split_merge_kernel<OUT_BF16, 4>), dim3(blocks), dim3(256), 0, s, p, D, rows_per_item); break;
+    case 5: hipLaunchKernelGGL((split_merge_kernel<OUT_BF16, 5>), dim3(blocks), dim3(256), 0, s, p, D, rows_per_item); break;
+    case 6: hipLaunchKernelGGL((split_merge_kernel<OUT_BF16, 6>), dim3(blocks), dim3(256), 0, s, p, D, rows_per_item); break;
+    case 7: hipLaunchKernelGGL((split_merge_kernel<OUT_BF16, 7>), dim3(blocks), dim3(256), 0, s, p, D, rows_per_item); break;
+    case 8: hipLaunchKernelGGL((split_merge_kernel<OUT_BF16, 8>), dim3(blocks), dim3(256), 0, s, p, D, rows_per_item); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 // Workgroups of one instantiation that a compute unit holds at once (1 when
@@ -1308,9 +1333,7 @@ hipError_t launch_one(const AttnParams& p, hipStream_t s) {
     if (e != hipSuccess || p.split_from == items) return e;
     constexpr int QT = rows_per_wg<SP, QB>();
     const int64_t threads = (int64_t)(items - p.split_from) * QT * (D / 4);
-    hipLaunchKernelGGL((split_merge_kernel<OB>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p, D,
-                       QT);
-    return hipGetLastError();
+    return launch_merge<OB>(p, D, QT, (unsigned)((threads + 255) / 256), s);
 }
 
 }  // namespace
