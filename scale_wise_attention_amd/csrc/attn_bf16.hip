@@ -43,8 +43,10 @@ int attn_bf16_resident_wgs(int D, bool out_bf16, bool sparse, int rows_per_tile)
 namespace {
 // Reconstruction workgroups that follow a block-sparse launch of n_attn
 // attention workgroups (cap resident at once): the slots its last round leaves
-// free, so that they run beside the attention, but at least 64 (they then
-// start as attention workgroups finish) and at most one per row group.
+// free, so that they run beside the attention, at most one per row group.
+// With fewer than 64 free slots they would mostly start as the attention
+// drains, one group after another, so the attention then runs alone and the
+// scatter launch follows it on the stream (the two write disjoint rows).
 template <int D, bool OB, int QB, bool WIDE>
 hipError_t launch_restore(AttnParams p, int64_t n_attn, int cus, hipStream_t s) {
     constexpr int NT = waves_per_wg<true, QB>() * 64;
@@ -53,9 +55,12 @@ hipError_t launch_restore(AttnParams p, int64_t n_attn, int cus, hipStream_t s) 
     const int64_t groups = (int64_t)p.rs.maps * ((n_out + p.rs_rows_per_group - 1) / p.rs_rows_per_group);
     const int64_t cap = (int64_t)cus * resident_wgs<D, OB, true, false, QB, WIDE, true>();
     const int64_t free = n_attn % cap ? cap - n_attn % cap : 0;
-    int64_t w = free > 64 ? free : 64;
-    w = w < groups ? w : groups;
-    p.rs_wgs = (int)(w > 1 ? w : 1);
+    if (free < 64) {
+        p.rs_wgs = 0;
+        const hipError_t e = launch_one<D, OB, true, false, QB, WIDE>(p, s);
+        return e != hipSuccess ? e : launch_scatter(p.rs, s);
+    }
+    p.rs_wgs = (int)(free < groups ? free : groups);
     return launch_one<D, OB, true, false, QB, WIDE, true>(p, s);
 }
 }  // namespace

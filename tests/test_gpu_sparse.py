@@ -562,6 +562,7 @@ def _restore_case(api, wl_name, seed, frac, B=None, H=None, out_dtype=torch.bflo
     ("var1024_sparse", 0.4, None, torch.bfloat16),    # 416 attention workgroups, two per compute unit
     ("var1024_sparse", 0.4, None, torch.float32),
     ("var1024_sparse", 0.4, (1, 2), torch.bfloat16),  # a few workgroups: the one-per-unit walk
+    ("var1024_sparse", 0.4, (2, 8), torch.bfloat16),  # 208 one-per-unit workgroups: too few free slots, two launches
     ("var1024_sparse", 0.05, None, torch.bfloat16),   # mostly reconstruction
     ("var256", 0.4, None, torch.bfloat16),            # head_dim 64
     ("var256", 1.0, None, torch.float32),             # every row retained: nothing from the base
