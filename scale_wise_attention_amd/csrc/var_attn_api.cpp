@@ -486,6 +486,8 @@ VAR_EXPORT var_status var_attn_block_sparse_restore(const var_schedule* sched, c
     if (desc->out_at_index != 1) return fail(VAR_ERR_RANGE, "the reconstruction call needs out_at_index = 1");
     if (desc->out_dtype != VAR_F32 && desc->out_dtype != VAR_BF16)
         return fail(VAR_ERR_UNSUPPORTED, "unknown out_dtype %d", (int)desc->out_dtype);
+    if (desc->head_dim != 64 && desc->head_dim != 128)
+        return fail(VAR_ERR_UNSUPPORTED, "bf16 input supports head_dim 64 or 128, got %d", desc->head_dim);
     if (desc->batch < 1 || desc->heads < 1 || (int64_t)desc->batch * desc->heads > (1 << 20))
         return fail(VAR_ERR_RANGE, "batch=%d heads=%d invalid", desc->batch, desc->heads);
     if (h_in < 1 || w_in < 1 || (int64_t)h_in * w_in >= kMaxTokens) return fail(VAR_ERR_RANGE, "base grid invalid");

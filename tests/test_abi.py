@@ -348,6 +348,7 @@ def test_restore_validation_errors(api):
     assert call(desc=_desc(api, out_at_index=1, q_scale_begin=11)) == E("VAR_ERR_RANGE")
     assert call(desc=_desc(api, out_at_index=0)) == E("VAR_ERR_RANGE")
     assert call(desc=_desc(api, out_at_index=1, head_dim=64, in_dtype=api.VAR_F32)) == E("VAR_ERR_UNSUPPORTED")
+    assert call(desc=_desc(api, out_at_index=1, head_dim=96)) == E("VAR_ERR_UNSUPPORTED")
     assert call(base=0) == E("VAR_ERR_NULL")
     assert call(base=FAKE + 8) == E("VAR_ERR_STRIDE")
     assert call(base_l=api.Layout(16 * 2304 * 132, 2304 * 132, 132)) == E("VAR_ERR_STRIDE")
