@@ -31,6 +31,7 @@ def test_graph_replays_match_eager():
     prev = torch.empty(2, 30, 576, 64, dtype=torch.bfloat16, device=dev)
     upd = torch.empty(2, 30, sel.numel(), 64, dtype=torch.bfloat16, device=dev)
     out = torch.empty(2, 30, 1024, 64, dtype=torch.bfloat16, device=dev)
+    out1 = torch.empty(2, 30, 1024, 64, dtype=torch.bfloat16, device=dev)   # one-launch reconstruction
 
     def run():
         api.var_attn_dense((wl.h, wl.w), qs, k, v, s, s + 1, out=dense)
@@ -38,10 +39,12 @@ def test_graph_replays_match_eager():
         api.var_build_tile_mask((wl.h, wl.w), s, s + 1, mp, q_index=sel, row_ptr=rp, col_idx=ci)
         api.var_attn_block_sparse((wl.h, wl.w), qs, k, v, s, s + 1, rp, ci, out=upd, q_index=sel)
         api.var_scatter_restore(prev, 24, 24, upd, sel, 32, 32, out=out)
+        api.var_attn_block_sparse_restore((wl.h, wl.w), qs, k, v, s, rp, ci, sel, prev, 24, 24, out=out1)
 
     run()
     torch.cuda.synchronize()
-    eager = [t.clone() for t in (dense, rp, ci[: int(rp[-1].item())], upd, out)]
+    eager = [t.clone() for t in (dense, rp, ci[: int(rp[-1].item())], upd, out, out1)]
+    assert torch.equal(out, out1), "one-launch reconstruction against attention + scatter"
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -53,12 +56,12 @@ def test_graph_replays_match_eager():
     with torch.cuda.graph(g):
         run()
     for rep in range(4):
-        for t in (dense, rp, ci, upd, out):
+        for t in (dense, rp, ci, upd, out, out1):
             t.fill_(0) if t.dtype != torch.int32 else t.fill_(-1)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = (dense, rp, ci[: int(rp[-1].item())], upd, out)
+        got = (dense, rp, ci[: int(rp[-1].item())], upd, out, out1)
         for a, b in zip(eager, got):
             assert torch.equal(a, b), f"replay {rep}"
         # eager work between replays
