@@ -303,7 +303,9 @@ var_status var_attn_block_sparse(const var_schedule* sched, const var_attn_desc*
  * row q_index[i] of the step's full grid o, and workgroups of the same
  * launch fill every other row of o from the nearest-upsampled base (source
  * (floor(y*h_in/h), floor(x*w_in/w)), the rule of var_scatter_restore), in
- * the compute-unit slots the attention leaves free.  The result equals
+ * the compute-unit slots the attention leaves free (when it leaves fewer
+ * than 64 free, the fill runs as a second launch right after the attention
+ * on the same stream).  The result equals
  * var_attn_block_sparse (out_at_index = 1) followed by var_scatter_restore
  * with upd = NULL, bit for bit.
  *  desc    bf16 input, out_at_index = 1, one step: q_scale_end =

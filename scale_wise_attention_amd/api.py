@@ -406,7 +406,8 @@ def var_attn_block_sparse(schedule, q, k, v, q_scale_begin, q_scale_end, row_ptr
 def var_attn_block_sparse_restore(schedule, q, k, v, step, row_ptr, col_idx, q_index, base, h_in, w_in, out=None,
                                   out_dtype=None, softmax_scale=0.0, return_lse=False, err_flag=None, tile_q=64,
                                   tile_k=64):
-    """Pruned block-sparse attention of one step plus its reconstruction, one launch.
+    """Pruned block-sparse attention of one step plus its reconstruction, in one launch
+    (two when the attention leaves fewer than 64 compute-unit slots free).
 
     Output row i of the attention over the queries q_index (ascending positions of
     the step's grid) goes to row q_index[i] of out [B, H, h*w, D]; every other row
